@@ -1,0 +1,279 @@
+"""CPU oracle for the DFlash batched verify forward -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import this
+package. The GPU library neither links nor calls it. ``oracle.c`` holds the arithmetic (plain C,
+double precision, rounded to the storage precisions); this file is a ctypes wrapper around it plus
+the build step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import List, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so (gcc, -O2, OpenMP)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wno-unused-function",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P, I, L64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_double
+        sig = {
+            "orc_q4_1_dequant": (None, [P, I, I, P]),
+            "orc_q4_1_matmul": (None, [P, I, I, P, I, P]),
+            "orc_bf16_matmul": (None, [P, I, I, P, I, P]),
+            "orc_rmsnorm_bf16": (None, [P, P, I, D, P]),
+            "orc_rope": (None, [P, I, L64, D, P]),
+            "orc_model_new": (P, [I, I, I, I, L64, I, D, D, I, I, P, P, I]),
+            "orc_model_free": (None, [P]),
+            "orc_set_layer": (None, [P, I] + [P] * 11),
+            "orc_set_globals": (None, [P, P, P, P, P]),
+            "orc_set_kv": (I, [P, I, P, L64]),
+            "orc_set_held": (None, [P, L64]),
+            "orc_positions_held": (L64, [P]),
+            "orc_plane": (ctypes.POINTER(ctypes.c_float), [P, I]),
+            "orc_kv_widths": (None, [P, P]),
+            "orc_plane_floats": (None, [P, P]),
+            "orc_cut_floats": (L64, [P, I, I, L64]),
+            "orc_step": (I, [P, I, P, P]),
+            "orc_verify_batch": (I, [P, P, I, P, P]),
+            "orc_commit_verify_rows": (I, [P, I]),
+            "orc_argmax": (I, [P, I]),
+            "orc_accept_greedy": (I, [P, I, I, P, P, P]),
+            "orc_snapshot_take": (P, [P]),
+            "orc_snapshot_floats": (L64, [P, I]),
+            "orc_snapshot_restore": (I, [P, P]),
+            "orc_snapshot_free": (None, [P]),
+            "orc_draft_append": (I, [P, P, I]),
+            "orc_draft_block": (I, [P, P, I, I, D, I, P, P]),
+            "orc_threads": (I, []),
+            "orc_attend": (None, [P, I, P, L64, P]),
+            "orc_layer_forward": (None, [P, I, I, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def threads() -> int:
+    return int(lib().orc_threads())
+
+
+# ---- kernels as functions -------------------------------------------------------------------
+def q4_1_dequant(img: np.ndarray, n_out: int, n_in: int) -> np.ndarray:
+    out = np.empty((n_out, n_in), dtype=np.float32)
+    lib().orc_q4_1_dequant(_p(np.ascontiguousarray(img)), n_out, n_in, _p(out))
+    return out
+
+
+def q4_1_matmul(img: np.ndarray, n_out: int, n_in: int, x_bf16: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1, n_in)
+    y = np.empty((x.shape[0], n_out), dtype=np.float32)
+    lib().orc_q4_1_matmul(_p(np.ascontiguousarray(img)), n_out, n_in, _p(x), x.shape[0], _p(y))
+    return y
+
+
+def bf16_matmul(w_bf16: np.ndarray, x_bf16: np.ndarray) -> np.ndarray:
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n_out, n_in = w.shape
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1, n_in)
+    y = np.empty((x.shape[0], n_out), dtype=np.float32)
+    lib().orc_bf16_matmul(_p(w), n_out, n_in, _p(x), x.shape[0], _p(y))
+    return y
+
+
+def rmsnorm_bf16(x: np.ndarray, g_bf16: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape[0], dtype=np.uint16)
+    lib().orc_rmsnorm_bf16(_p(x), _p(np.ascontiguousarray(g_bf16, dtype=np.uint16)), x.shape[0], eps, _p(out))
+    return out
+
+
+def rope(v: np.ndarray, p: int, base: float = 1e6) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty_like(v)
+    lib().orc_rope(_p(v), v.shape[0], p, base, _p(out))
+    return out
+
+
+def argmax(v: np.ndarray) -> int:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    return int(lib().orc_argmax(_p(v), v.shape[0]))
+
+
+def accept_greedy(logits_all: np.ndarray, tokens: np.ndarray):
+    """Returns (a, emitted tokens [a+1])."""
+    lg = np.ascontiguousarray(logits_all, dtype=np.float32)
+    k, V = lg.shape
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = np.zeros(k, dtype=np.int32)
+    a = ctypes.c_int(0)
+    lib().orc_accept_greedy(_p(lg), k, V, _p(t), _p(out), ctypes.byref(a))
+    return a.value, out[: a.value + 1].copy()
+
+
+def cut_floats(per, plane: int, positions: int) -> int:
+    per = np.ascontiguousarray(per, dtype=np.int64)
+    return int(lib().orc_cut_floats(_p(per), len(per), plane, positions))
+
+
+# ---- model ----------------------------------------------------------------------------------
+class Model:
+    """Oracle model over caller-owned host arrays (kept alive here)."""
+
+    def __init__(self, m, weights: dict):
+        self.m = m
+        fields = np.array([[L.attn, L.n_kv_heads, L.head_dim, L.window, L.ffn, L.kv_owner] for L in m.layers],
+                          dtype=np.int32)
+        taps = np.array(list(m.tap_layers) or [0], dtype=np.int32)
+        self._keep = [fields, taps, weights]
+        self.h = lib().orc_model_new(m.n_layers, m.hidden, m.n_q_heads, m.vocab, m.max_ctx, m.qk_norm,
+                                     m.rope_base, m.rms_eps, m.block_causal, m.draft_window,
+                                     _p(fields), _p(taps), len(m.tap_layers))
+        for l, d in enumerate(weights["layers"]):
+            g = lambda k: _p(d[k]) if k in d else None
+            lib().orc_set_layer(self.h, l, g("q"), g("k"), g("v"), g("o"), g("gate"), g("up"), g("down"),
+                                g("attn_norm"), g("mlp_norm"), g("q_norm"), g("k_norm"))
+        lib().orc_set_globals(self.h, _p(weights.get("embed")), _p(weights.get("final_norm")),
+                              _p(weights.get("fc")), _p(weights.get("hidden_norm")))
+
+    def __del__(self):
+        try:
+            if getattr(self, "h", None):
+                lib().orc_model_free(self.h)
+                self.h = None
+        except Exception:
+            pass
+
+    # state
+    def set_kv(self, kv_list, positions: int):
+        for l, kv in enumerate(kv_list):
+            if kv is None:
+                continue
+            kv = np.ascontiguousarray(kv[:positions], dtype=np.float32)
+            assert lib().orc_set_kv(self.h, l, _p(kv), positions) == 0
+        lib().orc_set_held(self.h, positions)
+
+    def held(self) -> int:
+        return int(lib().orc_positions_held(self.h))
+
+    def kv_widths(self) -> np.ndarray:
+        out = np.zeros(self.m.n_layers, dtype=np.int64)
+        lib().orc_kv_widths(self.h, _p(out))
+        return out
+
+    def plane_floats(self) -> np.ndarray:
+        out = np.zeros(self.m.n_layers, dtype=np.int64)
+        lib().orc_plane_floats(self.h, _p(out))
+        return out
+
+    def plane(self, l: int, positions: int) -> np.ndarray:
+        w = self.m.kv_width(l)
+        ptr = lib().orc_plane(self.h, l)
+        return np.ctypeslib.as_array(ptr, shape=(self.m.max_ctx, 2, w))[:positions].copy()
+
+    # forward
+    def step(self, token: int, with_taps: bool = False):
+        lg = np.empty(self.m.vocab, dtype=np.float32)
+        taps = np.empty((len(self.m.tap_layers), self.m.hidden), dtype=np.uint16) if with_taps else None
+        rc = lib().orc_step(self.h, int(token), _p(lg), _p(taps))
+        if rc:
+            raise RuntimeError(f"oracle step: status {rc}")
+        return (lg, taps) if with_taps else lg
+
+    def verify_batch(self, tokens, with_taps: bool = False):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        k = t.shape[0]
+        lg = np.empty((k, self.m.vocab), dtype=np.float32)
+        taps = np.empty((k, len(self.m.tap_layers), self.m.hidden), dtype=np.uint16) if with_taps else None
+        rc = lib().orc_verify_batch(self.h, _p(t), k, _p(lg), _p(taps))
+        if rc:
+            raise RuntimeError(f"oracle verify: status {rc}")
+        return (lg, taps) if with_taps else lg
+
+    def commit_verify_rows(self, n: int) -> int:
+        return int(lib().orc_commit_verify_rows(self.h, n))
+
+    def snapshot(self):
+        return Snapshot(lib().orc_snapshot_take(self.h), self.m.n_layers)
+
+    def restore(self, snap) -> int:
+        return int(lib().orc_snapshot_restore(self.h, snap.h))
+
+    def attend(self, l: int, q: np.ndarray, p: int) -> np.ndarray:
+        """Attention output of one row (before the bf16 rounding), q [Hq*hd] fp32."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        out = np.empty(q.shape[0], dtype=np.float64)
+        lib().orc_attend(self.h, l, _p(q), p, _p(out))
+        return out
+
+    def layer_forward(self, l: int, x: np.ndarray, pos) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, self.m.hidden)
+        pos = np.ascontiguousarray(pos, dtype=np.int64)
+        out = np.empty_like(x)
+        lib().orc_layer_forward(self.h, l, x.shape[0], _p(x), _p(pos), _p(out))
+        return out
+
+    # draft
+    def draft_append(self, taps: np.ndarray):
+        t = np.ascontiguousarray(taps, dtype=np.uint16)
+        rc = lib().orc_draft_append(self.h, _p(t), t.shape[0])
+        if rc:
+            raise RuntimeError(f"oracle draft append: status {rc}")
+
+    def draft_block(self, target: "Model", block: int, last_token: int, embedding_scale: float,
+                    mask_token: int, with_logits: bool = False):
+        props = np.zeros(block - 1, dtype=np.int32)
+        lg = np.empty((block - 1, target.m.vocab), dtype=np.float32) if with_logits else None
+        rc = lib().orc_draft_block(self.h, target.h, block, int(last_token), float(embedding_scale),
+                                   int(mask_token), _p(props), _p(lg))
+        if rc:
+            raise RuntimeError(f"oracle draft block: status {rc}")
+        return (props, lg) if with_logits else props
+
+
+class Snapshot:
+    def __init__(self, h, n_layers):
+        self.h = h
+        self.n_layers = n_layers
+
+    def floats(self) -> List[int]:
+        return [int(lib().orc_snapshot_floats(self.h, l)) for l in range(self.n_layers)]
+
+    def __del__(self):
+        try:
+            if getattr(self, "h", None):
+                lib().orc_snapshot_free(self.h)
+                self.h = None
+        except Exception:
+            pass
