@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched verify forward (DFlash block speculative decoding) on one MI355X.
+
+Workload (the target-shaped verify): 42 decoder layers, hidden 2560, 8 query heads of 256; sliding
+layers KV row 2 x 256 floats/position with window 512, every 6th layer full with 2 x 512; layers
+24..41 KV-shared; FFN 10240 (20480 on shared layers); Q4_1 weights; bf16 tied head of 262144
+rows; 1024 cached positions; k = 8 verified rows. All inputs are seeded synthetic draws (seed 0).
+
+A step = one verify pass over the k rows (embed, 42 layers, final norm, head, logits_all and taps),
+the greedy accept (argmax + longest prefix) and commit_verify_rows(0), which rolls the appended rows
+back so every step verifies at the same 1024 cached positions.
+
+Prints one JSON line: verified rows/s, the Q4_1 weight stream in GB/s and as a fraction of the
+8 TB/s HBM peak, the roofline of the dominant kernel (timed with HIP events on the model's stream),
+the k = 1 step for comparison, and the CPU oracle timed on this host's cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified rows/s and Q4_1 weight-stream HBM GB/s (% of peak), k=8 verify pass"
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_weights(m, seed: int, threads: int):
+    from block_verify_forward_amd import synth
+    out = {"layers": [None] * m.n_layers}
+
+    def layer(l):
+        d = {}
+        for key, (n_out, n_in) in synth.layer_matrix_shapes(m, l).items():
+            d[key] = synth.q4_1_image(seed, f"{m.name}.L{l}.{key}", n_out, n_in)
+        hd = m.layers[l].head_dim
+        d["attn_norm"] = synth.bf16_uniform(seed, f"{m.name}.L{l}.attn_norm", (m.hidden,), 0.5, 1.5)
+        d["mlp_norm"] = synth.bf16_uniform(seed, f"{m.name}.L{l}.mlp_norm", (m.hidden,), 0.5, 1.5)
+        d["q_norm"] = synth.bf16_uniform(seed, f"{m.name}.L{l}.q_norm", (hd,), 0.5, 1.5)
+        d["k_norm"] = synth.bf16_uniform(seed, f"{m.name}.L{l}.k_norm", (hd,), 0.5, 1.5)
+        out["layers"][l] = d
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(layer, range(m.n_layers)))
+    out["embed"] = synth.embedding_table(seed, m, threads)
+    out["final_norm"] = synth.bf16_uniform(seed, f"{m.name}.final_norm", (m.hidden,), 0.5, 1.5)
+    return out
+
+
+def cpu_baseline(m, w, kv, ctx, toks, budget_s: float):
+    """The CPU oracle, as it stands, on this host: one k-row verify of the same workload. If one
+    full pass would take longer than the budget, a prefix of the layers is timed and the pass time
+    is scaled by Q4_1 bytes (the sample is named in the result)."""
+    import oracle
+    from block_verify_forward_amd import synth
+    k = len(toks)
+    threads = oracle.threads()
+    # time a 1-layer model (plus head) to estimate the full pass
+    import dataclasses
+    m1 = dataclasses.replace(m, n_layers=1, layers=m.layers[:1], tap_layers=())
+    w1 = {"layers": w["layers"][:1], "embed": w["embed"], "final_norm": w["final_norm"]}
+    o1 = oracle.Model(m1, w1)
+    o1.set_kv(kv[:1], ctx)
+    t = time.perf_counter()
+    o1.verify_batch(toks)
+    t1 = time.perf_counter() - t
+    full_est = t1 * synth.q4_1_bytes(m) / synth.q4_1_bytes(m1)
+    if full_est <= budget_s:
+        o = oracle.Model(m, w)
+        o.set_kv(kv, ctx)
+        t = time.perf_counter()
+        o.verify_batch(toks)
+        dt = time.perf_counter() - t
+        sample = f"one full k={k} verify pass of the same workload ({m.n_layers} layers + head)"
+    else:
+        n_s = max(1, min(24, int(budget_s / t1)))
+        ms = dataclasses.replace(m, n_layers=n_s, layers=m.layers[:n_s], tap_layers=())
+        ws = {"layers": w["layers"][:n_s], "embed": w["embed"], "final_norm": w["final_norm"]}
+        o = oracle.Model(ms, ws)
+        o.set_kv(kv[:n_s], ctx)
+        t = time.perf_counter()
+        o.verify_batch(toks)
+        ds = time.perf_counter() - t
+        dt = ds * synth.q4_1_bytes(m) / synth.q4_1_bytes(ms)
+        sample = (f"first {n_s} layers + head of the workload, k={k}, timed {ds:.1f} s; pass time scaled by "
+                  f"Q4_1 bytes to {m.n_layers} layers")
+    return {"value": round(k / dt, 4), "unit": "verified rows/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds_per_pass": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--k", type=int, default=8)
+    ap.add_argument("--ctx", type=int, default=1024)
+    ap.add_argument("--layers", type=int, default=42, help="decoder layers (42 = the workload)")
+    ap.add_argument("--vocab", type=int, default=262144)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget-s", type=float, default=25.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="direct launches instead of the captured pass")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus}: this benchmark runs the verify pass on one GPU only; "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_verify_forward_amd import bvf, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    threads = min(16, os.cpu_count() or 8)
+    m = synth.target_model(max_ctx=args.ctx + 64, n_layers=args.layers, vocab=args.vocab)
+    t0 = time.time()
+    w = build_weights(m, args.seed, threads)
+    kv = synth.make_kv(m, args.ctx, args.seed)
+    log(f"synthetic weights and context drawn in {time.time() - t0:.1f} s")
+    t0 = time.time()
+    g = bvf.Model(m)
+    g.load_weights(w)
+    g.set_context(kv, args.ctx)
+    if not args.no_graph:
+        g.set_graph_mode(True)
+    torch.cuda.synchronize()
+    log(f"loaded and packed on the GPU in {time.time() - t0:.1f} s; arena {g.arena.numel() / 2**30:.2f} GiB")
+
+    k, V, H, T = args.k, m.vocab, m.hidden, len(m.tap_layers)
+    toks_h = synth.tokens(args.seed, "bench.tokens", k, V)
+    toks = torch.from_numpy(toks_h).cuda()
+    logits = torch.empty((k, V), dtype=torch.float32, device="cuda")
+    taps = torch.empty((k, T, H), dtype=torch.int16, device="cuda")
+    out_tok = torch.zeros(k, dtype=torch.int32, device="cuda")
+    n_acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step(tk, lg, tp):
+        g.verify_batch(tk, lg, tp)
+        g.accept_greedy(lg, tk, out_tok, n_acc)
+        g.commit_verify_rows(0)
+
+    def timed(nsteps, tk, lg, tp):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(nsteps):
+            step(tk, lg, tp)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / nsteps
+
+    for _ in range(args.warmup):
+        step(toks, logits, taps)
+    ms = timed(args.steps, toks, logits, taps)
+    log(f"k={k}: {ms:.3f} ms per step")
+    assert g.positions_held() == args.ctx
+
+    # k = 1 step (same kernels, one row)
+    toks1 = toks[:1].contiguous()
+    lg1 = torch.empty((1, V), dtype=torch.float32, device="cuda")
+    tp1 = torch.empty((1, T, H), dtype=torch.int16, device="cuda")
+    for _ in range(2):
+        step(toks1, lg1, tp1)
+    ms1 = timed(max(3, args.steps // 2), toks1, lg1, tp1)
+    log(f"k=1: {ms1:.3f} ms per step")
+
+    # per-class GEMM timing with HIP events on the model's stream (the launches of the pass)
+    cls_ms, cls_bytes = g.time_gemms(k, 3)
+    cls_ms = [float(v) for v in cls_ms]
+    cls_bytes = [int(v) for v in cls_bytes]
+    names = ["qkv", "o", "gate_up", "down", "head"]
+    per_pass = [m.n_layers] * 4 + [1]
+    cls_total_ms = [cls_ms[i] * per_pass[i] for i in range(5)]
+    q4_ms = sum(cls_total_ms[:4])
+    q4_bytes, head_bytes = g.pass_bytes()
+    q4_gbs = q4_bytes / (q4_ms * 1e-3) / 1e9
+    dom = int(np.argmax(cls_total_ms[:4]))
+    dom_gbs = float(cls_bytes[dom] / (cls_ms[dom] * 1e-3) / 1e9)
+    log("per-class GEMM ms/launch: " + ", ".join(f"{names[i]} {cls_ms[i]:.4f} ({cls_bytes[i] / cls_ms[i] / 1e6:.0f} GB/s)"
+                                                  for i in range(5)))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(m, w, kv, args.ctx, toks_h, args.cpu_budget_s)
+        log(f"cpu baseline in {time.time() - t0:.1f} s: {cpu}")
+
+    rows_s = k / (ms * 1e-3)
+    res = {
+        "metric": METRIC,
+        "value": round(rows_s, 1),
+        "unit": "verified rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_1 weights, bf16 x bf16 -> fp32 MFMA",
+        "data": "synthetic (seeded draws, seed 0)",
+        "config": {"workload": f"target-shaped verify: {m.n_layers} layers, hidden {H}, Q4_1, head {V}x{H} bf16, "
+                               f"{args.ctx} cached positions, k={k}",
+                   "k": k, "cached_positions": args.ctx, "layers": m.n_layers, "vocab": V},
+        "q4_1_weight_stream_gbs": round(q4_gbs, 1),
+        "q4_1_weight_stream_frac_of_peak": round(q4_gbs / HBM_PEAK_GBS, 4),
+        "q4_1_bytes_per_pass": q4_bytes,
+        "head_bytes_per_pass": head_bytes,
+        "pass_gbs_all_weights": round((q4_bytes + head_bytes) / (ms * 1e-3) / 1e9, 1),
+        "k1_ms_per_step": round(ms1, 4),
+        "k8_over_k1": round(ms / ms1, 4),
+        "gemm_ms_per_launch": {names[i]: round(float(cls_ms[i]), 5) for i in range(5)},
+        "gemm_gbs": {names[i]: round(float(cls_bytes[i] / (cls_ms[i] * 1e-3) / 1e9), 1) for i in range(5)},
+        "roofline": {"bound": "hbm", "kernel": f"Q4_1 GEMM, {names[dom]} class", "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,921 @@
+// C ABI of the batched verify forward (include/bvf.h): descriptor checks, the device arena layout,
+// weight loading (Q4_1 packed once at load, [PR2236] section 1), the per-layer KV-plane state
+// ([PR2303] "What changes" item 1) and the launch sequence of a verify pass, the accept, and the
+// DFlash draft block. Every entry point validates before it enqueues anything.
+#include "bvf.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "bvf_impl.hpp"
+
+using namespace bvf;
+
+namespace {
+
+thread_local std::string g_err;
+
+bvf_status fail(bvf_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+bvf_status ok() {
+    g_err.clear();
+    return BVF_OK;
+}
+
+#define HIP_TRY(expr)                                                                        \
+    do {                                                                                     \
+        hipError_t e_ = (expr);                                                              \
+        if (e_ != hipSuccess) return fail(BVF_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr size_t kPartialFloats = (size_t)16 << 20;  // split-K scratch (64 MiB)
+constexpr int kCounters = 16384;
+
+struct Mat {
+    WMat w;          // packed image (codes + sm), or bf16 matrix
+    int n_out = 0;   // columns of the packed image (fused)
+};
+
+struct Layer {
+    bvf_layer_desc d{};
+    int w = 0;             // KV width (own or owner's)
+    int qd = 0, kvd = 0;   // q width, own k/v width (0 on a shared layer)
+    Mat qkv, o, gu, down;
+    uint16_t *attn_norm = nullptr, *mlp_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
+    float* plane = nullptr;   // own plane [max_ctx][2][w]
+    const float2* rope = nullptr;
+    unsigned loaded = 0;      // bit i: matrix i; bits 8..11: norms
+};
+
+}  // namespace
+
+struct bvf_model {
+    bvf_model_desc d{};
+    std::vector<bvf_layer_desc> ld;
+    std::vector<int32_t> taps;
+    std::vector<Layer> L;
+    hipStream_t st = nullptr;
+    int device = 0;
+    uint8_t* arena = nullptr;
+    size_t arena_bytes = 0;
+    uint16_t *embed = nullptr, *final_norm = nullptr, *fc = nullptr, *hidden_norm = nullptr;
+    unsigned loaded = 0;     // bit t: bf16 tensor t (model-wide)
+    // scratch
+    float* x = nullptr;
+    uint16_t* act = nullptr;
+    float* qkv = nullptr;
+    float* qbuf = nullptr;
+    uint16_t* obuf = nullptr;
+    uint16_t* mbuf = nullptr;
+    float* fcout = nullptr;
+    float* partial = nullptr;
+    int* counters = nullptr;
+    float* attn_part = nullptr;
+    size_t attn_part_floats = 0;
+    float* ss_x = nullptr;     // [16][hidden / 16] per-tile sums of squares of the residual rows
+    float* ss_qkv = nullptr;   // [16][nqkv_max / 16] per-tile sums of squares of q | k | v
+    float* am_val = nullptr;
+    int* am_idx = nullptr;
+    int am_blocks = 0;
+    float* logits_scratch = nullptr;
+    float* logits_tmp = nullptr;     // verify model: head output of the GEMM timing entry
+    uint8_t* staging = nullptr;
+    size_t staging_bytes = 0;
+    std::vector<std::pair<int, float2*>> rope_tables;
+    int hd_max = 0, qd_max = 0, nqkv_max = 0, ffn_max = 0;
+    // state
+    int64_t held = 0;
+    int32_t pending = -1;
+    // graph replay of the verify pass: captured on cap_st, launched on st; valid for one
+    // (positions held, k, tokens, logits, taps) key
+    int use_graph = 0;
+    hipStream_t cap_st = nullptr;
+    hipGraphExec_t gexec = nullptr;
+    int64_t g_P = -1;
+    int32_t g_k = 0;
+    const void *g_tok = nullptr, *g_lg = nullptr, *g_taps = nullptr;
+    ~bvf_model() {
+        if (gexec) (void)hipGraphExecDestroy(gexec);
+        if (cap_st) (void)hipStreamDestroy(cap_st);
+    }
+};
+
+struct bvf_snapshot {
+    int n_layers = 0;
+    int64_t held = 0;
+    int device = 0;
+    std::vector<int64_t> per;
+    std::vector<int> shared;
+    std::vector<float*> data;
+};
+
+namespace {
+
+bool is_draft(const bvf_model_desc& d) { return d.block_causal == 0; }
+
+bvf_status check_desc(const bvf_model_desc* d) {
+    if (!d) return fail(BVF_E_INVALID, "descriptor is NULL");
+    if (d->n_layers < 1) return fail(BVF_E_INVALID, "n_layers %d < 1", d->n_layers);
+    if (d->hidden < 128 || d->hidden % 128) return fail(BVF_E_INVALID, "hidden %d is not a positive multiple of 128", d->hidden);
+    if (d->n_q_heads < 1) return fail(BVF_E_INVALID, "n_q_heads %d < 1", d->n_q_heads);
+    if (d->max_ctx < 1 || d->max_ctx > (1 << 24)) return fail(BVF_E_INVALID, "max_ctx %d out of range", d->max_ctx);
+    if (!d->layers) return fail(BVF_E_INVALID, "layers is NULL");
+    if (d->block_causal != 0 && d->block_causal != 1) return fail(BVF_E_INVALID, "block_causal must be 0 or 1");
+    if (d->rms_eps < 0.f || !(d->rope_base > 0.f)) return fail(BVF_E_INVALID, "rms_eps < 0 or rope_base <= 0");
+    if (d->vocab < 0 || d->vocab % 16) return fail(BVF_E_INVALID, "vocab %d must be a non-negative multiple of 16", d->vocab);
+    if (!is_draft(*d) && d->vocab < 16) return fail(BVF_E_INVALID, "a verify model needs vocab >= 16");
+    if (d->n_taps < 0 || d->n_taps > 64) return fail(BVF_E_INVALID, "n_taps %d out of range", d->n_taps);
+    if (d->n_taps > 0 && !d->tap_layers && !is_draft(*d)) return fail(BVF_E_INVALID, "tap_layers is NULL");
+    if (is_draft(*d) && d->n_taps < 1) return fail(BVF_E_INVALID, "a draft needs n_taps >= 1 (fc input rows)");
+    if (d->draft_window < 0) return fail(BVF_E_INVALID, "draft_window < 0");
+    if (!is_draft(*d))
+        for (int t = 0; t < d->n_taps; ++t)
+            if (d->tap_layers[t] < 0 || d->tap_layers[t] >= d->n_layers)
+                return fail(BVF_E_INVALID, "tap layer %d does not fit a %d-layer model", d->tap_layers[t], d->n_layers);
+    for (int l = 0; l < d->n_layers; ++l) {
+        const bvf_layer_desc& L = d->layers[l];
+        if (L.attn != BVF_ATTN_SLIDING && L.attn != BVF_ATTN_FULL) return fail(BVF_E_INVALID, "layer %d: attn %d", l, L.attn);
+        if (L.head_dim != 64 && L.head_dim != 128 && L.head_dim != 256)
+            return fail(BVF_E_INVALID, "layer %d: head_dim %d not in {64, 128, 256}", l, L.head_dim);
+        if (L.n_kv_heads < 1 || d->n_q_heads % L.n_kv_heads)
+            return fail(BVF_E_INVALID, "layer %d: n_kv_heads %d does not divide n_q_heads %d", l, L.n_kv_heads, d->n_q_heads);
+        if ((d->n_q_heads * L.head_dim) % 128) return fail(BVF_E_INVALID, "layer %d: n_q_heads * head_dim not a multiple of 128", l);
+        if (L.window < 0) return fail(BVF_E_INVALID, "layer %d: window < 0", l);
+        if (L.ffn < 128 || L.ffn % 128) return fail(BVF_E_INVALID, "layer %d: ffn %d not a positive multiple of 128", l, L.ffn);
+        if (L.kv_owner >= 0) {
+            if (is_draft(*d)) return fail(BVF_E_INVALID, "layer %d: a draft layer cannot share KV", l);
+            if (L.kv_owner >= l) return fail(BVF_E_INVALID, "layer %d: owner %d is not an earlier layer", l, L.kv_owner);
+            const bvf_layer_desc& O = d->layers[L.kv_owner];
+            if (O.kv_owner >= 0) return fail(BVF_E_INVALID, "layer %d: owner %d is itself shared", l, L.kv_owner);
+            if (O.attn != L.attn || O.n_kv_heads != L.n_kv_heads || O.head_dim != L.head_dim)
+                return fail(BVF_E_INVALID, "layer %d: owner %d has another attention type or geometry", l, L.kv_owner);
+        } else if (L.kv_owner != -1) {
+            return fail(BVF_E_INVALID, "layer %d: kv_owner %d", l, L.kv_owner);
+        }
+    }
+    return BVF_OK;
+}
+
+// Lays the model out in the arena (base == nullptr: sizes only). Returns the bytes needed.
+size_t layout(bvf_model* m, uint8_t* base) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> uint8_t* {
+        off = (off + kAlign - 1) / kAlign * kAlign;
+        uint8_t* p = base ? base + off : nullptr;
+        off += bytes;
+        return p;
+    };
+    const bvf_model_desc& d = m->d;
+    const int H = d.hidden;
+    auto mat = [&](Mat& M, int n_out, int K) {
+        M.n_out = n_out;
+        M.w.n_tiles = n_out / kTile;
+        M.w.G = K / kSuper;
+        M.w.K = K;
+        M.w.codes = take((size_t)M.w.n_tiles * M.w.G * 1024);
+        M.w.sm = take((size_t)M.w.n_tiles * M.w.G * 256);
+    };
+    m->hd_max = m->qd_max = m->nqkv_max = m->ffn_max = 0;
+    size_t staging = 0;
+    m->L.assign(d.n_layers, Layer{});
+    for (int l = 0; l < d.n_layers; ++l) {
+        Layer& L = m->L[l];
+        L.d = m->ld[l];
+        const int hd = L.d.head_dim;
+        L.qd = d.n_q_heads * hd;
+        const bool own = L.d.kv_owner < 0;
+        L.kvd = own ? L.d.n_kv_heads * hd : 0;
+        L.w = m->ld[own ? l : L.d.kv_owner].n_kv_heads * m->ld[own ? l : L.d.kv_owner].head_dim;
+        mat(L.qkv, L.qd + 2 * L.kvd, H);
+        mat(L.o, H, L.qd);
+        mat(L.gu, 2 * L.d.ffn, H);
+        mat(L.down, H, L.d.ffn);
+        L.attn_norm = (uint16_t*)take((size_t)H * 2);
+        L.mlp_norm = (uint16_t*)take((size_t)H * 2);
+        L.q_norm = (uint16_t*)take((size_t)hd * 2);
+        L.k_norm = (uint16_t*)take((size_t)hd * 2);
+        L.plane = own ? (float*)take((size_t)d.max_ctx * 2 * L.w * 4) : nullptr;
+        m->hd_max = std::max(m->hd_max, hd);
+        m->qd_max = std::max(m->qd_max, L.qd);
+        m->nqkv_max = std::max(m->nqkv_max, L.qd + 2 * L.kvd);
+        m->ffn_max = std::max(m->ffn_max, L.d.ffn);
+        // largest canonical image one load call brings in (Q, K, V, O, GATE, UP, DOWN separately)
+        for (size_t elems : {(size_t)L.qd * H, (size_t)L.kvd * H, (size_t)H * L.qd, (size_t)L.d.ffn * H})
+            staging = std::max(staging, elems / 32 * 20);
+    }
+    m->embed = d.vocab > 0 && !is_draft(d) ? (uint16_t*)take((size_t)d.vocab * H * 2) : nullptr;
+    m->final_norm = (uint16_t*)take((size_t)H * 2);
+    if (is_draft(d)) {
+        m->fc = (uint16_t*)take((size_t)H * d.n_taps * H * 2);
+        m->hidden_norm = (uint16_t*)take((size_t)H * 2);
+    }
+    // RoPE tables, one per distinct head_dim
+    m->rope_tables.clear();
+    for (int l = 0; l < d.n_layers; ++l) {
+        const int hd = m->L[l].d.head_dim;
+        size_t i = 0;
+        while (i < m->rope_tables.size() && m->rope_tables[i].first != hd) ++i;
+        if (i == m->rope_tables.size())
+            m->rope_tables.push_back({hd, (float2*)take((size_t)d.max_ctx * (hd / 2) * sizeof(float2))});
+        m->L[l].rope = m->rope_tables[i].second;
+    }
+    m->x = (float*)take((size_t)kMaxRows * H * 4);
+    m->act = (uint16_t*)take((size_t)kMaxRows * H * 2);
+    m->qkv = (float*)take((size_t)kMaxRows * m->nqkv_max * 4);
+    m->qbuf = (float*)take((size_t)kMaxRows * m->qd_max * 4);
+    m->obuf = (uint16_t*)take((size_t)kMaxRows * m->qd_max * 2);
+    m->mbuf = (uint16_t*)take((size_t)kMaxRows * m->ffn_max * 2);
+    m->fcout = (float*)take((size_t)kMaxRows * H * 4);
+    m->partial = (float*)take(kPartialFloats * 4);
+    m->counters = (int*)take((size_t)kCounters * 4);
+    // attention partials: at most max(384, Hq * (max_ctx / 4096 + 2)) workgroups of 16 rows
+    m->attn_part_floats = (size_t)std::max(384, d.n_q_heads * (d.max_ctx / 4096 + 2)) * 16 * (m->hd_max + 2);
+    m->attn_part = (float*)take(m->attn_part_floats * 4);
+    m->ss_x = (float*)take((size_t)kMaxRows * (H / kTile) * 4);
+    m->ss_qkv = (float*)take((size_t)kMaxRows * (m->nqkv_max / kTile) * 4);
+    const int V = d.vocab;
+    m->am_blocks = V > 0 ? argmax_blocks(V) : 1;
+    m->am_val = (float*)take((size_t)kMaxRows * m->am_blocks * 4);
+    m->am_idx = (int*)take((size_t)kMaxRows * m->am_blocks * 4);
+    m->logits_scratch = is_draft(d) && V > 0 ? (float*)take((size_t)kMaxRows * V * 4) : nullptr;
+    m->logits_tmp = !is_draft(d) ? (float*)take((size_t)kMaxRows * V * 4) : nullptr;
+    m->staging_bytes = staging;
+    m->staging = take(staging);
+    return (off + kAlign - 1) / kAlign * kAlign;
+}
+
+void copy_desc(bvf_model* m, const bvf_model_desc* d) {
+    m->d = *d;
+    m->ld.assign(d->layers, d->layers + d->n_layers);
+    m->taps.assign(d->tap_layers ? d->tap_layers : nullptr, d->tap_layers ? d->tap_layers + d->n_taps : nullptr);
+    if (is_draft(*d)) m->taps.clear();
+    m->d.layers = m->ld.data();
+    m->d.tap_layers = m->taps.empty() ? nullptr : m->taps.data();
+}
+
+// Which part of which packed image a matrix id names.
+struct Run {
+    const Mat* mat;
+    int tile0, stride, n_out, gu_mode, col0;
+};
+
+bvf_status matrix_run(const bvf_model* m, int layer, int matrix, Run& r) {
+    if (layer < 0 || layer >= m->d.n_layers) return fail(BVF_E_INVALID, "layer %d out of range", layer);
+    const Layer& L = m->L[layer];
+    switch (matrix) {
+        case BVF_Q: r = {&L.qkv, 0, 1, L.qd, 0, 0}; break;
+        case BVF_K:
+        case BVF_V:
+            if (L.kvd == 0) return fail(BVF_E_INVALID, "layer %d is KV-shared: it has no K/V projection", layer);
+            r = {&L.qkv, (L.qd + (matrix == BVF_V ? L.kvd : 0)) / kTile, 1, L.kvd, 0, L.qd + (matrix == BVF_V ? L.kvd : 0)};
+            break;
+        case BVF_O: r = {&L.o, 0, 1, m->d.hidden, 0, 0}; break;
+        case BVF_GATE: r = {&L.gu, 0, 1, L.d.ffn, 1, 0}; break;
+        case BVF_UP: r = {&L.gu, 0, 1, L.d.ffn, 2, 0}; break;
+        case BVF_DOWN: r = {&L.down, 0, 1, m->d.hidden, 0, 0}; break;
+        default: return fail(BVF_E_INVALID, "matrix id %d", matrix);
+    }
+    return BVF_OK;
+}
+
+unsigned layer_needs(const bvf_model* m, int l) {
+    const Layer& L = m->L[l];
+    unsigned need = (1u << BVF_Q) | (1u << BVF_O) | (1u << BVF_GATE) | (1u << BVF_UP) | (1u << BVF_DOWN);
+    if (L.kvd) need |= (1u << BVF_K) | (1u << BVF_V);
+    need |= (1u << (8 + 0)) | (1u << (8 + 1));          // attn_norm, mlp_norm
+    if (m->d.qk_norm) need |= (1u << (8 + 2)) | (1u << (8 + 3));
+    return need;
+}
+
+bvf_status check_loaded(const bvf_model* m) {
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        const unsigned need = layer_needs(m, l);
+        if ((m->L[l].loaded & need) != need) return fail(BVF_E_STATE, "layer %d: weights not all loaded", l);
+    }
+    unsigned need = 1u << BVF_FINAL_NORM;
+    if (!is_draft(m->d)) need |= 1u << BVF_EMBED;
+    else need |= (1u << BVF_FC) | (1u << BVF_HIDDEN_NORM);
+    if ((m->loaded & need) != need) return fail(BVF_E_STATE, "model-wide weights not all loaded");
+    return BVF_OK;
+}
+
+GemmLaunch gemm_for(const bvf_model* m, const Mat& mat, int epi) {
+    GemmLaunch g;
+    g.w = mat.w;
+    g.fmt = W_Q4_1;
+    g.epi = epi;
+    g.tile0 = 0;
+    g.tile_stride = 1;
+    g.n_run_tiles = mat.w.n_tiles;
+    g.partial = m->partial;
+    g.partial_floats = kPartialFloats;
+    g.counters = m->counters;
+    g.n_counters = kCounters;
+    return g;
+}
+
+// Head: logits[r] = E . a[r] over the tied bf16 table [V][H]; a is either the bf16 rows A or, if
+// xsrc is given, bf16(rmsnorm(xsrc rows) * gain) formed in the GEMM's staging (sums of squares of
+// xsrc in the scratch owner's ss_x).
+hipError_t launch_head(const bvf_model* target, const uint16_t* A, int rows, float* logits, hipStream_t st,
+                       const bvf_model* scratch_owner, const float* xsrc = nullptr, const uint16_t* gain = nullptr) {
+    GemmLaunch g;
+    g.w.codes = (const uint8_t*)target->embed;
+    g.w.n_tiles = target->d.vocab / kTile;
+    g.w.G = target->d.hidden / kSuper;
+    g.w.K = target->d.hidden;
+    g.fmt = W_BF16;
+    g.epi = EPI_STORE;
+    g.n_run_tiles = g.w.n_tiles;
+    g.A = A;
+    g.lda = target->d.hidden;
+    g.M = rows;
+    g.y = logits;
+    g.ldy = target->d.vocab;
+    g.partial = scratch_owner->partial;
+    g.partial_floats = kPartialFloats;
+    g.counters = scratch_owner->counters;
+    g.n_counters = kCounters;
+    if (xsrc) {
+        g.xsrc = xsrc; g.ldx = target->d.hidden; g.ss_in = scratch_owner->ss_x; g.n_ss = target->d.hidden / kTile;
+        g.gain = gain; g.eps = scratch_owner->d.rms_eps;
+    }
+    return launch_gemm(g, st);
+}
+
+// Attention arguments of a layer (the fused norm/rope/append/attention kernel).
+Attn attn_for(const bvf_model* m, const Layer& L, int rows) {
+    Attn at;
+    at.qkv = m->qkv; at.ss = m->ss_qkv; at.ldq = L.qkv.n_out;
+    at.q_norm = L.q_norm; at.k_norm = L.k_norm; at.qk_norm = m->d.qk_norm; at.eps = m->d.rms_eps;
+    at.rope = L.rope; at.w = L.w;
+    at.M = rows; at.Hq = m->d.n_q_heads; at.nkv = L.d.n_kv_heads; at.hd = L.d.head_dim;
+    at.out = m->obuf; at.part = m->attn_part; at.part_floats = m->attn_part_floats;
+    at.counters = m->counters; at.n_counters = kCounters;
+    return at;
+}
+
+// One verify layer over rows x [k][H] at positions P..P+k-1 (layer-major batched order, [PR2303]
+// "What changes"): attention half, then the SwiGLU MLP half; an own layer appends its K/V rows, a
+// KV-shared layer reads its owner's plane. The input rows' RMSNorms run inside the GEMMs' staging
+// from the per-tile sums of squares in ss_x (written by the previous layer's down projection, or
+// the embedding); the layer leaves ss_x for the next one. taps (optional): bf16 copy of the output.
+hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps, int ldt) {
+    Layer& L = m->L[l];
+    const int H = m->d.hidden;
+    hipStream_t st = m->st;
+    hipError_t e;
+    GemmLaunch g = gemm_for(m, L.qkv, EPI_STORE);
+    g.xsrc = x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile; g.gain = L.attn_norm; g.eps = m->d.rms_eps;
+    g.M = k; g.y = m->qkv; g.ldy = L.qkv.n_out; g.ss_out = m->ss_qkv;
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+    Attn at = attn_for(m, L, k);
+    at.plane = L.plane ? L.plane : m->L[L.d.kv_owner].plane;
+    at.own = L.plane != nullptr;
+    at.causal = 1; at.pos0 = P; at.window = L.d.attn == BVF_ATTN_SLIDING ? L.d.window : 0;
+    at.np0 = P; at.np1 = P + k; at.sp = P; at.r_lo = 0; at.r_hi = 0;
+    if ((e = launch_attention(at, st)) != hipSuccess) return e;
+    g = gemm_for(m, L.o, EPI_RESID);
+    g.A = m->obuf; g.lda = L.qd; g.M = k; g.y = x; g.ldy = H; g.ss_out = m->ss_x;
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+    g = gemm_for(m, L.gu, EPI_SWIGLU);
+    g.xsrc = x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile; g.gain = L.mlp_norm; g.eps = m->d.rms_eps;
+    g.M = k; g.out = m->mbuf; g.ldo = L.d.ffn;
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+    g = gemm_for(m, L.down, EPI_RESID);
+    g.A = m->mbuf; g.lda = L.d.ffn; g.M = k; g.y = x; g.ldy = H; g.ss_out = m->ss_x;
+    g.taps = taps; g.ldt = ldt;
+    return launch_gemm(g, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bvf_last_error(void) { return g_err.c_str(); }
+
+int64_t bvf_cut_floats(const int64_t* per, int32_t n_per, int32_t plane, int64_t positions) {
+    if (!per || n_per < 1 || plane < 0) return -1;
+    return positions * 2 * per[plane < n_per ? plane : n_per - 1];
+}
+
+size_t bvf_arena_bytes(const bvf_model_desc* desc) {
+    if (check_desc(desc) != BVF_OK) return 0;
+    bvf_model tmp;
+    copy_desc(&tmp, desc);
+    const size_t n = layout(&tmp, nullptr);
+    g_err.clear();
+    return n;
+}
+
+bvf_status bvf_create(const bvf_model_desc* desc, void* d_arena, size_t arena_bytes, void* hip_stream, bvf_model** out) {
+    if (!out) return fail(BVF_E_INVALID, "out is NULL");
+    *out = nullptr;
+    bvf_status s = check_desc(desc);
+    if (s) return s;
+    if (!d_arena) return fail(BVF_E_INVALID, "d_arena is NULL");
+    if ((uintptr_t)d_arena % kAlign) return fail(BVF_E_INVALID, "d_arena is not 256-byte aligned");
+    bvf_model* m = new bvf_model;
+    copy_desc(m, desc);
+    const size_t need = layout(m, nullptr);
+    if (arena_bytes < need) {
+        delete m;
+        return fail(BVF_E_CAPACITY, "arena of %zu bytes < %zu needed", arena_bytes, need);
+    }
+    layout(m, (uint8_t*)d_arena);
+    m->arena = (uint8_t*)d_arena;
+    m->arena_bytes = arena_bytes;
+    m->st = (hipStream_t)hip_stream;
+    hipError_t e = hipGetDevice(&m->device);
+    if (e == hipSuccess) e = hipMemsetAsync(d_arena, 0, need, m->st);
+    for (auto& pr : m->rope_tables)
+        if (e == hipSuccess) e = launch_rope_table(pr.second, m->d.max_ctx, pr.first, (double)m->d.rope_base, m->st);
+    if (e == hipSuccess) e = hipStreamSynchronize(m->st);
+    if (e != hipSuccess) {
+        delete m;
+        return fail(BVF_E_DEVICE, "create: %s", hipGetErrorString(e));
+    }
+    *out = m;
+    return ok();
+}
+
+void bvf_destroy(bvf_model* m) { delete m; }
+
+bvf_status bvf_load_q4_1(bvf_model* m, int32_t layer, int32_t matrix, const void* h_blocks, size_t bytes, int32_t n_out,
+                         int32_t n_in) {
+    if (!m) return fail(BVF_E_INVALID, "model is NULL");
+    Run r;
+    bvf_status s = matrix_run(m, layer, matrix, r);
+    if (s) return s;
+    if (n_out != r.n_out || n_in != r.mat->w.K)
+        return fail(BVF_E_INVALID, "layer %d matrix %d: shape %d x %d, expected %d x %d", layer, matrix, n_out, n_in, r.n_out,
+                    r.mat->w.K);
+    const size_t need = (size_t)n_out * (n_in / 32) * 20;
+    if (!h_blocks || bytes != need) return fail(BVF_E_INVALID, "Q4_1 image of %zu bytes, expected %zu", bytes, need);
+    if (need > m->staging_bytes) return fail(BVF_E_CAPACITY, "staging too small");
+    HIP_TRY(hipMemcpyAsync(m->staging, h_blocks, need, hipMemcpyHostToDevice, m->st));
+    HIP_TRY(launch_repack_q4_1(m->staging, n_out, n_in, (uint8_t*)r.mat->w.codes, (uint8_t*)r.mat->w.sm, r.mat->w.G, r.col0,
+                               r.gu_mode, m->st));
+    HIP_TRY(hipStreamSynchronize(m->st));
+    m->L[layer].loaded |= 1u << matrix;
+    return ok();
+}
+
+bvf_status bvf_load_bf16(bvf_model* m, int32_t tensor, int32_t layer, const uint16_t* h, size_t n) {
+    if (!m || !h) return fail(BVF_E_INVALID, "NULL argument");
+    const int H = m->d.hidden;
+    uint16_t* dst = nullptr;
+    size_t want = 0;
+    int bit = -1;
+    auto per_layer = [&](int which) -> bvf_status {
+        if (layer < 0 || layer >= m->d.n_layers) return fail(BVF_E_INVALID, "layer %d out of range", layer);
+        Layer& L = m->L[layer];
+        const int hd = L.d.head_dim;
+        uint16_t* ptrs[4] = {L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm};
+        size_t sizes[4] = {(size_t)H, (size_t)H, (size_t)hd, (size_t)hd};
+        dst = ptrs[which];
+        want = sizes[which];
+        bit = 8 + which;
+        return BVF_OK;
+    };
+    bvf_status s = BVF_OK;
+    switch (tensor) {
+        case BVF_EMBED:
+            if (is_draft(m->d)) return fail(BVF_E_INVALID, "a draft uses the target's embedding table");
+            dst = m->embed; want = (size_t)m->d.vocab * H; break;
+        case BVF_FINAL_NORM: dst = m->final_norm; want = H; break;
+        case BVF_ATTN_NORM: s = per_layer(0); break;
+        case BVF_MLP_NORM: s = per_layer(1); break;
+        case BVF_Q_NORM: s = per_layer(2); break;
+        case BVF_K_NORM: s = per_layer(3); break;
+        case BVF_FC:
+            if (!is_draft(m->d)) return fail(BVF_E_INVALID, "fc exists on a draft only");
+            dst = m->fc; want = (size_t)H * m->d.n_taps * H; break;
+        case BVF_HIDDEN_NORM:
+            if (!is_draft(m->d)) return fail(BVF_E_INVALID, "hidden norm exists on a draft only");
+            dst = m->hidden_norm; want = H; break;
+        default: return fail(BVF_E_INVALID, "tensor id %d", tensor);
+    }
+    if (s) return s;
+    if (n != want) return fail(BVF_E_INVALID, "tensor %d: %zu elements, expected %zu", tensor, n, want);
+    HIP_TRY(hipMemcpyAsync(dst, h, n * 2, hipMemcpyHostToDevice, m->st));
+    HIP_TRY(hipStreamSynchronize(m->st));
+    if (bit >= 0) m->L[layer].loaded |= 1u << bit;
+    else m->loaded |= 1u << tensor;
+    return ok();
+}
+
+bvf_status bvf_set_kv(bvf_model* m, int32_t layer, const float* h_kv, int64_t positions) {
+    if (!m || !h_kv) return fail(BVF_E_INVALID, "NULL argument");
+    if (layer < 0 || layer >= m->d.n_layers) return fail(BVF_E_INVALID, "layer %d out of range", layer);
+    Layer& L = m->L[layer];
+    if (!L.plane) return fail(BVF_E_INVALID, "layer %d is KV-shared: it holds no plane", layer);
+    if (positions < 0 || positions > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions %lld > max_ctx", (long long)positions);
+    HIP_TRY(hipMemcpyAsync(L.plane, h_kv, (size_t)positions * 2 * L.w * 4, hipMemcpyHostToDevice, m->st));
+    HIP_TRY(hipStreamSynchronize(m->st));
+    return ok();
+}
+
+bvf_status bvf_set_positions(bvf_model* m, int64_t positions) {
+    if (!m) return fail(BVF_E_INVALID, "model is NULL");
+    if (positions < 0 || positions > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions %lld out of [0, max_ctx]", (long long)positions);
+    m->held = positions;
+    m->pending = -1;
+    return ok();
+}
+
+bvf_status bvf_kv_widths(const bvf_model* m, int64_t* out, int32_t n) {
+    if (!m || !out || n != m->d.n_layers) return fail(BVF_E_INVALID, "need an array of n_layers entries");
+    for (int l = 0; l < n; ++l) out[l] = m->L[l].w;
+    return ok();
+}
+
+bvf_status bvf_plane_floats(const bvf_model* m, int64_t* out, int32_t n) {
+    if (!m || !out || n != m->d.n_layers) return fail(BVF_E_INVALID, "need an array of n_layers entries");
+    for (int l = 0; l < n; ++l) out[l] = m->L[l].plane ? m->held * 2 * m->L[l].w : 0;
+    return ok();
+}
+
+bvf_status bvf_positions_held(const bvf_model* m, int64_t* out) {
+    if (!m || !out) return fail(BVF_E_INVALID, "NULL argument");
+    *out = m->held;
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+// The verify pass's launches on stream st (positions P .. P + k - 1).
+hipError_t enqueue_verify(bvf_model* m, hipStream_t st, const int32_t* d_tokens, int k, float* d_logits_all,
+                          uint16_t* d_taps) {
+    const int H = m->d.hidden, V = m->d.vocab, P = (int)m->held;
+    const int T = (int)m->taps.size();
+    hipStream_t saved = m->st;
+    m->st = st;
+    hipError_t e = launch_embed(d_tokens, -1, k, m->embed, V, H, 1.0f, m->x, m->ss_x, st);
+    for (int l = 0; l < m->d.n_layers && e == hipSuccess; ++l) {
+        uint16_t* taps_l = nullptr;
+        if (d_taps)
+            for (int t = 0; t < T; ++t)
+                if (m->taps[t] == l) taps_l = d_taps + (size_t)t * H;
+        e = run_layer(m, l, m->x, k, P, taps_l, T * H);
+    }
+    if (e == hipSuccess) e = launch_head(m, nullptr, k, d_logits_all, st, m, m->x, m->final_norm);
+    m->st = saved;
+    return e;
+}
+}  // namespace
+
+extern "C" {
+
+bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, float* d_logits_all, uint16_t* d_taps) {
+    if (!m || !d_tokens || !d_logits_all) return fail(BVF_E_INVALID, "NULL argument");
+    if (is_draft(m->d)) return fail(BVF_E_INVALID, "verify on a draft model");
+    if (k < 1 || k > kMaxRows) return fail(BVF_E_INVALID, "k = %d outside [1, %d]", k, kMaxRows);
+    if (m->held + k > m->d.max_ctx)
+        return fail(BVF_E_CAPACITY, "%lld held + %d rows > max_ctx %d", (long long)m->held, k, m->d.max_ctx);
+    bvf_status s = check_loaded(m);
+    if (s) return s;
+    if (!m->use_graph) {
+        HIP_TRY(enqueue_verify(m, m->st, d_tokens, k, d_logits_all, d_taps));
+    } else {
+        if (!m->gexec || m->g_P != m->held || m->g_k != k || m->g_tok != d_tokens || m->g_lg != d_logits_all ||
+            m->g_taps != d_taps) {
+            if (m->gexec) {
+                HIP_TRY(hipGraphExecDestroy(m->gexec));
+                m->gexec = nullptr;
+            }
+            if (!m->cap_st) HIP_TRY(hipStreamCreateWithFlags(&m->cap_st, hipStreamNonBlocking));
+            hipGraph_t graph = nullptr;
+            HIP_TRY(hipStreamBeginCapture(m->cap_st, hipStreamCaptureModeThreadLocal));
+            hipError_t e = enqueue_verify(m, m->cap_st, d_tokens, k, d_logits_all, d_taps);
+            hipError_t e2 = hipStreamEndCapture(m->cap_st, &graph);
+            if (e != hipSuccess || e2 != hipSuccess) {
+                if (graph) (void)hipGraphDestroy(graph);
+                return fail(BVF_E_DEVICE, "graph capture: %s", hipGetErrorString(e != hipSuccess ? e : e2));
+            }
+            e = hipGraphInstantiate(&m->gexec, graph, nullptr, nullptr, 0);
+            (void)hipGraphDestroy(graph);
+            if (e != hipSuccess) {
+                m->gexec = nullptr;
+                return fail(BVF_E_DEVICE, "graph instantiate: %s", hipGetErrorString(e));
+            }
+            m->g_P = m->held; m->g_k = k; m->g_tok = d_tokens; m->g_lg = d_logits_all; m->g_taps = d_taps;
+        }
+        HIP_TRY(hipGraphLaunch(m->gexec, m->st));
+    }
+    m->held += k;
+    m->pending = k;
+    return ok();
+}
+
+bvf_status bvf_set_graph_mode(bvf_model* m, int32_t on) {
+    if (!m) return fail(BVF_E_INVALID, "model is NULL");
+    if (on != 0 && on != 1) return fail(BVF_E_INVALID, "graph mode must be 0 or 1");
+    m->use_graph = on;
+    return ok();
+}
+
+bvf_status bvf_accept_greedy(bvf_model* m, const float* d_logits_all, int32_t k, const int32_t* d_tokens,
+                             int32_t* d_out_tokens, int32_t* d_n_accepted) {
+    if (!m || !d_logits_all || !d_tokens || !d_out_tokens || !d_n_accepted) return fail(BVF_E_INVALID, "NULL argument");
+    if (is_draft(m->d)) return fail(BVF_E_INVALID, "accept on a draft model");
+    if (k < 1 || k > kMaxRows) return fail(BVF_E_INVALID, "k = %d outside [1, %d]", k, kMaxRows);
+    HIP_TRY(launch_argmax_accept(d_logits_all, k, m->d.vocab, d_tokens, m->am_val, m->am_idx, m->am_blocks, d_out_tokens,
+                                 d_n_accepted, nullptr, m->st));
+    return ok();
+}
+
+bvf_status bvf_steer_logits(bvf_model* m, float* d_logits_all, int32_t k, const int32_t* d_tok, const float* d_add) {
+    if (!m || !d_logits_all || !d_tok || !d_add) return fail(BVF_E_INVALID, "NULL argument");
+    if (k < 1 || k > kMaxRows) return fail(BVF_E_INVALID, "k = %d outside [1, %d]", k, kMaxRows);
+    HIP_TRY(launch_steer(d_logits_all, k, m->d.vocab, d_tok, d_add, m->st));
+    return ok();
+}
+
+bvf_status bvf_commit_verify_rows(bvf_model* m, int32_t n) {
+    if (!m) return fail(BVF_E_INVALID, "model is NULL");
+    if (m->pending < 0) return fail(BVF_E_STATE, "commit_verify_rows with no verify pending");
+    if (n < 0 || n > m->pending) return fail(BVF_E_STATE, "commit_verify_rows(%d) after a verify of %d rows", n, m->pending);
+    m->held = m->held - m->pending + n;
+    m->pending = -1;
+    return ok();
+}
+
+bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out) {
+    if (!m || !out) return fail(BVF_E_INVALID, "NULL argument");
+    *out = nullptr;
+    bvf_snapshot* s = new bvf_snapshot;
+    s->n_layers = m->d.n_layers;
+    s->held = m->held;
+    s->device = m->device;
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        s->per.push_back(m->L[l].w);
+        s->shared.push_back(m->L[l].plane ? 0 : 1);
+        s->data.push_back(nullptr);
+    }
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        if (s->shared[l] || s->held == 0) continue;
+        const size_t bytes = (size_t)bvf_cut_floats(s->per.data(), s->n_layers, l, s->held) * 4;
+        hipError_t e = hipMalloc((void**)&s->data[l], bytes);
+        if (e == hipSuccess) e = hipMemcpyAsync(s->data[l], m->L[l].plane, bytes, hipMemcpyDeviceToDevice, m->st);
+        if (e != hipSuccess) {
+            bvf_snapshot_free(s);
+            return fail(BVF_E_DEVICE, "snapshot: %s", hipGetErrorString(e));
+        }
+    }
+    hipError_t e = hipStreamSynchronize(m->st);
+    if (e != hipSuccess) {
+        bvf_snapshot_free(s);
+        return fail(BVF_E_DEVICE, "snapshot: %s", hipGetErrorString(e));
+    }
+    m->pending = -1;
+    *out = s;
+    return ok();
+}
+
+bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s) {
+    if (!m || !s) return fail(BVF_E_INVALID, "NULL argument");
+    if (s->n_layers != m->d.n_layers)
+        return fail(BVF_E_INVALID, "snapshot of %d layers, model of %d", s->n_layers, m->d.n_layers);
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        if (s->per[l] != m->L[l].w) return fail(BVF_E_INVALID, "layer %d: snapshot width %lld, model %d", l, (long long)s->per[l], m->L[l].w);
+        if (s->shared[l] != (m->L[l].plane ? 0 : 1)) return fail(BVF_E_INVALID, "layer %d: shared/own mismatch", l);
+    }
+    if (s->held > m->d.max_ctx) return fail(BVF_E_CAPACITY, "snapshot holds more positions than max_ctx");
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        if (s->shared[l] || !s->data[l]) continue;
+        const size_t bytes = (size_t)bvf_cut_floats(s->per.data(), s->n_layers, l, s->held) * 4;
+        HIP_TRY(hipMemcpyAsync(m->L[l].plane, s->data[l], bytes, hipMemcpyDeviceToDevice, m->st));
+    }
+    HIP_TRY(hipStreamSynchronize(m->st));
+    m->held = s->held;
+    m->pending = -1;
+    return ok();
+}
+
+bvf_status bvf_snapshot_floats(const bvf_snapshot* s, int64_t* out, int32_t n) {
+    if (!s || !out || n != s->n_layers) return fail(BVF_E_INVALID, "need an array of n_layers entries");
+    for (int l = 0; l < n; ++l) out[l] = s->shared[l] ? 0 : bvf_cut_floats(s->per.data(), s->n_layers, l, s->held);
+    return ok();
+}
+
+void bvf_snapshot_free(bvf_snapshot* s) {
+    if (!s) return;
+    for (float* p : s->data)
+        if (p) (void)hipFree(p);
+    delete s;
+}
+
+bvf_status bvf_draft_block_forward(bvf_model* dr, const bvf_model* tg, const uint16_t* d_new_taps, int32_t n_new,
+                                   const int32_t* d_last_token, int32_t block, float embedding_scale, int32_t mask_token,
+                                   int32_t* d_proposals, float* d_logits) {
+    if (!dr || !tg) return fail(BVF_E_INVALID, "NULL argument");
+    if (block != 0 && (!d_last_token || !d_proposals)) return fail(BVF_E_INVALID, "NULL argument");
+    if (!is_draft(dr->d)) return fail(BVF_E_INVALID, "the first model is not a draft");
+    if (is_draft(tg->d)) return fail(BVF_E_INVALID, "the second model is not a verify (target) model");
+    if (tg->d.hidden != dr->d.hidden) return fail(BVF_E_INVALID, "the target is %d wide and the draft %d: not a pair", tg->d.hidden, dr->d.hidden);
+    if (block != 0 && (block < 2 || block > kMaxRows)) return fail(BVF_E_INVALID, "block %d not 0 or in [2, %d]", block, kMaxRows);
+    if (n_new < 0 || n_new + block > kMaxRows) return fail(BVF_E_INVALID, "n_new %d + block %d > %d", n_new, block, kMaxRows);
+    if (block == 0 && n_new == 0) return ok();
+    if (n_new > 0 && !d_new_taps) return fail(BVF_E_INVALID, "d_new_taps is NULL");
+    const int V = tg->d.vocab;
+    if (block && (mask_token < 0 || mask_token >= V)) return fail(BVF_E_INVALID, "mask token %d outside the vocabulary", mask_token);
+    if (block && !d_logits && dr->d.vocab != V) return fail(BVF_E_INVALID, "no logits buffer and the draft's scratch is sized for vocab %d", dr->d.vocab);
+    const int64_t s = dr->held + n_new;
+    if (s + block > dr->d.max_ctx) return fail(BVF_E_CAPACITY, "%lld context + %d block rows > max_ctx %d", (long long)s, block, dr->d.max_ctx);
+    bvf_status stt = check_loaded(dr);
+    if (stt) return stt;
+    if (!(tg->loaded & (1u << BVF_EMBED))) return fail(BVF_E_STATE, "the target's embedding table is not loaded");
+    const int H = dr->d.hidden, T = dr->d.n_taps, B = block;
+    const int s_old = (int)dr->held, s_new = (int)s;
+    hipStream_t st = dr->st;
+    uint16_t* ctx_rows = dr->act + (size_t)B * H;   // context rows c follow the block rows in the A buffer
+    if (n_new > 0) {
+        GemmLaunch g;
+        g.w.codes = (const uint8_t*)dr->fc;
+        g.w.n_tiles = H / kTile;
+        g.w.G = T * H / kSuper;
+        g.w.K = T * H;
+        g.fmt = W_BF16;
+        g.epi = EPI_STORE;
+        g.n_run_tiles = g.w.n_tiles;
+        g.A = d_new_taps; g.lda = T * H; g.M = n_new; g.y = dr->fcout; g.ldy = H;
+        g.partial = dr->partial; g.partial_floats = kPartialFloats; g.counters = dr->counters; g.n_counters = kCounters;
+        HIP_TRY(launch_gemm(g, st));
+        HIP_TRY(launch_rmsnorm(dr->fcout, H, n_new, H, dr->hidden_norm, dr->d.rms_eps, ctx_rows, H, st));
+    }
+    if (B == 0) {
+        // append only: the context rows' K/V in every draft layer, no block
+        for (int l = 0; l < dr->d.n_layers; ++l) {
+            Layer& L = dr->L[l];
+            GemmLaunch g = gemm_for(dr, L.qkv, EPI_STORE);
+            g.A = ctx_rows; g.lda = H; g.M = n_new; g.y = dr->qkv; g.ldy = L.qkv.n_out;
+            HIP_TRY(launch_gemm(g, st));
+            RopeAppend ra;
+            ra.qkv = dr->qkv; ra.ldq = L.qkv.n_out; ra.rows_q = 0; ra.rows = n_new; ra.split_row = 0;
+            ra.pos0 = s_old; ra.pos1 = s_old;
+            ra.Hq = dr->d.n_q_heads; ra.nkv = L.d.n_kv_heads; ra.hd = L.d.head_dim; ra.own = 1;
+            ra.qk_norm = dr->d.qk_norm; ra.q_norm = L.q_norm; ra.k_norm = L.k_norm; ra.eps = dr->d.rms_eps;
+            ra.rope = L.rope; ra.plane = L.plane; ra.w = L.w; ra.q_out = dr->qbuf;
+            HIP_TRY(launch_rope_append(ra, st));
+        }
+        dr->held = s;
+        return ok();
+    }
+    HIP_TRY(launch_embed(d_last_token, mask_token, B, tg->embed, V, H, embedding_scale, dr->x, nullptr, st));
+    const int ctx_lo = (dr->d.draft_window > 0 && s_new - dr->d.draft_window > 0) ? s_new - dr->d.draft_window : 0;
+    for (int l = 0; l < dr->d.n_layers; ++l) {
+        Layer& L = dr->L[l];
+        const int hd = L.d.head_dim;
+        HIP_TRY(launch_rmsnorm(dr->x, H, B, H, L.attn_norm, dr->d.rms_eps, dr->act, H, st));
+        GemmLaunch g = gemm_for(dr, L.qkv, EPI_STORE);
+        g.A = dr->act; g.lda = H; g.M = B + n_new; g.y = dr->qkv; g.ldy = L.qkv.n_out; g.ss_out = dr->ss_qkv;
+        HIP_TRY(launch_gemm(g, st));
+        // block rows 0..B-1 at s .. s+B-1 and context rows B.. at s_old .. s-1 are appended; the
+        // block sees the context window and all block rows
+        Attn at = attn_for(dr, L, B);
+        at.plane = L.plane; at.own = 1;
+        at.causal = 0; at.pos0 = s_new; at.ctx_lo = ctx_lo; at.ctx_hi = s_new + B - 1;
+        at.np0 = s_old; at.np1 = s_new + B; at.sp = s_new; at.r_lo = B; at.r_hi = 0;
+        HIP_TRY(launch_attention(at, st));
+        g = gemm_for(dr, L.o, EPI_RESID);
+        g.A = dr->obuf; g.lda = L.qd; g.M = B; g.y = dr->x; g.ldy = H;
+        HIP_TRY(launch_gemm(g, st));
+        HIP_TRY(launch_rmsnorm(dr->x, H, B, H, L.mlp_norm, dr->d.rms_eps, dr->act, H, st));
+        g = gemm_for(dr, L.gu, EPI_SWIGLU);
+        g.A = dr->act; g.lda = H; g.M = B; g.out = dr->mbuf; g.ldo = L.d.ffn;
+        HIP_TRY(launch_gemm(g, st));
+        g = gemm_for(dr, L.down, EPI_RESID);
+        g.A = dr->mbuf; g.lda = L.d.ffn; g.M = B; g.y = dr->x; g.ldy = H;
+        HIP_TRY(launch_gemm(g, st));
+    }
+    // rows 1 .. B-1 through the final norm and the target's head
+    HIP_TRY(launch_rmsnorm(dr->x + H, H, B - 1, H, dr->final_norm, dr->d.rms_eps, dr->act, H, st));
+    float* logits = d_logits ? d_logits : dr->logits_scratch;
+    HIP_TRY(launch_head(tg, dr->act, B - 1, logits, st, dr));
+    HIP_TRY(launch_argmax_accept(logits, B - 1, V, nullptr, dr->am_val, dr->am_idx, argmax_blocks(V), nullptr, nullptr,
+                                 d_proposals, st));
+    dr->held = s;
+    return ok();
+}
+
+bvf_status bvf_q4_1_dequant(const bvf_model* m, int32_t layer, int32_t matrix, float* d_w) {
+    if (!m || !d_w) return fail(BVF_E_INVALID, "NULL argument");
+    Run r;
+    bvf_status s = matrix_run(m, layer, matrix, r);
+    if (s) return s;
+    if (!(m->L[layer].loaded & (1u << matrix))) return fail(BVF_E_STATE, "matrix not loaded");
+    HIP_TRY(launch_dequant_q4_1(r.mat->w, r.tile0, r.gu_mode, r.n_out, d_w, m->st));
+    return ok();
+}
+
+bvf_status bvf_q4_1_gemm(const bvf_model* m, int32_t layer, int32_t matrix, const uint16_t* d_x, int32_t rows, float* d_y) {
+    if (!m || !d_x || !d_y) return fail(BVF_E_INVALID, "NULL argument");
+    if (rows < 1 || rows > kMaxRows) return fail(BVF_E_INVALID, "rows %d outside [1, %d]", rows, kMaxRows);
+    Run r;
+    bvf_status s = matrix_run(m, layer, matrix, r);
+    if (s) return s;
+    if (!(m->L[layer].loaded & (1u << matrix))) return fail(BVF_E_STATE, "matrix not loaded");
+    GemmLaunch g = gemm_for(m, *r.mat, EPI_STORE);
+    g.tile0 = r.tile0;
+    g.tile_stride = 1;
+    g.n_run_tiles = r.gu_mode ? r.mat->w.n_tiles : r.n_out / kTile;
+    g.half = r.gu_mode - 1;
+    g.A = d_x; g.lda = r.mat->w.K; g.M = rows; g.y = d_y; g.ldy = r.n_out;
+    HIP_TRY(launch_gemm(g, m->st));
+    return ok();
+}
+
+bvf_status bvf_layer_forward(bvf_model* m, int32_t layer, float* d_x, int32_t rows) {
+    if (!m || !d_x) return fail(BVF_E_INVALID, "NULL argument");
+    if (is_draft(m->d)) return fail(BVF_E_INVALID, "layer_forward runs verify layers");
+    if (layer < 0 || layer >= m->d.n_layers) return fail(BVF_E_INVALID, "layer %d out of range", layer);
+    if (rows < 1 || rows > kMaxRows) return fail(BVF_E_INVALID, "rows %d outside [1, %d]", rows, kMaxRows);
+    if (m->held + rows > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions would exceed max_ctx");
+    bvf_status s = check_loaded(m);
+    if (s) return s;
+    HIP_TRY(launch_sumsq(d_x, m->d.hidden, rows, m->d.hidden, m->ss_x, m->st));
+    HIP_TRY(run_layer(m, layer, d_x, rows, (int)m->held, nullptr, 0));
+    return ok();
+}
+
+bvf_status bvf_time_gemms(bvf_model* m, int32_t rows, int32_t iters, float* h_ms, int64_t* h_bytes) {
+    if (!m || !h_ms || !h_bytes) return fail(BVF_E_INVALID, "NULL argument");
+    if (is_draft(m->d)) return fail(BVF_E_INVALID, "timing runs the verify model's GEMMs");
+    if (rows < 1 || rows > kMaxRows || iters < 1) return fail(BVF_E_INVALID, "rows in [1, 16], iters >= 1");
+    bvf_status s = check_loaded(m);
+    if (s) return s;
+    const int H = m->d.hidden;
+    hipEvent_t e0, e1;
+    HIP_TRY(hipEventCreate(&e0));
+    HIP_TRY(hipEventCreate(&e1));
+    for (int cls = 0; cls < 5; ++cls) {
+        int64_t bytes = 0;
+        int launches = 0;
+        HIP_TRY(hipEventRecord(e0, m->st));
+        for (int it = 0; it < iters; ++it) {
+            if (cls == 4) {   // the bf16 head
+                HIP_TRY(launch_head(m, nullptr, rows, m->logits_tmp, m->st, m, m->x, m->final_norm));
+                bytes += (int64_t)m->d.vocab * H * 2;
+                ++launches;
+                continue;
+            }
+            for (int l = 0; l < m->d.n_layers; ++l) {
+                Layer& L = m->L[l];
+                GemmLaunch g;
+                if (cls == 0 || cls == 2) {
+                    g = gemm_for(m, cls == 0 ? L.qkv : L.gu, cls == 0 ? EPI_STORE : EPI_SWIGLU);
+                    g.xsrc = m->x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile;
+                    g.gain = cls == 0 ? L.attn_norm : L.mlp_norm; g.eps = m->d.rms_eps;
+                    if (cls == 0) { g.y = m->qkv; g.ldy = L.qkv.n_out; g.ss_out = m->ss_qkv; }
+                    else { g.out = m->mbuf; g.ldo = L.d.ffn; }
+                } else if (cls == 1) {
+                    g = gemm_for(m, L.o, EPI_RESID); g.A = m->obuf; g.lda = L.qd; g.y = m->x; g.ldy = H; g.ss_out = m->ss_x;
+                } else {
+                    g = gemm_for(m, L.down, EPI_RESID); g.A = m->mbuf; g.lda = L.d.ffn; g.y = m->x; g.ldy = H; g.ss_out = m->ss_x;
+                }
+                g.M = rows;
+                HIP_TRY(launch_gemm(g, m->st));
+                bytes += (int64_t)g.w.n_tiles * g.w.G * (1024 + 256);
+                ++launches;
+            }
+        }
+        HIP_TRY(hipEventRecord(e1, m->st));
+        HIP_TRY(hipEventSynchronize(e1));
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+        h_ms[cls] = ms / launches;
+        h_bytes[cls] = bytes / launches;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return ok();
+}
+
+bvf_status bvf_pass_bytes(const bvf_model* m, int64_t* q4, int64_t* head) {
+    if (!m || !q4 || !head) return fail(BVF_E_INVALID, "NULL argument");
+    int64_t b = 0;
+    for (const Layer& L : m->L)
+        for (const Mat* M : {&L.qkv, &L.o, &L.gu, &L.down}) b += (int64_t)M->w.n_tiles * M->w.G * (1024 + 256);
+    *q4 = b;
+    *head = is_draft(m->d) ? 0 : (int64_t)m->d.vocab * m->d.hidden * 2;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+// Internal interface between the C ABI (bvf_api.cpp) and the gfx950 kernels (*.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace bvf {
+
+constexpr int kMaxRows = 16;      // k <= 16 rows per pass: one 16-row MFMA tile
+constexpr int kTile = 16;         // output columns per MFMA tile
+constexpr int kSuper = 128;       // K per superblock = 4 Q4_1 blocks of 32
+
+// A packed Q4_1 (or bf16) weight image, column-tiled for the small-M GEMM.
+//   Q4_1: codes  [n_tiles][G][64 lanes][4 x u32]: lane = sub * 16 + c holds, for block j of the
+//                superblock, the 8 codes of column c at k = 128 g + 32 j + 8 sub + e (e = 0..7),
+//                nibble (e >> 1) + 4 (e & 1) of dword j (so (w >> 4i) & 0x000F000F gives the pair
+//                (e = 2i, 2i + 1) in the low/high halves).
+//         sm     [n_tiles][G][16 columns][4 x u32]: dword j = fp16 scale | fp16 min << 16.
+//         A gate|up image interleaves by half tiles: tile t holds gate rows 8t..8t+7 in columns
+//         0..7 and up rows 8t..8t+7 in columns 8..15.
+//   BF16: codes points at a row-major bf16 [N][K] matrix; sm unused.
+struct WMat {
+    const uint8_t* codes = nullptr;
+    const uint8_t* sm = nullptr;
+    int n_tiles = 0;   // 16-column tiles of the packed (fused) image
+    int G = 0;         // K / 128
+    int K = 0;
+};
+
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum WFmt : int { W_Q4_1 = 0, W_BF16 = 1 };
+
+// One GEMM launch: y[m][n] (+)= sum_k A[m][k] W[n][k] over the tiles tile0 + i * tile_stride,
+// i = 0 .. n_run_tiles - 1; output column of tile i is 16 i + c.
+struct GemmLaunch {
+    WMat w;
+    int fmt = W_Q4_1;
+    int epi = EPI_STORE;
+    int tile0 = 0, tile_stride = 1, n_run_tiles = 0;
+    const uint16_t* A = nullptr;
+    int lda = 0;
+    int M = 0;
+    float* y = nullptr;          // STORE: y[m * ldy + n]; RESID: y[m * ldy + n] += ...
+    int ldy = 0;
+    uint16_t* out = nullptr;     // SWIGLU: out[m * ldo + n_half] bf16
+    int ldo = 0;
+    uint16_t* taps = nullptr;    // RESID: optional bf16 copy of the updated rows, taps[m * ldt + n]
+    int ldt = 0;
+    float* partial = nullptr;    // split-K scratch
+    size_t partial_floats = 0;
+    int* counters = nullptr;     // split-K arrival counters (zero between launches)
+    int n_counters = 0;
+    int half = -1;               // STORE on a gate|up image: -1 all columns, 0 gate, 1 up
+    // RMSNorm folded into the A staging: A = bf16(xsrc * rinv * gain), rinv from ss_in [M][n_ss]
+    const float* xsrc = nullptr;
+    int ldx = 0;
+    const float* ss_in = nullptr;
+    int n_ss = 0;
+    const uint16_t* gain = nullptr;
+    float eps = 0.f;
+    float* ss_out = nullptr;     // STORE/RESID: per (row, output tile) sums of squares [M][n_run_tiles]
+    // launch plan (0 = choose)
+    int NT = 0, S = 0;
+};
+
+struct GemmPlan {
+    int NT, S, sb_per_split, n_groups, items, grid;
+    size_t lds;   // dynamic LDS bytes (the workgroup's K range of the activation rows)
+};
+constexpr size_t kLdsBudgetQ4 = 40 * 1024;
+constexpr size_t kLdsBudgetBf16 = 64 * 1024;
+
+GemmPlan plan_gemm(const GemmLaunch& L);
+hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st);
+
+// ---- other kernels ---------------------------------------------------------------------------
+hipError_t launch_repack_q4_1(const uint8_t* canon, int n_out, int n_in, uint8_t* codes, uint8_t* sm, int G,
+                              int col0, int gu_mode, hipStream_t st);
+// gu: 0 plain run of tiles tile0.. (16 columns each); 1 / 2 the gate / up half of a gate|up image.
+hipError_t launch_dequant_q4_1(const WMat& w, int tile0, int gu, int n_out, float* out, hipStream_t st);
+hipError_t launch_rope_table(float2* table, int max_ctx, int hd, double base, hipStream_t st);
+hipError_t launch_embed(const int32_t* tokens, int fill_token, int rows, const uint16_t* embed, int V, int H,
+                        float scale, float* x, float* ss, hipStream_t st);
+hipError_t launch_sumsq(const float* x, int ldx, int rows, int H, float* ss, hipStream_t st);
+hipError_t launch_rmsnorm(const float* x, int ldx, int rows, int H, const uint16_t* g, float eps, uint16_t* out,
+                          int ldo, hipStream_t st);
+
+struct RopeAppend {
+    const float* qkv = nullptr;  // [rows][ldq]: q | k | v
+    int ldq = 0;
+    int rows_q = 0;              // rows whose q heads are produced (the first rows_q rows)
+    int rows = 0;                // rows whose k/v are appended (own plane)
+    int split_row = 0;           // rows < split_row at pos0 + r, rows >= split_row at pos1 + (r - split_row)
+    int pos0 = 0, pos1 = 0;
+    int Hq = 0, nkv = 0, hd = 0;
+    int own = 0;
+    int qk_norm = 0;
+    const uint16_t* q_norm = nullptr;
+    const uint16_t* k_norm = nullptr;
+    float eps = 0.f;
+    const float2* rope = nullptr;  // [max_ctx][hd / 2] (cos, sin)
+    float* plane = nullptr;        // own plane [max_ctx][2][w]
+    int w = 0;
+    float* q_out = nullptr;        // [rows_q][Hq][hd]
+};
+hipError_t launch_rope_append(const RopeAppend& a, hipStream_t st);
+
+struct Attn {
+    const float* qkv = nullptr;  // [rows][ldq] raw q | k | v of the layer's GEMM
+    const float* ss = nullptr;   // [rows][ldq / 16] per-tile sums of squares (GEMM epilogue)
+    int ldq = 0;
+    const uint16_t* q_norm = nullptr;
+    const uint16_t* k_norm = nullptr;
+    int qk_norm = 0;
+    float eps = 0.f;
+    const float2* rope = nullptr;
+    float* plane = nullptr;      // [max_ctx][2][w] (own or owner's)
+    int w = 0, own = 0;
+    int M = 0, Hq = 0, nkv = 0, hd = 0;
+    int causal = 1;              // 1: row m at pos0 + m sees [max(0, pos0 + m - window + 1), pos0 + m]
+    int pos0 = 0;
+    int window = 0;
+    int ctx_lo = 0, ctx_hi = 0;  // draft: every row sees [ctx_lo, ctx_hi]
+    // rows appended by this kernel (own layer): positions [np0, np1); row of p: p < sp ? r_lo + p - np0 : r_hi + p - sp
+    int np0 = 0, np1 = 0, sp = 0, r_lo = 0, r_hi = 0;
+    uint16_t* out = nullptr;     // [M][Hq * hd] bf16
+    float* part = nullptr;       // scratch
+    size_t part_floats = 0;
+    int* counters = nullptr;     // zero between launches
+    int n_counters = 0;
+};
+size_t attn_part_floats_needed(const Attn& a);
+hipError_t launch_attention(const Attn& a, hipStream_t st);
+
+hipError_t launch_argmax_accept(const float* logits, int k, int V, const int32_t* tokens, float* part_val,
+                                int* part_idx, int nb, int32_t* out_tokens, int32_t* n_acc, int32_t* argmax_out,
+                                hipStream_t st);
+int argmax_blocks(int V);
+hipError_t launch_steer(float* logits, int k, int V, const int32_t* tok, const float* add, hipStream_t st);
+
+}  // namespace bvf

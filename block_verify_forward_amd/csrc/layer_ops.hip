@@ -1,0 +1,693 @@
+// gfx950 kernels of the verify pass other than the weight-streaming GEMM: Q4_1 repack and debug
+// dequant, RoPE table, embedding gather, RMSNorm, QK-norm + RoPE + KV append, GQA block attention
+// over the per-layer KV planes, argmax + greedy accept.
+#include "bvf_impl.hpp"
+
+#include <algorithm>
+#include <cmath>
+
+namespace bvf {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes (each wave owns its own
+// LDS slice, so no workgroup barrier is needed; waves of a workgroup run different key ranges).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Q4_1 repack: canonical host blocks -> the column-tiled image the GEMM streams (one thread per
+// 32-weight block). Canonical block ([CARD], "Weights" row; byte order fixed by the header):
+// fp16 scale, fp16 min, 16 code bytes, code j < 16 in the low nibble of byte j, j + 16 in the high.
+// gu_mode: 0 plain (column col0 + n), 1 gate (tile n / 8, column n % 8), 2 up (column 8 + n % 8).
+// ---------------------------------------------------------------------------------------------
+__global__ void k_repack(const uint8_t* __restrict__ canon, int n_out, int nb, uint8_t* __restrict__ codes,
+                         uint8_t* __restrict__ sm, int G, int col0, int gu_mode) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)n_out * nb) return;
+    const int n = (int)(idx / nb), b = (int)(idx % nb);
+    const uint32_t* blk = (const uint32_t*)(canon + idx * 20);   // 20-byte blocks are 4-byte aligned
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) w[i] = blk[i];
+    int T, c;
+    if (gu_mode == 0) {
+        T = (col0 + n) >> 4;
+        c = (col0 + n) & 15;
+    } else {
+        T = n >> 3;
+        c = (n & 7) + (gu_mode == 2 ? 8 : 0);
+    }
+    const int g = b >> 2, j = b & 3;
+    const uint8_t* q8 = (const uint8_t*)&w[1];
+    for (int sub = 0; sub < 4; ++sub) {
+        uint32_t d = 0;
+        for (int e = 0; e < 8; ++e) {
+            const int kb = 8 * sub + e;
+            const uint32_t q = kb < 16 ? (q8[kb] & 15u) : (q8[kb - 16] >> 4);
+            d |= q << (4 * ((e >> 1) + 4 * (e & 1)));
+        }
+        ((uint32_t*)codes)[(((size_t)T * G + g) * 64 + sub * 16 + c) * 4 + j] = d;
+    }
+    ((uint32_t*)sm)[(((size_t)T * G + g) * 16 + c) * 4 + j] = w[0];   // scale | min << 16
+}
+
+// fp32 weights of one matrix from the packed image: weight = fma(scale, code, min), one rounding
+// of the exact value scale * code + min.
+__global__ void k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sm, int G, int tile0,
+                          int gu, int n_out, int n_in, float* __restrict__ out) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)n_out * n_in) return;
+    const int n = (int)(idx / n_in), k = (int)(idx % n_in);
+    const int T = gu ? (n >> 3) : tile0 + (n >> 4);
+    const int c = gu ? (n & 7) + (gu == 2 ? 8 : 0) : (n & 15);
+    const int g = k >> 7, j = (k >> 5) & 3, kb = k & 31, sub = kb >> 3, e = kb & 7;
+    const uint32_t d = ((const uint32_t*)codes)[(((size_t)T * G + g) * 64 + sub * 16 + c) * 4 + j];
+    const uint32_t q = (d >> (4 * ((e >> 1) + 4 * (e & 1)))) & 15u;
+    const uint32_t s = ((const uint32_t*)sm)[(((size_t)T * G + g) * 16 + c) * 4 + j];
+    const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(s & 0xffffu));
+    const float mn = (float)__builtin_bit_cast(_Float16, (uint16_t)(s >> 16));
+    out[idx] = fmaf(sc, (float)q, mn);
+}
+
+// RoPE table [max_ctx][hd / 2] of (cos, sin) of p * base^(-2i / hd), evaluated in double.
+__global__ void k_rope_table(float2* table, int max_ctx, int hd, double base) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int h = hd / 2;
+    if (idx >= (size_t)max_ctx * h) return;
+    const int p = (int)(idx / h), i = (int)(idx % h);
+    const double th = (double)p * pow(base, -2.0 * i / hd);
+    table[idx] = make_float2((float)cos(th), (float)sin(th));
+}
+
+// x[r][:] = E[token_r] * scale (fp32). fill_token >= 0: row 0 takes tokens[0], the other rows
+// fill_token (the draft block). Token ids outside [0, V) are clamped. ss (optional): per row and
+// 16-column tile, the sum of squares of x (what the next GEMM's folded RMSNorm reads).
+__global__ void k_embed(const int32_t* __restrict__ tokens, int fill_token, const uint16_t* __restrict__ E, int V,
+                        int H, float scale, float* __restrict__ x, float* __restrict__ ss) {
+    const int r = blockIdx.y;
+    int t = (fill_token >= 0 && r > 0) ? fill_token : tokens[fill_token >= 0 ? 0 : r];
+    t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;   // grid covers H exactly (H % 256 == 0 ... or masked)
+    const float v = i < H ? bf16_to_f32(E[(size_t)t * H + i]) * scale : 0.f;
+    if (i < H) x[(size_t)r * H + i] = v;
+    if (ss) {
+        float q = v * v;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) q += __shfl_xor(q, o);
+        if ((i & 15) == 0 && i < H) ss[(size_t)r * (H / 16) + i / 16] = q;
+    }
+}
+
+// ss[r][j] = sum of x[r][16 j .. 16 j + 15]^2
+__global__ void k_sumsq(const float* __restrict__ x, int ldx, int H, float* __restrict__ ss) {
+    const int r = blockIdx.y;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const float v = i < H ? x[(size_t)r * ldx + i] : 0.f;
+    float q = v * v;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) q += __shfl_xor(q, o);
+    if ((i & 15) == 0 && i < H) ss[(size_t)r * (H / 16) + i / 16] = q;
+}
+
+// out[r][i] = bf16(x[r][i] / sqrt(mean_i x[r][i]^2 + eps) * g[i]); one workgroup per row.
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int ldx, int H,
+                                                 const uint16_t* __restrict__ g, float eps, uint16_t* __restrict__ out,
+                                                 int ldo) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    const float* xr = x + (size_t)r * ldx;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += 256) ss = fmaf(xr[i], xr[i], ss);
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    ss = red[0] + red[1] + red[2] + red[3];
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int i = threadIdx.x; i < H; i += 256)
+        out[(size_t)r * ldo + i] = f32_to_bf16(xr[i] * inv * bf16_to_f32(g[i]));
+}
+
+// One wave per (row, head): per-head RMSNorm (optional), rotate-half RoPE at the row's position;
+// q heads go to q_out, k/v heads of an own layer are written into the plane at the position.
+__global__ __launch_bounds__(64) void k_rope_append(RopeAppend a) {
+    const int row = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
+    const int hd = a.hd, h2 = hd / 2;
+    const int p = row < a.split_row ? a.pos0 + row : a.pos1 + (row - a.split_row);
+    const float* src;
+    float* dst;
+    const uint16_t* gain;
+    const int qd = a.Hq * hd, kvd = a.nkv * hd;
+    if (head < a.Hq) {
+        if (row >= a.rows_q) return;
+        src = a.qkv + (size_t)row * a.ldq + head * hd;
+        dst = a.q_out + ((size_t)row * a.Hq + head) * hd;
+        gain = a.q_norm;
+    } else {
+        if (!a.own || row >= a.rows) return;
+        const int gh = head - a.Hq;
+        src = a.qkv + (size_t)row * a.ldq + qd + gh * hd;
+        float* prow = a.plane + (size_t)p * 2 * a.w;
+        dst = prow + gh * hd;
+        gain = a.k_norm;
+        const float* vs = a.qkv + (size_t)row * a.ldq + qd + kvd + gh * hd;
+        for (int i = lane; i < hd; i += 64) prow[a.w + gh * hd + i] = vs[i];
+    }
+    float lo[4], hi[4];
+    float ss = 0.f;
+    const int per = (h2 + 63) / 64;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int i = lane + 64 * t;
+        lo[t] = (t < per && i < h2) ? src[i] : 0.f;
+        hi[t] = (t < per && i < h2) ? src[i + h2] : 0.f;
+        ss = fmaf(lo[t], lo[t], fmaf(hi[t], hi[t], ss));
+    }
+    float inv = 1.f;
+    if (a.qk_norm) inv = 1.0f / sqrtf(wave_sum(ss) / (float)hd + a.eps);
+    const float2* rt = a.rope + (size_t)p * h2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int i = lane + 64 * t;
+        if (t >= per || i >= h2) continue;
+        float x0 = lo[t] * inv, x1 = hi[t] * inv;
+        if (a.qk_norm) {
+            x0 *= bf16_to_f32(gain[i]);
+            x1 *= bf16_to_f32(gain[i + h2]);
+        }
+        const float2 cs = rt[i];
+        dst[i] = x0 * cs.x - x1 * cs.y;
+        dst[i + h2] = x0 * cs.y + x1 * cs.x;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// GQA block attention, one kernel per layer ([PR2303] "What changes": a KV-shared layer reads its
+// owner's cache and appends nothing). A workgroup owns 16 query vectors (qv = m * Hg + head in the
+// group) of one KV head g and one chunk of keys:
+//   1. the 16 queries: per-head RMSNorm (sums of squares from the q|k|v GEMM's epilogue) and
+//      rotate-half RoPE at the row's position, into LDS;
+//   2. on an own layer, the chunk's new rows (the rows of this pass): K normalised and rotated, V
+//      copied, appended to the plane at their positions;
+//   3. each of the 4 waves runs 16 keys per step with fp32 MFMA (v_mfma_f32_16x16x4_f32):
+//      S = Q K^T, online softmax, O += P V (P through LDS to the A layout, V rows staged in LDS);
+//   4. the waves merge (max, sum, O) in LDS; the workgroup stores its chunk's partial at device
+//      scope and bumps the (q tile, head) arrival counter; the last chunk to arrive merges all
+//      chunks in order and writes bf16 O.
+// Row m (position pos(m)) sees keys [max(0, pos - window + 1), pos] (causal; window 0 = all) or,
+// in a draft block, [ctx_lo, ctx_hi].
+// ---------------------------------------------------------------------------------------------
+constexpr int kKeysPerStep = 16;
+
+struct AttnK {
+    const float* qkv;        // [rows][ldq] raw q | k | v (GEMM output)
+    const float* ss;         // [rows][ldq / 16] per-tile sums of squares of qkv
+    int ldq;
+    const uint16_t* q_norm;
+    const uint16_t* k_norm;
+    int qk_norm;
+    float eps;
+    const float2* rope;      // [max_ctx][hd / 2]
+    float* plane;            // own or owner's plane [max_ctx][2][w]
+    int w, own;
+    int M, Hq, nkv, Hg, NQ, n_qt;
+    int causal, pos0, window, ctx_lo, ctx_hi;
+    int np0, np1, sp, r_lo, r_hi;   // new rows: positions [np0, np1); row of p: p < sp ? r_lo + p - np0 : r_hi + p - sp
+    int key_lo, n_keys, spw, n_chunks;   // keys [key_lo, key_lo + n_keys); spw 16-key steps per wave
+    float* part;             // [n_qt][nkv][n_chunks][16][hd + 2] partials
+    int* counters;           // [n_qt * nkv]
+    uint16_t* out;           // [M][Hq * hd] bf16
+};
+
+__device__ __forceinline__ void row_range(const AttnK& a, int m, int& lo, int& hi) {
+    if (a.causal) {
+        hi = a.pos0 + m;
+        lo = (a.window > 0 && hi - a.window + 1 > 0) ? hi - a.window + 1 : 0;
+    } else {
+        lo = a.ctx_lo;
+        hi = a.ctx_hi;
+    }
+}
+
+// sum of squares of a head (hd columns from column c0 of row r) from the per-tile partials
+__device__ __forceinline__ float head_ss(const AttnK& a, int r, int c0, int hd) {
+    float q = 0.f;
+    const float* p = a.ss + (size_t)r * (a.ldq / 16) + c0 / 16;
+    for (int i = 0; i < hd / 16; ++i) q += p[i];
+    return q;
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attention(AttnK a) {
+    constexpr int NDT = HD / 16;
+    constexpr int H2 = HD / 2;
+    __shared__ float Qs[16][HD + 4];
+    __shared__ float Vs[4][kKeysPerStep][HD];      // V staging; reused for the workgroup merge
+    __shared__ float Ps[4][16][17];
+    __shared__ float MLs[4][16][2];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int chunk = blockIdx.x % a.n_chunks;
+    const int g = (blockIdx.x / a.n_chunks) % a.nkv;
+    const int qt = blockIdx.x / (a.n_chunks * a.nkv);
+    const int col = lane & 15, grp = lane >> 4;
+    const int qd = a.Hq * HD;
+    const int chunk_keys = 4 * a.spw * kKeysPerStep;
+    const int c0 = a.key_lo + chunk * chunk_keys;
+    const int c1 = min(a.key_lo + a.n_keys, c0 + chunk_keys);
+    const size_t prow = (size_t)2 * a.w;
+
+    // 1. queries of this tile, normalised and rotated, into LDS (one wave per 4 qvs)
+    for (int i = wave; i < 16; i += 4) {
+        const int qv = qt * 16 + i;
+        if (qv >= a.NQ) {
+            for (int d = lane; d < HD; d += 64) Qs[i][d] = 0.f;
+            continue;
+        }
+        const int m = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
+        const float* src = a.qkv + (size_t)m * a.ldq + h * HD;
+        const float inv = a.qk_norm ? 1.0f / sqrtf(head_ss(a, m, h * HD, HD) / (float)HD + a.eps) : 1.f;
+        const float2* rt = a.rope + (size_t)(a.pos0 + m) * H2;
+        for (int d = lane; d < H2; d += 64) {
+            float x0 = src[d] * inv, x1 = src[d + H2] * inv;
+            if (a.qk_norm) {
+                x0 *= bf16_to_f32(a.q_norm[d]);
+                x1 *= bf16_to_f32(a.q_norm[d + H2]);
+            }
+            const float2 cs = rt[d];
+            Qs[i][d] = x0 * cs.x - x1 * cs.y;
+            Qs[i][d + H2] = x0 * cs.y + x1 * cs.x;
+        }
+    }
+    // 2. new rows inside this chunk (own layer): K normalised + rotated, V copied, into the plane
+    if (a.own) {
+        const int p_lo = max(c0, a.np0), p_hi = min(c1, a.np1);
+        for (int p = p_lo + wave; p < p_hi; p += 4) {
+            const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
+            const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
+            const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
+            float* dst = a.plane + (size_t)p * prow + g * HD;
+            const float inv = a.qk_norm ? 1.0f / sqrtf(head_ss(a, r, qd + g * HD, HD) / (float)HD + a.eps) : 1.f;
+            const float2* rt = a.rope + (size_t)p * H2;
+            for (int d = lane; d < H2; d += 64) {
+                float x0 = ks[d] * inv, x1 = ks[d + H2] * inv;
+                if (a.qk_norm) {
+                    x0 *= bf16_to_f32(a.k_norm[d]);
+                    x1 *= bf16_to_f32(a.k_norm[d + H2]);
+                }
+                const float2 cs = rt[d];
+                dst[d] = x0 * cs.x - x1 * cs.y;
+                dst[d + H2] = x0 * cs.y + x1 * cs.x;
+                dst[a.w + d] = vs[d];
+                dst[a.w + d + H2] = vs[d + H2];
+            }
+        }
+    }
+    __threadfence_block();
+    __syncthreads();
+
+    // 3. this wave's keys
+    int lo_r[4], hi_r[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int qv = qt * 16 + 4 * grp + r;
+        if (qv < a.NQ) row_range(a, qv / a.Hg, lo_r[r], hi_r[r]);
+        else { lo_r[r] = 1; hi_r[r] = 0; }
+    }
+    const float scale = 1.0f / sqrtf((float)HD);
+    floatx4 o[NDT];
+#pragma unroll
+    for (int d = 0; d < NDT; ++d) o[d] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
+    const int w0 = c0 + wave * a.spw * kKeysPerStep;
+    const int w1 = min(c1, w0 + a.spw * kKeysPerStep);
+    for (int k0 = w0; k0 < w1; k0 += kKeysPerStep) {
+        for (int idx = lane; idx < kKeysPerStep * HD / 4; idx += 64) {
+            const int kk = idx / (HD / 4), d4 = idx % (HD / 4);
+            const int key = k0 + kk;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (key < w1) v = *(const float4*)(a.plane + key * prow + a.w + g * HD + 4 * d4);
+            *(float4*)&Vs[wave][kk][4 * d4] = v;
+        }
+        const int key_b = k0 + col;
+        const bool kb_live = key_b < w1;
+        const float* krow = a.plane + (kb_live ? key_b : w0) * prow + g * HD;
+        floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int t = 0; t < HD / 16; ++t) {
+            const int d = 16 * t + 4 * grp;
+            const float4 qa = *(const float4*)&Qs[col][d];
+            const float4 kb = kb_live ? *(const float4*)(krow + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, kb.x, sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, kb.y, sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.z, kb.z, sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.w, kb.w, sacc, 0, 0, 0);
+        }
+        const int key = k0 + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = (key >= lo_r[r] && key <= hi_r[r] && key < w1) ? sacc[r] * scale : -INFINITY;
+            float mx = v;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float m_new = fmaxf(m_run[r], mx);
+            const float alpha = (m_run[r] == -INFINITY) ? 0.f : expf(m_run[r] - m_new);
+            const float pv = (v == -INFINITY) ? 0.f : expf(v - m_new);
+            float ps = pv;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off);
+            l_run[r] = l_run[r] * alpha + ps;
+            m_run[r] = m_new;
+#pragma unroll
+            for (int d = 0; d < NDT; ++d) o[d][r] *= alpha;
+            Ps[wave][4 * grp + r][col] = pv;
+        }
+        wave_sync();
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const float pa = Ps[wave][col][4 * st + grp];
+#pragma unroll
+            for (int d = 0; d < NDT; ++d)
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vs[wave][4 * st + grp][16 * d + col], o[d], 0, 0, 0);
+        }
+        wave_sync();
+    }
+
+    // 4. merge the four waves in LDS (Vs becomes Os[wave][qv][d])
+    __syncthreads();
+    float* Os = &Vs[0][0][0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int qvl = 4 * grp + r;
+#pragma unroll
+        for (int d = 0; d < NDT; ++d) Os[((size_t)wave * 16 + qvl) * HD + 16 * d + col] = o[d][r];
+        if (col == 0) {
+            MLs[wave][qvl][0] = m_run[r];
+            MLs[wave][qvl][1] = l_run[r];
+        }
+    }
+    __syncthreads();
+    const size_t tile_base = ((size_t)qt * a.nkv + g) * a.n_chunks;
+    float* part = a.part + (tile_base + chunk) * 16 * (HD + 2);
+    for (int idx = tid; idx < 16 * HD; idx += 256) {
+        const int qvl = idx / HD, d = idx % HD;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, MLs[w][qvl][0]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float mw = MLs[w][qvl][0];
+            const float e = mw == -INFINITY ? 0.f : expf(mw - mx);
+            num += e * Os[((size_t)w * 16 + qvl) * HD + d];
+            den += e * MLs[w][qvl][1];
+        }
+        __hip_atomic_store(part + (size_t)qvl * (HD + 2) + d, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+            __hip_atomic_store(part + (size_t)qvl * (HD + 2) + HD, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + (size_t)qvl * (HD + 2) + HD + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // 5. the last chunk of this (q tile, head) merges all chunks in chunk order
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ int last;
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(&a.counters[qt * a.nkv + g], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == a.n_chunks - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    const float* base = a.part + tile_base * 16 * (HD + 2);
+    for (int idx = tid; idx < 16 * HD; idx += 256) {
+        const int qvl = idx / HD, d = idx % HD;
+        const int qv = qt * 16 + qvl;
+        if (qv >= a.NQ) continue;
+        float mx = -INFINITY;
+        for (int c = 0; c < a.n_chunks; ++c)
+            mx = fmaxf(mx, __hip_atomic_load(base + ((size_t)c * 16 + qvl) * (HD + 2) + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        float num = 0.f, den = 0.f;
+        for (int c0i = 0; c0i < a.n_chunks; c0i += 8) {
+            float pm[8], pl[8], po[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = c0i + i;
+                const float* pc = base + ((size_t)c * 16 + qvl) * (HD + 2);
+                const bool ok = c < a.n_chunks;
+                pm[i] = ok ? __hip_atomic_load(pc + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
+                pl[i] = ok ? __hip_atomic_load(pc + HD + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+                po[i] = ok ? __hip_atomic_load(pc + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float e = pm[i] == -INFINITY ? 0.f : expf(pm[i] - mx);
+                num += e * po[i];
+                den += e * pl[i];
+            }
+        }
+        const int m = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
+        a.out[(size_t)m * qd + (size_t)h * HD + d] = f32_to_bf16(num / den);
+    }
+    if (tid == 0) __hip_atomic_store(&a.counters[qt * a.nkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------------------------
+// argmax (first index of the maximum, NaN never wins) and the greedy longest-prefix accept
+// ([CARD], "How it is used"; [PR2236], the acceptance tool).
+// ---------------------------------------------------------------------------------------------
+constexpr int kArgmaxSpan = 4096;
+
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+    // (v, i) beats (bv, bi) if v is a number and (bv is not, or v > bv, or v == bv and i < bi)
+    if (v != v) return;
+    if (bi < 0 || bv != bv || v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+__global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict__ logits, int V, int nb,
+                                                        float* __restrict__ pv, int* __restrict__ pi) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int b = blockIdx.x, row = blockIdx.y;
+    const int lo = b * kArgmaxSpan, hi = min(V, lo + kArgmaxSpan);
+    const float* lr = logits + (size_t)row * V;
+    float bv = 0.f;
+    int bi = -1;
+    for (int i = lo + threadIdx.x; i < hi; i += 256) better(bv, bi, lr[i], i);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (oi >= 0) better(bv, bi, ov, oi);
+    }
+    if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        bv = sv[0];
+        bi = si[0];
+        for (int w = 1; w < 4; ++w) if (si[w] >= 0) better(bv, bi, sv[w], si[w]);
+        pv[(size_t)row * nb + b] = bv;
+        pi[(size_t)row * nb + b] = bi;
+    }
+}
+
+__global__ __launch_bounds__(64) void k_accept(const float* __restrict__ pv, const int* __restrict__ pi, int nb, int k,
+                                               const int32_t* __restrict__ tokens, int32_t* __restrict__ out_tokens,
+                                               int32_t* __restrict__ n_acc, int32_t* __restrict__ argmax_out) {
+    __shared__ int y[kMaxRows];
+    const int lane = threadIdx.x;
+    for (int row = 0; row < k; ++row) {
+        float bv = 0.f;
+        int bi = -1;
+        for (int b = lane; b < nb; b += 64) if (pi[(size_t)row * nb + b] >= 0) better(bv, bi, pv[(size_t)row * nb + b], pi[(size_t)row * nb + b]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            if (oi >= 0) better(bv, bi, ov, oi);
+        }
+        if (lane == 0) y[row] = bi < 0 ? 0 : bi;
+    }
+    __syncthreads();
+    if (lane == 0) {
+        if (argmax_out) for (int r = 0; r < k; ++r) argmax_out[r] = y[r];
+        if (tokens) {
+            int acc = 0;
+            while (acc < k - 1 && tokens[acc + 1] == y[acc]) ++acc;
+            for (int i = 0; i < acc; ++i) out_tokens[i] = tokens[i + 1];
+            out_tokens[acc] = y[acc];
+            n_acc[0] = acc;
+        }
+    }
+}
+
+__global__ void k_steer(float* logits, int k, int V, const int32_t* tok, const float* add) {
+    const int i = threadIdx.x;
+    if (i < k) {
+        const int t = tok[i];
+        if (t >= 0 && t < V) logits[(size_t)i * V + t] += add[i];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_repack_q4_1(const uint8_t* canon, int n_out, int n_in, uint8_t* codes, uint8_t* sm, int G, int col0,
+                              int gu_mode, hipStream_t st) {
+    const int nb = n_in / 32;
+    const size_t n = (size_t)n_out * nb;
+    hipLaunchKernelGGL(k_repack, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, canon, n_out, nb, codes, sm, G,
+                       col0, gu_mode);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q4_1(const WMat& w, int tile0, int gu, int n_out, float* out, hipStream_t st) {
+    const size_t n = (size_t)n_out * w.K;
+    hipLaunchKernelGGL(k_dequant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, w.codes, w.sm, w.G, tile0, gu,
+                       n_out, w.K, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2* table, int max_ctx, int hd, double base, hipStream_t st) {
+    const size_t n = (size_t)max_ctx * (hd / 2);
+    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, table, max_ctx, hd, base);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed(const int32_t* tokens, int fill_token, int rows, const uint16_t* embed, int V, int H,
+                        float scale, float* x, float* ss, hipStream_t st) {
+    hipLaunchKernelGGL(k_embed, dim3((H + 255) / 256, rows), dim3(256), 0, st, tokens, fill_token, embed, V, H, scale,
+                       x, ss);
+    return hipGetLastError();
+}
+
+hipError_t launch_sumsq(const float* x, int ldx, int rows, int H, float* ss, hipStream_t st) {
+    hipLaunchKernelGGL(k_sumsq, dim3((H + 255) / 256, rows), dim3(256), 0, st, x, ldx, H, ss);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float* x, int ldx, int rows, int H, const uint16_t* g, float eps, uint16_t* out, int ldo,
+                          hipStream_t st) {
+    hipLaunchKernelGGL(k_rmsnorm, dim3(rows), dim3(256), 0, st, x, ldx, H, g, eps, out, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_append(const RopeAppend& a, hipStream_t st) {
+    const int rows = a.rows > a.rows_q ? a.rows : a.rows_q;
+    hipLaunchKernelGGL(k_rope_append, dim3(rows, a.Hq + a.nkv), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+namespace {
+AttnK make_attn(const Attn& x) {
+    AttnK a{};
+    a.qkv = x.qkv;
+    a.ss = x.ss;
+    a.ldq = x.ldq;
+    a.q_norm = x.q_norm;
+    a.k_norm = x.k_norm;
+    a.qk_norm = x.qk_norm;
+    a.eps = x.eps;
+    a.rope = x.rope;
+    a.plane = x.plane;
+    a.w = x.w;
+    a.own = x.own;
+    a.M = x.M;
+    a.Hq = x.Hq;
+    a.nkv = x.nkv;
+    a.Hg = x.Hq / x.nkv;
+    a.NQ = x.M * a.Hg;
+    a.n_qt = (a.NQ + 15) / 16;
+    a.causal = x.causal;
+    a.pos0 = x.pos0;
+    a.window = x.window;
+    a.ctx_lo = x.ctx_lo;
+    a.ctx_hi = x.ctx_hi;
+    a.np0 = x.np0;
+    a.np1 = x.np1;
+    a.sp = x.sp;
+    a.r_lo = x.r_lo;
+    a.r_hi = x.r_hi;
+    int lo, hi;
+    if (x.causal) {
+        hi = x.pos0 + x.M - 1;
+        lo = (x.window > 0 && x.pos0 - x.window + 1 > 0) ? x.pos0 - x.window + 1 : 0;
+    } else {
+        lo = x.ctx_lo;
+        hi = x.ctx_hi;
+    }
+    // the new rows must lie inside the key range (they are appended by the chunk that holds them)
+    if (x.own && x.np1 > x.np0) {
+        lo = std::min(lo, x.np0);
+        hi = std::max(hi, x.np1 - 1);
+    }
+    a.key_lo = lo;
+    a.n_keys = hi - lo + 1;
+    // 16-key steps per wave: enough workgroups to spread the keys, few enough chunks to merge
+    const int steps = (a.n_keys + kKeysPerStep - 1) / kKeysPerStep;
+    const int want_wgs = 384;
+    int spw = 1;
+    while (spw < 64 && (long)((steps + 4 * spw - 1) / (4 * spw)) * a.n_qt * a.nkv > want_wgs) spw *= 2;
+    a.spw = spw;
+    a.n_chunks = (steps + 4 * spw - 1) / (4 * spw);
+    a.part = x.part;
+    a.counters = x.counters;
+    a.out = x.out;
+    return a;
+}
+}  // namespace
+
+size_t attn_part_floats_needed(const Attn& x) {
+    const AttnK a = make_attn(x);
+    return (size_t)a.n_qt * a.nkv * a.n_chunks * 16 * (x.hd + 2);
+}
+
+hipError_t launch_attention(const Attn& x, hipStream_t st) {
+    const AttnK a = make_attn(x);
+    if (attn_part_floats_needed(x) > x.part_floats || a.n_qt * a.nkv > x.n_counters) return hipErrorInvalidValue;
+    const int grid = a.n_chunks * a.nkv * a.n_qt;
+    switch (x.hd) {
+        case 64: hipLaunchKernelGGL(k_attention<64>, dim3(grid), dim3(256), 0, st, a); break;
+        case 128: hipLaunchKernelGGL(k_attention<128>, dim3(grid), dim3(256), 0, st, a); break;
+        case 256: hipLaunchKernelGGL(k_attention<256>, dim3(grid), dim3(256), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int argmax_blocks(int V) { return (V + kArgmaxSpan - 1) / kArgmaxSpan; }
+
+hipError_t launch_argmax_accept(const float* logits, int k, int V, const int32_t* tokens, float* part_val, int* part_idx,
+                                int nb, int32_t* out_tokens, int32_t* n_acc, int32_t* argmax_out, hipStream_t st) {
+    hipLaunchKernelGGL(k_argmax_partial, dim3(nb, k), dim3(256), 0, st, logits, V, nb, part_val, part_idx);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, st, part_val, part_idx, nb, k, tokens, out_tokens, n_acc,
+                       argmax_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_steer(float* logits, int k, int V, const int32_t* tok, const float* add, hipStream_t st) {
+    hipLaunchKernelGGL(k_steer, dim3(1), dim3(64), 0, st, logits, k, V, tok, add);
+    return hipGetLastError();
+}
+
+}  // namespace bvf

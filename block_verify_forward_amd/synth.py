@@ -137,12 +137,16 @@ def f16_bits(x64: np.ndarray) -> np.ndarray:
 
 
 def bf16_bits(x64: np.ndarray) -> np.ndarray:
-    """float64 -> bfloat16 bits, round to nearest even directly from float64 (normal range)."""
-    x = np.asarray(x64, dtype=np.float64)
-    m, e = np.frexp(x)                      # x = m * 2**e, 0.5 <= |m| < 1
-    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # 8 significant bits, ties to even
-    r = np.where(np.abs(x) < 2.0 ** -126, 0.0, r)   # draws never land there; flush for safety
-    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    """float64 -> bfloat16 bits, round to nearest even directly from float64 (normal range):
+    round the float64 significand to 8 bits (ties to even) on its bit pattern, then the value is
+    exact in float32 and its top 16 bits are the bfloat16."""
+    x0 = np.asarray(x64, dtype=np.float64)
+    x = np.ascontiguousarray(x0.reshape(-1))
+    u = x.view(np.uint64)
+    r = (u + (np.uint64((1 << 44) - 1) + ((u >> np.uint64(45)) & np.uint64(1)))) & ~np.uint64((1 << 45) - 1)
+    f = r.view(np.float64)
+    f = np.where(np.abs(x) < 2.0 ** -126, 0.0, f)   # draws never land there; flush for safety
+    return (f.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16).reshape(x0.shape)
 
 
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:
@@ -185,12 +189,27 @@ def q4_1_from_parts(codes: np.ndarray, scale: np.ndarray, mins: np.ndarray) -> n
     return img
 
 
+_CHUNK = 1 << 24
+
+
+def _chunked_bf16(draw, shape) -> np.ndarray:
+    """bf16 bits of a long float64 draw, drawn and rounded in chunks (the generator's sequence does
+    not depend on the chunking); keeps the float64 temporaries small."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for i in range(0, n, _CHUNK):
+        out[i:i + _CHUNK] = bf16_bits(draw(min(_CHUNK, n - i)))
+    return out.reshape(shape)
+
+
 def bf16_normal(seed: int, name: str, shape, std: float = 1.0) -> np.ndarray:
-    return bf16_bits(stream(seed, name).standard_normal(size=shape) * std)
+    g = stream(seed, name)
+    return _chunked_bf16(lambda n: g.standard_normal(size=n) * std, shape)
 
 
 def bf16_uniform(seed: int, name: str, shape, lo: float, hi: float) -> np.ndarray:
-    return bf16_bits(stream(seed, name).uniform(lo, hi, size=shape))
+    g = stream(seed, name)
+    return _chunked_bf16(lambda n: g.uniform(lo, hi, size=n), shape)
 
 
 def f32_normal(seed: int, name: str, shape) -> np.ndarray:
@@ -232,13 +251,32 @@ def make_weights(m: Model, seed: int = 0, with_head: bool = True) -> dict:
         d["q_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.q_norm", (hd,), 0.5, 1.5)
         d["k_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.k_norm", (hd,), 0.5, 1.5)
         out["layers"].append(d)
-    if with_head and m.vocab > 0:
-        out["embed"] = bf16_normal(seed, f"{m.name}.embed", (m.vocab, m.hidden))
+    if with_head and m.vocab > 0 and m.block_causal == 1:
+        out["embed"] = embedding_table(seed, m)
     out["final_norm"] = bf16_uniform(seed, f"{m.name}.final_norm", (m.hidden,), 0.5, 1.5)
     if m.block_causal == 0:
         T = len(m.tap_layers)
         out["fc"] = bf16_normal(seed, f"{m.name}.fc", (m.hidden, T * m.hidden), std=1.0 / np.sqrt(T * m.hidden))
         out["hidden_norm"] = bf16_uniform(seed, f"{m.name}.hidden_norm", (m.hidden,), 0.5, 1.5)
+    return out
+
+
+EMBED_ROWS_PER_STREAM = 16384
+
+
+def embedding_table(seed: int, m: Model, threads: int = 8) -> np.ndarray:
+    """The tied bf16 embedding/head table [V, H], N(0,1): row block b (16384 rows) is drawn from the
+    sub-stream '<model>.embed.<b>' so blocks can be drawn in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty((m.vocab, m.hidden), dtype=np.uint16)
+    blocks = range(0, m.vocab, EMBED_ROWS_PER_STREAM)
+
+    def one(r0):
+        r1 = min(m.vocab, r0 + EMBED_ROWS_PER_STREAM)
+        out[r0:r1] = bf16_normal(seed, f"{m.name}.embed.{r0 // EMBED_ROWS_PER_STREAM}", (r1 - r0, m.hidden))
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, blocks))
     return out
 
 

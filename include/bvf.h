@@ -1,0 +1,219 @@
+/*
+ * bvf.h -- C ABI of the MI355X (gfx950) batched verify forward for DFlash block speculative decoding.
+ *
+ * What the library computes (sources are web pages, cited by title and section):
+ *   [PR2303] engine PR #2303 "npu forward: Gemma4 verifies a draft in one batched pass; KV row width
+ *            per layer": the batched body runs all k drafted rows through every layer in one pass over
+ *            the weights ("What changes"); a KV-shared layer reads its owner's cache and appends
+ *            nothing; every row's logits are returned; KV row width is per layer (item 1);
+ *            commit_verify_rows keeps n of the k verified rows ("Proof": 3 + 2 = 5 positions held).
+ *   [CARD]   "FastFlowLM build: Nemotron-3.5-Bolt-E4B-DFlash-NPU2": Q4_1 weights (32-weight blocks,
+ *            scale + minimum, 5 bits per weight; "Weights" row), the draft's geometry ("Draft" row),
+ *            its taps ("Taps" row), the greedy longest-prefix accept ("How it is used").
+ *   [PR2236] engine PR #2236 "npu: a Gemma4 pack stops re-reading its weights every token;
+ *            tools/dflash_acceptance": weights packed once at load (section 1); the draft block
+ *            [token s, mask, ...] over tapped context rows, rows >= 1 through the target head
+ *            (section 2, the acceptance tool's header).
+ *
+ * Conventions
+ *   - Every pointer named d_* is device memory on the model's device; h_* is host memory. The caller
+ *     owns every pointer it passes. Host inputs are copied before the call returns.
+ *   - All device work is enqueued on the stream given at bvf_create; outputs are valid once that
+ *     stream has been synchronised. Calls on one model must not overlap (one stream, one caller).
+ *   - Every call validates its arguments and the model state before it enqueues anything: a
+ *     non-zero status means nothing was enqueued and no state changed. bvf_last_error() returns a
+ *     thread-local message for the last failing call on this thread.
+ *   - Numbers: residual stream fp32; GEMM inputs bf16 (round to nearest even); GEMM accumulation and
+ *     outputs fp32; K/V planes fp32; logits fp32; Q4_1 weights are dequantised exactly.
+ */
+#ifndef BVF_H
+#define BVF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BVF_OK = 0,
+    BVF_E_INVALID = 1,   /* an argument is out of range or inconsistent with the model */
+    BVF_E_STATE = 2,     /* the call does not fit the model's state (e.g. commit with no verify) */
+    BVF_E_CAPACITY = 3,  /* positions would exceed max_ctx, or a buffer is too small */
+    BVF_E_DEVICE = 4     /* a HIP runtime call failed */
+} bvf_status;
+
+enum { BVF_ATTN_SLIDING = 0, BVF_ATTN_FULL = 1 };
+
+/* Q4_1 matrices of a layer. The library fuses Q|K|V into one packed matrix and interleaves GATE and
+ * UP by 16-column tiles; each load call fills its part of the packed image. */
+enum { BVF_Q = 0, BVF_K = 1, BVF_V = 2, BVF_O = 3, BVF_GATE = 4, BVF_UP = 5, BVF_DOWN = 6 };
+
+/* bf16 tensors. */
+enum {
+    BVF_EMBED = 0,       /* [vocab][hidden]: tied embedding table and output head (target only) */
+    BVF_FINAL_NORM = 1,  /* [hidden] */
+    BVF_ATTN_NORM = 2,   /* per layer [hidden] */
+    BVF_MLP_NORM = 3,    /* per layer [hidden] */
+    BVF_Q_NORM = 4,      /* per layer [head_dim] */
+    BVF_K_NORM = 5,      /* per layer [head_dim] */
+    BVF_FC = 6,          /* draft only: [hidden][n_taps * hidden], fuses the tapped target rows */
+    BVF_HIDDEN_NORM = 7  /* draft only: [hidden], RMSNorm gain applied after fc */
+};
+
+typedef struct {
+    int32_t attn;        /* BVF_ATTN_SLIDING or BVF_ATTN_FULL */
+    int32_t n_kv_heads;  /* KV row width of the layer w = n_kv_heads * head_dim floats (K; V the same) */
+    int32_t head_dim;    /* multiple of 64, <= 256 */
+    int32_t window;      /* sliding layer: a row at position p sees keys [p - window + 1, p]; 0 = all */
+    int32_t ffn;         /* SwiGLU width */
+    int32_t kv_owner;    /* -1: the layer holds its own KV plane. Else the index of an earlier own
+                            layer of the same attention type and geometry whose plane it reads; the
+                            layer then has no K/V projection and appends nothing [PR2303]. */
+} bvf_layer_desc;
+
+typedef struct {
+    int32_t n_layers;
+    int32_t hidden;        /* multiple of 128 */
+    int32_t n_q_heads;     /* multiple of every layer's n_kv_heads */
+    int32_t vocab;         /* target: rows of the embedding/head table; draft: 0 */
+    int32_t max_ctx;       /* plane capacity in positions (cached context + rows in flight) */
+    int32_t qk_norm;       /* 1: per-head RMSNorm on q and k before RoPE */
+    int32_t block_causal;  /* 1: a verify model (rows causal, appended to the planes);
+                              0: a DFlash draft (block rows see each other and the context) */
+    int32_t draft_window;  /* draft: the block sees the last draft_window context rows; 0 = all */
+    int32_t n_taps;        /* target: layers whose outputs are tapped; draft: taps fused by fc */
+    const int32_t* tap_layers; /* target: n_taps zero-based layer ids, written in this order */
+    float rope_base;       /* rotate-half RoPE, pairs (i, i + head_dim/2), angle p * base^(-2i/hd) */
+    float rms_eps;         /* RMSNorm: x / sqrt(mean(x^2) + eps) * gain */
+    const bvf_layer_desc* layers;
+} bvf_model_desc;
+
+typedef struct bvf_model bvf_model;
+typedef struct bvf_snapshot bvf_snapshot;
+
+/* Thread-local message of the last failing call ("" if none). Never NULL. */
+const char* bvf_last_error(void);
+
+/* Device bytes the caller must provide to bvf_create for this descriptor (weights, KV planes,
+ * activations and scratch; 256-byte aligned). Returns 0 and sets the error for an invalid
+ * descriptor. No device call is made. */
+size_t bvf_arena_bytes(const bvf_model_desc* desc);
+
+/* Create a model inside the caller's device arena (at least bvf_arena_bytes(desc) bytes, 256-byte
+ * aligned, on the current device). hip_stream: the hipStream_t all work is enqueued on (NULL = the
+ * null stream). The arena is zero-filled; the descriptor is copied. */
+bvf_status bvf_create(const bvf_model_desc* desc, void* d_arena, size_t arena_bytes, void* hip_stream,
+                      bvf_model** out);
+void bvf_destroy(bvf_model* m);
+
+/* Load one Q4_1 matrix of a layer from its canonical host image (packed once; [PR2236] section 1):
+ * n_out rows of n_in/32 blocks of 20 bytes {fp16 scale, fp16 min, 16 code bytes}; code j < 16 in the
+ * low nibble of byte j, code j + 16 in the high nibble; weight = scale * code + min ([CARD],
+ * "Weights" row). n_in must be the matrix's input width (a multiple of 128), n_out its output width.
+ * BVF_K / BVF_V on a KV-shared layer are refused. */
+bvf_status bvf_load_q4_1(bvf_model* m, int32_t layer, int32_t matrix, const void* h_blocks, size_t bytes,
+                         int32_t n_out, int32_t n_in);
+
+/* Load a bf16 tensor (see the enum for shapes; layer ignored for model-wide tensors). n = elements. */
+bvf_status bvf_load_bf16(bvf_model* m, int32_t tensor, int32_t layer, const uint16_t* h, size_t n);
+
+/* Cached context of an own plane: h_kv [positions][2][w] fp32 (K then V per position, K already
+ * normalised and rotated). The same `positions` must be set on every own plane before a verify;
+ * bvf_set_positions then fixes the count. Refused on a shared layer. */
+bvf_status bvf_set_kv(bvf_model* m, int32_t layer, const float* h_kv, int64_t positions);
+bvf_status bvf_set_positions(bvf_model* m, int64_t positions);
+
+/* Per-layer KV bookkeeping [PR2303, "What changes" item 1]. kv_widths: w of each layer (a shared
+ * layer reports its owner's width). plane_floats: floats held by each layer's own plane (held
+ * positions x 2 x w; 0 on a shared layer). positions_held: positions held (same on every own plane).
+ * n must equal n_layers. */
+bvf_status bvf_kv_widths(const bvf_model* m, int64_t* h_out, int32_t n);
+bvf_status bvf_plane_floats(const bvf_model* m, int64_t* h_out, int32_t n);
+bvf_status bvf_positions_held(const bvf_model* m, int64_t* h_out);
+
+/* The batched verify [PR2303, "What changes"]: rows d_tokens[0..k) at positions P..P+k-1
+ * (P = positions held) go through every layer in one pass over the packed weights; a KV-shared layer
+ * reads its owner's plane. Writes every row's logits, d_logits_all [k][vocab] fp32, and, if d_taps is
+ * not NULL, the tapped layer outputs d_taps [k][n_taps][hidden] bf16. Appends k rows to every own
+ * plane (positions held = P + k) until bvf_commit_verify_rows cuts them back. 1 <= k <= 16. */
+bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, float* d_logits_all,
+                            uint16_t* d_taps);
+
+/* Graph replay of bvf_verify_batch (1) or direct launches (0, the default). With 1 the pass is
+ * captured once into a HIP graph (on a private stream) and replayed on the model's stream; the
+ * capture is reused while positions held, k and the three buffer pointers stay the same, and is
+ * taken again when any of them changes. Results are identical in both modes. */
+bvf_status bvf_set_graph_mode(bvf_model* m, int32_t on);
+
+/* Greedy longest-prefix accept ([CARD], "How it is used"; [PR2236], the acceptance tool): y_i is the
+ * first index of the maximum of row i of d_logits_all [k][vocab] (NaN never wins); the drafts are
+ * d_tokens[1..k); a = the largest j <= k-1 with d_tokens[m] == y_{m-1} for all 1 <= m <= j. Writes
+ * d_out_tokens[0..a] = d_tokens[1..a], y_a (the a accepted drafts and the target's own token), and
+ * d_n_accepted[0] = a. Device outputs; no host synchronisation. */
+bvf_status bvf_accept_greedy(bvf_model* m, const float* d_logits_all, int32_t k, const int32_t* d_tokens,
+                             int32_t* d_out_tokens, int32_t* d_n_accepted);
+
+/* Harness hook for seeded acceptance (not part of the method): d_logits_all[i][d_tok[i]] += d_add[i]. */
+bvf_status bvf_steer_logits(bvf_model* m, float* d_logits_all, int32_t k, const int32_t* d_tok,
+                            const float* d_add);
+
+/* Keep n (0 <= n <= k) of the k rows of the last verify on every own plane: positions held becomes
+ * P + n; shared planes stay empty [PR2303, "What changes" item 1, "Proof"]. Moves no data. Refused
+ * with BVF_E_STATE if no verify is pending or n > k. */
+bvf_status bvf_commit_verify_rows(bvf_model* m, int32_t n);
+
+/* Snapshot / restore of the held prefix of every own plane at its own width; shared planes stay
+ * empty [PR2303, "What changes" item 1]. The library allocates and owns the snapshot's device copy
+ * until bvf_snapshot_free. Restore refuses a snapshot whose layer count or widths differ. Both clear
+ * a pending verify. snapshot_floats: floats kept per layer (0 on shared layers). */
+bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out);
+bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s);
+bvf_status bvf_snapshot_floats(const bvf_snapshot* s, int64_t* h_out, int32_t n);
+void bvf_snapshot_free(bvf_snapshot* s);
+
+/* DFlash draft block forward ([CARD] "Draft", "Taps", "How it is used"; [PR2236] section 2):
+ * appends n_new context rows from their taps d_new_taps [n_new][n_taps][hidden] bf16 (fc, then
+ * RMSNorm with the hidden-norm gain, then K/V in every draft layer at positions s - n_new .. s - 1,
+ * s = the draft's new positions held), runs the block [d_last_token[0], mask x (block - 1)] (target
+ * embeddings times embedding_scale, positions s .. s + block - 1; rows see each other and the last
+ * draft_window context rows), the final norm, the target's head on rows 1 .. block-1 and writes their
+ * argmax to d_proposals [block - 1]. d_logits (optional) receives those rows' logits [block-1][vocab].
+ * 2 <= block <= 16, 0 <= n_new, n_new + block <= 16. block = 0 only appends the n_new (<= 16)
+ * context rows (prefill of the draft context); d_last_token and d_proposals may then be NULL. */
+bvf_status bvf_draft_block_forward(bvf_model* draft, const bvf_model* target, const uint16_t* d_new_taps,
+                                   int32_t n_new, const int32_t* d_last_token, int32_t block,
+                                   float embedding_scale, int32_t mask_token, int32_t* d_proposals,
+                                   float* d_logits);
+
+/* Kernel-level entry points (parity tests and measurement). */
+/* Dequantised fp32 weights of one loaded Q4_1 matrix, d_w [n_out][n_in]. */
+bvf_status bvf_q4_1_dequant(const bvf_model* m, int32_t layer, int32_t matrix, float* d_w);
+/* d_y [rows][n_out] fp32 = d_x [rows][n_in] bf16 times the matrix (the fused-matrix kernel, run on
+ * the one matrix's columns; GATE and UP give their own halves). 1 <= rows <= 16. */
+bvf_status bvf_q4_1_gemm(const bvf_model* m, int32_t layer, int32_t matrix, const uint16_t* d_x, int32_t rows,
+                         float* d_y);
+/* One verify layer (the kernels of bvf_verify_batch) over d_x [rows][hidden] fp32, in place, at
+ * positions P .. P + rows - 1 (P = positions held). An own layer writes its K/V rows into its plane
+ * at those positions; the positions held do not change. For layer-by-layer parity tests. */
+bvf_status bvf_layer_forward(bvf_model* m, int32_t layer, float* d_x, int32_t rows);
+/* Measurement: launches each GEMM class of the verify pass exactly as the pass does (same kernels,
+ * plans and epilogues, into the model's scratch) for every layer, `iters` times, between two HIP
+ * events recorded on the model's stream, and synchronises. Class 0 = fused q|k|v, 1 = o (+residual),
+ * 2 = gate|up (+SwiGLU), 3 = down (+residual), 4 = the bf16 head. h_ms[5]: average milliseconds per
+ * launch; h_bytes[5]: average weight bytes streamed per launch. Overwrites the scratch activations. */
+bvf_status bvf_time_gemms(bvf_model* m, int32_t rows, int32_t iters, float* h_ms, int64_t* h_bytes);
+/* Q4_1 bytes (packed image: 5 bits per weight) and bf16 head bytes one verify pass streams. */
+bvf_status bvf_pass_bytes(const bvf_model* m, int64_t* h_q4_1_bytes, int64_t* h_head_bytes);
+
+/* Host-only KV-plane arithmetic, exported for CPU tests of the state rules (no device call):
+ * floats of plane `plane` cut at `positions` with the per-plane width list per[0..n_per): plane i
+ * uses per[i], a plane past the end of the list uses per[n_per - 1] [PR2303, review
+ * "VERDICT at 4d10370: READY"]. Returns -1 for n_per < 1. */
+int64_t bvf_cut_floats(const int64_t* per, int32_t n_per, int32_t plane, int64_t positions);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BVF_H */

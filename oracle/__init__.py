@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
             "orc_threads": (I, []),
             "orc_attend": (None, [P, I, P, L64, P]),
             "orc_layer_forward": (None, [P, I, I, P, P, P]),
+            "orc_verify_embedded": (I, [P, P, I, P, P]),
+            "orc_draft_block_embedded": (I, [P, P, I, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -221,6 +223,17 @@ class Model:
             raise RuntimeError(f"oracle verify: status {rc}")
         return (lg, taps) if with_taps else lg
 
+    def verify_embedded(self, x0: np.ndarray, with_taps: bool = False):
+        """A verify whose rows enter as given fp32 residual rows x0 [k][H]."""
+        x0 = np.ascontiguousarray(x0, dtype=np.float32).reshape(-1, self.m.hidden)
+        k = x0.shape[0]
+        lg = np.empty((k, self.m.vocab), dtype=np.float32)
+        taps = np.empty((k, len(self.m.tap_layers), self.m.hidden), dtype=np.uint16) if with_taps else None
+        rc = lib().orc_verify_embedded(self.h, _p(x0), k, _p(lg), _p(taps))
+        if rc:
+            raise RuntimeError(f"oracle verify: status {rc}")
+        return (lg, taps) if with_taps else lg
+
     def commit_verify_rows(self, n: int) -> int:
         return int(lib().orc_commit_verify_rows(self.h, n))
 
@@ -260,6 +273,18 @@ class Model:
         if rc:
             raise RuntimeError(f"oracle draft block: status {rc}")
         return (props, lg) if with_logits else props
+
+
+def draft_block_embedded(draft: Model, target: Model, x0: np.ndarray):
+    """The draft block from given fp32 block rows x0 [B][H]; returns (proposals, logits [B-1][V])."""
+    x0 = np.ascontiguousarray(x0, dtype=np.float32).reshape(-1, draft.m.hidden)
+    B = x0.shape[0]
+    props = np.zeros(B - 1, dtype=np.int32)
+    lg = np.empty((B - 1, target.m.vocab), dtype=np.float32)
+    rc = lib().orc_draft_block_embedded(draft.h, target.h, B, _p(x0), _p(props), _p(lg))
+    if rc:
+        raise RuntimeError(f"oracle draft block: status {rc}")
+    return props, lg
 
 
 class Snapshot:

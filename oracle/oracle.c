@@ -503,14 +503,12 @@ static void head_logits(const orc_model* target, const uint16_t* final_norm, int
     free(a); free(t); free(y);
 }
 
-/* Run rows through every layer in layer-major order. taps: [m][n_taps][H] bf16 or NULL
- * ([CARD, "Taps" row]: zero-based layer outputs). */
-static void forward_rows(orc_model* md, const int* tokens, int m, const long* pos, float* logits,
-                         uint16_t* taps) {
+/* Run rows x0 [m][H] (fp32 residual rows) through every layer in layer-major order.
+ * taps: [m][n_taps][H] bf16 or NULL ([CARD, "Taps" row]: zero-based layer outputs). */
+static void forward_x(orc_model* md, const double* x0, int m, const long* pos, float* logits, uint16_t* taps) {
     const int H = md->hidden;
     double* x = malloc(sizeof(double) * (size_t)m * H);
-    for (int r = 0; r < m; r++)
-        for (int i = 0; i < H; i++) x[(size_t)r * H + i] = bf16_to_double(md->embed[(size_t)tokens[r] * H + i]);
+    memcpy(x, x0, sizeof(double) * (size_t)m * H);
     for (int l = 0; l < md->n_layers; l++) {
         target_layer(md, l, m, x, pos);
         for (int ti = 0; ti < md->n_taps; ti++) {
@@ -522,6 +520,34 @@ static void forward_rows(orc_model* md, const int* tokens, int m, const long* po
     }
     if (logits) head_logits(md, md->final_norm, m, x, logits);
     free(x);
+}
+
+/* The rows of the tied embedding table for the tokens. */
+static void forward_rows(orc_model* md, const int* tokens, int m, const long* pos, float* logits,
+                         uint16_t* taps) {
+    const int H = md->hidden;
+    double* x = malloc(sizeof(double) * (size_t)m * H);
+    for (int r = 0; r < m; r++)
+        for (int i = 0; i < H; i++) x[(size_t)r * H + i] = bf16_to_double(md->embed[(size_t)tokens[r] * H + i]);
+    forward_x(md, x, m, pos, logits, taps);
+    free(x);
+}
+
+/* A verify whose rows enter as given residual rows x0 [k][H] instead of token embeddings (the
+ * injected-embedding form of a batch). Test hook: it lets a test perturb the entry rows. */
+int orc_verify_embedded(orc_model* md, const float* x0, int k, float* logits_all, uint16_t* taps) {
+    if (k < 1) return 1;
+    if (md->held + k > md->max_ctx) return 3;
+    long* pos = malloc(sizeof(long) * k);
+    double* x = malloc(sizeof(double) * (size_t)k * md->hidden);
+    for (int r = 0; r < k; r++) pos[r] = md->held + r;
+    for (size_t i = 0; i < (size_t)k * md->hidden; i++) x[i] = x0[i];
+    forward_x(md, x, k, pos, logits_all, taps);
+    free(pos);
+    free(x);
+    md->held += k;
+    md->pending = k;
+    return 0;
 }
 
 /* One decode step: the token at position `held`; appends one position. */
@@ -695,11 +721,12 @@ int orc_draft_append(orc_model* dr, const uint16_t* taps, int n) {
     return 0;
 }
 
+static int draft_block_x(orc_model* dr, const orc_model* target, int B, double* x, int* proposals, float* logits);
+
 /* The block forward. Block size B (<= 16); proposals[B-1]; logits (optional) [B-1][V]. */
 int orc_draft_block(orc_model* dr, const orc_model* target, int B, int last_token, double embedding_scale,
                     int mask_token, int* proposals, float* logits) {
-    const int H = dr->hidden, Hq = dr->n_q_heads;
-    const long s = dr->held;
+    const int H = dr->hidden;
     if (B < 2 || B > 16) return 1;
     double* x = malloc(sizeof(double) * (size_t)B * H);
     for (int i = 0; i < B; i++) {
@@ -707,6 +734,22 @@ int orc_draft_block(orc_model* dr, const orc_model* target, int B, int last_toke
         for (int j = 0; j < H; j++)
             x[(size_t)i * H + j] = round_f32(bf16_to_double(target->embed[(size_t)tok * H + j]) * embedding_scale);
     }
+    return draft_block_x(dr, target, B, x, proposals, logits);
+}
+
+/* Test hook: the block forward from given block rows x0 [B][H] (fp32). */
+int orc_draft_block_embedded(orc_model* dr, const orc_model* target, int B, const float* x0, int* proposals,
+                             float* logits) {
+    if (B < 2 || B > 16) return 1;
+    double* x = malloc(sizeof(double) * (size_t)B * dr->hidden);
+    for (size_t i = 0; i < (size_t)B * dr->hidden; i++) x[i] = x0[i];
+    return draft_block_x(dr, target, B, x, proposals, logits);
+}
+
+/* The draft layers, final norm and target head over the block rows x [B][H] (consumed). */
+static int draft_block_x(orc_model* dr, const orc_model* target, int B, double* x, int* proposals, float* logits) {
+    const int H = dr->hidden, Hq = dr->n_q_heads;
+    const long s = dr->held;
     long lo = 0;
     if (dr->draft_window > 0 && s - dr->draft_window > 0) lo = s - dr->draft_window;
     for (int l = 0; l < dr->n_layers; l++) {

@@ -1,0 +1,510 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI (small and ragged shapes).
+
+Bars: dequantised weights, KV position counts, accepted lengths and emitted tokens bit-exact;
+logits rel-L1 <= 2e-3 per row (sum|g - o| / sum|o|); GEMM outputs and K/V planes to fp32
+accumulation-order tolerance."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from block_verify_forward_amd import bvf, synth
+from tests.util import golden, noise_floor, rel_l1
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 2e-3          # rel-L1 per row, bf16 inputs with fp32 accumulation
+GEMM_TOL = 2e-5           # rel-L1 per row of a single GEMM (fp32 vs fp64 accumulation order)
+
+
+def stack_tol(run_oracle, arrays):
+    """Whole-stack logits bar: the 2e-3 bar, or three times the oracle's own spread under
+    fp32-level perturbation of its inputs when one bf16 rounding flip already moves a row by more
+    (stacks of several layers with these weight distributions). run_oracle(arrays) -> logits."""
+    return max(LOGIT_TOL, 3.0 * noise_floor(run_oracle, arrays))
+
+
+def embed_rows(w, toks):
+    return synth.bf16_to_f32(w["embed"][np.asarray(toks)]).astype(np.float32)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    bvf.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def ragged_model(max_ctx=96):
+    """Shapes that leave ragged tiles and splits: hidden 384 (3 superblocks), FFN 640 (5)."""
+    layers = (synth.Layer(synth.ATTN_SLIDING, 1, 64, 12, 640, -1), synth.Layer(synth.ATTN_FULL, 2, 64, 0, 384, -1),
+              synth.Layer(synth.ATTN_SLIDING, 1, 64, 12, 640, 0))
+    return synth.Model("ragged", 3, 384, 4, 528, max_ctx, layers, tap_layers=(0, 2))
+
+
+def build_pair(m, P, seed=0):
+    w = synth.make_weights(m, seed)
+    kv = synth.make_kv(m, P, seed)
+    g = bvf.Model(m)
+    g.load_weights(w)
+    g.set_context(kv, P)
+    o = oracle.Model(m, w)
+    o.set_kv(kv, P)
+    return g, o, w, kv
+
+
+# ------------------------------------------------------------------------------------------
+# kernels
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("mk", [synth.tiny_two_width_model, ragged_model])
+def test_dequant_bit_exact(mk):
+    m = mk()
+    g, o, w, kv = build_pair(m, 4)
+    for l in range(m.n_layers):
+        for key, (n_out, n_in) in synth.layer_matrix_shapes(m, l).items():
+            out = torch.empty((n_out, n_in), dtype=torch.float32, device="cuda")
+            g.q4_1_dequant(l, bvf.MATRIX_IDS[key], out)
+            ref = oracle.q4_1_dequant(w["layers"][l][key], n_out, n_in)
+            assert np.array_equal(host(out), ref), f"layer {l} {key}"
+
+
+@pytest.mark.parametrize("rows", [1, 3, 8, 16])
+@pytest.mark.parametrize("mk", [synth.tiny_two_width_model, ragged_model])
+def test_q4_1_gemm_parity(mk, rows):
+    m = mk()
+    g, o, w, kv = build_pair(m, 4)
+    for l in range(m.n_layers):
+        for key, (n_out, n_in) in synth.layer_matrix_shapes(m, l).items():
+            x = synth.bf16_normal(rows, f"gemm.x.{l}.{key}", (rows, n_in))
+            y = torch.empty((rows, n_out), dtype=torch.float32, device="cuda")
+            g.q4_1_gemm(l, bvf.MATRIX_IDS[key], dev(x), rows, y)
+            ref = oracle.q4_1_matmul(w["layers"][l][key], n_out, n_in, x)
+            assert rel_l1(host(y), ref) < GEMM_TOL, f"layer {l} {key} rows {rows}"
+
+
+def test_q4_1_gemm_hand_off_diagonal():
+    """One nonzero weight at (n=5, k=40) of the tiny model's down projection input side."""
+    m = synth.tiny_model()
+    w = synth.make_weights(m)
+    W = np.zeros((256, 512), dtype=np.int64)
+    W[5, 40] = 3
+    nb = 512 // 32
+    w["layers"][0]["down"] = synth.q4_1_from_parts(W, np.full((256, nb), 0.25), np.zeros((256, nb)))
+    g = bvf.Model(m)
+    g.load_weights(w)
+    x = synth.bf16_normal(0, "hand.x", (2, 512))
+    y = torch.empty((2, 256), dtype=torch.float32, device="cuda")
+    g.q4_1_gemm(0, bvf.DOWN, dev(x), 2, y)
+    y = host(y)
+    xf = synth.bf16_to_f32(x)
+    assert np.all(y[:, 5] == np.float32(0.75) * xf[:, 40])
+    y[:, 5] = 0
+    assert not y.any()
+
+
+# ------------------------------------------------------------------------------------------
+# the verify pass
+# ------------------------------------------------------------------------------------------
+def run_verify(g, m, toks, with_taps=True):
+    k = len(toks)
+    lg = torch.empty((k, m.vocab), dtype=torch.float32, device="cuda")
+    taps = torch.empty((k, len(m.tap_layers), m.hidden), dtype=torch.int16, device="cuda") if with_taps else None
+    g.verify_batch(dev(toks), lg, taps)
+    return host(lg), (host(taps).view(np.uint16) if with_taps else None)
+
+
+def compare_taps(got, ref, tol):
+    a = synth.bf16_to_f32(got).astype(np.float64)
+    b = synth.bf16_to_f32(ref).astype(np.float64)
+    err = rel_l1(a.reshape(-1, a.shape[-1]), b.reshape(-1, b.shape[-1]))
+    print(f"taps rel-L1 {err:.2e}")
+    assert err < tol
+
+
+@pytest.mark.parametrize("mk, P, k", [(synth.tiny_model, 64, 8), (synth.tiny_two_width_model, 40, 8),
+                                      (synth.tiny_two_width_model, 0, 5), (ragged_model, 30, 16),
+                                      (ragged_model, 7, 1)])
+def test_verify_parity(mk, P, k):
+    m = mk()
+    g, o, w, kv = build_pair(m, P)
+    toks = synth.tokens(0, f"verify.{m.name}", k, m.vocab)
+    lg, taps = run_verify(g, m, toks)
+    rlg, rtaps = o.verify_batch(toks, with_taps=True)
+
+    def run_oracle(arrs):
+        x = oracle.Model(m, w)
+        x.set_kv(arrs[1:], P)
+        return x.verify_embedded(arrs[0])
+
+    err, tol = rel_l1(lg, rlg), stack_tol(run_oracle, [embed_rows(w, toks)] + kv)
+    print(f"logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    assert err < tol
+    if m.tap_layers:
+        compare_taps(taps, rtaps, tol)
+    assert g.positions_held() == o.held() == P + k
+    assert np.array_equal(g.plane_floats(), o.plane_floats())
+    assert np.array_equal(g.kv_widths(), o.kv_widths())
+    # greedy tokens agree wherever the top-2 margin is clear
+    for i in range(k):
+        top2 = np.sort(rlg[i])[-2:]
+        if top2[1] - top2[0] > 0.02 * np.sqrt(np.mean(rlg[i].astype(np.float64) ** 2)):
+            assert lg[i].argmax() == rlg[i].argmax()
+
+
+def test_verify_parity_config1_logits_tight():
+    """Config 1 (tiny Qwen3-style decoder, 64 cached positions, k = 8, seed 0): the rows agree to
+    fp32 accumulation order (far inside the 2e-3 bar)."""
+    m = synth.tiny_model()
+    g, o, w, kv = build_pair(m, 64)
+    toks = synth.tokens(0, "config1.tokens", 8, m.vocab)
+    lg, _ = run_verify(g, m, toks, with_taps=False)
+    rlg = o.verify_batch(toks)
+    err = rel_l1(lg, rlg)
+    print(f"config 1 logits rel-L1 {err:.2e}")
+    assert err < LOGIT_TOL
+
+
+@pytest.mark.parametrize("mk, P, k", [(synth.tiny_two_width_model, 40, 8), (ragged_model, 30, 16),
+                                      (synth.tiny_two_width_model, 3, 1)])
+def test_layer_by_layer_parity(mk, P, k):
+    """Teacher-forced: every layer gets the same input rows on both sides, so no error carries
+    from layer to layer. The layer's contribution (x_out - x_in) must agree per row."""
+    m = mk()
+    g, o, w, kv = build_pair(m, P)
+    for l in range(m.n_layers):
+        x = (synth.f32_normal(l, f"layer.x.{m.name}", (k, m.hidden)) * 3.0).astype(np.float32)
+        xg = dev(x)
+        g.layer_forward(l, xg, k)
+        xo = o.layer_forward(l, x, np.arange(P, P + k))
+        got = host(xg).astype(np.float64) - x
+        ref = xo.astype(np.float64) - x
+        err = rel_l1(got, ref)
+        print(f"layer {l}: contribution rel-L1 {err:.2e}")
+        assert err < LOGIT_TOL, f"layer {l}"
+
+
+# ------------------------------------------------------------------------------------------
+# accept
+# ------------------------------------------------------------------------------------------
+def accept_gpu(g, lg_dev, toks):
+    out = torch.zeros(len(toks), dtype=torch.int32, device="cuda")
+    na = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.accept_greedy(lg_dev, dev(toks), out, na)
+    a = int(host(na)[0])
+    return a, host(out)[: a + 1]
+
+
+def test_accept_constructed_mismatch_positions():
+    m = synth.tiny_model()
+    g = bvf.Model(m)
+    g.load_weights(synth.make_weights(m))
+    rng = np.random.default_rng(5)
+    k, V = 8, m.vocab
+    lg = rng.standard_normal((k, V)).astype(np.float32)
+    y = lg.argmax(axis=1)
+    for j in range(k):
+        toks = np.zeros(k, dtype=np.int32)
+        toks[0] = 3
+        toks[1:j + 1] = y[:j]
+        if j + 1 < k:
+            toks[j + 1] = (y[j] + 1) % V
+            toks[j + 2:] = y[j + 1:k - 1]
+        a, out = accept_gpu(g, dev(lg), toks)
+        ra, rout = oracle.accept_greedy(lg, toks)
+        assert a == ra == j
+        assert out.tolist() == rout.tolist()
+
+
+def test_accept_ties_and_nan():
+    m = synth.tiny_model()
+    g = bvf.Model(m)
+    g.load_weights(synth.make_weights(m))
+    lg = np.zeros((2, m.vocab), dtype=np.float32)
+    lg[0, 700] = lg[0, 300] = 5.0            # tie: the lower id wins
+    lg[0, 0] = np.nan                        # NaN never wins
+    lg[1, :] = np.nan                        # all NaN: id 0
+    toks = np.array([1, 300], dtype=np.int32)
+    a, out = accept_gpu(g, dev(lg), toks)
+    assert (a, out.tolist()) == (1, [300, 0])
+    assert oracle.accept_greedy(lg, toks)[0] == 1
+
+
+def test_accept_after_verify_and_steering():
+    m = synth.tiny_two_width_model()
+    g, o, w, kv = build_pair(m, 20)
+    toks = synth.tokens(0, "steer.toks", 8, m.vocab)
+    lg = torch.empty((8, m.vocab), dtype=torch.float32, device="cuda")
+    g.verify_batch(dev(toks), lg, None)
+    # steer: rows 0..2 get a bonus on the next draft, row 3 a penalty on its draft
+    a_target = 3
+    tok = np.array([toks[i + 1] for i in range(7)] + [0], dtype=np.int32)
+    add = np.array([1e4] * a_target + [-1e4] + [0.0] * 4, dtype=np.float32)
+    g.steer_logits(lg, dev(tok), dev(add))
+    a, out = accept_gpu(g, lg, toks)
+    ref = o.verify_batch(toks)
+    for i in range(8):
+        ref[i, tok[i]] += add[i]
+    ra, rout = oracle.accept_greedy(ref, toks)
+    assert a == ra == a_target
+    assert out[:a].tolist() == toks[1:a + 1].tolist()
+    assert out.tolist() == rout.tolist()
+
+
+# ------------------------------------------------------------------------------------------
+# commit / rollback / snapshot (per-layer widths, shared planes)
+# ------------------------------------------------------------------------------------------
+def test_commit_worked_case_and_next_step():
+    gc = golden("commit_worked_case")
+    m = synth.tiny_two_width_model()
+    g, o, w, kv = build_pair(m, gc["prefix"])
+    toks = synth.tokens(0, "commit.toks", gc["k"], m.vocab)
+    run_verify(g, m, toks, with_taps=False)
+    g.commit_verify_rows(gc["commit"])
+    assert g.positions_held() == gc["held_after"]
+    floats = g.plane_floats()
+    for l in range(m.n_layers):
+        assert floats[l] == (gc["held_after"] * 2 * m.kv_width(l) if m.own(l) else 0)
+    # the next pass equals a forward that only ever saw the accepted rows
+    nxt = synth.tokens(1, "commit.next", 3, m.vocab)
+    lg, _ = run_verify(g, m, nxt, with_taps=False)
+
+    def run_oracle(arrs):
+        x = oracle.Model(m, w)
+        x.set_kv(arrs[1:], gc["prefix"])
+        for t in toks[: gc["commit"]]:
+            x.step(int(t))
+        return x.verify_embedded(arrs[0])
+
+    arrs = [embed_rows(w, nxt)] + kv
+    assert rel_l1(lg, run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+
+
+@pytest.mark.parametrize("n", range(0, 9))
+def test_commit_every_n(n):
+    m = synth.tiny_two_width_model()
+    g, o, w, kv = build_pair(m, 24)
+    toks = synth.tokens(0, "commit_n.toks", 8, m.vocab)
+    run_verify(g, m, toks, with_taps=False)
+    g.commit_verify_rows(n)
+    assert g.positions_held() == 24 + n
+    nxt = synth.tokens(2, "commit_n.next", 4, m.vocab)
+    lg, _ = run_verify(g, m, nxt, with_taps=False)
+
+    def run_oracle(arrs):
+        x = oracle.Model(m, w)
+        x.set_kv(arrs[1:], 24)
+        for t in toks[:n]:
+            x.step(int(t))
+        return x.verify_embedded(arrs[0])
+
+    arrs = [embed_rows(w, nxt)] + kv
+    assert rel_l1(lg, run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+
+
+def test_commit_refusals_leave_state_unchanged():
+    m = synth.tiny_two_width_model()
+    g, o, w, kv = build_pair(m, 10)
+    with pytest.raises(bvf.BvfError) as e:
+        g.commit_verify_rows(0)
+    assert e.value.status == bvf.BVF_E_STATE
+    run_verify(g, m, np.array([1, 2, 3], dtype=np.int32), with_taps=False)
+    with pytest.raises(bvf.BvfError) as e:
+        g.commit_verify_rows(4)
+    assert e.value.status == bvf.BVF_E_STATE
+    assert g.positions_held() == 13
+    g.commit_verify_rows(3)
+    with pytest.raises(bvf.BvfError):
+        g.commit_verify_rows(1)
+    with pytest.raises(bvf.BvfError) as e:
+        run_verify(g, m, np.zeros(17, dtype=np.int32), with_taps=False)
+    assert e.value.status == bvf.BVF_E_INVALID
+    assert g.positions_held() == 13
+
+
+def test_capacity_refusal():
+    m = synth.tiny_model(max_ctx=70)
+    g, o, w, kv = build_pair(m, 64)
+    with pytest.raises(bvf.BvfError) as e:
+        run_verify(g, m, np.zeros(8, dtype=np.int32), with_taps=False)
+    assert e.value.status == bvf.BVF_E_CAPACITY
+    assert g.positions_held() == 64
+
+
+def test_snapshot_restore_per_layer_widths():
+    m = synth.tiny_two_width_model()
+    g, o, w, kv = build_pair(m, 18)
+    snap = g.snapshot_take()
+    assert snap.floats().tolist() == [18 * 2 * m.kv_width(l) if m.own(l) else 0 for l in range(m.n_layers)]
+    run_verify(g, m, synth.tokens(0, "snap.a", 6, m.vocab), with_taps=False)
+    g.commit_verify_rows(6)
+    g.restore(snap)
+    assert g.positions_held() == 18
+    assert np.array_equal(g.plane_floats(), o.plane_floats())
+    toks = synth.tokens(0, "snap.b", 5, m.vocab)
+    lg, _ = run_verify(g, m, toks, with_taps=False)
+
+    def run_oracle(arrs):
+        x = oracle.Model(m, w)
+        x.set_kv(arrs[1:], 18)
+        return x.verify_embedded(arrs[0])
+
+    arrs = [embed_rows(w, toks)] + kv
+    assert rel_l1(lg, run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+    # a snapshot of another geometry is refused
+    m2 = synth.tiny_model(max_ctx=m.max_ctx)
+    g2 = bvf.Model(m2)
+    with pytest.raises(bvf.BvfError) as e:
+        g2.restore(snap)
+    assert e.value.status == bvf.BVF_E_INVALID
+
+
+def test_shared_layers_read_owner_planes():
+    """Perturbing an owner's cached plane changes the logits; shared planes stay empty."""
+    m = synth.tiny_two_width_model()
+    g, o, w, kv = build_pair(m, 12)
+    toks = synth.tokens(0, "shared.toks", 4, m.vocab)
+    lg0, _ = run_verify(g, m, toks, with_taps=False)
+    assert all(g.plane_floats()[l] == 0 for l in range(m.n_layers) if not m.own(l))
+    kv2 = [None if a is None else a.copy() for a in kv]
+    kv2[3][:, 1] += 0.5                    # layer 3 owns layer 4's keys
+    g2, o2, _, _ = build_pair(m, 12)
+    g2.set_context(kv2, 12)
+    o2.set_kv(kv2, 12)
+    lg1, _ = run_verify(g2, m, toks, with_taps=False)
+
+    def run_oracle(arrs):
+        x = oracle.Model(m, w)
+        x.set_kv(arrs[1:], 12)
+        return x.verify_embedded(arrs[0])
+
+    arrs = [embed_rows(w, toks)] + kv2
+    tol = stack_tol(run_oracle, arrs)
+    assert rel_l1(lg1, run_oracle(arrs)) < tol
+    assert rel_l1(lg1, lg0) > 3 * tol
+
+
+# ------------------------------------------------------------------------------------------
+# DFlash draft block
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("window, n_ctx, n_new, block", [(0, 12, 4, 8), (6, 20, 3, 8), (0, 0, 8, 8), (0, 9, 1, 4),
+                                                     (0, 30, 0, 8)])
+def test_draft_block_parity(window, n_ctx, n_new, block):
+    """Context: n_ctx rows of cached draft K/V (set directly) plus n_new rows appended from taps;
+    then the block [17, mask x (block - 1)] and the target head on rows 1.."""
+    tm = synth.tiny_model(max_ctx=64)
+    tw = synth.make_weights(tm)
+    dm = synth.tiny_draft_model(max_ctx=64, window=window)
+    dmg = dataclasses.replace(dm, vocab=tm.vocab)      # the draft's logits scratch takes the target's vocab
+    dw = synth.make_weights(dm)
+    kvd = synth.make_kv(dm, n_ctx)
+    taps = synth.bf16_normal(0, "draft.taps", (n_new, len(dm.tap_layers), dm.hidden))
+    T = bvf.Model(tm)
+    T.load_weights(tw)
+    D = bvf.Model(dmg)
+    D.load_weights(dw)
+    D.set_context(kvd, n_ctx)
+    To = oracle.Model(tm, tw)
+    props = torch.zeros(block - 1, dtype=torch.int32, device="cuda")
+    lg = torch.empty((block - 1, tm.vocab), dtype=torch.float32, device="cuda")
+    last = dev(np.array([17], dtype=np.int32))
+    D.draft_block_forward(T, dev(taps) if n_new else None, n_new, last, block, 1.0, tm.vocab - 1, props, lg)
+    assert D.positions_held() == n_ctx + n_new
+
+    x0 = embed_rows(tw, [17] + [tm.vocab - 1] * (block - 1))
+
+    def run_oracle(arrs):
+        Do = oracle.Model(dm, dw)
+        Do.set_kv(arrs[1:], n_ctx)
+        if n_new:
+            Do.draft_append(taps)
+        return oracle.draft_block_embedded(Do, To, arrs[0])
+
+    rp, rlg = run_oracle([x0] + kvd)
+    glg = host(lg)
+    err, tol = rel_l1(glg, rlg), stack_tol(lambda a: run_oracle(a)[1], [x0] + kvd)
+    print(f"draft logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    assert err < tol
+    gp = host(props)
+    for i in range(block - 1):
+        top2 = np.sort(rlg[i])[-2:]
+        if top2[1] - top2[0] > 0.02 * np.sqrt(np.mean(rlg[i].astype(np.float64) ** 2)):
+            assert gp[i] == rp[i]
+
+
+def test_draft_append_only_then_block():
+    """block = 0 appends context rows only; a later block sees them like rows appended with a block."""
+    tm = synth.tiny_model(max_ctx=64)
+    tw = synth.make_weights(tm)
+    dm = synth.tiny_draft_model(max_ctx=64)
+    dmg = dataclasses.replace(dm, vocab=tm.vocab)
+    dw = synth.make_weights(dm)
+    taps = synth.bf16_normal(1, "draft.taps2", (20, len(dm.tap_layers), dm.hidden))
+    T = bvf.Model(tm)
+    T.load_weights(tw)
+    D = bvf.Model(dmg)
+    D.load_weights(dw)
+    D.set_positions(0)
+    D.draft_block_forward(T, dev(taps[:16]), 16, None, 0, 1.0, 0, None, None)
+    assert D.positions_held() == 16
+    props = torch.zeros(7, dtype=torch.int32, device="cuda")
+    lg = torch.empty((7, tm.vocab), dtype=torch.float32, device="cuda")
+    D.draft_block_forward(T, dev(taps[16:]), 4, dev(np.array([5], dtype=np.int32)), 8, 1.0, tm.vocab - 1, props, lg)
+    To = oracle.Model(tm, tw)
+
+    def run_oracle(arrs):
+        Do = oracle.Model(dm, dw)
+        Do.draft_append(taps)
+        return oracle.draft_block_embedded(Do, To, arrs[0])[1]
+
+    arrs = [embed_rows(tw, [5] + [tm.vocab - 1] * 7)]
+    assert rel_l1(host(lg), run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+
+
+# ------------------------------------------------------------------------------------------
+# graph replay
+# ------------------------------------------------------------------------------------------
+def test_graph_replay_matches_direct_launches():
+    """The captured pass replays bit-identically to direct launches, over several replays with
+    other device work in between, and is re-captured when the positions held change."""
+    m = synth.tiny_two_width_model()
+    g, o, w, kv = build_pair(m, 20)
+    toks = dev(synth.tokens(0, "graph.toks", 8, m.vocab))
+    ref = torch.empty((8, m.vocab), dtype=torch.float32, device="cuda")
+    g.verify_batch(toks, ref, None)
+    g.commit_verify_rows(0)
+    ref = host(ref)
+    g.set_graph_mode(True)
+    lg = torch.empty((8, m.vocab), dtype=torch.float32, device="cuda")
+    x = dev(synth.bf16_normal(0, "graph.x", (8, m.hidden)))
+    y = torch.empty((8, 2 * m.layers[0].n_kv_heads * 64 + 256), dtype=torch.float32, device="cuda")
+    for rep in range(4):
+        lg.fill_(float("nan"))
+        g.verify_batch(toks, lg, None)
+        g.commit_verify_rows(0)
+        assert np.array_equal(host(lg), ref), f"replay {rep}"
+        g.q4_1_gemm(0, bvf.Q, x, 8, y[:, :256])      # eager work between replays
+        torch.cuda.synchronize()
+    # new positions: the graph is captured again and still matches direct launches
+    g.verify_batch(toks, lg, None)
+    g.commit_verify_rows(3)
+    g.verify_batch(toks, lg, None)
+    got = host(lg)
+    g.commit_verify_rows(0)
+    g.set_graph_mode(False)
+    g.verify_batch(toks, lg, None)
+    assert np.array_equal(host(lg), got)

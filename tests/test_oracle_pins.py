@@ -585,3 +585,20 @@ def test_attention_ignores_positions_after_the_row():
     kv[0][10, 1] += 1.0
     om.set_kv(kv, 21)
     assert not np.array_equal(om.attend(0, q, 10), base)
+
+
+def test_embedded_entries_equal_token_entries():
+    """The injected-row hooks are the token paths with the embedding rows given explicitly."""
+    m, w, kv = _two_width(positions=5)
+    toks = synth.tokens(0, "pin.embedded", 4, m.vocab)
+    A = oracle.Model(m, w); A.set_kv(kv, 5)
+    B = oracle.Model(m, w); B.set_kv(kv, 5)
+    la, ta = A.verify_batch(toks, with_taps=True)
+    lb, tb = B.verify_embedded(synth.bf16_to_f32(w["embed"][toks]), with_taps=True)
+    assert np.array_equal(la, lb) and np.array_equal(ta, tb) and B.held() == 9
+    tm, dm, T, D, dw, taps = _draft_pair()
+    D.draft_append(taps)
+    p1, l1 = D.draft_block(T, 8, 3, 0.5, tm.vocab - 1, with_logits=True)
+    x0 = synth.bf16_to_f32(T._keep[2]["embed"][[3] + [tm.vocab - 1] * 7]) * np.float32(0.5)
+    p2, l2 = oracle.draft_block_embedded(D, T, x0)
+    assert np.array_equal(l1, l2) and np.array_equal(p1, p2)

@@ -74,3 +74,19 @@ def rel_l1(got: np.ndarray, ref: np.ndarray) -> float:
     num = np.abs(got - ref).sum(axis=1)
     den = np.abs(ref).sum(axis=1)
     return float(np.max(num / np.maximum(den, 1e-300)))
+
+
+def perturbed(kv_list, eps: float, seed: int):
+    """Cached K/V with a relative perturbation of size eps (float64 draw, rounded back to fp32)."""
+    rng = np.random.default_rng(seed)
+    return [None if x is None else (x.astype(np.float64) * (1.0 + eps * rng.standard_normal(x.shape))).astype(np.float32)
+            for x in kv_list]
+
+
+def noise_floor(run, arrays, eps: float = 1e-5, seeds=(1, 2, 3)) -> float:
+    """How far the oracle's own logits move when its fp32 inputs (entry rows, cached K/V) carry a
+    relative perturbation of eps: every bf16 rounding point in the stack can then flip by one step,
+    as it can between any two fp32 implementations that sum in different orders.
+    run(arrays) -> logits. Returns the largest rel-L1 over the seeds."""
+    base = run(arrays)
+    return max(rel_l1(run(perturbed(arrays, eps, s)), base) for s in seeds)
