@@ -209,9 +209,8 @@ __global__ __launch_bounds__(64) void k_rope_append(RopeAppend a) {
 //      copied, appended to the plane at their positions;
 //   3. each of the 4 waves runs 16 keys per step with fp32 MFMA (v_mfma_f32_16x16x4_f32):
 //      S = Q K^T, online softmax, O += P V (P through LDS to the A layout, V rows staged in LDS);
-//   4. the waves merge (max, sum, O) in LDS; the workgroup stores its chunk's partial at device
-//      scope and bumps the (q tile, head) arrival counter; the last chunk to arrive merges all
-//      chunks in order and writes bf16 O.
+//   4. the waves merge (max, sum, O) in LDS and the workgroup stores its chunk's partial;
+//      k_attn_combine then merges the chunks in chunk order and writes bf16 O.
 // Row m (position pos(m)) sees keys [max(0, pos - window + 1), pos] (causal; window 0 = all) or,
 // in a draft block, [ctx_lo, ctx_hi].
 // ---------------------------------------------------------------------------------------------
@@ -353,7 +352,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         const bool kb_live = key_b < w1;
         const float* krow = a.plane + (kb_live ? key_b : w0) * prow + g * HD;
         floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll
         for (int t = 0; t < HD / 16; ++t) {
             const int d = 16 * t + 4 * grp;
             const float4 qa = *(const float4*)&Qs[col][d];
@@ -422,53 +421,56 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             num += e * Os[((size_t)w * 16 + qvl) * HD + d];
             den += e * MLs[w][qvl][1];
         }
-        __hip_atomic_store(part + (size_t)qvl * (HD + 2) + d, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        part[(size_t)qvl * (HD + 2) + d] = num;
         if (d == 0) {
-            __hip_atomic_store(part + (size_t)qvl * (HD + 2) + HD, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(part + (size_t)qvl * (HD + 2) + HD + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            part[(size_t)qvl * (HD + 2) + HD] = mx;
+            part[(size_t)qvl * (HD + 2) + HD + 1] = den;
         }
     }
-    // 5. the last chunk of this (q tile, head) merges all chunks in chunk order
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    __shared__ int last;
-    if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(&a.counters[qt * a.nkv + g], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = old == a.n_chunks - 1;
-    }
-    __syncthreads();
-    if (!last) return;
-    const float* base = a.part + tile_base * 16 * (HD + 2);
-    for (int idx = tid; idx < 16 * HD; idx += 256) {
-        const int qvl = idx / HD, d = idx % HD;
-        const int qv = qt * 16 + qvl;
-        if (qv >= a.NQ) continue;
-        float mx = -INFINITY;
-        for (int c = 0; c < a.n_chunks; ++c)
-            mx = fmaxf(mx, __hip_atomic_load(base + ((size_t)c * 16 + qvl) * (HD + 2) + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        float num = 0.f, den = 0.f;
-        for (int c0i = 0; c0i < a.n_chunks; c0i += 8) {
-            float pm[8], pl[8], po[8];
+}
+
+// Merge of the chunks of one (q tile, KV head): one 64-thread block per (query vector, 64 dims);
+// every thread reads its column of all chunks at once and sums them in chunk order.
+template <int HD>
+__global__ __launch_bounds__(64) void k_attn_combine(AttnK a) {
+    constexpr int MAXC = 64;
+    __shared__ float wgt[MAXC];
+    __shared__ float inv_den;
+    const int dgroups = HD / 64;
+    const int dg = blockIdx.x % dgroups;
+    const int qvl = (blockIdx.x / dgroups) % 16;
+    const int tile = blockIdx.x / (dgroups * 16);            // qt * nkv + g
+    const int g = tile % a.nkv, qt = tile / a.nkv;
+    const int qv = qt * 16 + qvl;
+    if (qv >= a.NQ) return;
+    const int lane = threadIdx.x;
+    const int nc = a.n_chunks;
+    const float* base = a.part + (size_t)tile * nc * 16 * (HD + 2) + (size_t)qvl * (HD + 2);
+    // chunk weights e^(m_c - M) and the denominator (nc <= 64: one chunk per lane)
+    const float mc = lane < nc ? base[(size_t)lane * 16 * (HD + 2) + HD] : -INFINITY;
+    const float lc = lane < nc ? base[(size_t)lane * 16 * (HD + 2) + HD + 1] : 0.f;
+    float mx = mc;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = c0i + i;
-                const float* pc = base + ((size_t)c * 16 + qvl) * (HD + 2);
-                const bool ok = c < a.n_chunks;
-                pm[i] = ok ? __hip_atomic_load(pc + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
-                pl[i] = ok ? __hip_atomic_load(pc + HD + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-                po[i] = ok ? __hip_atomic_load(pc + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-            }
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float e = mc == -INFINITY ? 0.f : expf(mc - mx);
+    if (lane < MAXC) wgt[lane] = e;
+    // denominator summed in chunk order
+    float den = 0.f;
+    for (int c = 0; c < nc; ++c) den += __shfl(e, c) * __shfl(lc, c);
+    if (lane == 0) inv_den = 1.0f / den;
+    __syncthreads();
+    const int d = dg * 64 + lane;
+    float num = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += 16) {
+        float v[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float e = pm[i] == -INFINITY ? 0.f : expf(pm[i] - mx);
-                num += e * po[i];
-                den += e * pl[i];
-            }
-        }
-        const int m = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
-        a.out[(size_t)m * qd + (size_t)h * HD + d] = f32_to_bf16(num / den);
+        for (int i = 0; i < 16; ++i) v[i] = c0 + i < nc ? base[(size_t)(c0 + i) * 16 * (HD + 2) + d] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (c0 + i < nc) num += wgt[c0 + i] * v[i];
     }
-    if (tid == 0) __hip_atomic_store(&a.counters[qt * a.nkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int m = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
+    a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + d] = f32_to_bf16(num * inv_den);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -645,7 +647,9 @@ AttnK make_attn(const Attn& x) {
     const int steps = (a.n_keys + kKeysPerStep - 1) / kKeysPerStep;
     const int want_wgs = 384;
     int spw = 1;
-    while (spw < 64 && (long)((steps + 4 * spw - 1) / (4 * spw)) * a.n_qt * a.nkv > want_wgs) spw *= 2;
+    while (spw < 256 && ((long)((steps + 4 * spw - 1) / (4 * spw)) * a.n_qt * a.nkv > want_wgs ||
+                         (steps + 4 * spw - 1) / (4 * spw) > 64))
+        spw *= 2;
     a.spw = spw;
     a.n_chunks = (steps + 4 * spw - 1) / (4 * spw);
     a.part = x.part;
@@ -663,11 +667,22 @@ size_t attn_part_floats_needed(const Attn& x) {
 hipError_t launch_attention(const Attn& x, hipStream_t st) {
     const AttnK a = make_attn(x);
     if (attn_part_floats_needed(x) > x.part_floats || a.n_qt * a.nkv > x.n_counters) return hipErrorInvalidValue;
+    if (a.n_chunks > 64) return hipErrorInvalidValue;
     const int grid = a.n_chunks * a.nkv * a.n_qt;
+    const int cgrid = a.n_qt * a.nkv * 16 * (x.hd / 64);
     switch (x.hd) {
-        case 64: hipLaunchKernelGGL(k_attention<64>, dim3(grid), dim3(256), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(k_attention<128>, dim3(grid), dim3(256), 0, st, a); break;
-        case 256: hipLaunchKernelGGL(k_attention<256>, dim3(grid), dim3(256), 0, st, a); break;
+        case 64:
+            hipLaunchKernelGGL(k_attention<64>, dim3(grid), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k_attn_combine<64>, dim3(cgrid), dim3(64), 0, st, a);
+            break;
+        case 128:
+            hipLaunchKernelGGL(k_attention<128>, dim3(grid), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k_attn_combine<128>, dim3(cgrid), dim3(64), 0, st, a);
+            break;
+        case 256:
+            hipLaunchKernelGGL(k_attention<256>, dim3(grid), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k_attn_combine<256>, dim3(cgrid), dim3(64), 0, st, a);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
