@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="direct launches instead of the captured pass")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a plain fp32 copy kernel (neg) of this many MiB three times first: the known-size "
+                         "dispatch that scales HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: this benchmark runs the verify pass on one GPU only; "
@@ -133,6 +136,16 @@ def main():
         g.set_graph_mode(True)
     torch.cuda.synchronize()
     log(f"loaded and packed on the GPU in {time.time() - t0:.1f} s; arena {g.arena.numel() / 2**30:.2f} GiB")
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: 3 x neg over {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
 
     k, V, H, T = args.k, m.vocab, m.hidden, len(m.tap_layers)
     toks_h = synth.tokens(args.seed, "bench.tokens", k, V)

@@ -71,6 +71,7 @@ struct bvf_model {
     std::vector<Layer> L;
     hipStream_t st = nullptr;
     int device = 0;
+    int n_cu = 256;          // compute units of the device (GEMM planning)
     uint8_t* arena = nullptr;
     size_t arena_bytes = 0;
     uint16_t *embed = nullptr, *final_norm = nullptr, *fc = nullptr, *hidden_norm = nullptr;
@@ -326,6 +327,7 @@ GemmLaunch gemm_for(const bvf_model* m, const Mat& mat, int epi) {
     g.partial_floats = kPartialFloats;
     g.counters = m->counters;
     g.n_counters = kCounters;
+    g.n_cu = m->n_cu;
     return g;
 }
 
@@ -351,6 +353,7 @@ hipError_t launch_head(const bvf_model* target, const uint16_t* A, int rows, flo
     g.partial_floats = kPartialFloats;
     g.counters = scratch_owner->counters;
     g.n_counters = kCounters;
+    g.n_cu = scratch_owner->n_cu;
     if (xsrc) {
         g.xsrc = xsrc; g.ldx = target->d.hidden; g.ss_in = scratch_owner->ss_x; g.n_ss = target->d.hidden / kTile;
         g.gain = gain; g.eps = scratch_owner->d.rms_eps;
@@ -442,6 +445,10 @@ bvf_status bvf_create(const bvf_model_desc* desc, void* d_arena, size_t arena_by
     m->arena_bytes = arena_bytes;
     m->st = (hipStream_t)hip_stream;
     hipError_t e = hipGetDevice(&m->device);
+    if (e == hipSuccess) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, m->device) == hipSuccess && n > 0) m->n_cu = n;
+    }
     if (e == hipSuccess) e = hipMemsetAsync(d_arena, 0, need, m->st);
     for (auto& pr : m->rope_tables)
         if (e == hipSuccess) e = launch_rope_table(pr.second, m->d.max_ctx, pr.first, (double)m->d.rope_base, m->st);
@@ -757,6 +764,7 @@ bvf_status bvf_draft_block_forward(bvf_model* dr, const bvf_model* tg, const uin
         g.n_run_tiles = g.w.n_tiles;
         g.A = d_new_taps; g.lda = T * H; g.M = n_new; g.y = dr->fcout; g.ldy = H;
         g.partial = dr->partial; g.partial_floats = kPartialFloats; g.counters = dr->counters; g.n_counters = kCounters;
+        g.n_cu = dr->n_cu;
         HIP_TRY(launch_gemm(g, st));
         HIP_TRY(launch_rmsnorm(dr->fcout, H, n_new, H, dr->hidden_norm, dr->d.rms_eps, ctx_rows, H, st));
     }

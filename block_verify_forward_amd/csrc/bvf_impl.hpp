@@ -59,16 +59,24 @@ struct GemmLaunch {
     const uint16_t* gain = nullptr;
     float eps = 0.f;
     float* ss_out = nullptr;     // STORE/RESID: per (row, output tile) sums of squares [M][n_run_tiles]
-    // launch plan (0 = choose)
-    int NT = 0, S = 0;
+    int n_cu = 0;                // compute units of the device (0: 256)
+    int force_S = 0, force_R = 0, force_ipw = 0, force_W = 0, force_KS = 0;   // a fixed plan (all > 0), else the planner's
 };
 
 struct GemmPlan {
-    int NT, S, sb_per_split, n_groups, items, grid;
-    size_t lds;   // dynamic LDS bytes (the workgroup's K range of the activation rows)
+    int S;              // K splits (-1: no plan fits)
+    int sb_per_split;   // superblocks of 128 K per split
+    int waves;          // waves per workgroup (4, 8 or 16)
+    int KS;             // K parts per tile inside a workgroup (summed in LDS)
+    int R;              // weight ring depth per wave (superblocks in flight)
+    int ring_slots;     // LDS slots per ring: min(R, superblocks per wave)
+    int grid;           // workgroups (all resident at once)
+    size_t lds;         // dynamic LDS bytes: weight rings, block sums, activation rows
 };
-constexpr size_t kLdsBudgetQ4 = 40 * 1024;
-constexpr size_t kLdsBudgetBf16 = 64 * 1024;
+constexpr size_t kLdsPerCu = 160 * 1024;            // gfx950 LDS per compute unit
+constexpr size_t kGemmLdsMax = 160 * 1024 - 1024;   // per workgroup (static LDS sits beside it)
+
+size_t gemm_lds_bytes(int fmt, int M, int sb, int waves, int ring, int KS);
 
 GemmPlan plan_gemm(const GemmLaunch& L);
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st);

@@ -8,17 +8,29 @@
 //
 // Q4_1 ([CARD], "Weights" row): weight = scale * code + min over 32-weight blocks. The dequant is
 // factored and exact: the code q is placed in a bf16 as 0x4180 | q << 3 = 16 + q (exact: at 16 the
-// bf16 step is 1/8), one MFMA per 32-weight block gives C' = sum_k x_k (16 + q_k), a second MFMA
-// against ones gives the block sum S = sum_k x_k, and the block contributes
-// scale * C' + (min - 16 scale) * S, i.e. exactly sum_k x_k (scale q_k + min). Products bf16 x bf16
-// are exact in fp32; accumulation is fp32. The offset 16 (not 128) keeps the cancellation small.
+// bf16 step is 1/8), one MFMA per 32-weight block gives C' = sum_k x_k (16 + q_k), and the block
+// contributes scale * C' + (min - 16 scale) * S with S = sum_k x_k, i.e. exactly
+// sum_k x_k (scale q_k + min). The S terms of the four blocks of a superblock are one fp32 MFMA
+// 16x16x4 (rows x blocks times blocks x columns) from block sums computed once per workgroup.
+// Products bf16 x bf16 are exact in fp32; accumulation is fp32. The offset 16 (not 128) keeps the
+// cancellation small.
 //
-// Work split: an item = one wave = NT column tiles (16 columns each) over a K range of
-// superblocks (128 K); items of one column group are consecutive and split K when the matrix has
-// few columns. Split-K partials are summed in a fixed order by the last wave to arrive (integer
-// arrival counter), so results are deterministic. Workgroup ids are remapped so consecutive
-// logical workgroups share an XCD (the hardware deals workgroups round-robin over the 8 XCDs).
+// Weight streaming: every wave owns a ring of R superblock slots in LDS, filled by direct
+// global->LDS loads (global_load_lds_dwordx4), R superblocks ahead of the MFMAs. The ring holds no
+// loop-carried registers, so the loads stay in flight across loop iterations; the wave waits with
+// s_waitcnt vmcnt for exactly the slot it consumes next (vector-memory loads complete in order).
+//
+// Work split: an item = one 16-column tile over one K range (split). A workgroup = 4 waves that
+// share one split; it stages the M activation rows of that K range in LDS once (RMSNorm folded in
+// when requested), then each wave streams its items (tiles wv, wv + WV, ...) through its ring.
+// Split-K partials are summed in a fixed order by the last wave to arrive (integer arrival
+// counter), so results are deterministic.
 #include "bvf_impl.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <unordered_map>
 
 namespace bvf {
 namespace {
@@ -26,6 +38,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kSlotQ4 = 1280;     // codes 1024 B + scale|min 256 B per (tile, superblock)
+constexpr int kSlotBf16 = 4096;   // 16 columns x 128 bf16
 
 struct KArgs {
     const uint8_t* codes;
@@ -42,7 +58,9 @@ struct KArgs {
     int ldt;
     float* partial;
     int* counters;
-    int S, sb_per_split, n_groups, n_cols;
+    int S, sb_per_split, n_tiles, n_cols;
+    int ring_slots;   // LDS slots per wave ring (min(R, superblocks per wave))
+    int KS;           // K parts per tile inside a workgroup (waves per tile)
     int half;   // STORE on a gate|up image: -1 all 16 columns, 0 the gate half, 1 the up half
     // RMSNorm folded into the staging of A (xsrc != nullptr): A = bf16(x * rinv * gain) with
     // rinv = 1 / sqrt(sum(ss_in[m][0 .. n_ss)) / K + eps)
@@ -69,359 +87,554 @@ __device__ __forceinline__ float half_hi(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
-// Logical workgroup id: consecutive ids live on the same XCD.
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-    const int q = n >> 3, r = n & 7, x = b & 7, i = b >> 3;
-    return x * q + (x < r ? x : r) + i;
+// (x & m) | o in one VALU op (m in a scalar register, o in a vector register).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+    return r;
 }
 
-template <int FMT, int NT>
-struct Frag;
+// Sum over the four lanes of a quad (lanes 4i .. 4i + 3) with DPP quad permutations.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+    return v;
+}
 
-template <int NT>
-struct Frag<W_Q4_1, NT> {
-    u32x4 cw[NT];
-    u32x4 sm[NT];
-};
+__device__ __forceinline__ float bf16x8_sum(const u32x4& o) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += __builtin_bit_cast(float, o[q] << 16) + __builtin_bit_cast(float, o[q] & 0xffff0000u);
+    return s;
+}
 
-template <int NT>
-struct Frag<W_BF16, NT> {
-    u32x4 bw[NT][4];
-};
+// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_lds() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
-// Weight bytes of superblock g for this lane (the only loads of the main loop).
-template <int FMT, int NT>
-__device__ __forceinline__ void load_frag(Frag<FMT, NT>& f, const KArgs& a, const int (&T)[NT], int g, int lane) {
-    const int c = lane & 15, sub = lane >> 4;
+// Direct loads of one (tile, superblock) of weights into a ring slot of this wave.
+template <int FMT>
+__device__ __forceinline__ void issue_slot(const KArgs& a, int tile_phys, int g, uint8_t* slot, int lane) {
     if constexpr (FMT == W_Q4_1) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const size_t base = (size_t)T[t] * a.G + g;
-            f.cw[t] = __builtin_nontemporal_load((const u32x4*)a.codes + base * 64 + lane);
-            f.sm[t] = __builtin_nontemporal_load((const u32x4*)a.sm + base * 16 + c);
-        }
+        const size_t base = (size_t)tile_phys * a.G + g;
+        __builtin_amdgcn_global_load_lds((const void*)((const u32x4*)a.codes + base * 64 + lane), (lds_void*)slot, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((const uint32_t*)a.sm + base * 64 + lane), (lds_void*)(slot + 1024), 4, 0, 0);
     } else {
-        const uint16_t* W = (const uint16_t*)a.codes;
+        const int c = lane & 15, sub = lane >> 4;
+        const uint16_t* row = (const uint16_t*)a.codes + (size_t)(tile_phys * kTile + c) * a.K + (size_t)g * kSuper + sub * 8;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const uint16_t* row = W + (size_t)(T[t] * kTile + c) * a.K + (size_t)g * kSuper + sub * 8;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) f.bw[t][j] = __builtin_nontemporal_load((const u32x4*)(row + j * 32));
-        }
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(row + j * 32), (lds_void*)(slot + j * 1024), 16, 0, 0);
     }
 }
+template <int FMT>
+constexpr int loads_per_slot() { return FMT == W_Q4_1 ? 2 : 4; }
 
-// One superblock: A (this lane's row, 4 blocks of 8 bf16) comes from the LDS copy of the rows.
-template <int FMT, int NT>
-__device__ __forceinline__ void compute_frag(const Frag<FMT, NT>& f, const uint16_t* As_row, bool a_live,
-                                             floatx4 (&acc)[NT]) {
+// One superblock from a ring slot. A (this lane's row, 4 blocks of 8 bf16) comes from the LDS
+// copy of the rows; lanes of rows >= M read the zero row.
+//
+// Q4_1: block j contributes scale_j * C'_j (bf16 MFMA + VALU FMAs) and the min terms of the four
+// blocks are one fp32 MFMA 16x16x4 into accm, fed by the block sums the staging step left in LDS
+// (this lane's value: S[m = lane % 16][j = lane / 16]) and MM[j][c] = min - 16 scale.
+template <int FMT>
+__device__ __forceinline__ void compute_slot(const uint8_t* slot, const uint16_t* As_row, float s_val, int lane,
+                                             floatx4& acc, floatx4& accm) {
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int c = lane & 15, sub = lane >> 4;
     u32x4 av4[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) av4[j] = a_live ? *(const u32x4*)(As_row + j * 32) : z;
+    for (int j = 0; j < 4; ++j) av4[j] = *(const u32x4*)(As_row + j * 32);
     if constexpr (FMT == W_Q4_1) {
-        // Block j's two MFMAs are issued before block j-1's scale/min FMAs, so the MFMA latency is
-        // covered while at most two blocks of results are live (sched barriers stop the scheduler
-        // from hoisting every MFMA of the pipeline, which costs registers and occupancy).
-        const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-        floatx4 bs[2], cc[2][NT];
+        const u32x4 cw = *(const u32x4*)(slot + lane * 16);
+        const u32x4 sm = *(const u32x4*)(slot + 1024 + c * 16);
+        const uint32_t smj = *(const uint32_t*)(slot + 1024 + (c * 4 + sub) * 4);   // column c, block sub
+        const float mm = fmaf(-16.f, half_lo(smj), half_hi(smj));
+        accm = __builtin_amdgcn_mfma_f32_16x16x4f32(s_val, mm, accm, 0, 0, 0);
+        // block j's MFMA is issued before block j-1's scale FMAs (covers the MFMA latency with two
+        // blocks of results live; the sched barriers keep the scheduler from hoisting all MFMAs)
+        floatx4 cc[2];
+        uint32_t O;   // bf16 pair 16 | 16 with the code bits clear; the nibble lands in mantissa bits 3..6
+        asm("v_mov_b32 %0, 0x41804180" : "=v"(O));
+        const uint32_t M4 = 0x00780078u;
 #pragma unroll
         for (int j = 0; j < 5; ++j) {
             if (j < 4) {
                 const bf16x8 av = __builtin_bit_cast(bf16x8, av4[j]);
-                bs[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ones), zero, 0, 0, 0);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const uint32_t w = f.cw[t][j];
-                    const uint32_t M4 = 0x00780078u, O = 0x41804180u;   // nibble -> mantissa bits 3..6
-                    const u32x4 b = {((w << 3) & M4) | O, ((w >> 1) & M4) | O, ((w >> 5) & M4) | O, ((w >> 9) & M4) | O};
-                    cc[j & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
-                }
+                const uint32_t w = cw[j];
+                const u32x4 b = {and_or(w << 3, M4, O), and_or(w >> 1, M4, O), and_or(w >> 5, M4, O), and_or(w >> 9, M4, O)};
+                cc[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
             }
             if (j > 0) {
                 const int jp = j - 1;
+                const float s = half_lo(sm[jp]);
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const uint32_t smv = f.sm[t][jp];
-                    const float s = half_lo(smv), mn = half_hi(smv);
-                    const float mp = fmaf(-16.f, s, mn);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(s, cc[jp & 1][t][r], fmaf(mp, bs[jp & 1][r], acc[t][r]));
-                }
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(s, cc[jp & 1][r], acc[r]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
+        (void)s_val; (void)accm; (void)c; (void)sub;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bf16x8 av = __builtin_bit_cast(bf16x8, av4[j]);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, f.bw[t][j]), acc[t], 0, 0, 0);
+            const u32x4 bw = *(const u32x4*)(slot + j * 1024 + lane * 16);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av4[j]), __builtin_bit_cast(bf16x8, bw), acc, 0, 0, 0);
         }
     }
 }
 
-template <int EPI, int NT>
-__device__ __forceinline__ void epilogue(const KArgs& a, const floatx4 (&acc)[NT], int group, int lane) {
+template <int EPI>
+__device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int tile, int lane) {
     const int c = lane & 15, sub = lane >> 4;
+    const int n = tile * kTile + c;
+    if constexpr (EPI == EPI_SWIGLU) {
+        // a gate|up tile holds gate columns in lanes c < 8 and the matching up columns in c + 8
+        floatx4 up;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int n = (group * NT + t) * kTile + c;
-        if constexpr (EPI == EPI_SWIGLU) {
-            // a gate|up tile holds gate columns in lanes c < 8 and the matching up columns in c + 8
-            floatx4 up;
+        for (int r = 0; r < 4; ++r) up[r] = __shfl_xor(acc[r], 8);
+        if (c < 8) {
+            const int nh = tile * 8 + c;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) up[r] = __shfl_xor(acc[t][r], 8);
-            if (c < 8) {
-                const int nh = (group * NT + t) * 8 + c;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = 4 * sub + r;
-                    if (m >= a.M) continue;
-                    const float g = acc[t][r];
-                    a.out[(size_t)m * a.ldo + nh] = f32_to_bf16(g / (1.0f + expf(-g)) * up[r]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * sub + r;
+                if (m >= a.M) continue;
+                const float g = acc[r];
+                a.out[(size_t)m * a.ldo + nh] = f32_to_bf16(g / (1.0f + expf(-g)) * up[r]);
             }
-            continue;
         }
-        float vout[4];
+        return;
+    }
+    float vout[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * sub + r;
+        vout[r] = 0.f;
+        if (m >= a.M) continue;
+        if constexpr (EPI == EPI_STORE) {
+            vout[r] = acc[r];
+            if (a.half < 0) {
+                a.y[(size_t)m * a.ldy + n] = acc[r];
+            } else if ((c >> 3) == a.half) {
+                a.y[(size_t)m * a.ldy + tile * 8 + (c & 7)] = acc[r];
+            }
+        } else {
+            const float v = a.y[(size_t)m * a.ldy + n] + acc[r];
+            vout[r] = v;
+            a.y[(size_t)m * a.ldy + n] = v;
+            if (a.taps) a.taps[(size_t)m * a.ldt + n] = f32_to_bf16(v);
+        }
+    }
+    if (a.ss_out) {
+        // per row, the sum of squares over this tile's 16 columns (lanes c = 0..15 of a row group)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            float q = vout[r] * vout[r];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) q += __shfl_xor(q, o);
             const int m = 4 * sub + r;
-            vout[r] = 0.f;
-            if (m >= a.M) continue;
-            if constexpr (EPI == EPI_STORE) {
-                vout[r] = acc[t][r];
-                if (a.half < 0) {
-                    a.y[(size_t)m * a.ldy + n] = acc[t][r];
-                } else if ((c >> 3) == a.half) {
-                    a.y[(size_t)m * a.ldy + (group * NT + t) * 8 + (c & 7)] = acc[t][r];
-                }
-            } else {
-                const float v = a.y[(size_t)m * a.ldy + n] + acc[t][r];
-                vout[r] = v;
-                a.y[(size_t)m * a.ldy + n] = v;
-                if (a.taps) a.taps[(size_t)m * a.ldt + n] = f32_to_bf16(v);
-            }
-        }
-        if (a.ss_out) {
-            // per row, the sum of squares over this tile's 16 columns (lanes c = 0..15 of a row group)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float q = vout[r] * vout[r];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) q += __shfl_xor(q, o);
-                const int m = 4 * sub + r;
-                if (c == 0 && m < a.M) a.ss_out[(size_t)m * (a.n_cols / kTile) + group * NT + t] = q;
-            }
+            if (c == 0 && m < a.M) a.ss_out[(size_t)m * (a.n_cols / kTile) + tile] = q;
         }
     }
 }
 
-// A workgroup = 4 waves = 4 column groups that share one K range (split). The workgroup copies
-// its K range of the M activation rows into LDS once; each wave then streams only weight bytes,
-// DEPTH superblocks ahead. At least 4 waves per SIMD (<= 128 registers) keep enough loads in
-// flight to cover HBM latency.
-template <int FMT, int EPI, int NT, int DEPTH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemm(KArgs a) {
-    extern __shared__ uint16_t As[];   // [M][lds_ld] bf16, lds_ld = sb_per_split * 128 + 8
+// Split-K: every wave stores its partial tile at device scope (sc1) as soon as the tile's K range
+// is done. After its whole stream the wave waits until its stores are performed, bumps the arrival
+// counter of each of its tiles, and for the tiles where it arrived last reads the S partials at
+// device scope and sums them in split order. No fence flushes a cache.
+__device__ __forceinline__ void splitk_store(const KArgs& a, const floatx4& acc, int tile, int split, int lane) {
+    const int c = lane & 15, sub = lane >> 4;
+    const int n = tile * kTile + c;
+    float* P = a.partial + (size_t)split * a.M * a.n_cols;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * sub + r;
+        if (m < a.M) __hip_atomic_store(P + (size_t)m * a.n_cols + n, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__device__ __forceinline__ floatx4 splitk_sum(const KArgs& a, int tile, int lane) {
+    const int c = lane & 15, sub = lane >> 4;
+    const int n = tile * kTile + c;
+    const size_t stride = (size_t)a.M * a.n_cols;
+    floatx4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * sub + r;
+        const float* src = a.partial + (size_t)(m < a.M ? m : 0) * a.n_cols + n;
+        float s = 0.f;
+        for (int sp0 = 0; sp0 < a.S; sp0 += 8) {   // loads issued eight at a time, summed in order
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = sp0 + i < a.S ? __hip_atomic_load(src + (size_t)(sp0 + i) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s += v[i];
+        }
+        acc[r] = s;
+    }
+    return acc;
+}
+
+// Workgroup b of W = blockDim / 64 waves: split b % S (cross-workgroup K split), index u = b / S
+// among the U = grid / S workgroups of that split. The W waves are T = W / KS tiles times KS parts
+// of the split's K range (wave w: tile slot w / KS, part w % KS). Item i of the workgroup covers
+// tiles (u + i U) T + 0 .. T - 1; the KS partial tiles of an item are summed in LDS in part order.
+// Rows >= M of the MFMA tile read arbitrary LDS data: they only feed output rows that are never
+// stored.
+template <int FMT, int EPI, int R>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemm(KArgs a) {
+    // dynamic LDS: [ring: W waves x ring_slots slots] [Q4_1: block sums S[sb_per_split * 4][16] fp32]
+    //              [A: M rows x lds_ld bf16] [KS > 1: partial tiles W x 64 lanes x 4 fp32]
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+    constexpr int SLOT = FMT == W_Q4_1 ? kSlotQ4 : kSlotBf16;
+    constexpr int LPS = loads_per_slot<FMT>();
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: loop control stays scalar
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int quad = wg / a.S;
-    const int split = wg - quad * a.S;
-    const int group = quad * 4 + wave;
-    if (quad * 4 >= a.n_groups) return;      // grid padding (whole workgroup, before any barrier)
-    const bool live = group < a.n_groups;
+    const int nw = blockDim.x >> 6;
+    const int nthr = blockDim.x;
+    const int KS = a.KS, T = nw / KS;
+    const int ts = wave / KS, kp = wave - ts * KS;
+    const int S = a.S;
+    const int split = blockIdx.x % S;
+    const int u = blockIdx.x / S;
+    const int U = gridDim.x / S;
     const int g0 = split * a.sb_per_split;
-    const int g1 = min(a.G, g0 + a.sb_per_split);
-    const int nsb = g1 - g0;
+    const int nsb = min(a.G, g0 + a.sb_per_split) - g0;
+    const int spk = (nsb + KS - 1) / KS;
+    const int kb0 = min(nsb, kp * spk), nkp = min(nsb, kb0 + spk) - kb0;   // this wave's superblocks
     const int lds_ld = a.sb_per_split * kSuper + 8;
+    uint8_t* ring = lds_raw + (size_t)wave * a.ring_slots * SLOT;
+    float* Ss = (float*)(lds_raw + (size_t)nw * a.ring_slots * SLOT);
+    uint16_t* As = (uint16_t*)((uint8_t*)Ss + (FMT == W_Q4_1 ? (size_t)a.sb_per_split * 64 * 4 : 0));
+    float* red = (float*)(As + (size_t)a.M * lds_ld);
 
-    int T[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) T[t] = a.tile0 + ((live ? group : 0) * NT + t) * a.tile_stride;
+    const int first = u * T;            // first tile of item 0
+    const int stride = U * T;           // tiles between items
+    const int items = first < a.n_tiles ? (a.n_tiles - 1 - first) / stride + 1 : 0;   // uniform in the workgroup
+    // this wave's valid items: tile = first + i stride + ts < n_tiles
+    const int my_items = first + ts < a.n_tiles ? (a.n_tiles - 1 - first - ts) / stride + 1 : 0;
+    const int total = my_items * nkp;   // superblocks this wave streams
 
-    // weight prefetch first, then the activation rows into LDS
-    Frag<FMT, NT> f[DEPTH];
-    if (live) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d)
-            if (d < nsb) load_frag<FMT, NT>(f[d], a, T, g0 + d, lane);
+    // bf16 activation rows: direct global->LDS copies (1 KB = 4 superblocks of one row per
+    // instruction), issued before the ring so the wave's first wait covers them
+    const int chunks = (nsb + 3) / 4;
+    if (!a.xsrc) {
+        for (int i = wave; i < a.M * chunks; i += nw) {
+            const int m = i / chunks, q = i - m * chunks;
+            const int e = q * 512 + lane * 8;   // element offset in the K range
+            if (e < nsb * kSuper)
+                __builtin_amdgcn_global_load_lds((const void*)(a.A + (size_t)m * a.lda + (size_t)g0 * kSuper + e),
+                                                 (lds_void*)(As + m * lds_ld + q * 512), 16, 0, 0);
+        }
     }
+    // RMSNorm folded in: the loads of the first batch (the sums of squares of the rows, and per
+    // thread piece p = 8 elements of K of up to 8 rows plus the gains) are issued before the ring,
+    // so they are not queued behind the weight stream
+    __shared__ float rinv_s[kMaxRows];
+    const int pieces = nsb * (kSuper / 8);
+    const int p0 = threadIdx.x;
+    const int rows0 = min(a.M, 8);
+    float4 xv[8][2];
+    u32x4 gv0 = {0u, 0u, 0u, 0u};
+    float sv[4][4];   // sums of squares of rows wave + nw r (r < 4), lanes lane + 64 t (t < 4)
     if (a.xsrc) {
-        // RMSNorm of the rows: rinv from the producer's per-tile sums of squares, then the scaled
-        // bf16 rows of this K range into LDS
-        __shared__ float rinv_s[kMaxRows];
-        for (int m = wave; m < a.M; m += 4) {
-            float ssum = 0.f;
-            for (int i = lane; i < a.n_ss; i += 64) ssum += a.ss_in[(size_t)m * a.n_ss + i];
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) ssum += __shfl_xor(ssum, o);
-            if (lane == 0) rinv_s[m] = 1.0f / sqrtf(ssum / (float)a.K + a.eps);
+        for (int r = 0; r < 4; ++r) {
+            const int m = wave + nw * r;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int i = lane + 64 * t;
+                sv[r][t] = m < a.M && i < a.n_ss ? a.ss_in[(size_t)m * a.n_ss + i] : 0.f;
+            }
+        }
+        if (p0 < pieces) {
+            const int k0 = g0 * kSuper + p0 * 8;
+            gv0 = *(const u32x4*)(a.gain + k0);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int m = r < rows0 ? r : rows0 - 1;
+                xv[r][0] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0);
+                xv[r][1] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0 + 4);
+            }
+        }
+    }
+    // fill the ring: the weight loads overlap the staging of the activation rows
+    int s_issue = 0, is_item = 0, is_g = 0;
+    for (; s_issue < R && s_issue < total; ++s_issue) {
+        issue_slot<FMT>(a, a.tile0 + (first + is_item * stride + ts) * a.tile_stride, g0 + kb0 + is_g, ring + s_issue * SLOT, lane);
+        if (++is_g == nkp) { is_g = 0; ++is_item; }
+    }
+
+    if (a.xsrc) {
+        // rinv from the producer's per-tile sums of squares (n_ss > 256 continues in a loop)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = wave + nw * r;
+            if (m >= a.M) break;
+            float q = (sv[r][0] + sv[r][1]) + (sv[r][2] + sv[r][3]);
+            for (int i = lane + 256; i < a.n_ss; i += 64) q += a.ss_in[(size_t)m * a.n_ss + i];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) q += __shfl_xor(q, o);
+            if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
         }
         __syncthreads();
-        const int per_row = nsb * (kSuper / 8);   // 8-element pieces per row
-        for (int idx = threadIdx.x; idx < a.M * per_row; idx += 256) {
-            const int m = idx / per_row, c8 = idx - m * per_row;
-            const int k0 = g0 * kSuper + c8 * 8;
-            const float4 x0 = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0);
-            const float4 x1 = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0 + 4);
-            const u32x4 gv = *(const u32x4*)(a.gain + k0);
-            const float r = rinv_s[m];
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            u32x4 o;
+        auto convert = [&](int p, int m0, int nrows, const u32x4& gv, const float4 (&xr)[8][2]) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float g_lo = __builtin_bit_cast(float, gv[q] << 16);
-                const float g_hi = __builtin_bit_cast(float, gv[q] & 0xffff0000u);
-                o[q] = (uint32_t)f32_to_bf16(xs[2 * q] * r * g_lo) | ((uint32_t)f32_to_bf16(xs[2 * q + 1] * r * g_hi) << 16);
+            for (int r = 0; r < 8; ++r) {
+                if (r >= nrows) break;
+                const int m = m0 + r;
+                const float rv = rinv_s[m];
+                const float xs[8] = {xr[r][0].x, xr[r][0].y, xr[r][0].z, xr[r][0].w, xr[r][1].x, xr[r][1].y, xr[r][1].z, xr[r][1].w};
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float g_lo = __builtin_bit_cast(float, gv[q] << 16);
+                    const float g_hi = __builtin_bit_cast(float, gv[q] & 0xffff0000u);
+                    o[q] = (uint32_t)f32_to_bf16(xs[2 * q] * rv * g_lo) | ((uint32_t)f32_to_bf16(xs[2 * q + 1] * rv * g_hi) << 16);
+                }
+                *(u32x4*)(As + m * lds_ld + p * 8) = o;
+                if constexpr (FMT == W_Q4_1) {
+                    // block sum of the 32 bf16 of block p / 4 (the quad of lanes holding its pieces)
+                    const float bs = quad_sum(bf16x8_sum(o));
+                    if ((p & 3) == 0) Ss[(p >> 2) * kTile + m] = bs;
+                }
             }
-            *(u32x4*)(As + m * lds_ld + c8 * 8) = o;
+        };
+        if (p0 < pieces) convert(p0, 0, rows0, gv0, xv);
+        // the remaining batches: rows 8.. of the first pieces, then further pieces
+        for (int p = p0; p < pieces; p += nthr) {
+            const int k0 = g0 * kSuper + p * 8;
+            const u32x4 gv = *(const u32x4*)(a.gain + k0);
+            for (int m0 = p == p0 ? 8 : 0; m0 < a.M; m0 += 8) {
+                const int nrows = min(8, a.M - m0);
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int m = m0 + (r < nrows ? r : nrows - 1);
+                    xv[r][0] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0);
+                    xv[r][1] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0 + 4);
+                }
+                convert(p, m0, nrows, gv, xv);
+            }
         }
     } else {
-        const int per_row = nsb * (kSuper / 8);   // 16-byte pieces per row
-        for (int idx = threadIdx.x; idx < a.M * per_row; idx += 256) {
-            const int m = idx / per_row, c16 = idx - m * per_row;
-            *(u32x4*)(As + m * lds_ld + c16 * 8) =
-                *(const u32x4*)(a.A + (size_t)m * a.lda + (size_t)g0 * kSuper + c16 * 8);
-        }
+        // this wave's activation copies have landed (they are older than its ring loads)
+        if (s_issue == R) wait_vm<LPS * R>();
+        else wait_vm<0>();
     }
     __syncthreads();
-    if (!live) return;
+    if (FMT == W_Q4_1 && !a.xsrc) {
+        // block sums S[b][m] = sum of the 32 bf16 of block b of row m < M (the copied rows; the
+        // normalised rows got theirs while being converted); the four pieces of a block sit in
+        // four consecutive lanes; eight rows' LDS reads are issued together
+        for (int p = threadIdx.x; p < pieces; p += nthr) {
+            for (int m0 = 0; m0 < a.M; m0 += 8) {
+                u32x4 o[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) o[r] = *(const u32x4*)(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float bs = quad_sum(bf16x8_sum(o[r]));
+                    if (m0 + r < a.M && (p & 3) == 0) Ss[(p >> 2) * kTile + m0 + r] = bs;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (items == 0) return;   // uniform in the workgroup
 
     const int m_a = lane & 15, sub = lane >> 4;
-    const bool a_live = m_a < a.M;
-    const uint16_t* As_row = As + (a_live ? m_a : 0) * lds_ld + sub * 8;
+    const uint16_t* As_row = As + (m_a < a.M ? m_a : 0) * lds_ld + sub * 8 + kb0 * kSuper;
+    const float* Ss_l = Ss + lane + 64 * kb0;   // superblock i of this wave's part: Ss_l[64 i]
 
-    floatx4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = (floatx4){0.f, 0.f, 0.f, 0.f};
-
-    int i = 0;
-    for (; i + 2 * DEPTH <= nsb; i += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            compute_frag<FMT, NT>(f[d], As_row + (i + d) * kSuper, a_live, acc);
-            load_frag<FMT, NT>(f[d], a, T, g0 + i + d + DEPTH, lane);
-        }
-    }
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-        if (i + d < nsb) {
-            compute_frag<FMT, NT>(f[d], As_row + (i + d) * kSuper, a_live, acc);
-            if (i + d + DEPTH < nsb) load_frag<FMT, NT>(f[d], a, T, g0 + i + d + DEPTH, lane);
-        }
-    }
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if (i + DEPTH + d < nsb) compute_frag<FMT, NT>(f[d], As_row + (i + DEPTH + d) * kSuper, a_live, acc);
-
-    if (a.S > 1) {
-        // Split-K hand-off without cache flushes: partials are stored at device scope (sc1), the
-        // wave waits until its stores are performed, then bumps the group's arrival counter; the
-        // last wave to arrive reads the partials at device scope and sums them in split order.
-        const int c = lane & 15;
-        float* P = a.partial + (size_t)split * a.M * a.n_cols;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int n = (group * NT + t) * kTile + c;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 4 * sub + r;
-                if (m < a.M) __hip_atomic_store(P + (size_t)m * a.n_cols + n, acc[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        int old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(&a.counters[group], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __shfl(old, 0);
-        if (old != a.S - 1) return;
-        // sum the splits in order; the device-scope loads are issued eight at a time
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int n = (group * NT + t) * kTile + c;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 4 * sub + r;
-                const int mm = m < a.M ? m : 0;
-                const float* src = a.partial + (size_t)mm * a.n_cols + n;
-                const size_t stride = (size_t)a.M * a.n_cols;
-                float s = 0.f;
-                for (int sp0 = 0; sp0 < a.S; sp0 += 8) {
-                    float v[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        v[i] = (sp0 + i < a.S && sp0 + i != split)
-                                   ? __hip_atomic_load(src + (size_t)(sp0 + i) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                   : 0.f;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (sp0 + i < a.S) s += (sp0 + i == split) ? acc[t][r] : v[i];
+    int s = 0;
+    uint32_t last = 0;   // split-K: bit i set where this wave arrived last on item i (reducer waves)
+    for (int it = 0; it < items; ++it) {
+        const int tile = first + it * stride + ts;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f}, accm = {0.f, 0.f, 0.f, 0.f};
+        if (it < my_items) {
+#pragma nounroll
+            for (int gi = 0; gi < nkp; ++gi, ++s) {
+                // younger slots in flight: s_issue - 1 - s (R - 1 in the steady state)
+                if (s_issue - s == R) wait_vm<LPS * (R - 1)>();
+                else wait_vm<0>();
+                const uint8_t* slot = ring + (s % R) * SLOT;
+                compute_slot<FMT>(slot, As_row + gi * kSuper, FMT == W_Q4_1 ? Ss_l[64 * gi] : 0.f, lane, acc, accm);
+                wait_lds();   // the slot's LDS reads have returned before the refill overwrites it
+                if (s_issue < total) {
+                    issue_slot<FMT>(a, a.tile0 + (first + is_item * stride + ts) * a.tile_stride, g0 + kb0 + is_g,
+                                    ring + (s_issue % R) * SLOT, lane);
+                    if (++is_g == nkp) { is_g = 0; ++is_item; }
+                    ++s_issue;
                 }
-                acc[t][r] = s;
             }
+            if constexpr (FMT == W_Q4_1) acc += accm;
         }
-        if (lane == 0) __hip_atomic_store(&a.counters[group], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (KS > 1) {
+            // the KS parts of each tile meet in LDS; part 0 sums them in part order
+            *(floatx4*)(red + ((size_t)wave * 64 + lane) * 4) = acc;
+            __syncthreads();
+            if (kp == 0) {
+                for (int q = 1; q < KS; ++q) acc += *(const floatx4*)(red + ((size_t)(wave + q) * 64 + lane) * 4);
+            }
+            __syncthreads();
+        }
+        if (kp != 0 || it >= my_items) continue;
+        if (S == 1) {
+            epilogue<EPI>(a, acc, tile, lane);
+        } else {
+            splitk_store(a, acc, tile, split, lane);
+        }
     }
-    epilogue<EPI, NT>(a, acc, group, lane);
+    if (S > 1 && kp == 0 && my_items > 0) {
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are performed
+        if (lane == 0) {
+            for (int it = 0; it < my_items; ++it)
+                if (__hip_atomic_fetch_add(&a.counters[first + it * stride + ts], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1)
+                    last |= 1u << it;
+        }
+        last = __shfl(last, 0);
+        for (int it = 0; it < my_items; ++it) {
+            if (!((last >> it) & 1u)) continue;
+            const int tile = first + it * stride + ts;
+            epilogue<EPI>(a, splitk_sum(a, tile, lane), tile, lane);
+            if (lane == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
-// One 16-column tile per wave; the pipeline is 3 (Q4_1: 8 weight registers per stage) or 2 (bf16:
-// 16 per stage) superblocks deep, which fits 128 registers without spills.
-template <int FMT, int EPI>
-hipError_t launch_nt(int NT, const KArgs& k, int grid, size_t lds, hipStream_t st) {
-    if (NT != 1) return hipErrorInvalidValue;
-    constexpr int D = FMT == W_Q4_1 ? 3 : 2;
-    hipLaunchKernelGGL((k_gemm<FMT, EPI, 1, D>), dim3(grid), dim3(256), lds, st, k);
+template <int FMT, int EPI, int R>
+hipError_t launch_r(const KArgs& k, int grid, int waves, size_t lds, hipStream_t st) {
+    static bool attr_set = false;   // raise the dynamic LDS limit once per instantiation
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_gemm<FMT, EPI, R>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)kGemmLdsMax);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_gemm<FMT, EPI, R>), dim3(grid), dim3(64 * waves), lds, st, k);
     return hipGetLastError();
+}
+
+template <int FMT, int EPI>
+hipError_t launch_fe(int R, const KArgs& k, int grid, int waves, size_t lds, hipStream_t st) {
+    switch (R) {
+        case 2: return launch_r<FMT, EPI, 2>(k, grid, waves, lds, st);
+        case 4: return launch_r<FMT, EPI, 4>(k, grid, waves, lds, st);
+        case 8: return launch_r<FMT, EPI, 8>(k, grid, waves, lds, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+size_t gemm_lds_bytes(int fmt, int M, int sb, int waves, int ring, int KS) {
+    const size_t slot = fmt == W_Q4_1 ? kSlotQ4 : kSlotBf16;
+    return (size_t)waves * ring * slot + (fmt == W_Q4_1 ? (size_t)sb * 256 : 0) + (size_t)M * ((size_t)sb * kSuper + 8) * 2 +
+           (KS > 1 ? (size_t)waves * 1024 : 0);
+}
+
+// Plan: choose the cross-workgroup K split S, the waves per workgroup W = T tiles x KS parts, the
+// ring depth R, the items per workgroup and the grid. Every workgroup of the grid must be resident
+// at once (one round: no tail). Cost estimate per launch: the activation staging (rounds of L2
+// loads when the RMSNorm is folded in), the weight stream (bytes at the HBM rate, the wave's
+// serial work per superblock, or its superblocks R at a time per memory latency), the in-LDS
+// reduction of the parts and the split-K hand-off.
 GemmPlan plan_gemm(const GemmLaunch& L) {
-    GemmPlan p{};
-    const int tiles = L.n_run_tiles, G = L.w.G;
-    const int NT = 1;
-    const int groups = tiles / NT;
-    const int quads = (groups + 3) / 4;
-    // LDS holds the workgroup's K range of the M rows: bounds the superblocks per split
-    const size_t budget = L.fmt == W_Q4_1 ? kLdsBudgetQ4 : kLdsBudgetBf16;
-    int sb_max = (int)((budget / (2 * (size_t)L.M) - 8) / kSuper);
-    if (sb_max < 1) sb_max = 1;
-    int S = L.S;
-    if (S == 0) {
-        const int target_waves = 2048;
-        S = (target_waves + groups - 1) / groups;
-        if (S > G) S = G;
-        if (S < 1) S = 1;
+    GemmPlan best{};
+    best.S = -1;
+    const int tiles = L.n_run_tiles, G = L.w.G, M = L.M;
+    const int cus = L.n_cu > 0 ? L.n_cu : 256;
+    const size_t slot_bytes = L.fmt == W_Q4_1 ? kSlotQ4 : kSlotBf16;
+    const double bytes = (double)tiles * G * slot_bytes;
+    const double hbm = 5.5e12, lat = 1.5e-6, per_sb = 0.25e-6, l2_round = 0.8e-6, handoff = 4.0e-6, reduce = 0.3e-6;
+    const bool norm = L.xsrc != nullptr;
+    double best_t = 1e30;
+    auto consider = [&](int Se, int sb, int W, int KS, int R, int ipw, bool forced) {
+        const int T = W / KS;
+        const int U = (tiles + T * ipw - 1) / (T * ipw);
+        const int spk = (sb + KS - 1) / KS;
+        const int ring = std::min(R, ipw * spk);
+        const size_t lds = gemm_lds_bytes(L.fmt, M, sb, W, ring, KS);
+        if (lds > kGemmLdsMax) return false;
+        const int wg_cu = (int)std::min<size_t>(16 / W, kLdsPerCu / lds);
+        if (wg_cu < 1) return false;
+        if (!forced && (long)Se * U > (long)cus * wg_cu) return false;   // not resident in one round
+        const double pieces = (double)sb * (kSuper / 8);
+        const double staging = norm ? (1.0 + std::ceil(pieces / (64.0 * W)) * std::ceil(M / 8.0)) * l2_round : 0.3e-6;
+        const double wsb = (double)ipw * spk;   // superblocks per wave
+        const double stream = lat + std::max({bytes / hbm, wsb * per_sb, std::ceil(wsb / R) * lat});
+        const double t = staging + stream + (KS > 1 ? ipw * reduce : 0.0) + (Se > 1 ? handoff : 0.0);
+        if (forced || t < best_t * 0.98) {
+            best_t = t;
+            best.S = Se;
+            best.sb_per_split = sb;
+            best.waves = W;
+            best.KS = KS;
+            best.R = R;
+            best.ring_slots = ring;
+            best.grid = Se * U;
+            best.lds = lds;
+        }
+        return true;
+    };
+    int prev_sb = -1;
+    for (int S = 1; S <= G && S <= 64; ++S) {
+        const int sb = (G + S - 1) / S;
+        if (sb == prev_sb) continue;
+        prev_sb = sb;
+        const int Se = (G + sb - 1) / sb;
+        if (Se > 1 && ((size_t)Se * M * tiles * kTile > L.partial_floats || tiles > L.n_counters)) continue;
+        for (int W : {4, 8, 16})
+            for (int KS = 1; KS <= W; KS *= 2)
+                for (int R : {8, 4, 2}) {
+                    if (L.fmt == W_BF16 && R == 8) continue;
+                    // the fewest items per workgroup for which the grid is resident
+                    for (int ipw = 1; ipw <= tiles && (Se == 1 || ipw <= 32); ++ipw)
+                        if (consider(Se, sb, W, KS, R, ipw, false)) break;
+                }
     }
-    int sb = (G + S - 1) / S;
-    if (sb > sb_max) sb = sb_max;
-    S = (G + sb - 1) / sb;
-    if (S > 1 && ((size_t)S * L.M * tiles * kTile > L.partial_floats || groups > L.n_counters)) S = -1;  // no fit
-    p.NT = NT;
-    p.S = S;
-    p.sb_per_split = sb;
-    p.n_groups = groups;
-    p.items = groups * (S > 0 ? S : 0);
-    // The grid is a multiple of 8 * S, so each XCD's contiguous range of logical workgroup ids holds
-    // whole column groups: all splits of a group run on one XCD (one L2).
-    p.grid = quads * (S > 0 ? S : 0);
-    if (S > 1) {
-        const int unit = 8 * S;
-        p.grid = (p.grid + unit - 1) / unit * unit;
+    if (L.force_S > 0 && L.force_R > 0 && L.force_ipw > 0 && L.force_W > 0 && L.force_KS > 0 && L.force_W % L.force_KS == 0) {
+        const int sb = (G + L.force_S - 1) / L.force_S;
+        const int Se = (G + sb - 1) / sb;
+        if (Se == 1 || ((size_t)Se * M * tiles * kTile <= L.partial_floats && tiles <= L.n_counters))
+            consider(Se, sb, L.force_W, L.force_KS, L.force_R, L.force_ipw, true);
     }
-    p.lds = (size_t)L.M * (sb * kSuper + 8) * 2;
+    return best;
+}
+
+// Plans depend only on the launch's shape; the search runs once per shape.
+static GemmPlan cached_plan(const GemmLaunch& L) {
+    if (L.force_S > 0) return plan_gemm(L);
+    static std::mutex mu;
+    static std::unordered_map<uint64_t, GemmPlan> cache;
+    uint64_t key = (uint64_t)L.n_run_tiles;
+    key = key * 1000003u + (uint64_t)L.w.G;
+    key = key * 131u + (uint64_t)L.M;
+    key = key * 7u + (uint64_t)(L.fmt * 2 + (L.xsrc != nullptr));
+    key = key * 4099u + (uint64_t)L.n_cu;
+    key = key * 1000003u + (uint64_t)(L.partial_floats >> 10);
+    key = key * 65537u + (uint64_t)L.n_counters;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    const GemmPlan p = plan_gemm(L);
+    cache.emplace(key, p);
     return p;
 }
 
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
     if (L.M < 1 || L.M > kMaxRows) return hipErrorInvalidValue;
-    const GemmPlan p = plan_gemm(L);
-    if (p.S < 1 || L.n_run_tiles % p.NT != 0) return hipErrorInvalidValue;
+    const GemmPlan p = cached_plan(L);
+    if (p.S < 1) return hipErrorInvalidValue;
     KArgs k;
     k.codes = L.w.codes;
     k.sm = L.w.sm;
@@ -442,7 +655,9 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
     k.counters = L.counters;
     k.S = p.S;
     k.sb_per_split = p.sb_per_split;
-    k.n_groups = p.n_groups;
+    k.ring_slots = p.ring_slots;
+    k.KS = p.KS;
+    k.n_tiles = L.n_run_tiles;
     k.n_cols = L.n_run_tiles * kTile;
     k.half = L.half;
     k.xsrc = L.xsrc;
@@ -454,12 +669,12 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
     k.ss_out = L.ss_out;
     if (L.fmt == W_Q4_1) {
         switch (L.epi) {
-            case EPI_STORE: return launch_nt<W_Q4_1, EPI_STORE>(p.NT, k, p.grid, p.lds, st);
-            case EPI_RESID: return launch_nt<W_Q4_1, EPI_RESID>(p.NT, k, p.grid, p.lds, st);
-            case EPI_SWIGLU: return launch_nt<W_Q4_1, EPI_SWIGLU>(p.NT, k, p.grid, p.lds, st);
+            case EPI_STORE: return launch_fe<W_Q4_1, EPI_STORE>(p.R, k, p.grid, p.waves, p.lds, st);
+            case EPI_RESID: return launch_fe<W_Q4_1, EPI_RESID>(p.R, k, p.grid, p.waves, p.lds, st);
+            case EPI_SWIGLU: return launch_fe<W_Q4_1, EPI_SWIGLU>(p.R, k, p.grid, p.waves, p.lds, st);
         }
     } else if (L.epi == EPI_STORE) {
-        return launch_nt<W_BF16, EPI_STORE>(p.NT, k, p.grid, p.lds, st);
+        return launch_fe<W_BF16, EPI_STORE>(p.R, k, p.grid, p.waves, p.lds, st);
     }
     return hipErrorInvalidValue;
 }

@@ -183,19 +183,30 @@ def test_verify_parity_config1_logits_tight():
                                       (synth.tiny_two_width_model, 3, 1)])
 def test_layer_by_layer_parity(mk, P, k):
     """Teacher-forced: every layer gets the same input rows on both sides, so no error carries
-    from layer to layer. The layer's contribution (x_out - x_in) must agree per row."""
+    from layer to layer. The layer's contribution (x_out - x_in) must agree per row, within the
+    2e-3 bar or three times the oracle's own spread under fp32-level input perturbation: a single
+    bf16 rounding flip of the attention output or the SwiGLU product already moves a row's
+    contribution by 1e-3 .. 2e-3 with these weight distributions."""
     m = mk()
     g, o, w, kv = build_pair(m, P)
+    pos = np.arange(P, P + k)
     for l in range(m.n_layers):
         x = (synth.f32_normal(l, f"layer.x.{m.name}", (k, m.hidden)) * 3.0).astype(np.float32)
         xg = dev(x)
         g.layer_forward(l, xg, k)
-        xo = o.layer_forward(l, x, np.arange(P, P + k))
+        xo = o.layer_forward(l, x, pos)
         got = host(xg).astype(np.float64) - x
         ref = xo.astype(np.float64) - x
         err = rel_l1(got, ref)
-        print(f"layer {l}: contribution rel-L1 {err:.2e}")
-        assert err < LOGIT_TOL, f"layer {l}"
+
+        def run_oracle(arrs, l=l):
+            xx = oracle.Model(m, w)
+            xx.set_kv(arrs[1:], P)
+            return xx.layer_forward(l, arrs[0], pos).astype(np.float64) - x
+
+        tol = max(LOGIT_TOL, 3.0 * noise_floor(run_oracle, [x] + list(kv)))
+        print(f"layer {l}: contribution rel-L1 {err:.2e} (bar {tol:.2e})")
+        assert err < tol, f"layer {l}"
 
 
 # ------------------------------------------------------------------------------------------
