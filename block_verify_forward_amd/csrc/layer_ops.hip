@@ -230,7 +230,7 @@ struct AttnK {
     int M, Hq, nkv, Hg, NQ, n_qt;
     int causal, pos0, window, ctx_lo, ctx_hi;
     int np0, np1, sp, r_lo, r_hi;   // new rows: positions [np0, np1); row of p: p < sp ? r_lo + p - np0 : r_hi + p - sp
-    int key_lo, n_keys, spw, n_chunks;   // keys [key_lo, key_lo + n_keys); spw 16-key steps per wave
+    int key_lo, n_keys, spw, n_chunks;   // keys [key_lo, key_lo + n_keys); spw sub-chunks per workgroup
     float* part;             // [n_qt][nkv][n_chunks][16][hd + 2] partials
     int* counters;           // [n_qt * nkv]
     uint16_t* out;           // [M][Hq * hd] bf16
@@ -254,14 +254,24 @@ __device__ __forceinline__ float head_ss(const AttnK& a, int r, int c0, int hd) 
     return q;
 }
 
+// Keys per sub-chunk: the K and V tiles of a sub-chunk take 32 KB each in LDS.
+template <int HD>
+constexpr int attn_ck() { return 8192 / HD; }
+
 template <int HD>
 __global__ __launch_bounds__(256) void k_attention(AttnK a) {
-    constexpr int NDT = HD / 16;
+    constexpr int CK = attn_ck<HD>();    // keys per sub-chunk
+    constexpr int KB = CK / 16;          // 16-key blocks per sub-chunk
+    constexpr int DW = HD / 4;           // dims owned by each wave (scores over them, then O for them)
     constexpr int H2 = HD / 2;
-    __shared__ float Qs[16][HD + 4];
-    __shared__ float Vs[4][kKeysPerStep][HD];      // V staging; reused for the workgroup merge
-    __shared__ float Ps[4][16][17];
-    __shared__ float MLs[4][16][2];
+    constexpr int PPT = H2 / 16;         // rotate-half pairs per thread (16 threads per vector)
+    constexpr int LD = HD + 4;           // padded LDS row (float4 reads of 16 rows hit distinct banks)
+    constexpr int UPR = HD / 4;          // 16-byte units per K or V row
+    __shared__ __attribute__((aligned(16))) float Ks[CK][LD];
+    __shared__ __attribute__((aligned(16))) float Vs[CK][LD];
+    __shared__ __attribute__((aligned(16))) float Qs[16][LD];
+    __shared__ float Sp[4][16][CK + 1];   // per-wave partial scores (over the wave's dims)
+    __shared__ float Ps[4][16][CK + 1];   // per-wave probabilities
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int chunk = blockIdx.x % a.n_chunks;
@@ -269,61 +279,46 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     const int qt = blockIdx.x / (a.n_chunks * a.nkv);
     const int col = lane & 15, grp = lane >> 4;
     const int qd = a.Hq * HD;
-    const int chunk_keys = 4 * a.spw * kKeysPerStep;
-    const int c0 = a.key_lo + chunk * chunk_keys;
-    const int c1 = min(a.key_lo + a.n_keys, c0 + chunk_keys);
     const size_t prow = (size_t)2 * a.w;
+    const int wk0 = a.key_lo + chunk * a.spw * CK;                   // this workgroup's keys [wk0, wk1)
+    const int wk1 = min(a.key_lo + a.n_keys, wk0 + a.spw * CK);
 
-    // 1. queries of this tile, normalised and rotated, into LDS (one wave per 4 qvs)
-    for (int i = wave; i < 16; i += 4) {
-        const int qv = qt * 16 + i;
-        if (qv >= a.NQ) {
-            for (int d = lane; d < HD; d += 64) Qs[i][d] = 0.f;
-            continue;
-        }
-        const int m = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
+    // 1. the 16 query vectors of the tile: per-head RMSNorm (sums of squares from the q|k|v GEMM's
+    //    epilogue) and rotate-half RoPE at the row's position, into LDS; 16 threads per vector,
+    //    all loads issued before any use
+    {
+        const int qi = tid >> 4, j = tid & 15;
+        const int qv = qt * 16 + qi;
+        const bool live = qv < a.NQ;
+        const int m = live ? qv / a.Hg : 0, h = live ? g * a.Hg + qv % a.Hg : 0;
         const float* src = a.qkv + (size_t)m * a.ldq + h * HD;
-        const float inv = a.qk_norm ? 1.0f / sqrtf(head_ss(a, m, h * HD, HD) / (float)HD + a.eps) : 1.f;
         const float2* rt = a.rope + (size_t)(a.pos0 + m) * H2;
-        for (int d = lane; d < H2; d += 64) {
-            float x0 = src[d] * inv, x1 = src[d + H2] * inv;
-            if (a.qk_norm) {
-                x0 *= bf16_to_f32(a.q_norm[d]);
-                x1 *= bf16_to_f32(a.q_norm[d + H2]);
-            }
-            const float2 cs = rt[d];
-            Qs[i][d] = x0 * cs.x - x1 * cs.y;
-            Qs[i][d + H2] = x0 * cs.y + x1 * cs.x;
+        float x0[PPT], x1[PPT], g0[PPT], g1[PPT];
+        float2 cs[PPT];
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int d = j + 16 * i;
+            x0[i] = src[d];
+            x1[i] = src[d + H2];
+            cs[i] = rt[d];
+            g0[i] = a.qk_norm ? bf16_to_f32(a.q_norm[d]) : 1.f;
+            g1[i] = a.qk_norm ? bf16_to_f32(a.q_norm[d + H2]) : 1.f;
+        }
+        float ssq = 0.f;
+        if (a.qk_norm)
+            for (int t = j; t < HD / 16; t += 16) ssq += a.ss[(size_t)m * (a.ldq / 16) + h * (HD / 16) + t];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) ssq += __shfl_xor(ssq, o);
+        const float inv = a.qk_norm ? 1.0f / sqrtf(ssq / (float)HD + a.eps) : 1.f;
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int d = j + 16 * i;
+            const float y0 = x0[i] * inv * g0[i], y1 = x1[i] * inv * g1[i];
+            Qs[qi][d] = live ? y0 * cs[i].x - y1 * cs[i].y : 0.f;
+            Qs[qi][d + H2] = live ? y0 * cs[i].y + y1 * cs[i].x : 0.f;
         }
     }
-    // 2. new rows inside this chunk (own layer): K normalised + rotated, V copied, into the plane
-    if (a.own) {
-        const int p_lo = max(c0, a.np0), p_hi = min(c1, a.np1);
-        for (int p = p_lo + wave; p < p_hi; p += 4) {
-            const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
-            const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
-            const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
-            float* dst = a.plane + (size_t)p * prow + g * HD;
-            const float inv = a.qk_norm ? 1.0f / sqrtf(head_ss(a, r, qd + g * HD, HD) / (float)HD + a.eps) : 1.f;
-            const float2* rt = a.rope + (size_t)p * H2;
-            for (int d = lane; d < H2; d += 64) {
-                float x0 = ks[d] * inv, x1 = ks[d + H2] * inv;
-                if (a.qk_norm) {
-                    x0 *= bf16_to_f32(a.k_norm[d]);
-                    x1 *= bf16_to_f32(a.k_norm[d + H2]);
-                }
-                const float2 cs = rt[d];
-                dst[d] = x0 * cs.x - x1 * cs.y;
-                dst[d + H2] = x0 * cs.y + x1 * cs.x;
-                dst[a.w + d] = vs[d];
-                dst[a.w + d + H2] = vs[d + H2];
-            }
-        }
-    }
-    __threadfence_block();
-    __syncthreads();
 
-    // 3. this wave's keys
     int lo_r[4], hi_r[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -332,99 +327,162 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         else { lo_r[r] = 1; hi_r[r] = 0; }
     }
     const float scale = 1.0f / sqrtf((float)HD);
+    constexpr int NDT = DW / 16;
     floatx4 o[NDT];
 #pragma unroll
     for (int d = 0; d < NDT; ++d) o[d] = (floatx4){0.f, 0.f, 0.f, 0.f};
     float m_run[4], l_run[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
-    const int w0 = c0 + wave * a.spw * kKeysPerStep;
-    const int w1 = min(c1, w0 + a.spw * kKeysPerStep);
-    for (int k0 = w0; k0 < w1; k0 += kKeysPerStep) {
-        for (int idx = lane; idx < kKeysPerStep * HD / 4; idx += 64) {
-            const int kk = idx / (HD / 4), d4 = idx % (HD / 4);
-            const int key = k0 + kk;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (key < w1) v = *(const float4*)(a.plane + key * prow + a.w + g * HD + 4 * d4);
-            *(float4*)&Vs[wave][kk][4 * d4] = v;
+
+    for (int c0 = wk0; c0 < wk1; c0 += CK) {
+        const int c1 = min(wk1, c0 + CK);
+        // 2. K and V rows of the sub-chunk: direct global->LDS copies, one row (UPR 16-byte units)
+        //    per instruction; rows past c1 repeat row c0 (finite; masked below)
+        for (int i = wave; i < 2 * CK * ((UPR + 63) / 64); i += 4) {
+            const int ipr = (UPR + 63) / 64;               // instructions per row
+            const int kv = i / (CK * ipr), rem = i - kv * CK * ipr;
+            const int kk = rem / ipr, part = rem - kk * ipr;
+            const int unit = part * 64 + lane;
+            const int key = c0 + kk < c1 ? c0 + kk : c0;
+            if (unit < UPR) {
+                const float* srcp = a.plane + (size_t)key * prow + (size_t)kv * a.w + g * HD + unit * 4;
+                float* dst = (kv ? &Vs[kk][0] : &Ks[kk][0]) + part * 256;
+                __builtin_amdgcn_global_load_lds((const void*)srcp, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            }
         }
-        const int key_b = k0 + col;
-        const bool kb_live = key_b < w1;
-        const float* krow = a.plane + (kb_live ? key_b : w0) * prow + g * HD;
-        floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // 3. new rows of an own layer inside the sub-chunk: K normalised and rotated, V copied, into
+        //    LDS and the plane (16 threads per row)
+        if (a.own) {
+            const int p_lo = max(c0, a.np0), p_hi = min(c1, a.np1);
+            if (p_lo < p_hi) {
+                for (int pr = p_lo; pr < p_hi; pr += 16) {
+                    const int ri = tid >> 4, j = tid & 15;
+                    const int p = pr + ri;
+                    if (p < p_hi) {
+                        const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
+                        const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
+                        const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
+                        const float2* rt = a.rope + (size_t)p * H2;
+                        float ssq = 0.f;
+                        if (a.qk_norm)
+                            for (int t = j; t < HD / 16; t += 16) ssq += a.ss[(size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + t];
 #pragma unroll
-        for (int t = 0; t < HD / 16; ++t) {
-            const int d = 16 * t + 4 * grp;
-            const float4 qa = *(const float4*)&Qs[col][d];
-            const float4 kb = kb_live ? *(const float4*)(krow + d) : make_float4(0.f, 0.f, 0.f, 0.f);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, kb.x, sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, kb.y, sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.z, kb.z, sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.w, kb.w, sacc, 0, 0, 0);
+                        for (int o2 = 1; o2 < 16; o2 <<= 1) ssq += __shfl_xor(ssq, o2);
+                        const float inv = a.qk_norm ? 1.0f / sqrtf(ssq / (float)HD + a.eps) : 1.f;
+                        float* dst = a.plane + (size_t)p * prow + g * HD;
+                        const int kk = p - c0;
+#pragma unroll
+                        for (int i = 0; i < PPT; ++i) {
+                            const int d = j + 16 * i;
+                            const float y0 = ks[d] * inv * (a.qk_norm ? bf16_to_f32(a.k_norm[d]) : 1.f);
+                            const float y1 = ks[d + H2] * inv * (a.qk_norm ? bf16_to_f32(a.k_norm[d + H2]) : 1.f);
+                            const float2 csv = rt[d];
+                            const float k0 = y0 * csv.x - y1 * csv.y, k1 = y0 * csv.y + y1 * csv.x;
+                            const float v0 = vs[d], v1 = vs[d + H2];
+                            dst[d] = k0;
+                            dst[d + H2] = k1;
+                            dst[a.w + d] = v0;
+                            dst[a.w + d + H2] = v1;
+                            Ks[kk][d] = k0;
+                            Ks[kk][d + H2] = k1;
+                            Vs[kk][d] = v0;
+                            Vs[kk][d + H2] = v1;
+                        }
+                    } else {
+                        // keep the shuffles above uniform within the 16-thread group
+                        float ssq = 0.f;
+#pragma unroll
+                        for (int o2 = 1; o2 < 16; o2 <<= 1) ssq += __shfl_xor(ssq, o2);
+                        (void)ssq;
+                    }
+                }
+                __syncthreads();
+            }
         }
-        const int key = k0 + col;
+
+        // 4. partial scores over this wave's dims: S[qv][key] for the CK keys
+        floatx4 sacc[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < DW / 16; ++t) {
+            const int d = wave * DW + 16 * t + 4 * grp;
+            const float4 qa = *(const float4*)&Qs[col][d];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const float4 kv4 = *(const float4*)&Ks[kb * 16 + col][d];
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, kv4.x, sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, kv4.y, sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.z, kv4.z, sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.w, kv4.w, sacc[kb], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sp[wave][4 * grp + r][kb * 16 + col] = sacc[kb][r];
+        __syncthreads();
+
+        // 5. softmax update over the sub-chunk (every wave for all 16 vectors; the sums over the
+        //    four waves' dims are taken in wave order), probabilities into this wave's LDS slice
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float v = (key >= lo_r[r] && key <= hi_r[r] && key < w1) ? sacc[r] * scale : -INFINITY;
-            float mx = v;
+            const int qvl = 4 * grp + r;
+            float sv[KB];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int key = c0 + kb * 16 + col;
+                const float sum = ((Sp[0][qvl][kb * 16 + col] + Sp[1][qvl][kb * 16 + col]) + Sp[2][qvl][kb * 16 + col]) +
+                                  Sp[3][qvl][kb * 16 + col];
+                sv[kb] = (key < c1 && key >= lo_r[r] && key <= hi_r[r]) ? sum * scale : -INFINITY;
+                mx = fmaxf(mx, sv[kb]);
+            }
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
             const float m_new = fmaxf(m_run[r], mx);
             const float alpha = (m_run[r] == -INFINITY) ? 0.f : expf(m_run[r] - m_new);
-            const float pv = (v == -INFINITY) ? 0.f : expf(v - m_new);
-            float ps = pv;
+            float ps = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const float pv = (sv[kb] == -INFINITY) ? 0.f : expf(sv[kb] - m_new);
+                ps += pv;
+                Ps[wave][qvl][kb * 16 + col] = pv;
+            }
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off);
             l_run[r] = l_run[r] * alpha + ps;
             m_run[r] = m_new;
 #pragma unroll
             for (int d = 0; d < NDT; ++d) o[d][r] *= alpha;
-            Ps[wave][4 * grp + r][col] = pv;
         }
         wave_sync();
+
+        // 6. O += P V for this wave's dims
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < CK / 4; ++st) {
             const float pa = Ps[wave][col][4 * st + grp];
 #pragma unroll
             for (int d = 0; d < NDT; ++d)
-                o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vs[wave][4 * st + grp][16 * d + col], o[d], 0, 0, 0);
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vs[4 * st + grp][wave * DW + 16 * d + col], o[d], 0, 0, 0);
         }
-        wave_sync();
+        __syncthreads();   // every wave is done with Ks, Vs before the next sub-chunk's copies
     }
 
-    // 4. merge the four waves in LDS (Vs becomes Os[wave][qv][d])
-    __syncthreads();
-    float* Os = &Vs[0][0][0];
+    // 7. this workgroup's partial: unnormalised O (each wave its dims), the running max and sum
+    const size_t tile_base = ((size_t)qt * a.nkv + g) * a.n_chunks;
+    float* part = a.part + (tile_base + chunk) * 16 * (HD + 2);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int qvl = 4 * grp + r;
 #pragma unroll
-        for (int d = 0; d < NDT; ++d) Os[((size_t)wave * 16 + qvl) * HD + 16 * d + col] = o[d][r];
-        if (col == 0) {
-            MLs[wave][qvl][0] = m_run[r];
-            MLs[wave][qvl][1] = l_run[r];
-        }
-    }
-    __syncthreads();
-    const size_t tile_base = ((size_t)qt * a.nkv + g) * a.n_chunks;
-    float* part = a.part + (tile_base + chunk) * 16 * (HD + 2);
-    for (int idx = tid; idx < 16 * HD; idx += 256) {
-        const int qvl = idx / HD, d = idx % HD;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, MLs[w][qvl][0]);
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float mw = MLs[w][qvl][0];
-            const float e = mw == -INFINITY ? 0.f : expf(mw - mx);
-            num += e * Os[((size_t)w * 16 + qvl) * HD + d];
-            den += e * MLs[w][qvl][1];
-        }
-        part[(size_t)qvl * (HD + 2) + d] = num;
-        if (d == 0) {
-            part[(size_t)qvl * (HD + 2) + HD] = mx;
-            part[(size_t)qvl * (HD + 2) + HD + 1] = den;
+        for (int d = 0; d < NDT; ++d) part[(size_t)qvl * (HD + 2) + wave * DW + 16 * d + col] = o[d][r];
+        if (wave == 0 && col == 0) {
+            part[(size_t)qvl * (HD + 2) + HD] = m_run[r];
+            part[(size_t)qvl * (HD + 2) + HD + 1] = l_run[r];
         }
     }
 }
@@ -643,15 +701,14 @@ AttnK make_attn(const Attn& x) {
     }
     a.key_lo = lo;
     a.n_keys = hi - lo + 1;
-    // 16-key steps per wave: enough workgroups to spread the keys, few enough chunks to merge
-    const int steps = (a.n_keys + kKeysPerStep - 1) / kKeysPerStep;
-    const int want_wgs = 384;
+    // sub-chunks of attn_ck<hd> keys per workgroup: enough workgroups to spread the keys, few enough
+    // chunks for the merge (at most 64)
+    const int ck = 8192 / x.hd;
+    const int subs = (a.n_keys + ck - 1) / ck;
     int spw = 1;
-    while (spw < 256 && ((long)((steps + 4 * spw - 1) / (4 * spw)) * a.n_qt * a.nkv > want_wgs ||
-                         (steps + 4 * spw - 1) / (4 * spw) > 64))
-        spw *= 2;
+    while (spw < 4096 && ((long)((subs + spw - 1) / spw) * a.n_qt * a.nkv > 512 || (subs + spw - 1) / spw > 64)) spw *= 2;
     a.spw = spw;
-    a.n_chunks = (steps + 4 * spw - 1) / (4 * spw);
+    a.n_chunks = (subs + spw - 1) / spw;
     a.part = x.part;
     a.counters = x.counters;
     a.out = x.out;
