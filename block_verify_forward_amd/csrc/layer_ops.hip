@@ -283,6 +283,25 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     const int wk0 = a.key_lo + chunk * a.spw * CK;                   // this workgroup's keys [wk0, wk1)
     const int wk1 = min(a.key_lo + a.n_keys, wk0 + a.spw * CK);
 
+    // K and V rows of a sub-chunk: direct global->LDS copies, one row (UPR 16-byte units) per
+    // instruction; rows past c1 repeat row c0 (finite; masked below)
+    auto issue_kv = [&](int c0) {
+        const int c1 = min(wk1, c0 + CK);
+        constexpr int ipr = (UPR + 63) / 64;   // instructions per row
+        for (int i = wave; i < 2 * CK * ipr; i += 4) {
+            const int kv = i / (CK * ipr), rem = i - kv * CK * ipr;
+            const int kk = rem / ipr, part = rem - kk * ipr;
+            const int unit = part * 64 + lane;
+            const int key = c0 + kk < c1 ? c0 + kk : c0;
+            if (unit < UPR) {
+                const float* srcp = a.plane + (size_t)key * prow + (size_t)kv * a.w + g * HD + unit * 4;
+                float* dst = (kv ? &Vs[kk][0] : &Ks[kk][0]) + part * 256;
+                __builtin_amdgcn_global_load_lds((const void*)srcp, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            }
+        }
+    };
+    if (wk0 < wk1) issue_kv(wk0);
+
     // 1. the 16 query vectors of the tile: per-head RMSNorm (sums of squares from the q|k|v GEMM's
     //    epilogue) and rotate-half RoPE at the row's position, into LDS; 16 threads per vector,
     //    all loads issued before any use
@@ -337,70 +356,64 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 
     for (int c0 = wk0; c0 < wk1; c0 += CK) {
         const int c1 = min(wk1, c0 + CK);
-        // 2. K and V rows of the sub-chunk: direct global->LDS copies, one row (UPR 16-byte units)
-        //    per instruction; rows past c1 repeat row c0 (finite; masked below)
-        for (int i = wave; i < 2 * CK * ((UPR + 63) / 64); i += 4) {
-            const int ipr = (UPR + 63) / 64;               // instructions per row
-            const int kv = i / (CK * ipr), rem = i - kv * CK * ipr;
-            const int kk = rem / ipr, part = rem - kk * ipr;
-            const int unit = part * 64 + lane;
-            const int key = c0 + kk < c1 ? c0 + kk : c0;
-            if (unit < UPR) {
-                const float* srcp = a.plane + (size_t)key * prow + (size_t)kv * a.w + g * HD + unit * 4;
-                float* dst = (kv ? &Vs[kk][0] : &Ks[kk][0]) + part * 256;
-                __builtin_amdgcn_global_load_lds((const void*)srcp, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        // 2. new rows of an own layer inside the sub-chunk (16 threads per row): the loads of the
+        //    first sixteen rows go out before the wait for the K/V copies
+        const int p_lo = a.own ? max(c0, a.np0) : 0, p_hi = a.own ? min(c1, a.np1) : 0;
+        const int ri = tid >> 4, j = tid & 15;
+        float kr0[PPT], kr1[PPT], vr0[PPT], vr1[PPT], ssq = 0.f;
+        float2 csr[PPT];
+        auto load_row = [&](int p) {
+            const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
+            const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
+            const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
+            const float2* rt = a.rope + (size_t)p * H2;
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int d = j + 16 * i;
+                kr0[i] = ks[d];
+                kr1[i] = ks[d + H2];
+                vr0[i] = vs[d];
+                vr1[i] = vs[d + H2];
+                csr[i] = rt[d];
             }
-        }
+            ssq = 0.f;
+            if (a.qk_norm)
+                for (int t = j; t < HD / 16; t += 16) ssq += a.ss[(size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + t];
+        };
+        auto store_row = [&](int p) {
+#pragma unroll
+            for (int o2 = 1; o2 < 16; o2 <<= 1) ssq += __shfl_xor(ssq, o2);
+            const float inv = a.qk_norm ? 1.0f / sqrtf(ssq / (float)HD + a.eps) : 1.f;
+            float* dst = a.plane + (size_t)p * prow + g * HD;
+            const int kk = p - c0;
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int d = j + 16 * i;
+                const float y0 = kr0[i] * inv * (a.qk_norm ? bf16_to_f32(a.k_norm[d]) : 1.f);
+                const float y1 = kr1[i] * inv * (a.qk_norm ? bf16_to_f32(a.k_norm[d + H2]) : 1.f);
+                const float k0 = y0 * csr[i].x - y1 * csr[i].y, k1 = y0 * csr[i].y + y1 * csr[i].x;
+                dst[d] = k0;
+                dst[d + H2] = k1;
+                dst[a.w + d] = vr0[i];
+                dst[a.w + d + H2] = vr1[i];
+                Ks[kk][d] = k0;
+                Ks[kk][d + H2] = k1;
+                Vs[kk][d] = vr0[i];
+                Vs[kk][d + H2] = vr1[i];
+            }
+        };
+        if (p_lo + ri < p_hi) load_row(p_lo + ri);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        // 3. new rows of an own layer inside the sub-chunk: K normalised and rotated, V copied, into
-        //    LDS and the plane (16 threads per row)
-        if (a.own) {
-            const int p_lo = max(c0, a.np0), p_hi = min(c1, a.np1);
-            if (p_lo < p_hi) {
-                for (int pr = p_lo; pr < p_hi; pr += 16) {
-                    const int ri = tid >> 4, j = tid & 15;
-                    const int p = pr + ri;
-                    if (p < p_hi) {
-                        const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
-                        const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
-                        const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
-                        const float2* rt = a.rope + (size_t)p * H2;
-                        float ssq = 0.f;
-                        if (a.qk_norm)
-                            for (int t = j; t < HD / 16; t += 16) ssq += a.ss[(size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + t];
-#pragma unroll
-                        for (int o2 = 1; o2 < 16; o2 <<= 1) ssq += __shfl_xor(ssq, o2);
-                        const float inv = a.qk_norm ? 1.0f / sqrtf(ssq / (float)HD + a.eps) : 1.f;
-                        float* dst = a.plane + (size_t)p * prow + g * HD;
-                        const int kk = p - c0;
-#pragma unroll
-                        for (int i = 0; i < PPT; ++i) {
-                            const int d = j + 16 * i;
-                            const float y0 = ks[d] * inv * (a.qk_norm ? bf16_to_f32(a.k_norm[d]) : 1.f);
-                            const float y1 = ks[d + H2] * inv * (a.qk_norm ? bf16_to_f32(a.k_norm[d + H2]) : 1.f);
-                            const float2 csv = rt[d];
-                            const float k0 = y0 * csv.x - y1 * csv.y, k1 = y0 * csv.y + y1 * csv.x;
-                            const float v0 = vs[d], v1 = vs[d + H2];
-                            dst[d] = k0;
-                            dst[d + H2] = k1;
-                            dst[a.w + d] = v0;
-                            dst[a.w + d + H2] = v1;
-                            Ks[kk][d] = k0;
-                            Ks[kk][d + H2] = k1;
-                            Vs[kk][d] = v0;
-                            Vs[kk][d + H2] = v1;
-                        }
-                    } else {
-                        // keep the shuffles above uniform within the 16-thread group
-                        float ssq = 0.f;
-#pragma unroll
-                        for (int o2 = 1; o2 < 16; o2 <<= 1) ssq += __shfl_xor(ssq, o2);
-                        (void)ssq;
-                    }
+        __syncthreads();   // the K/V copies of every wave (and, the first time, the queries) are in LDS
+        if (p_lo < p_hi) {
+            // the 16-thread groups are whole, so the shuffles in store_row stay inside live groups
+            if (p_lo + ri < p_hi) store_row(p_lo + ri);
+            for (int pr = p_lo + 16; pr < p_hi; pr += 16)
+                if (pr + ri < p_hi) {
+                    load_row(pr + ri);
+                    store_row(pr + ri);
                 }
-                __syncthreads();
-            }
+            __syncthreads();
         }
 
         // 4. partial scores over this wave's dims: S[qv][key] for the CK keys
@@ -470,6 +483,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
                 o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vs[4 * st + grp][wave * DW + 16 * d + col], o[d], 0, 0, 0);
         }
         __syncthreads();   // every wave is done with Ks, Vs before the next sub-chunk's copies
+        if (c0 + CK < wk1) issue_kv(c0 + CK);
     }
 
     // 7. this workgroup's partial: unnormalised O (each wave its dims), the running max and sum
