@@ -22,8 +22,6 @@ import json
 import os
 import sys
 import time
-from concurrent.futures import ThreadPoolExecutor
-
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
@@ -55,24 +53,7 @@ def log(msg: str):
 
 def build_weights(m, seed: int, threads: int):
     from block_verify_forward_amd import synth
-    out = {"layers": [None] * m.n_layers}
-
-    def layer(l):
-        d = {}
-        for key, (n_out, n_in) in synth.layer_matrix_shapes(m, l).items():
-            d[key] = synth.q4_1_image(seed, f"{m.name}.L{l}.{key}", n_out, n_in)
-        hd = m.layers[l].head_dim
-        d["attn_norm"] = synth.bf16_uniform(seed, f"{m.name}.L{l}.attn_norm", (m.hidden,), 0.5, 1.5)
-        d["mlp_norm"] = synth.bf16_uniform(seed, f"{m.name}.L{l}.mlp_norm", (m.hidden,), 0.5, 1.5)
-        d["q_norm"] = synth.bf16_uniform(seed, f"{m.name}.L{l}.q_norm", (hd,), 0.5, 1.5)
-        d["k_norm"] = synth.bf16_uniform(seed, f"{m.name}.L{l}.k_norm", (hd,), 0.5, 1.5)
-        out["layers"][l] = d
-
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(layer, range(m.n_layers)))
-    out["embed"] = synth.embedding_table(seed, m, threads)
-    out["final_norm"] = synth.bf16_uniform(seed, f"{m.name}.final_norm", (m.hidden,), 0.5, 1.5)
-    return out
+    return synth.make_weights(m, seed, threads=threads)
 
 
 def cpu_baseline(m, w, kv, ctx, toks, budget_s: float):
@@ -123,6 +104,72 @@ def cpu_baseline(m, w, kv, ctx, toks, budget_s: float):
             "sample": sample, "seconds_per_pass": round(dt, 3)}
 
 
+def run_loop(args):
+    """The full speculative loop: target (42 layers) and draft (5 layers, hidden 2560, block 8) at full
+    size, args.ctx cached positions on both, rounds until args.loop tokens; per round the accept
+    length is drawn from the truncated geometric of the acceptance workload (mean 3.8) and imposed
+    by steering the verify logits (synthetic weights accept nothing by themselves)."""
+    import dataclasses
+    import torch
+    from block_verify_forward_amd import bvf, synth
+    from block_verify_forward_amd.loop import SpecLoop
+
+    threads = min(16, os.cpu_count() or 8)
+    max_ctx = args.ctx + args.loop + 64
+    m = synth.target_model(max_ctx=max_ctx, n_layers=args.layers, vocab=args.vocab)
+    dm = synth.draft_model(max_ctx=max_ctx)
+    t0 = time.time()
+    w = synth.make_weights(m, args.seed, threads=threads)
+    dw = synth.make_weights(dm, args.seed, threads=threads)
+    kv = synth.make_kv(m, args.ctx, args.seed, threads=threads)
+    kvd = synth.make_kv(dm, args.ctx, args.seed, threads=threads)
+    log(f"synthetic target, draft and contexts drawn in {time.time() - t0:.1f} s")
+    T = bvf.Model(m)
+    T.load_weights(w)
+    T.set_context(kv, args.ctx)
+    D = bvf.Model(dataclasses.replace(dm, vocab=m.vocab))
+    D.load_weights(dw)
+    D.set_context(kvd, args.ctx)
+    if not args.no_graph:
+        T.set_graph_mode(True)
+    rounds_max = args.loop
+    steer = synth.accept_lengths(args.seed, rounds_max, max_a=7)
+    loop = SpecLoop(T, D, 8)
+    snap_t, snap_d = T.snapshot_take(), D.snapshot_take()
+    loop.start(17)
+    for i in range(3):   # warm-up rounds, then back to the start
+        loop.round(int(steer[i]))
+    T.restore(snap_t)
+    D.restore(snap_d)
+    loop.start(17)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    toks = loop.run(args.loop, steer)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    rounds = len(loop.accepted)
+    assert loop.accepted == [int(a) for a in steer[:rounds]], "steered accept lengths not reproduced"
+    res = {
+        "metric": "speculative decode tokens/s (draft block 8 + batched verify k=8 + greedy accept + commit)",
+        "value": round(len(toks) / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "data": f"synthetic (seeded draws, seed {args.seed}); acceptance steered: truncated geometric p=0.8467",
+        "config": {"workload": f"speculative loop: target {m.n_layers} layers hidden {m.hidden} Q4_1, draft 5 layers "
+                               f"hidden 2560, block 8, {args.ctx} cached positions, {args.loop} tokens"},
+        "tokens": len(toks),
+        "rounds": rounds,
+        "tokens_per_target_pass": round(len(toks) / rounds, 3),
+        "mean_accepted_drafts": round(float(np.mean(loop.accepted)), 3),
+        "ms_per_round": round(ms / rounds, 4),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +183,9 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="direct launches instead of the captured pass")
+    ap.add_argument("--loop", type=int, default=0,
+                    help="instead of the verify step: the speculative loop (draft block of 8 + batched verify + "
+                         "accept + commit) until this many tokens, steered acceptance, full-size draft and target")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain fp32 copy kernel (neg) of this many MiB three times first: the known-size "
                          "dispatch that scales HBM counters")
@@ -149,6 +199,8 @@ def main():
     from block_verify_forward_amd import bvf, synth
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    if args.loop > 0:
+        return run_loop(args)
     threads = min(16, os.cpu_count() or 8)
     m = synth.target_model(max_ctx=args.ctx + 64, n_layers=args.layers, vocab=args.vocab)
     t0 = time.time()

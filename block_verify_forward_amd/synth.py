@@ -236,12 +236,12 @@ def layer_matrix_shapes(m: Model, l: int) -> Dict[str, tuple]:
     return s
 
 
-def make_weights(m: Model, seed: int = 0, with_head: bool = True) -> dict:
+def make_weights(m: Model, seed: int = 0, with_head: bool = True, threads: int = 1) -> dict:
     """All weights of a target-style model (or the layer part of a draft). Keys:
     'layers': list of dicts {q,k,v,o,gate,up,down: Q4_1 images; attn_norm, mlp_norm, q_norm, k_norm:
-    bf16}; 'embed': bf16 [V, H] (tied embedding table and output head); 'final_norm': bf16 [H]."""
-    out = {"layers": []}
-    for l in range(m.n_layers):
+    bf16}; 'embed': bf16 [V, H] (tied embedding table and output head); 'final_norm': bf16 [H].
+    Every tensor has its own named stream, so drawing layers on several threads gives the same arrays."""
+    def layer(l):
         d = {}
         for key, (n_out, n_in) in layer_matrix_shapes(m, l).items():
             d[key] = q4_1_image(seed, f"{m.name}.L{l}.{key}", n_out, n_in)
@@ -250,9 +250,16 @@ def make_weights(m: Model, seed: int = 0, with_head: bool = True) -> dict:
         d["mlp_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.mlp_norm", (m.hidden,), 0.5, 1.5)
         d["q_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.q_norm", (hd,), 0.5, 1.5)
         d["k_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.k_norm", (hd,), 0.5, 1.5)
-        out["layers"].append(d)
+        return d
+
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            out = {"layers": list(ex.map(layer, range(m.n_layers)))}
+    else:
+        out = {"layers": [layer(l) for l in range(m.n_layers)]}
     if with_head and m.vocab > 0 and m.block_causal == 1:
-        out["embed"] = embedding_table(seed, m)
+        out["embed"] = embedding_table(seed, m, max(threads, 8))
     out["final_norm"] = bf16_uniform(seed, f"{m.name}.final_norm", (m.hidden,), 0.5, 1.5)
     if m.block_causal == 0:
         T = len(m.tap_layers)
@@ -280,15 +287,18 @@ def embedding_table(seed: int, m: Model, threads: int = 8) -> np.ndarray:
     return out
 
 
-def make_kv(m: Model, positions: int, seed: int = 0) -> List[Optional[np.ndarray]]:
+def make_kv(m: Model, positions: int, seed: int = 0, threads: int = 1) -> List[Optional[np.ndarray]]:
     """Cached K/V for every own plane: fp32 [positions, 2, w_l] N(0,1) (K read as already roped)."""
-    out = []
-    for l in range(m.n_layers):
+    def plane(l):
         if m.layers[l].kv_owner < 0:
-            out.append(f32_normal(seed, f"{m.name}.kv{l}", (positions, 2, m.kv_width(l))))
-        else:
-            out.append(None)
-    return out
+            return f32_normal(seed, f"{m.name}.kv{l}", (positions, 2, m.kv_width(l)))
+        return None
+
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            return list(ex.map(plane, range(m.n_layers)))
+    return [plane(l) for l in range(m.n_layers)]
 
 
 def q4_1_bytes(m: Model) -> int:
