@@ -245,7 +245,8 @@ size_t layout(bvf_model* m, uint8_t* base) {
     m->partial = (float*)take(kPartialFloats * 4);
     m->counters = (int*)take((size_t)kCounters * 4);
     // attention partials: at most max(384, Hq * (max_ctx / 4096 + 2)) workgroups of 16 rows
-    m->attn_part_floats = (size_t)std::max(384, d.n_q_heads * (d.max_ctx / 4096 + 2)) * 16 * (m->hd_max + 2);
+    // attention partials: (query tiles x KV heads) <= n_q_heads at 16 rows, up to kAttnMaxChunks chunks each
+    m->attn_part_floats = (size_t)d.n_q_heads * kAttnMaxChunks * 16 * (m->hd_max + 2);
     m->attn_part = (float*)take(m->attn_part_floats * 4);
     m->ss_x = (float*)take((size_t)kMaxRows * (H / kTile) * 4);
     m->ss_qkv = (float*)take((size_t)kMaxRows * (m->nqkv_max / kTile) * 4);

@@ -27,6 +27,79 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15) without LDS traffic: quad
+// swaps, then the half-row and row mirrors; every lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));    // lane ^ 1
+    v = fmaxf(v, dpp<0x4E>(v));    // lane ^ 2
+    v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp<0x140>(v));   // row_mirror
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x140>(v);
+    return v;
+}
+
+// N consecutive floats (N a multiple of 4, or 2) through 16- or 8-byte accesses; the addresses are
+// aligned to the access size.
+template <int N>
+__device__ __forceinline__ void load_vec(float* v, const float* p) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 t = *(const float4*)(p + i);
+            v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 2) {
+            const float2 t = *(const float2*)(p + i);
+            v[i] = t.x; v[i + 1] = t.y;
+        }
+    }
+}
+template <int N>
+__device__ __forceinline__ void store_vec(float* p, const float* v) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) *(float4*)(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 2) *(float2*)(p + i) = make_float2(v[i], v[i + 1]);
+    }
+}
+// N consecutive bf16 (N a multiple of 2) as floats
+template <int N>
+__device__ __forceinline__ void load_bf16_vec(float* v, const uint16_t* p) {
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 8) {
+            const uint4 t = *(const uint4*)(p + i);
+            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[i + 2 * q] = __builtin_bit_cast(float, w[q] << 16);
+                v[i + 2 * q + 1] = __builtin_bit_cast(float, w[q] & 0xffff0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 2) {
+            const uint32_t w = *(const uint32_t*)(p + i);
+            v[i] = __builtin_bit_cast(float, w << 16);
+            v[i + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
+        }
+    }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -254,9 +327,10 @@ __device__ __forceinline__ float head_ss(const AttnK& a, int r, int c0, int hd) 
     return q;
 }
 
-// Keys per sub-chunk: the K and V tiles of a sub-chunk take 32 KB each in LDS.
+// Keys per sub-chunk: the K and V tiles of a sub-chunk take 16 KB each in LDS (16 keys at hd 256:
+// small chunks spread the K/V reads over many compute units), at least one 16-key MFMA block.
 template <int HD>
-constexpr int attn_ck() { return 8192 / HD; }
+constexpr int attn_ck() { return 4096 / HD > 16 ? 4096 / HD : 16; }
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attention(AttnK a) {
@@ -284,27 +358,87 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     const int wk1 = min(a.key_lo + a.n_keys, wk0 + a.spw * CK);
 
     // K and V rows of a sub-chunk: direct global->LDS copies, one row (UPR 16-byte units) per
-    // instruction; rows past c1 repeat row c0 (finite; masked below)
+    // instruction, a fixed number per wave; rows past c1 repeat row c0 (finite; masked below)
     auto issue_kv = [&](int c0) {
         const int c1 = min(wk1, c0 + CK);
         constexpr int ipr = (UPR + 63) / 64;   // instructions per row
-        for (int i = wave; i < 2 * CK * ipr; i += 4) {
+        static_assert((2 * CK * ipr) % 4 == 0, "K/V copies split evenly over the 4 waves");
+#pragma unroll
+        for (int t = 0; t < 2 * CK * ipr / 4; ++t) {
+            const int i = wave + 4 * t;
             const int kv = i / (CK * ipr), rem = i - kv * CK * ipr;
             const int kk = rem / ipr, part = rem - kk * ipr;
             const int unit = part * 64 + lane;
             const int key = c0 + kk < c1 ? c0 + kk : c0;
-            if (unit < UPR) {
+            if (UPR >= 64 || unit < UPR) {
                 const float* srcp = a.plane + (size_t)key * prow + (size_t)kv * a.w + g * HD + unit * 4;
                 float* dst = (kv ? &Vs[kk][0] : &Ks[kk][0]) + part * 256;
                 __builtin_amdgcn_global_load_lds((const void*)srcp, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
             }
         }
     };
-    if (wk0 < wk1) issue_kv(wk0);
+
+    // new rows of an own layer (16 threads per row): raw K, V, RoPE row and the head's sums of
+    // squares into registers; store_row normalises, rotates and writes them to LDS and the plane
+    const int ri = tid >> 4, jr = tid & 15;
+    float kr0[PPT], kr1[PPT], vr0[PPT], vr1[PPT], ssr = 0.f;
+    float2 csr[PPT];
+    auto load_row = [&](int p) {
+        const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
+        const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
+        const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
+        const float2* rt = a.rope + (size_t)p * H2;
+        const int d0 = jr * PPT;
+        load_vec<PPT>(kr0, ks + d0);
+        load_vec<PPT>(kr1, ks + d0 + H2);
+        load_vec<PPT>(vr0, vs + d0);
+        load_vec<PPT>(vr1, vs + d0 + H2);
+        load_vec<2 * PPT>((float*)csr, (const float*)(rt + d0));
+        ssr = 0.f;
+        if (a.qk_norm) {
+#pragma unroll
+            for (int u = 0; u < (HD / 16 + 15) / 16; ++u)
+                if (jr + 16 * u < HD / 16) ssr += a.ss[(size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + jr + 16 * u];
+        }
+    };
+    auto store_row = [&](int p, int c0) {
+        const float inv = a.qk_norm ? 1.0f / sqrtf(row16_sum(ssr) / (float)HD + a.eps) : 1.f;
+        float* dst = a.plane + (size_t)p * prow + g * HD;
+        const int kk = p - c0;
+        const int d0 = jr * PPT;
+        float gk0[PPT], gk1[PPT], k0[PPT], k1[PPT];
+        if (a.qk_norm) {
+            load_bf16_vec<PPT>(gk0, a.k_norm + d0);
+            load_bf16_vec<PPT>(gk1, a.k_norm + d0 + H2);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) gk0[i] = gk1[i] = 1.f;
+        }
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const float y0 = kr0[i] * inv * gk0[i], y1 = kr1[i] * inv * gk1[i];
+            k0[i] = y0 * csr[i].x - y1 * csr[i].y;
+            k1[i] = y0 * csr[i].y + y1 * csr[i].x;
+        }
+        store_vec<PPT>(dst + d0, k0);
+        store_vec<PPT>(dst + d0 + H2, k1);
+        store_vec<PPT>(dst + a.w + d0, vr0);
+        store_vec<PPT>(dst + a.w + d0 + H2, vr1);
+        store_vec<PPT>(&Ks[kk][d0], k0);
+        store_vec<PPT>(&Ks[kk][d0 + H2], k1);
+        store_vec<PPT>(&Vs[kk][d0], vr0);
+        store_vec<PPT>(&Vs[kk][d0 + H2], vr1);
+    };
+    auto new_rows = [&](int c0, int& p_lo, int& p_hi) {
+        const int c1 = min(wk1, c0 + CK);
+        p_lo = a.own ? max(c0, a.np0) : 0;
+        p_hi = a.own ? min(c1, a.np1) : 0;
+    };
 
     // 1. the 16 query vectors of the tile: per-head RMSNorm (sums of squares from the q|k|v GEMM's
-    //    epilogue) and rotate-half RoPE at the row's position, into LDS; 16 threads per vector,
-    //    all loads issued before any use
+    //    epilogue) and rotate-half RoPE at the row's position, into LDS; 16 threads per vector.
+    //    Their loads, and those of the first sub-chunk's new rows, go out before the K/V copies
+    //    (a wave's loads return in order).
     {
         const int qi = tid >> 4, j = tid & 15;
         const int qv = qt * 16 + qi;
@@ -314,28 +448,39 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         const float2* rt = a.rope + (size_t)(a.pos0 + m) * H2;
         float x0[PPT], x1[PPT], g0[PPT], g1[PPT];
         float2 cs[PPT];
+        const int d0 = j * PPT;   // this thread's PPT consecutive pairs (d0 + i, d0 + i + H2)
+        load_vec<PPT>(x0, src + d0);
+        load_vec<PPT>(x1, src + d0 + H2);
+        load_vec<2 * PPT>((float*)cs, (const float*)(rt + d0));
+        if (a.qk_norm) {
+            load_bf16_vec<PPT>(g0, a.q_norm + d0);
+            load_bf16_vec<PPT>(g1, a.q_norm + d0 + H2);
+        } else {
 #pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int d = j + 16 * i;
-            x0[i] = src[d];
-            x1[i] = src[d + H2];
-            cs[i] = rt[d];
-            g0[i] = a.qk_norm ? bf16_to_f32(a.q_norm[d]) : 1.f;
-            g1[i] = a.qk_norm ? bf16_to_f32(a.q_norm[d + H2]) : 1.f;
+            for (int i = 0; i < PPT; ++i) g0[i] = g1[i] = 1.f;
         }
         float ssq = 0.f;
-        if (a.qk_norm)
-            for (int t = j; t < HD / 16; t += 16) ssq += a.ss[(size_t)m * (a.ldq / 16) + h * (HD / 16) + t];
+        if (a.qk_norm) {
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) ssq += __shfl_xor(ssq, o);
-        const float inv = a.qk_norm ? 1.0f / sqrtf(ssq / (float)HD + a.eps) : 1.f;
+            for (int u = 0; u < (HD / 16 + 15) / 16; ++u)
+                if (j + 16 * u < HD / 16) ssq += a.ss[(size_t)m * (a.ldq / 16) + h * (HD / 16) + j + 16 * u];
+        }
+        int p_lo, p_hi;
+        new_rows(wk0, p_lo, p_hi);
+        if (p_lo + ri < p_hi) load_row(p_lo + ri);
+        asm volatile("" ::: "memory");   // these loads leave before the K/V copies
+        __builtin_amdgcn_sched_barrier(0);
+        if (wk0 < wk1) issue_kv(wk0);
+        const float inv = a.qk_norm ? 1.0f / sqrtf(row16_sum(ssq) / (float)HD + a.eps) : 1.f;
+        float q0[PPT], q1[PPT];
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            const int d = j + 16 * i;
             const float y0 = x0[i] * inv * g0[i], y1 = x1[i] * inv * g1[i];
-            Qs[qi][d] = live ? y0 * cs[i].x - y1 * cs[i].y : 0.f;
-            Qs[qi][d + H2] = live ? y0 * cs[i].y + y1 * cs[i].x : 0.f;
+            q0[i] = live ? y0 * cs[i].x - y1 * cs[i].y : 0.f;
+            q1[i] = live ? y0 * cs[i].y + y1 * cs[i].x : 0.f;
         }
+        store_vec<PPT>(&Qs[qi][d0], q0);
+        store_vec<PPT>(&Qs[qi][d0 + H2], q1);
     }
 
     int lo_r[4], hi_r[4];
@@ -356,62 +501,19 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 
     for (int c0 = wk0; c0 < wk1; c0 += CK) {
         const int c1 = min(wk1, c0 + CK);
-        // 2. new rows of an own layer inside the sub-chunk (16 threads per row): the loads of the
-        //    first sixteen rows go out before the wait for the K/V copies
-        const int p_lo = a.own ? max(c0, a.np0) : 0, p_hi = a.own ? min(c1, a.np1) : 0;
-        const int ri = tid >> 4, j = tid & 15;
-        float kr0[PPT], kr1[PPT], vr0[PPT], vr1[PPT], ssq = 0.f;
-        float2 csr[PPT];
-        auto load_row = [&](int p) {
-            const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
-            const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
-            const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
-            const float2* rt = a.rope + (size_t)p * H2;
-#pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                const int d = j + 16 * i;
-                kr0[i] = ks[d];
-                kr1[i] = ks[d + H2];
-                vr0[i] = vs[d];
-                vr1[i] = vs[d + H2];
-                csr[i] = rt[d];
-            }
-            ssq = 0.f;
-            if (a.qk_norm)
-                for (int t = j; t < HD / 16; t += 16) ssq += a.ss[(size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + t];
-        };
-        auto store_row = [&](int p) {
-#pragma unroll
-            for (int o2 = 1; o2 < 16; o2 <<= 1) ssq += __shfl_xor(ssq, o2);
-            const float inv = a.qk_norm ? 1.0f / sqrtf(ssq / (float)HD + a.eps) : 1.f;
-            float* dst = a.plane + (size_t)p * prow + g * HD;
-            const int kk = p - c0;
-#pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                const int d = j + 16 * i;
-                const float y0 = kr0[i] * inv * (a.qk_norm ? bf16_to_f32(a.k_norm[d]) : 1.f);
-                const float y1 = kr1[i] * inv * (a.qk_norm ? bf16_to_f32(a.k_norm[d + H2]) : 1.f);
-                const float k0 = y0 * csr[i].x - y1 * csr[i].y, k1 = y0 * csr[i].y + y1 * csr[i].x;
-                dst[d] = k0;
-                dst[d + H2] = k1;
-                dst[a.w + d] = vr0[i];
-                dst[a.w + d + H2] = vr1[i];
-                Ks[kk][d] = k0;
-                Ks[kk][d + H2] = k1;
-                Vs[kk][d] = vr0[i];
-                Vs[kk][d + H2] = vr1[i];
-            }
-        };
-        if (p_lo + ri < p_hi) load_row(p_lo + ri);
+        // 2. the sub-chunk's K/V copies (and its first new rows, loaded before them) have landed;
+        //    own layers then write the new rows, normalised and rotated, into LDS and the plane
+        int p_lo, p_hi;
+        new_rows(c0, p_lo, p_hi);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();   // the K/V copies of every wave (and, the first time, the queries) are in LDS
         if (p_lo < p_hi) {
-            // the 16-thread groups are whole, so the shuffles in store_row stay inside live groups
-            if (p_lo + ri < p_hi) store_row(p_lo + ri);
+            // the 16-thread groups are whole, so the row sums in store_row stay inside live groups
+            if (p_lo + ri < p_hi) store_row(p_lo + ri, c0);
             for (int pr = p_lo + 16; pr < p_hi; pr += 16)
                 if (pr + ri < p_hi) {
                     load_row(pr + ri);
-                    store_row(pr + ri);
+                    store_row(pr + ri, c0);
                 }
             __syncthreads();
         }
@@ -454,8 +556,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
                 sv[kb] = (key < c1 && key >= lo_r[r] && key <= hi_r[r]) ? sum * scale : -INFINITY;
                 mx = fmaxf(mx, sv[kb]);
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            mx = row16_max(mx);
             const float m_new = fmaxf(m_run[r], mx);
             const float alpha = (m_run[r] == -INFINITY) ? 0.f : expf(m_run[r] - m_new);
             float ps = 0.f;
@@ -465,8 +566,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
                 ps += pv;
                 Ps[wave][qvl][kb * 16 + col] = pv;
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off);
+            ps = row16_sum(ps);
             l_run[r] = l_run[r] * alpha + ps;
             m_run[r] = m_new;
 #pragma unroll
@@ -483,7 +583,12 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
                 o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vs[4 * st + grp][wave * DW + 16 * d + col], o[d], 0, 0, 0);
         }
         __syncthreads();   // every wave is done with Ks, Vs before the next sub-chunk's copies
-        if (c0 + CK < wk1) issue_kv(c0 + CK);
+        if (c0 + CK < wk1) {
+            int n_lo, n_hi;
+            new_rows(c0 + CK, n_lo, n_hi);
+            if (n_lo + ri < n_hi) load_row(n_lo + ri);
+            issue_kv(c0 + CK);
+        }
     }
 
     // 7. this workgroup's partial: unnormalised O (each wave its dims), the running max and sum
@@ -505,8 +610,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 // every thread reads its column of all chunks at once and sums them in chunk order.
 template <int HD>
 __global__ __launch_bounds__(64) void k_attn_combine(AttnK a) {
-    constexpr int MAXC = 64;
-    __shared__ float wgt[MAXC];
+    constexpr int MAXC = kAttnMaxChunks;   // two chunks per lane
+    __shared__ float wgt[MAXC], lsum[MAXC];
     __shared__ float inv_den;
     const int dgroups = HD / 64;
     const int dg = blockIdx.x % dgroups;
@@ -518,18 +623,27 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnK a) {
     const int lane = threadIdx.x;
     const int nc = a.n_chunks;
     const float* base = a.part + (size_t)tile * nc * 16 * (HD + 2) + (size_t)qvl * (HD + 2);
-    // chunk weights e^(m_c - M) and the denominator (nc <= 64: one chunk per lane)
-    const float mc = lane < nc ? base[(size_t)lane * 16 * (HD + 2) + HD] : -INFINITY;
-    const float lc = lane < nc ? base[(size_t)lane * 16 * (HD + 2) + HD + 1] : 0.f;
-    float mx = mc;
+    // chunk weights e^(m_c - M): chunks lane and lane + 64
+    const int c0 = lane, c1 = lane + 64;
+    const float m0 = c0 < nc ? base[(size_t)c0 * 16 * (HD + 2) + HD] : -INFINITY;
+    const float m1 = c1 < nc ? base[(size_t)c1 * 16 * (HD + 2) + HD] : -INFINITY;
+    const float l0 = c0 < nc ? base[(size_t)c0 * 16 * (HD + 2) + HD + 1] : 0.f;
+    const float l1 = c1 < nc ? base[(size_t)c1 * 16 * (HD + 2) + HD + 1] : 0.f;
+    float mx = fmaxf(m0, m1);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float e = mc == -INFINITY ? 0.f : expf(mc - mx);
-    if (lane < MAXC) wgt[lane] = e;
-    // denominator summed in chunk order
-    float den = 0.f;
-    for (int c = 0; c < nc; ++c) den += __shfl(e, c) * __shfl(lc, c);
-    if (lane == 0) inv_den = 1.0f / den;
+    const float e0 = m0 == -INFINITY ? 0.f : expf(m0 - mx);
+    const float e1 = m1 == -INFINITY ? 0.f : expf(m1 - mx);
+    wgt[c0] = e0;
+    wgt[c1] = e1;
+    lsum[c0] = e0 * l0;
+    lsum[c1] = e1 * l1;
+    __syncthreads();
+    if (lane == 0) {   // the denominator summed in chunk order
+        float den = 0.f;
+        for (int c = 0; c < nc; ++c) den += lsum[c];
+        inv_den = 1.0f / den;
+    }
     __syncthreads();
     const int d = dg * 64 + lane;
     float num = 0.f;
@@ -716,11 +830,11 @@ AttnK make_attn(const Attn& x) {
     a.key_lo = lo;
     a.n_keys = hi - lo + 1;
     // sub-chunks of attn_ck<hd> keys per workgroup: enough workgroups to spread the keys, few enough
-    // chunks for the merge (at most 64)
-    const int ck = 8192 / x.hd;
+    // chunks for the merge (at most kAttnMaxChunks)
+    const int ck = std::max(16, 4096 / x.hd);
     const int subs = (a.n_keys + ck - 1) / ck;
     int spw = 1;
-    while (spw < 4096 && ((long)((subs + spw - 1) / spw) * a.n_qt * a.nkv > 512 || (subs + spw - 1) / spw > 64)) spw *= 2;
+    while (spw < 4096 && ((long)((subs + spw - 1) / spw) * a.n_qt * a.nkv > 768 || (subs + spw - 1) / spw > kAttnMaxChunks)) spw *= 2;
     a.spw = spw;
     a.n_chunks = (subs + spw - 1) / spw;
     a.part = x.part;
@@ -738,7 +852,7 @@ size_t attn_part_floats_needed(const Attn& x) {
 hipError_t launch_attention(const Attn& x, hipStream_t st) {
     const AttnK a = make_attn(x);
     if (attn_part_floats_needed(x) > x.part_floats || a.n_qt * a.nkv > x.n_counters) return hipErrorInvalidValue;
-    if (a.n_chunks > 64) return hipErrorInvalidValue;
+    if (a.n_chunks > kAttnMaxChunks) return hipErrorInvalidValue;
     const int grid = a.n_chunks * a.nkv * a.n_qt;
     const int cgrid = a.n_qt * a.nkv * 16 * (x.hd / 64);
     switch (x.hd) {
