@@ -70,7 +70,7 @@ struct GemmPlan {
     int waves;          // waves per workgroup (4, 8 or 16)
     int KS;             // K parts per tile inside a workgroup (summed in LDS)
     int R;              // weight ring depth per wave (superblocks in flight)
-    int ring_slots;     // LDS slots per ring: min(R, superblocks per wave)
+    int ring_slots;     // LDS slots per ring (R)
     int grid;           // workgroups (all resident at once)
     size_t lds;         // dynamic LDS bytes: weight rings, block sums, activation rows
 };

@@ -59,7 +59,7 @@ struct KArgs {
     float* partial;
     int* counters;
     int S, sb_per_split, n_tiles, n_cols;
-    int ring_slots;   // LDS slots per wave ring (min(R, superblocks per wave))
+    int ring_slots;   // LDS slots per wave ring (R)
     int KS;           // K parts per tile inside a workgroup (waves per tile)
     int half;   // STORE on a gate|up image: -1 all 16 columns, 0 the gate half, 1 the up half
     // RMSNorm folded into the staging of A (xsrc != nullptr): A = bf16(x * rinv * gain) with
@@ -73,11 +73,12 @@ struct KArgs {
     float* ss_out;   // STORE / RESID: per row and 16-column tile, the sum of squares of the outputs
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32; NaN stays a NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float half_lo(uint32_t v) {
@@ -99,6 +100,18 @@ __device__ __forceinline__ float quad_sum(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
     return v;
+}
+
+// Sum over all 64 lanes without LDS traffic: the 16-lane rows by DPP (quad swaps, half-row and
+// row mirrors), then the four row sums in row order; every lane gets the same bits.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    const int b = __builtin_bit_cast(int, v);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) + __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) + __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
 }
 
 __device__ __forceinline__ float bf16x8_sum(const u32x4& o) {
@@ -367,12 +380,20 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
             }
         }
     }
-    // fill the ring: the weight loads overlap the staging of the activation rows
-    int s_issue = 0, is_item = 0, is_g = 0;
-    for (; s_issue < R && s_issue < total; ++s_issue) {
-        issue_slot<FMT>(a, a.tile0 + (first + is_item * stride + ts) * a.tile_stride, g0 + kb0 + is_g, ring + s_issue * SLOT, lane);
-        if (++is_g == nkp) { is_g = 0; ++is_item; }
+    // fill the ring: the weight loads overlap the staging of the activation rows. Exactly R slots
+    // are filled (slots past the wave's stream repeat a valid superblock and are never read), so
+    // the staging's own waits can count the copies that follow its loads.
+    asm volatile("" ::: "memory");   // the staging loads above leave before the weight copies
+    __builtin_amdgcn_sched_barrier(0);
+    int is_item = 0, is_g = 0;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const bool real = t < total;
+        const int tile = real ? first + is_item * stride + ts : 0;
+        issue_slot<FMT>(a, a.tile0 + tile * a.tile_stride, g0 + (real ? kb0 + is_g : 0), ring + t * SLOT, lane);
+        if (real && ++is_g == nkp) { is_g = 0; ++is_item; }
     }
+    int s_issue = total < R ? total : R;
 
     if (a.xsrc) {
         // rinv from the producer's per-tile sums of squares (n_ss > 256 continues in a loop)
@@ -382,8 +403,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
             if (m >= a.M) break;
             float q = (sv[r][0] + sv[r][1]) + (sv[r][2] + sv[r][3]);
             for (int i = lane + 256; i < a.n_ss; i += 64) q += a.ss_in[(size_t)m * a.n_ss + i];
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) q += __shfl_xor(q, o);
+            q = wave_sum_dpp(q);
             if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
         }
         __syncthreads();
@@ -399,7 +419,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
                 for (int q = 0; q < 4; ++q) {
                     const float g_lo = __builtin_bit_cast(float, gv[q] << 16);
                     const float g_hi = __builtin_bit_cast(float, gv[q] & 0xffff0000u);
-                    o[q] = (uint32_t)f32_to_bf16(xs[2 * q] * rv * g_lo) | ((uint32_t)f32_to_bf16(xs[2 * q + 1] * rv * g_hi) << 16);
+                    o[q] = pack_bf16x2(xs[2 * q] * rv * g_lo, xs[2 * q + 1] * rv * g_hi);
                 }
                 *(u32x4*)(As + m * lds_ld + p * 8) = o;
                 if constexpr (FMT == W_Q4_1) {
@@ -426,9 +446,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
             }
         }
     } else {
-        // this wave's activation copies have landed (they are older than its ring loads)
-        if (s_issue == R) wait_vm<LPS * R>();
-        else wait_vm<0>();
+        // this wave's activation copies have landed (they are older than its R ring slots)
+        wait_vm<LPS * R>();
     }
     __syncthreads();
     if (FMT == W_Q4_1 && !a.xsrc) {
@@ -562,7 +581,7 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
         const int T = W / KS;
         const int U = (tiles + T * ipw - 1) / (T * ipw);
         const int spk = (sb + KS - 1) / KS;
-        const int ring = std::min(R, ipw * spk);
+        const int ring = R;   // every wave fills all R slots once (unused ones with a repeat)
         const size_t lds = gemm_lds_bytes(L.fmt, M, sb, W, ring, KS);
         if (lds > kGemmLdsMax) return false;
         const int wg_cu = (int)std::min<size_t>(16 / W, kLdsPerCu / lds);
