@@ -381,16 +381,16 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
         }
     }
     // fill the ring: the weight loads overlap the staging of the activation rows. Exactly R slots
-    // are filled (slots past the wave's stream repeat a valid superblock and are never read), so
-    // the staging's own waits can count the copies that follow its loads.
+    // are filled (slots past the wave's stream repeat its first superblock, an L2 hit, and are never
+    // read), so the staging's own waits can count the copies that follow its loads.
     asm volatile("" ::: "memory");   // the staging loads above leave before the weight copies
     __builtin_amdgcn_sched_barrier(0);
     int is_item = 0, is_g = 0;
 #pragma unroll
     for (int t = 0; t < R; ++t) {
         const bool real = t < total;
-        const int tile = real ? first + is_item * stride + ts : 0;
-        issue_slot<FMT>(a, a.tile0 + tile * a.tile_stride, g0 + (real ? kb0 + is_g : 0), ring + t * SLOT, lane);
+        const int tile = real ? first + is_item * stride + ts : (total > 0 ? first + ts : 0);
+        issue_slot<FMT>(a, a.tile0 + tile * a.tile_stride, g0 + (real ? kb0 + is_g : (total > 0 ? kb0 : 0)), ring + t * SLOT, lane);
         if (real && ++is_g == nkp) { is_g = 0; ++is_item; }
     }
     int s_issue = total < R ? total : R;
@@ -574,6 +574,8 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
     const int cus = L.n_cu > 0 ? L.n_cu : 256;
     const size_t slot_bytes = L.fmt == W_Q4_1 ? kSlotQ4 : kSlotBf16;
     const double bytes = (double)tiles * G * slot_bytes;
+    // HBM rate, memory latency, compute per superblock and wave, L2 round trip of the staging,
+    // split-K hand-off, in-LDS part reduction
     const double hbm = 5.5e12, lat = 1.5e-6, per_sb = 0.25e-6, l2_round = 0.8e-6, handoff = 4.0e-6, reduce = 0.3e-6;
     const bool norm = L.xsrc != nullptr;
     double best_t = 1e30;
@@ -581,10 +583,11 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
         const int T = W / KS;
         const int U = (tiles + T * ipw - 1) / (T * ipw);
         const int spk = (sb + KS - 1) / KS;
+        if ((KS - 1) * spk >= sb) return false;   // every K part has superblocks
         const int ring = R;   // every wave fills all R slots once (unused ones with a repeat)
         const size_t lds = gemm_lds_bytes(L.fmt, M, sb, W, ring, KS);
         if (lds > kGemmLdsMax) return false;
-        const int wg_cu = (int)std::min<size_t>(16 / W, kLdsPerCu / lds);
+        const int wg_cu = (int)std::min<size_t>(16 / W, kLdsPerCu / lds);   // at most 16 waves per CU
         if (wg_cu < 1) return false;
         if (!forced && (long)Se * U > (long)cus * wg_cu) return false;   // not resident in one round
         const double pieces = (double)sb * (kSuper / 8);
@@ -612,14 +615,16 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
         prev_sb = sb;
         const int Se = (G + sb - 1) / sb;
         if (Se > 1 && ((size_t)Se * M * tiles * kTile > L.partial_floats || tiles > L.n_counters)) continue;
-        for (int W : {4, 8, 16})
-            for (int KS = 1; KS <= W; KS *= 2)
+        for (int W = 4; W <= 16; ++W)
+            for (int KS = 1; KS <= W; ++KS) {
+                if (W % KS) continue;
                 for (int R : {8, 4, 2}) {
                     if (L.fmt == W_BF16 && R == 8) continue;
                     // the fewest items per workgroup for which the grid is resident
                     for (int ipw = 1; ipw <= tiles && (Se == 1 || ipw <= 32); ++ipw)
                         if (consider(Se, sb, W, KS, R, ipw, false)) break;
                 }
+            }
     }
     if (L.force_S > 0 && L.force_R > 0 && L.force_ipw > 0 && L.force_W > 0 && L.force_KS > 0 && L.force_W % L.force_KS == 0) {
         const int sb = (G + L.force_S - 1) / L.force_S;
