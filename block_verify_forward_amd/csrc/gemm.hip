@@ -135,6 +135,27 @@ __device__ __forceinline__ void wait_lds() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Workgroup barrier over LDS traffic only: this wave's LDS reads and writes are complete, then
+// s_barrier. (__syncthreads also waits for every outstanding global load, the weight ring's
+// included, which would serialise the ring fill with the staging.)
+__device__ __forceinline__ void lds_barrier() {
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// 16-byte LDS read that the compiler's wait-count insertion does not see. A plain LDS read of a
+// region that direct global->LDS copies wrote makes the compiler wait for every outstanding global
+// load, the weight ring's included; the caller orders this read itself (the copies it depends on
+// are complete after its own wait and a barrier) and calls wait_lds() before using the value.
+__device__ __forceinline__ u32x4 lds_read16_untracked(const void* p) {
+    u32x4 v;
+    const uint32_t addr = (uint32_t)(uintptr_t)(lds_void*)p;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
 // Direct loads of one (tile, superblock) of weights into a ring slot of this wave.
 template <int FMT>
 __device__ __forceinline__ void issue_slot(const KArgs& a, int tile_phys, int g, uint8_t* slot, int lane) {
@@ -396,6 +417,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     int s_issue = total < R ? total : R;
 
     if (a.xsrc) {
+        // the staging loads have returned once only the R ring slots are younger
+        wait_vm<LPS * R>();
         // rinv from the producer's per-tile sums of squares (n_ss > 256 continues in a loop)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -406,13 +429,16 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
             q = wave_sum_dpp(q);
             if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
         }
-        __syncthreads();
+        lds_barrier();
         auto convert = [&](int p, int m0, int nrows, const u32x4& gv, const float4 (&xr)[8][2]) {
+            float rvs[8];   // the eight rows' factors in registers before any LDS write of the batch
+#pragma unroll
+            for (int r = 0; r < 8; ++r) rvs[r] = rinv_s[m0 + r];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 if (r >= nrows) break;
                 const int m = m0 + r;
-                const float rv = rinv_s[m];
+                const float rv = rvs[r];
                 const float xs[8] = {xr[r][0].x, xr[r][0].y, xr[r][0].z, xr[r][0].w, xr[r][1].x, xr[r][1].y, xr[r][1].z, xr[r][1].w};
                 u32x4 o;
 #pragma unroll
@@ -449,7 +475,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
         // this wave's activation copies have landed (they are older than its R ring slots)
         wait_vm<LPS * R>();
     }
-    __syncthreads();
+    lds_barrier();
     if (FMT == W_Q4_1 && !a.xsrc) {
         // block sums S[b][m] = sum of the 32 bf16 of block b of row m < M (the copied rows; the
         // normalised rows got theirs while being converted); the four pieces of a block sit in
@@ -458,7 +484,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
             for (int m0 = 0; m0 < a.M; m0 += 8) {
                 u32x4 o[8];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) o[r] = *(const u32x4*)(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
+                for (int r = 0; r < 8; ++r) o[r] = lds_read16_untracked(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
+                wait_lds();
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const float bs = quad_sum(bf16x8_sum(o[r]));
@@ -466,7 +493,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (items == 0) return;   // uniform in the workgroup
 
@@ -500,11 +527,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
         if (KS > 1) {
             // the KS parts of each tile meet in LDS; part 0 sums them in part order
             *(floatx4*)(red + ((size_t)wave * 64 + lane) * 4) = acc;
-            __syncthreads();
+            lds_barrier();
             if (kp == 0) {
                 for (int q = 1; q < KS; ++q) acc += *(const floatx4*)(red + ((size_t)(wave + q) * 64 + lane) * 4);
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (kp != 0 || it >= my_items) continue;
         if (S == 1) {
