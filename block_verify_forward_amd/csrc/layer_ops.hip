@@ -607,12 +607,15 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     }
 }
 
-// Merge of the chunks of one (q tile, KV head): one 64-thread block per (query vector, 64 dims);
-// every thread reads its column of all chunks at once and sums them in chunk order.
+// Merge of the chunks of one (q tile, KV head): one 256-thread block per (query vector, 64 dims).
+// Wave w takes the chunks [w q, (w + 1) q), q = ceil(n_chunks / 4), lane = dim: every value load of
+// the block goes out at once, before the chunk maxima are known. The chunk weights e^(m_c - M) and
+// the denominator are summed in chunk order, and so are the four waves' partial numerators.
 template <int HD>
-__global__ __launch_bounds__(64) void k_attn_combine(AttnK a) {
-    constexpr int MAXC = kAttnMaxChunks;   // two chunks per lane
-    __shared__ float wgt[MAXC], lsum[MAXC];
+__global__ __launch_bounds__(256) void k_attn_combine(AttnK a) {
+    constexpr int MAXC = kAttnMaxChunks;
+    constexpr int QMAX = MAXC / 4;   // chunks per wave at most
+    __shared__ float wgt[MAXC], lsum[MAXC], mxw[4], numw[4][64];
     __shared__ float inv_den;
     const int dgroups = HD / 64;
     const int dg = blockIdx.x % dgroups;
@@ -620,44 +623,53 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnK a) {
     const int tile = blockIdx.x / (dgroups * 16);            // qt * nkv + g
     const int g = tile % a.nkv, qt = tile / a.nkv;
     const int qv = qt * 16 + qvl;
-    if (qv >= a.NQ) return;
-    const int lane = threadIdx.x;
+    if (qv >= a.NQ) return;   // uniform in the block
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nc = a.n_chunks;
-    const float* base = a.part + (size_t)tile * nc * 16 * (HD + 2) + (size_t)qvl * (HD + 2);
-    // chunk weights e^(m_c - M): chunks lane and lane + 64
-    const int c0 = lane, c1 = lane + 64;
-    const float m0 = c0 < nc ? base[(size_t)c0 * 16 * (HD + 2) + HD] : -INFINITY;
-    const float m1 = c1 < nc ? base[(size_t)c1 * 16 * (HD + 2) + HD] : -INFINITY;
-    const float l0 = c0 < nc ? base[(size_t)c0 * 16 * (HD + 2) + HD + 1] : 0.f;
-    const float l1 = c1 < nc ? base[(size_t)c1 * 16 * (HD + 2) + HD + 1] : 0.f;
-    float mx = fmaxf(m0, m1);
+    const int q = (nc + 3) / 4;
+    const size_t cstride = (size_t)16 * (HD + 2);
+    const float* base = a.part + (size_t)tile * nc * cstride + (size_t)qvl * (HD + 2);
+    const int d = dg * 64 + lane;
+    // this thread's values (chunks of its wave, dim d), then the chunk statistics
+    float v[QMAX];
+#pragma unroll
+    for (int i = 0; i < QMAX; ++i) {
+        const int c = wave * q + i;
+        v[i] = (i < q && c < nc) ? base[(size_t)c * cstride + d] : 0.f;
+    }
+    const bool has = tid < nc;
+    const float m_c = has ? base[(size_t)tid * cstride + HD] : -INFINITY;
+    const float l_c = has ? base[(size_t)tid * cstride + HD + 1] : 0.f;
+    float mx = m_c;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float e0 = m0 == -INFINITY ? 0.f : expf(m0 - mx);
-    const float e1 = m1 == -INFINITY ? 0.f : expf(m1 - mx);
-    wgt[c0] = e0;
-    wgt[c1] = e1;
-    lsum[c0] = e0 * l0;
-    lsum[c1] = e1 * l1;
+    if (lane == 0) mxw[wave] = mx;
     __syncthreads();
-    if (lane == 0) {   // the denominator summed in chunk order
+    mx = fmaxf(fmaxf(mxw[0], mxw[1]), fmaxf(mxw[2], mxw[3]));
+    if (tid < MAXC) {
+        const float e = (!has || m_c == -INFINITY) ? 0.f : expf(m_c - mx);
+        wgt[tid] = e;
+        lsum[tid] = e * l_c;
+    }
+    __syncthreads();
+    if (tid == 0) {   // the denominator in chunk order
         float den = 0.f;
         for (int c = 0; c < nc; ++c) den += lsum[c];
         inv_den = 1.0f / den;
     }
-    __syncthreads();
-    const int d = dg * 64 + lane;
     float num = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += 16) {
-        float v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = c0 + i < nc ? base[(size_t)(c0 + i) * 16 * (HD + 2) + d] : 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (c0 + i < nc) num += wgt[c0 + i] * v[i];
+    for (int i = 0; i < QMAX; ++i) {
+        const int c = wave * q + i;
+        if (i < q && c < nc) num += wgt[c] * v[i];
     }
-    const int m = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
-    a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + d] = f32_to_bf16(num * inv_den);
+    numw[wave][lane] = num;
+    __syncthreads();
+    if (wave == 0) {
+        const float t = ((numw[0][lane] + numw[1][lane]) + numw[2][lane]) + numw[3][lane];
+        const int m = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
+        a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + d] = f32_to_bf16(t * inv_den);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -859,15 +871,15 @@ hipError_t launch_attention(const Attn& x, hipStream_t st) {
     switch (x.hd) {
         case 64:
             hipLaunchKernelGGL(k_attention<64>, dim3(grid), dim3(256), 0, st, a);
-            hipLaunchKernelGGL(k_attn_combine<64>, dim3(cgrid), dim3(64), 0, st, a);
+            hipLaunchKernelGGL(k_attn_combine<64>, dim3(cgrid), dim3(256), 0, st, a);
             break;
         case 128:
             hipLaunchKernelGGL(k_attention<128>, dim3(grid), dim3(256), 0, st, a);
-            hipLaunchKernelGGL(k_attn_combine<128>, dim3(cgrid), dim3(64), 0, st, a);
+            hipLaunchKernelGGL(k_attn_combine<128>, dim3(cgrid), dim3(256), 0, st, a);
             break;
         case 256:
             hipLaunchKernelGGL(k_attention<256>, dim3(grid), dim3(256), 0, st, a);
-            hipLaunchKernelGGL(k_attn_combine<256>, dim3(cgrid), dim3(64), 0, st, a);
+            hipLaunchKernelGGL(k_attn_combine<256>, dim3(cgrid), dim3(256), 0, st, a);
             break;
         default: return hipErrorInvalidValue;
     }
