@@ -156,16 +156,18 @@ __device__ __forceinline__ u32x4 lds_read16_untracked(const void* p) {
     return v;
 }
 
-// Direct loads of one (tile, superblock) of weights into a ring slot of this wave.
+// Direct loads of one (tile, superblock) of weights into a ring slot of this wave. The slot's
+// index idx = tile * TG + superblock (TG = G for Q4_1, 16 G for bf16 rows) is wave-uniform: the
+// address arithmetic stays scalar and each lane adds its fixed offset.
 template <int FMT>
-__device__ __forceinline__ void issue_slot(const KArgs& a, int tile_phys, int g, uint8_t* slot, int lane) {
+__device__ __forceinline__ void issue_slot(const KArgs& a, int idx, uint8_t* slot, int lane) {
+    const size_t u = (size_t)__builtin_amdgcn_readfirstlane(idx);
     if constexpr (FMT == W_Q4_1) {
-        const size_t base = (size_t)tile_phys * a.G + g;
-        __builtin_amdgcn_global_load_lds((const void*)((const u32x4*)a.codes + base * 64 + lane), (lds_void*)slot, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)((const uint32_t*)a.sm + base * 64 + lane), (lds_void*)(slot + 1024), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((const u32x4*)a.codes + u * 64 + lane), (lds_void*)slot, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((const uint32_t*)a.sm + u * 64 + lane), (lds_void*)(slot + 1024), 4, 0, 0);
     } else {
         const int c = lane & 15, sub = lane >> 4;
-        const uint16_t* row = (const uint16_t*)a.codes + (size_t)(tile_phys * kTile + c) * a.K + (size_t)g * kSuper + sub * 8;
+        const uint16_t* row = (const uint16_t*)a.codes + u * kSuper + (size_t)c * a.K + sub * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             __builtin_amdgcn_global_load_lds((const void*)(row + j * 32), (lds_void*)(slot + j * 1024), 16, 0, 0);
@@ -406,13 +408,21 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     // read), so the staging's own waits can count the copies that follow its loads.
     asm volatile("" ::: "memory");   // the staging loads above leave before the weight copies
     __builtin_amdgcn_sched_barrier(0);
-    int is_item = 0, is_g = 0;
+    // slot index of the next copy (uniform): +1 per superblock, + wrap from an item's last
+    // superblock to the next item's first; a wave with nothing to stream repeats a valid index
+    const int TG = FMT == W_Q4_1 ? a.G : kTile * a.G;
+    int ib = total > 0 ? (a.tile0 + (first + ts) * a.tile_stride) * TG + g0 + kb0 : a.tile0 * TG + g0;
+    const int ib_first = ib;
+    const int ib_wrap = stride * a.tile_stride * TG - (nkp - 1);
+    int is_g = 0;
 #pragma unroll
     for (int t = 0; t < R; ++t) {
         const bool real = t < total;
-        const int tile = real ? first + is_item * stride + ts : (total > 0 ? first + ts : 0);
-        issue_slot<FMT>(a, a.tile0 + tile * a.tile_stride, g0 + (real ? kb0 + is_g : (total > 0 ? kb0 : 0)), ring + t * SLOT, lane);
-        if (real && ++is_g == nkp) { is_g = 0; ++is_item; }
+        issue_slot<FMT>(a, real ? ib : ib_first, ring + t * SLOT, lane);
+        if (real) {
+            if (++is_g == nkp) { is_g = 0; ib += ib_wrap; }
+            else ++ib;
+        }
     }
     int s_issue = total < R ? total : R;
 
@@ -516,9 +526,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
                 compute_slot<FMT>(slot, As_row + gi * kSuper, FMT == W_Q4_1 ? Ss_l[64 * gi] : 0.f, lane, acc, accm);
                 wait_lds();   // the slot's LDS reads have returned before the refill overwrites it
                 if (s_issue < total) {
-                    issue_slot<FMT>(a, a.tile0 + (first + is_item * stride + ts) * a.tile_stride, g0 + kb0 + is_g,
-                                    ring + (s_issue % R) * SLOT, lane);
-                    if (++is_g == nkp) { is_g = 0; ++is_item; }
+                    issue_slot<FMT>(a, ib, ring + (s_issue % R) * SLOT, lane);
+                    if (++is_g == nkp) { is_g = 0; ib += ib_wrap; }
+                    else ++ib;
                     ++s_issue;
                 }
             }
