@@ -511,26 +511,28 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     const uint16_t* As_row = As + (m_a < a.M ? m_a : 0) * lds_ld + sub * 8 + kb0 * kSuper;
     const float* Ss_l = Ss + lane + 64 * kb0;   // superblock i of this wave's part: Ss_l[64 i]
 
-    int s = 0;
+    int s_off = 0;   // ring offset of the next slot to use
     uint32_t last = 0;   // split-K: bit i set where this wave arrived last on item i (reducer waves)
     for (int it = 0; it < items; ++it) {
         const int tile = first + it * stride + ts;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f}, accm = {0.f, 0.f, 0.f, 0.f};
         if (it < my_items) {
 #pragma nounroll
-            for (int gi = 0; gi < nkp; ++gi, ++s) {
-                // younger slots in flight: s_issue - 1 - s (R - 1 in the steady state)
-                if (s_issue - s == R) wait_vm<LPS * (R - 1)>();
-                else wait_vm<0>();
-                const uint8_t* slot = ring + (s % R) * SLOT;
+            for (int gi = 0; gi < nkp; ++gi) {
+                // R slots are always in flight (past the stream's end the refills repeat a valid
+                // superblock into the slot just used), so the oldest has landed at R - 1 younger
+                wait_vm<LPS * (R - 1)>();
+                uint8_t* slot = ring + s_off;
                 compute_slot<FMT>(slot, As_row + gi * kSuper, FMT == W_Q4_1 ? Ss_l[64 * gi] : 0.f, lane, acc, accm);
                 wait_lds();   // the slot's LDS reads have returned before the refill overwrites it
-                if (s_issue < total) {
-                    issue_slot<FMT>(a, ib, ring + (s_issue % R) * SLOT, lane);
+                const bool real = s_issue < total;
+                issue_slot<FMT>(a, real ? ib : ib_first, slot, lane);
+                if (real) {
+                    ++s_issue;
                     if (++is_g == nkp) { is_g = 0; ib += ib_wrap; }
                     else ++ib;
-                    ++s_issue;
                 }
+                s_off = s_off + SLOT == R * SLOT ? 0 : s_off + SLOT;
             }
             if constexpr (FMT == W_Q4_1) acc += accm;
         }
@@ -550,6 +552,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
             splitk_store(a, acc, tile, split, lane);
         }
     }
+    wait_vm<0>();   // no copy into this wave's ring is left in flight
     if (S > 1 && kp == 0 && my_items > 0) {
         __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are performed
         if (lane == 0) {
