@@ -615,9 +615,11 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
     const size_t slot_bytes = L.fmt == W_Q4_1 ? kSlotQ4 : kSlotBf16;
     const double bytes = (double)tiles * G * slot_bytes;
     // HBM rate, memory latency, compute per superblock and wave, L2 round trip of the staging,
-    // split-K hand-off, in-LDS part reduction
-    const double hbm = 5.5e12, lat = 1.5e-6, per_sb = 0.25e-6, l2_round = 0.8e-6, handoff = 4.0e-6, reduce = 0.3e-6;
+    // split-K hand-off and its cost per split, in-LDS part reduction
+    const double hbm = 5.5e12, lat = 1.5e-6, per_sb = 0.25e-6, l2_round = 0.8e-6, handoff = 3.0e-6, per_split = 0.25e-6,
+                 reduce = 0.3e-6;
     const bool norm = L.xsrc != nullptr;
+    const bool long_stream = L.fmt == W_Q4_1 && (long)tiles * G >= 48L * cus;
     double best_t = 1e30;
     auto consider = [&](int Se, int sb, int W, int KS, int R, int ipw, bool forced) {
         const int T = W / KS;
@@ -634,7 +636,8 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
         const double staging = norm ? (1.0 + std::ceil(pieces / (64.0 * W)) * std::ceil(M / 8.0)) * l2_round : 0.3e-6;
         const double wsb = (double)ipw * spk;   // superblocks per wave
         const double stream = lat + std::max({bytes / hbm, wsb * per_sb, std::ceil(wsb / R) * lat});
-        const double t = staging + stream + (KS > 1 ? ipw * reduce : 0.0) + (Se > 1 ? handoff : 0.0);
+        // the split-K hand-off: arrival, then the last arriver's loads of the Se partials
+        const double t = staging + stream + (KS > 1 ? ipw * reduce : 0.0) + (Se > 1 ? handoff + Se * per_split : 0.0);
         if (forced || t < best_t * 0.98) {
             best_t = t;
             best.S = Se;
@@ -660,6 +663,10 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
                 if (W % KS) continue;
                 for (int R : {8, 4, 2}) {
                     if (L.fmt == W_BF16 && R == 8) continue;
+                    // long Q4_1 streams (>= 48 superblocks per compute unit) take at least 8 waves
+                    // with rings of 4: measured on MI355X, the extra waves hide the per-superblock
+                    // latency better than deeper rings (which the estimate below does not model)
+                    if (long_stream && (W < 8 || R != 4)) continue;
                     // the fewest items per workgroup for which the grid is resident
                     for (int ipw = 1; ipw <= tiles && (Se == 1 || ipw <= 32); ++ipw)
                         if (consider(Se, sb, W, KS, R, ipw, false)) break;
