@@ -26,13 +26,13 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_1_gemm_gate_up.target_k8.pmc_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_1_gemm.target_k8.pmc_traffic.txt")
 GEMM_SRC = os.path.join(ROOT, "block_verify_forward_amd", "csrc", "gemm.hip")
 
 
-def measured_traffic():
-    """HBM bytes per gate|up launch from the committed rocprofv3 counter summary, or None when the
-    GEMM source has changed since the counters were taken."""
+def measured_traffic(cls: str):
+    """HBM bytes per launch of a GEMM class (gate_up, down) from the committed rocprofv3 counter
+    summary, or None when the GEMM source has changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     fields = {}
@@ -41,9 +41,10 @@ def measured_traffic():
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-    if fields.get("gemm_hip_sha256") != src or "traffic_bytes_per_launch" not in fields:
+    key = f"traffic_bytes_per_launch.{cls}"
+    if fields.get("gemm_hip_sha256") != src or key not in fields:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return int(fields[key])
 METRIC = "verified rows/s and Q4_1 weight-stream HBM GB/s (% of peak), k=8 verify pass"
 
 
@@ -314,7 +315,7 @@ def main():
         "gemm_alg_bytes": {names[i]: cls_bytes[i] for i in range(5)},
         "roofline": {"bound": "hbm", "kernel": f"Q4_1 GEMM, {names[dom]} class", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if names[dom] == "gate_up" else None},
+                     "traffic": measured_traffic(names[dom])},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
