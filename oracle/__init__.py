@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
             "orc_commit_verify_rows": (I, [P, I]),
             "orc_argmax": (I, [P, I]),
             "orc_accept_greedy": (I, [P, I, I, P, P, P]),
+            "orc_philox4x32_10": (None, [P, P, P]),
+            "orc_sample_scores": (None, [P, I, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, I, P]),
+            "orc_sample_rows": (None, [P, I, I, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, P]),
+            "orc_accept_sampled": (I, [P, I, I, P, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, P, P, P]),
             "orc_snapshot_take": (P, [P]),
             "orc_snapshot_floats": (L64, [P, I]),
             "orc_snapshot_restore": (I, [P, P]),
@@ -142,6 +146,45 @@ def accept_greedy(logits_all: np.ndarray, tokens: np.ndarray):
     a = ctypes.c_int(0)
     lib().orc_accept_greedy(_p(lg), k, V, _p(t), _p(out), ctypes.byref(a))
     return a.value, out[: a.value + 1].copy()
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    """One Philox4x32-10 block: 4 counter words, 2 key words -> 4 output words (uint32)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def sample_scores(z_row: np.ndarray, temperature: float, seed: int, offset: int, row: int) -> np.ndarray:
+    """fp32 Gumbel-perturbed scores z / T + g of one row (the sampled verify's draw is their argmax)."""
+    z = np.ascontiguousarray(z_row, dtype=np.float32)
+    out = np.empty(z.size, dtype=np.float32)
+    lib().orc_sample_scores(_p(z), z.size, float(temperature), int(seed), int(offset), int(row), _p(out))
+    return out
+
+
+def sample_rows(logits: np.ndarray, temperature: float, seed: int, offset: int) -> np.ndarray:
+    """The draws y_i of every row of logits [k][V] (row i uses counter row i)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    k, V = lg.shape
+    y = np.zeros(k, dtype=np.int32)
+    lib().orc_sample_rows(_p(lg), k, V, float(temperature), int(seed), int(offset), _p(y))
+    return y
+
+
+def accept_sampled(logits_all: np.ndarray, tokens: np.ndarray, temperature: float, seed: int, offset: int):
+    """Sampled longest-prefix accept: returns (a, emitted tokens [a+1], draws [k])."""
+    lg = np.ascontiguousarray(logits_all, dtype=np.float32)
+    k, V = lg.shape
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = np.zeros(k, dtype=np.int32)
+    draws = np.zeros(k, dtype=np.int32)
+    a = ctypes.c_int(0)
+    lib().orc_accept_sampled(_p(lg), k, V, _p(t), float(temperature), int(seed), int(offset), _p(out),
+                             ctypes.byref(a), _p(draws))
+    return a.value, out[: a.value + 1].copy(), draws
 
 
 def cut_floats(per, plane: int, positions: int) -> int:

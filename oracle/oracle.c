@@ -609,6 +609,81 @@ int orc_accept_greedy(const float* logits_all, int k, int V, const int* tokens, 
     return 0;
 }
 
+/* ---- sampled verify (temperature T > 0) ---------------------------------------------------
+ * [CARD, "How it is used"]: with a sampler every position is sampled and compared with the draft,
+ * so the output distribution is the target's. Reading (the pages name no sampler): row i's token
+ * y_i is a draw from softmax(z_i / T); draft d_m is kept while it equals y_{m-1}; the emitted
+ * tokens are d_1..d_a and y_a -- the greedy accept with the argmax replaced by the draw.
+ * The draw is the Gumbel-max method: the index of the largest z_ij / T + g_ij, with g = -log(-log u)
+ * and u_ij uniform on (0, 1), is distributed as softmax(z_i / T).
+ * The uniforms come from the counter-based generator Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011) under key (seed bits 0-31, 32-63) and
+ * counter (j / 4, i, offset bits 0-31, 32-63): x = output word j % 4, u = (floor(x / 2^8) + 1/2) / 2^24
+ * (exact in fp32). The decision is taken in fp32, the kernel's precision: inv_t = 1 / T rounded to
+ * fp32, score = fmaf(z, inv_t, g) with g = -logf(-logf(u)); the first index of the maximum wins;
+ * NaN scores never win. */
+static void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; r++) {
+        if (r > 0) {   /* the key is bumped by the Weyl constants before every round after the first */
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+void orc_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out) { philox4x32_10(ctr, key, out); }
+
+/* fp32 scores z_ij / T + g_ij of row i (V entries) */
+void orc_sample_scores(const float* z, int V, float temperature, uint64_t seed, uint64_t offset, int row,
+                       float* scores) {
+    const float inv_t = 1.0f / temperature;
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    for (int q = 0; q * 4 < V; q++) {
+        const uint32_t ctr[4] = {(uint32_t)q, (uint32_t)row, (uint32_t)offset, (uint32_t)(offset >> 32)};
+        uint32_t x[4];
+        philox4x32_10(ctr, key, x);
+        for (int w = 0; w < 4 && 4 * q + w < V; w++) {
+            const float u = ((float)(x[w] >> 8) + 0.5f) * (1.0f / 16777216.0f);
+            const float g = -logf(-logf(u));
+            scores[4 * q + w] = fmaf(z[4 * q + w], inv_t, g);
+        }
+    }
+}
+
+/* the draws of k rows (row index i of the counter = row i) */
+void orc_sample_rows(const float* z, int k, int V, float temperature, uint64_t seed, uint64_t offset, int* y) {
+    float* sc = (float*)malloc(sizeof(float) * (size_t)V);
+    for (int i = 0; i < k; i++) {
+        orc_sample_scores(z + (size_t)i * V, V, temperature, seed, offset, i, sc);
+        y[i] = argmax_row(sc, V);
+    }
+    free(sc);
+}
+
+int orc_accept_sampled(const float* logits_all, int k, int V, const int* tokens, float temperature, uint64_t seed,
+                       uint64_t offset, int* out_tokens, int* n_accepted, int* draws) {
+    int* y = (int*)malloc(sizeof(int) * (size_t)k);
+    orc_sample_rows(logits_all, k, V, temperature, seed, offset, y);
+    int a = 0;
+    while (a < k - 1 && tokens[a + 1] == y[a]) a++;
+    for (int i = 0; i < a; i++) out_tokens[i] = tokens[i + 1];
+    out_tokens[a] = y[a];
+    *n_accepted = a;
+    if (draws) memcpy(draws, y, sizeof(int) * (size_t)k);
+    free(y);
+    return 0;
+}
+
 /* ---- snapshot / restore with per-layer widths [PR2303, "What changes" item 1] -------------- */
 typedef struct orc_snapshot {
     int n_layers;

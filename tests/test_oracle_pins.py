@@ -1,6 +1,8 @@
 """Pins of the CPU oracle against what the pages and the mathematics fix (closed forms, hand cases,
 invariants, brute force on tiny inputs). No GPU; no HIP library."""
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -602,3 +604,92 @@ def test_embedded_entries_equal_token_entries():
     x0 = synth.bf16_to_f32(T._keep[2]["embed"][[3] + [tm.vocab - 1] * 7]) * np.float32(0.5)
     p2, l2 = oracle.draft_block_embedded(D, T, x0)
     assert np.array_equal(l1, l2) and np.array_equal(p1, p2)
+
+
+# ------------------------------------------------------------------------------------------
+# Sampled verify: Philox4x32-10 uniforms, Gumbel-max draws, the sampled accept
+# ------------------------------------------------------------------------------------------
+def test_philox_known_answers():
+    """The generator against the published known-answer vectors of Philox4x32-10."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")) as f:
+        kat = json.load(f)
+    for v in kat["vectors"]:
+        ctr = [int(x, 16) for x in v["counter"]]
+        key = [int(x, 16) for x in v["key"]]
+        out = oracle.philox4x32_10(ctr, key)
+        assert ["%08x" % x for x in out] == v["out"]
+
+
+@pytest.mark.parametrize("temperature", [0.7, 2.0])
+def test_sampled_draws_follow_softmax_of_logits_over_temperature(temperature):
+    """60000 draws of one row (row index i of the counter = draw i): the counts against
+    softmax(z / T) by a chi-square test at df = 5 (the 1e-6 quantile is 35.9). A sign error in the
+    Gumbel noise, a missing temperature or a biased uniform fails it."""
+    z = np.array([0.5, -1.0, 2.0, 0.0, 1.5, -0.3], dtype=np.float32)
+    n = 60000
+    y = oracle.sample_rows(np.repeat(z[None, :], n, axis=0), temperature, 12345, 7)
+    cnt = np.bincount(y, minlength=6)
+    p = np.exp(z.astype(np.float64) / temperature)
+    p /= p.sum()
+    chi2 = float(((cnt - n * p) ** 2 / (n * p)).sum())
+    assert chi2 < 35.9, (cnt, n * p)
+    # the other temperature's distribution is rejected (the test has power)
+    q = np.exp(z.astype(np.float64) / (temperature * 3.0))
+    q /= q.sum()
+    assert float(((cnt - n * q) ** 2 / (n * q)).sum()) > 200.0
+
+
+def test_sampled_draws_depend_on_seed_offset_and_row_only():
+    z = synth.f32_normal(0, "pins.sample.z", (3, 1000)).astype(np.float32)
+    a = oracle.sample_rows(z, 1.0, 1, 2)
+    assert np.array_equal(a, oracle.sample_rows(z, 1.0, 1, 2))           # deterministic
+    same = oracle.sample_rows(np.repeat(z[1:2], 64, 0), 1.0, 1, 2)
+    assert len(set(same.tolist())) > 1                                     # each row draws anew
+    assert not np.array_equal(oracle.sample_rows(np.repeat(z[:1], 64, 0), 1.0, 1, 2),
+                              oracle.sample_rows(np.repeat(z[:1], 64, 0), 1.0, 1, 3))   # offset matters
+    assert not np.array_equal(oracle.sample_rows(np.repeat(z[:1], 64, 0), 1.0, 1, 2),
+                              oracle.sample_rows(np.repeat(z[:1], 64, 0), 1.0, 2, 2))   # seed matters
+
+
+def test_sampled_scores_closed_form():
+    """One score written out from the definition: word j % 4 of the Philox block at counter
+    (j / 4, row, offset), u = (x >> 8 + 1/2) / 2^24, score = z / T - log(-log u), in fp32."""
+    z = np.linspace(-3, 3, 11).astype(np.float32)
+    T, seed, offset, row = 0.8, 0x1234567890ABCDEF, 0x0000000100000002, 3
+    sc = oracle.sample_scores(z, T, seed, offset, row)
+    for j in range(11):
+        x = oracle.philox4x32_10([j // 4, row, offset & 0xFFFFFFFF, offset >> 32], [seed & 0xFFFFFFFF, seed >> 32])[j % 4]
+        u = ((int(x) >> 8) + 0.5) / 2.0 ** 24
+        expect = float(z[j]) / T - math.log(-math.log(u))
+        assert abs(float(sc[j]) - expect) < 1e-5 * max(1.0, abs(expect))
+
+
+def test_sampled_small_temperature_is_greedy():
+    """T -> 0: the Gumbel noise (|g| < 18 for u in (2^-25, 1 - 2^-25)) is negligible next to
+    (z_max - z_second) / T, so the draw is the argmax."""
+    z = synth.f32_normal(0, "pins.sample.greedy", (8, 2000)).astype(np.float32)
+    top2 = np.sort(z, axis=1)[:, -2:]
+    assert np.all(top2[:, 1] - top2[:, 0] > 1e-4)
+    y = oracle.sample_rows(z, 1e-6, 99, 0)
+    assert np.array_equal(y, np.argmax(z, axis=1))
+
+
+def test_sampled_accept_with_concentrated_rows():
+    """Rows whose mass sits on one token (z = 60 there, 0 elsewhere, T = 1: every other token has
+    probability below e^-50) accept exactly like the greedy accept; the accept stops at the first
+    row whose draw differs from the next draft, and that draw is emitted."""
+    k, V = 6, 50
+    lg = np.zeros((k, V), dtype=np.float32)
+    target = [3, 7, 11, 13, 17, 19]
+    for i, t in enumerate(target):
+        lg[i, t] = 60.0
+    for mism in range(k):
+        toks = np.array([1] + target[:5], dtype=np.int32)
+        if mism < k - 1:
+            toks[mism + 1] = 0
+        a, em, draws = oracle.accept_sampled(lg, toks, 1.0, 5, 9)
+        assert draws.tolist() == target
+        ga, gem = oracle.accept_greedy(lg, toks)
+        assert (a, em.tolist()) == (ga, gem.tolist())
+        assert a == min(mism, k - 1)
+        assert em.tolist() == target[:a] + [target[a]]
