@@ -58,6 +58,7 @@ SIGNATURES = {
     "bvf_verify_batch": (_I32, [_P, _P, _I32, _P, _P]),
     "bvf_set_graph_mode": (_I32, [_P, _I32]),
     "bvf_accept_greedy": (_I32, [_P, _P, _I32, _P, _P, _P]),
+    "bvf_accept_sampled": (_I32, [_P, _P, _I32, _P, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, _P, _P, _P]),
     "bvf_steer_logits": (_I32, [_P, _P, _I32, _P, _P]),
     "bvf_commit_verify_rows": (_I32, [_P, _I32]),
     "bvf_snapshot_take": (_I32, [_P, ctypes.POINTER(_P)]),
@@ -228,6 +229,13 @@ class Model:
     def accept_greedy(self, d_logits_all, d_tokens, d_out_tokens, d_n_accepted):
         _check(lib().bvf_accept_greedy(self.h, _ptr(d_logits_all), int(d_tokens.numel()), _ptr(d_tokens),
                                        _ptr(d_out_tokens), _ptr(d_n_accepted)))
+
+    def accept_sampled(self, d_logits_all, d_tokens, d_out_tokens, d_n_accepted, temperature: float, seed: int,
+                       offset: int, d_draws=None):
+        _check(lib().bvf_accept_sampled(self.h, _ptr(d_logits_all), int(d_tokens.numel()), _ptr(d_tokens),
+                                        float(temperature), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
+                                        _ptr(d_out_tokens), _ptr(d_n_accepted),
+                                        None if d_draws is None else _ptr(d_draws)))
 
     def steer_logits(self, d_logits_all, d_tok, d_add):
         _check(lib().bvf_steer_logits(self.h, _ptr(d_logits_all), int(d_tok.numel()), _ptr(d_tok), _ptr(d_add)))

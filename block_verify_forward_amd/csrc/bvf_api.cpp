@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -646,6 +647,25 @@ bvf_status bvf_accept_greedy(bvf_model* m, const float* d_logits_all, int32_t k,
     if (k < 1 || k > kMaxRows) return fail(BVF_E_INVALID, "k = %d outside [1, %d]", k, kMaxRows);
     HIP_TRY(launch_argmax_accept(d_logits_all, k, m->d.vocab, d_tokens, m->am_val, m->am_idx, m->am_blocks, d_out_tokens,
                                  d_n_accepted, nullptr, m->st));
+    return ok();
+}
+
+bvf_status bvf_accept_sampled(bvf_model* m, const float* d_logits_all, int32_t k, const int32_t* d_tokens, float temperature,
+                              uint64_t seed, uint64_t offset, int32_t* d_out_tokens, int32_t* d_n_accepted,
+                              int32_t* d_draws) {
+    if (!m || !d_logits_all || !d_tokens || !d_out_tokens || !d_n_accepted) return fail(BVF_E_INVALID, "NULL argument");
+    if (is_draft(m->d)) return fail(BVF_E_INVALID, "accept on a draft model");
+    if (k < 1 || k > kMaxRows) return fail(BVF_E_INVALID, "k = %d outside [1, %d]", k, kMaxRows);
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return fail(BVF_E_INVALID, "temperature must be finite and > 0 (the greedy accept covers T = 0)");
+    SampleArgs sa;
+    sa.inv_t = 1.0f / temperature;
+    sa.key0 = (uint32_t)seed;
+    sa.key1 = (uint32_t)(seed >> 32);
+    sa.off0 = (uint32_t)offset;
+    sa.off1 = (uint32_t)(offset >> 32);
+    HIP_TRY(launch_argmax_accept(d_logits_all, k, m->d.vocab, d_tokens, m->am_val, m->am_idx, m->am_blocks, d_out_tokens,
+                                 d_n_accepted, d_draws, m->st, &sa));
     return ok();
 }
 

@@ -141,9 +141,14 @@ struct Attn {
 size_t attn_part_floats_needed(const Attn& a);
 hipError_t launch_attention(const Attn& a, hipStream_t st);
 
+// Sampled draws instead of the argmax: 1/T (fp32), Philox key (seed) and counter offset words.
+struct SampleArgs {
+    float inv_t;
+    uint32_t key0, key1, off0, off1;
+};
 hipError_t launch_argmax_accept(const float* logits, int k, int V, const int32_t* tokens, float* part_val,
                                 int* part_idx, int nb, int32_t* out_tokens, int32_t* n_acc, int32_t* argmax_out,
-                                hipStream_t st);
+                                hipStream_t st, const SampleArgs* sample = nullptr);
 int argmax_blocks(int V);
 hipError_t launch_steer(float* logits, int k, int V, const int32_t* tok, const float* add, hipStream_t st);
 

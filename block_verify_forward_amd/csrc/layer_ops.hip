@@ -711,6 +711,74 @@ __global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict_
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Sampled rows (temperature T > 0; [CARD] "How it is used": every position is sampled and compared
+// with the draft). Row i's draw is the first index of the maximum of the Gumbel-perturbed scores
+// fmaf(z_ij, 1/T, -log(-log u_ij)), which follows softmax(z_i / T). u_ij = ((x >> 8) + 1/2) / 2^24
+// with x the word j % 4 of one Philox4x32-10 block (Salmon, Moraes, Dror, Shaw, SC 2011) at counter
+// (j / 4, i, offset low, offset high) under key (seed low, seed high): each thread draws four
+// consecutive entries from one block and reads them with one 16-byte load.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {   // the key takes a Weyl step before every round after the first
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+
+__global__ __launch_bounds__(256) void k_sample_partial(const float* __restrict__ logits, int V, int nb,
+                                                        float* __restrict__ pv, int* __restrict__ pi, SampleArgs sa) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int b = blockIdx.x, row = blockIdx.y;
+    const int lo = b * kArgmaxSpan, hi = min(V, lo + kArgmaxSpan);   // lo is a multiple of 4
+    const float* lr = logits + (size_t)row * V;
+    float bv = 0.f;
+    int bi = -1;
+    for (int q = (lo >> 2) + (int)threadIdx.x; 4 * q < hi; q += 256) {
+        const uint4 x = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)row, sa.off0, sa.off1), sa.key0, sa.key1);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+        float z[4];
+        const int j0 = 4 * q;
+        if (j0 + 4 <= hi && (V & 3) == 0) {
+            const float4 v = *(const float4*)(lr + j0);
+            z[0] = v.x; z[1] = v.y; z[2] = v.z; z[3] = v.w;
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) z[w] = j0 + w < hi ? lr[j0 + w] : 0.f;
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (j0 + w >= hi) break;
+            const float u = ((float)(xs[w] >> 8) + 0.5f) * (1.0f / 16777216.0f);
+            const float g = -logf(-logf(u));
+            better(bv, bi, __builtin_fmaf(z[w], sa.inv_t, g), j0 + w);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (oi >= 0) better(bv, bi, ov, oi);
+    }
+    if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        bv = sv[0];
+        bi = si[0];
+        for (int w = 1; w < 4; ++w) if (si[w] >= 0) better(bv, bi, sv[w], si[w]);
+        pv[(size_t)row * nb + b] = bv;
+        pi[(size_t)row * nb + b] = bi;
+    }
+}
+
 __global__ __launch_bounds__(64) void k_accept(const float* __restrict__ pv, const int* __restrict__ pi, int nb, int k,
                                                const int32_t* __restrict__ tokens, int32_t* __restrict__ out_tokens,
                                                int32_t* __restrict__ n_acc, int32_t* __restrict__ argmax_out) {
@@ -889,8 +957,12 @@ hipError_t launch_attention(const Attn& x, hipStream_t st) {
 int argmax_blocks(int V) { return (V + kArgmaxSpan - 1) / kArgmaxSpan; }
 
 hipError_t launch_argmax_accept(const float* logits, int k, int V, const int32_t* tokens, float* part_val, int* part_idx,
-                                int nb, int32_t* out_tokens, int32_t* n_acc, int32_t* argmax_out, hipStream_t st) {
-    hipLaunchKernelGGL(k_argmax_partial, dim3(nb, k), dim3(256), 0, st, logits, V, nb, part_val, part_idx);
+                                int nb, int32_t* out_tokens, int32_t* n_acc, int32_t* argmax_out, hipStream_t st,
+                                const SampleArgs* sample) {
+    if (sample)
+        hipLaunchKernelGGL(k_sample_partial, dim3(nb, k), dim3(256), 0, st, logits, V, nb, part_val, part_idx, *sample);
+    else
+        hipLaunchKernelGGL(k_argmax_partial, dim3(nb, k), dim3(256), 0, st, logits, V, nb, part_val, part_idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, st, part_val, part_idx, nb, k, tokens, out_tokens, n_acc,

@@ -155,6 +155,20 @@ bvf_status bvf_set_graph_mode(bvf_model* m, int32_t on);
 bvf_status bvf_accept_greedy(bvf_model* m, const float* d_logits_all, int32_t k, const int32_t* d_tokens,
                              int32_t* d_out_tokens, int32_t* d_n_accepted);
 
+/* Sampled accept at temperature T > 0 ([CARD], "How it is used": with a sampler every position is
+ * sampled and compared with the draft, so the output follows the target's distribution). Row i's
+ * draw y_i is the first index of the maximum of fmaf(z_ij, 1/T, -log(-log u_ij)) in fp32 (the
+ * Gumbel-max method: y_i follows softmax(z_i / T)); u_ij = ((x >> 8) + 1/2) / 2^24 where x is the word
+ * j % 4 of the Philox4x32-10 block (Salmon, Moraes, Dror, Shaw, SC 2011) at counter
+ * (j / 4, i, offset bits 0-31, offset bits 32-63) under key (seed bits 0-31, seed bits 32-63). The accept
+ * then runs as in bvf_accept_greedy with y in place of the argmax. d_draws (NULL allowed) receives
+ * y [k]. The same (logits, seed, offset) always give the same draws; callers advance offset per call.
+ * Refuses a temperature that is not finite or not > 0 (BVF_E_INVALID). Device outputs; no host
+ * synchronisation. */
+bvf_status bvf_accept_sampled(bvf_model* m, const float* d_logits_all, int32_t k, const int32_t* d_tokens,
+                              float temperature, uint64_t seed, uint64_t offset, int32_t* d_out_tokens,
+                              int32_t* d_n_accepted, int32_t* d_draws);
+
 /* Harness hook for seeded acceptance (not part of the method): d_logits_all[i][d_tok[i]] += d_add[i]. */
 bvf_status bvf_steer_logits(bvf_model* m, float* d_logits_all, int32_t k, const int32_t* d_tok,
                             const float* d_add);
