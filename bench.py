@@ -135,7 +135,7 @@ def run_loop(args):
         T.set_graph_mode(True)
     rounds_max = args.loop
     steer = synth.accept_lengths(args.seed, rounds_max, max_a=7)
-    loop = SpecLoop(T, D, 8)
+    loop = SpecLoop(T, D, 8, temperature=args.temperature, seed=args.seed)
     snap_t, snap_d = T.snapshot_take(), D.snapshot_take()
     loop.start(17)
     for i in range(3):   # warm-up rounds, then back to the start
@@ -153,7 +153,8 @@ def run_loop(args):
     rounds = len(loop.accepted)
     assert loop.accepted == [int(a) for a in steer[:rounds]], "steered accept lengths not reproduced"
     res = {
-        "metric": "speculative decode tokens/s (draft block 8 + batched verify k=8 + greedy accept + commit)",
+        "metric": "speculative decode tokens/s (draft block 8 + batched verify k=8 + "
+                  + (f"sampled accept T={args.temperature}" if args.temperature > 0 else "greedy accept") + " + commit)",
         "value": round(len(toks) / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -181,6 +182,8 @@ def main():
     ap.add_argument("--layers", type=int, default=42, help="decoder layers (42 = the workload)")
     ap.add_argument("--vocab", type=int, default=262144)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: the step (or the loop) uses the sampled accept at this temperature instead of greedy")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="direct launches instead of the captured pass")
@@ -235,9 +238,15 @@ def main():
     out_tok = torch.zeros(k, dtype=torch.int32, device="cuda")
     n_acc = torch.zeros(1, dtype=torch.int32, device="cuda")
 
+    n_steps = [0]
+
     def step(tk, lg, tp):
         g.verify_batch(tk, lg, tp)
-        g.accept_greedy(lg, tk, out_tok, n_acc)
+        if args.temperature > 0:
+            g.accept_sampled(lg, tk, out_tok, n_acc, args.temperature, args.seed, n_steps[0])
+            n_steps[0] += 1
+        else:
+            g.accept_greedy(lg, tk, out_tok, n_acc)
         g.commit_verify_rows(0)
 
     def timed(nsteps, tk, lg, tp):
@@ -302,7 +311,8 @@ def main():
         "data": "synthetic (seeded draws, seed 0)",
         "config": {"workload": f"target-shaped verify: {m.n_layers} layers, hidden {H}, Q4_1, head {V}x{H} bf16, "
                                f"{args.ctx} cached positions, k={k}",
-                   "k": k, "cached_positions": args.ctx, "layers": m.n_layers, "vocab": V},
+                   "k": k, "cached_positions": args.ctx, "layers": m.n_layers, "vocab": V,
+                   "accept": "greedy" if args.temperature <= 0 else f"sampled, T={args.temperature}"},
         "q4_1_weight_stream_gbs": round(q4_gbs, 1),
         "q4_1_weight_stream_frac_of_peak": round(q4_gbs / HBM_PEAK_GBS, 4),
         "q4_1_bytes_per_pass": q4_bytes,

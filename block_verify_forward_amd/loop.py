@@ -12,6 +12,10 @@ context rows without leaving the device.
 Optional steering (seeded acceptance for synthetic weights): before the accept, row m < a gets a
 large bonus on proposal m + 1 and row a a large penalty on proposal a + 1, so exactly a proposals
 are accepted whatever the weights.
+
+With a temperature above 0 every verify row is sampled ([CARD] "How it is used") through the
+library's sampled accept: the Philox key is the loop's seed and the counter offset is the round
+number, so a run is reproducible and every round draws fresh uniforms.
 """
 from __future__ import annotations
 
@@ -25,7 +29,7 @@ from . import bvf
 
 class SpecLoop:
     def __init__(self, target: bvf.Model, draft: bvf.Model, block: int = 8, mask_token: Optional[int] = None,
-                 embedding_scale: float = 1.0, steer_bonus: float = 1.0e4):
+                 embedding_scale: float = 1.0, steer_bonus: float = 1.0e4, temperature: float = 0.0, seed: int = 0):
         self.T, self.D = target, draft
         self.block = block
         m = target.m
@@ -39,6 +43,10 @@ class SpecLoop:
         self.out = torch.zeros(block, dtype=torch.int32, device=dev)
         self.n_acc = torch.zeros(1, dtype=torch.int32, device=dev)
         self.add = torch.zeros(block - 1, dtype=torch.float32, device=dev)
+        self.draws = torch.zeros(block, dtype=torch.int32, device=dev)
+        self.temperature = float(temperature)
+        self.seed = int(seed)
+        self.n_rounds = 0
         self.n_new = 0
 
     def start(self, last_token: int):
@@ -59,7 +67,12 @@ class SpecLoop:
                 add[steer_a] = -self.bonus
             self.add.copy_(torch.from_numpy(add))
             self.T.steer_logits(self.logits, self.toks[1:], self.add)
-        self.T.accept_greedy(self.logits, self.toks, self.out, self.n_acc)
+        if self.temperature > 0.0:
+            self.T.accept_sampled(self.logits, self.toks, self.out, self.n_acc, self.temperature, self.seed,
+                                  self.n_rounds, self.draws)
+        else:
+            self.T.accept_greedy(self.logits, self.toks, self.out, self.n_acc)
+        self.n_rounds += 1
         a = int(self.n_acc.item())
         self.T.commit_verify_rows(a + 1)
         emitted = self.out[: a + 1].cpu().numpy().tolist()

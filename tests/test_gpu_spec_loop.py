@@ -125,3 +125,42 @@ def test_spec_loop_equals_greedy_decoding():
         prev = spec[i]
         tok.copy_(dev(np.array([prev], dtype=np.int32)))
     assert compared >= 12
+
+
+def test_spec_loop_sampled_matches_oracle():
+    """Eight rounds at temperature 0.8 without steering. Per round the oracle, teacher-forced with the
+    rows the GPU verified ([last token, the GPU draft's proposals]), computes the logits and draws
+    with the same key and counter offset (the round number). Each row's draw is compared where the
+    oracle's perturbed-score margin clears the logits' rounding differences; the accepted length and
+    the emitted tokens where every draw they depend on was compared."""
+    T_, SEED = 0.8, 31337
+    tm, dm, tw, dw, kv, kvd = models()
+    T, D = gpu_pair(tm, dm, tw, dw, kv, kvd)
+    To = oracle.Model(tm, tw)
+    To.set_kv(kv, P0)
+    loop = SpecLoop(T, D, BLOCK, temperature=T_, seed=SEED)
+    last = 17
+    loop.start(last)
+    compared_draws = compared_a = 0
+    for r in range(8):
+        a, emitted = loop.round()
+        rows = np.concatenate([[last], host(loop.toks)[1:]]).astype(np.int32)
+        draws = host(loop.draws)
+        lg = To.verify_batch(rows)
+        ra, remitted, rdraws = oracle.accept_sampled(lg, rows, T_, SEED, r)
+        clear = []
+        for i in range(BLOCK):
+            sc = oracle.sample_scores(lg[i], T_, SEED, r, i)
+            top = np.sort(sc)[-2:]
+            bar = 0.02 * np.sqrt(np.mean(lg[i].astype(np.float64) ** 2)) / T_
+            clear.append(bool(top[1] - top[0] > bar))
+            if clear[-1]:
+                assert draws[i] == rdraws[i], f"round {r} row {i}"
+                compared_draws += 1
+        if all(clear[: max(a, ra) + 1]):
+            assert a == ra and emitted == remitted.tolist(), f"round {r}"
+            compared_a += 1
+        To.commit_verify_rows(a + 1)
+        assert T.positions_held() == To.held()
+        last = emitted[a]
+    assert compared_draws >= 40 and compared_a >= 4
