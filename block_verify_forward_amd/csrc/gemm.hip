@@ -228,8 +228,21 @@ __device__ __forceinline__ void compute_slot(const uint8_t* slot, const uint16_t
     }
 }
 
+// RESID rows of a tile, loaded ahead (the split-K tail issues them before its arrival)
+__device__ __forceinline__ floatx4 load_resid_rows(const KArgs& a, int tile, int lane) {
+    const int c = lane & 15, sub = lane >> 4;
+    floatx4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * sub + r;
+        y[r] = m < a.M ? a.y[(size_t)m * a.ldy + tile * kTile + c] : 0.f;
+    }
+    return y;
+}
+
 template <int EPI>
-__device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int tile, int lane) {
+__device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int tile, int lane,
+                                         const floatx4* y_pre = nullptr) {
     const int c = lane & 15, sub = lane >> 4;
     const int n = tile * kTile + c;
     if constexpr (EPI == EPI_SWIGLU) {
@@ -263,7 +276,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
                 a.y[(size_t)m * a.ldy + tile * 8 + (c & 7)] = acc[r];
             }
         } else {
-            const float v = a.y[(size_t)m * a.ldy + n] + acc[r];
+            const float v = (y_pre ? (*y_pre)[r] : a.y[(size_t)m * a.ldy + n]) + acc[r];
             vout[r] = v;
             a.y[(size_t)m * a.ldy + n] = v;
             if (a.taps) a.taps[(size_t)m * a.ldt + n] = f32_to_bf16(v);
@@ -299,23 +312,25 @@ __device__ __forceinline__ void splitk_store(const KArgs& a, const floatx4& acc,
 
 __device__ __forceinline__ floatx4 splitk_sum(const KArgs& a, int tile, int lane) {
     const int c = lane & 15, sub = lane >> 4;
-    const int n = tile * kTile + c;
-    const size_t stride = (size_t)a.M * a.n_cols;
-    floatx4 acc;
+    const float* base = a.partial + tile * kTile + c;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    // the loads of four splits of the four rows go out together (one round for S <= 4); the sums
+    // run in split order
+    for (int sp0 = 0; sp0 < a.S; sp0 += 4) {
+        float v[4][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int m = 4 * sub + r;
-        const float* src = a.partial + (size_t)(m < a.M ? m : 0) * a.n_cols + n;
-        float s = 0.f;
-        for (int sp0 = 0; sp0 < a.S; sp0 += 8) {   // loads issued eight at a time, summed in order
-            float v[8];
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * sub + r < a.M ? 4 * sub + r : 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = sp0 + i < a.S ? __hip_atomic_load(src + (size_t)(sp0 + i) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s += v[i];
+            for (int i = 0; i < 4; ++i)
+                v[r][i] = sp0 + i < a.S
+                              ? __hip_atomic_load(base + ((sp0 + i) * a.M + m) * a.n_cols, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.f;
         }
-        acc[r] = s;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[r] += v[r][i];
     }
     return acc;
 }
@@ -554,6 +569,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     }
     wait_vm<0>();   // no copy into this wave's ring is left in flight
     if (S > 1 && kp == 0 && my_items > 0) {
+        // a single item's residual rows are loaded now, in the shadow of the stores and the arrival
+        floatx4 y_pre = {0.f, 0.f, 0.f, 0.f};
+        if (EPI == EPI_RESID && my_items == 1) y_pre = load_resid_rows(a, first + ts, lane);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are performed
         if (lane == 0) {
             for (int it = 0; it < my_items; ++it)
@@ -564,7 +582,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
         for (int it = 0; it < my_items; ++it) {
             if (!((last >> it) & 1u)) continue;
             const int tile = first + it * stride + ts;
-            epilogue<EPI>(a, splitk_sum(a, tile, lane), tile, lane);
+            epilogue<EPI>(a, splitk_sum(a, tile, lane), tile, lane, EPI == EPI_RESID && my_items == 1 ? &y_pre : nullptr);
             if (lane == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
