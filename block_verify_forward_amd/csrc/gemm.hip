@@ -242,7 +242,7 @@ __device__ __forceinline__ floatx4 load_resid_rows(const KArgs& a, int tile, int
 
 template <int EPI>
 __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int tile, int lane,
-                                         const floatx4* y_pre = nullptr) {
+                                         bool have_pre = false, floatx4 y_pre = {0.f, 0.f, 0.f, 0.f}) {
     const int c = lane & 15, sub = lane >> 4;
     const int n = tile * kTile + c;
     if constexpr (EPI == EPI_SWIGLU) {
@@ -276,7 +276,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
                 a.y[(size_t)m * a.ldy + tile * 8 + (c & 7)] = acc[r];
             }
         } else {
-            const float v = (y_pre ? (*y_pre)[r] : a.y[(size_t)m * a.ldy + n]) + acc[r];
+            const float v = (have_pre ? y_pre[r] : a.y[(size_t)m * a.ldy + n]) + acc[r];
             vout[r] = v;
             a.y[(size_t)m * a.ldy + n] = v;
             if (a.taps) a.taps[(size_t)m * a.ldt + n] = f32_to_bf16(v);
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
         for (int it = 0; it < my_items; ++it) {
             if (!((last >> it) & 1u)) continue;
             const int tile = first + it * stride + ts;
-            epilogue<EPI>(a, splitk_sum(a, tile, lane), tile, lane, EPI == EPI_RESID && my_items == 1 ? &y_pre : nullptr);
+            epilogue<EPI>(a, splitk_sum(a, tile, lane), tile, lane, EPI == EPI_RESID && my_items == 1, y_pre);
             if (lane == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
