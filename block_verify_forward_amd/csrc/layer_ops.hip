@@ -714,10 +714,11 @@ __global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict_
 // ---------------------------------------------------------------------------------------------
 // Sampled rows (temperature T > 0; [CARD] "How it is used": every position is sampled and compared
 // with the draft). Row i's draw is the first index of the maximum of the Gumbel-perturbed scores
-// fmaf(z_ij, 1/T, -log(-log u_ij)), which follows softmax(z_i / T). u_ij = ((x >> 8) + 1/2) / 2^24
+// fmaf(z_ij, 1/T, -log(-log u_ij)), which follows softmax(z_i / T). u_ij = ((x >> 9) + 1/2) / 2^23
 // with x the word j % 4 of one Philox4x32-10 block (Salmon, Moraes, Dror, Shaw, SC 2011) at counter
-// (j / 4, i, offset low, offset high) under key (seed low, seed high): each thread draws four
-// consecutive entries from one block and reads them with one 16-byte load.
+// (j / 4, i, offset low, offset high) under key (seed low, seed high); every such u is exact in fp32
+// and lies in [2^-24, 1 - 2^-24], so the noise is finite. Each thread draws four consecutive entries
+// from one block and reads them with one 16-byte load.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -757,7 +758,7 @@ __global__ __launch_bounds__(256) void k_sample_partial(const float* __restrict_
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             if (j0 + w >= hi) break;
-            const float u = ((float)(xs[w] >> 8) + 0.5f) * (1.0f / 16777216.0f);
+            const float u = ((float)(xs[w] >> 9) + 0.5f) * (1.0f / 8388608.0f);
             const float g = -logf(-logf(u));
             better(bv, bi, __builtin_fmaf(z[w], sa.inv_t, g), j0 + w);
         }

@@ -158,7 +158,7 @@ bvf_status bvf_accept_greedy(bvf_model* m, const float* d_logits_all, int32_t k,
 /* Sampled accept at temperature T > 0 ([CARD], "How it is used": with a sampler every position is
  * sampled and compared with the draft, so the output follows the target's distribution). Row i's
  * draw y_i is the first index of the maximum of fmaf(z_ij, 1/T, -log(-log u_ij)) in fp32 (the
- * Gumbel-max method: y_i follows softmax(z_i / T)); u_ij = ((x >> 8) + 1/2) / 2^24 where x is the word
+ * Gumbel-max method: y_i follows softmax(z_i / T)); u_ij = ((x >> 9) + 1/2) / 2^23 where x is the word
  * j % 4 of the Philox4x32-10 block (Salmon, Moraes, Dror, Shaw, SC 2011) at counter
  * (j / 4, i, offset bits 0-31, offset bits 32-63) under key (seed bits 0-31, seed bits 32-63). The accept
  * then runs as in bvf_accept_greedy with y in place of the argmax. d_draws (NULL allowed) receives

@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "orc_argmax": (I, [P, I]),
             "orc_accept_greedy": (I, [P, I, I, P, P, P]),
             "orc_philox4x32_10": (None, [P, P, P]),
+            "orc_gumbel_of_word": (ctypes.c_float, [ctypes.c_uint32]),
             "orc_sample_scores": (None, [P, I, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, I, P]),
             "orc_sample_rows": (None, [P, I, I, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, P]),
             "orc_accept_sampled": (I, [P, I, I, P, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, P, P, P]),
@@ -155,6 +156,11 @@ def philox4x32_10(counter, key) -> np.ndarray:
     out = np.zeros(4, dtype=np.uint32)
     lib().orc_philox4x32_10(_p(c), _p(k), _p(out))
     return out
+
+
+def gumbel_of_word(x: int) -> float:
+    """The Gumbel noise -log(-log u) of one 32-bit generator word (fp32)."""
+    return float(lib().orc_gumbel_of_word(int(x) & 0xFFFFFFFF))
 
 
 def sample_scores(z_row: np.ndarray, temperature: float, seed: int, offset: int, row: int) -> np.ndarray:

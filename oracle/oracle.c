@@ -618,10 +618,10 @@ int orc_accept_greedy(const float* logits_all, int k, int V, const int* tokens, 
  * and u_ij uniform on (0, 1), is distributed as softmax(z_i / T).
  * The uniforms come from the counter-based generator Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
  * "Parallel random numbers: as easy as 1, 2, 3", SC 2011) under key (seed bits 0-31, 32-63) and
- * counter (j / 4, i, offset bits 0-31, 32-63): x = output word j % 4, u = (floor(x / 2^8) + 1/2) / 2^24
- * (exact in fp32). The decision is taken in fp32, the kernel's precision: inv_t = 1 / T rounded to
- * fp32, score = fmaf(z, inv_t, g) with g = -logf(-logf(u)); the first index of the maximum wins;
- * NaN scores never win. */
+ * counter (j / 4, i, offset bits 0-31, 32-63): x = output word j % 4, u = (floor(x / 2^9) + 1/2) / 2^23,
+ * every value of which is exact in fp32 and lies in [2^-24, 1 - 2^-24], so g is finite. The decision
+ * is taken in fp32, the kernel's precision: inv_t = 1 / T rounded to fp32, score = fmaf(z, inv_t, g)
+ * with g = -logf(-logf(u)); the first index of the maximum wins; NaN scores never win. */
 static void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
     uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
     uint32_t k0 = key[0], k1 = key[1];
@@ -643,6 +643,14 @@ static void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t
 
 void orc_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out) { philox4x32_10(ctr, key, out); }
 
+/* the Gumbel noise of one generator word */
+static float gumbel_of_word(uint32_t x) {
+    const float u = ((float)(x >> 9) + 0.5f) * (1.0f / 8388608.0f);
+    return -logf(-logf(u));
+}
+
+float orc_gumbel_of_word(uint32_t x) { return gumbel_of_word(x); }
+
 /* fp32 scores z_ij / T + g_ij of row i (V entries) */
 void orc_sample_scores(const float* z, int V, float temperature, uint64_t seed, uint64_t offset, int row,
                        float* scores) {
@@ -653,9 +661,7 @@ void orc_sample_scores(const float* z, int V, float temperature, uint64_t seed, 
         uint32_t x[4];
         philox4x32_10(ctr, key, x);
         for (int w = 0; w < 4 && 4 * q + w < V; w++) {
-            const float u = ((float)(x[w] >> 8) + 0.5f) * (1.0f / 16777216.0f);
-            const float g = -logf(-logf(u));
-            scores[4 * q + w] = fmaf(z[4 * q + w], inv_t, g);
+            scores[4 * q + w] = fmaf(z[4 * q + w], inv_t, gumbel_of_word(x[w]));
         }
     }
 }

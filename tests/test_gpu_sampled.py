@@ -116,3 +116,17 @@ def test_sampled_refusals():
     for T in (0.0, -1.0, float("nan"), float("inf")):
         with pytest.raises(Exception):
             sampled_gpu(g, lg, np.zeros(2, dtype=np.int32), T, 1, 1)
+
+
+def test_sampled_dominant_token_always_drawn(full_vocab):
+    """A token 5000 above every other (T = 1) is drawn in every row and at every counter offset:
+    the noise is bounded (|g| < 17), so no other entry can win. 16 rows x 64 offsets x 262144
+    entries; a mapping of the generator word that let u reach 1 (infinite noise) would fail here
+    about 16 times."""
+    k, V = 16, 262144
+    lg = synth.f32_normal(0, "sampled.dominant", (k, V)).astype(np.float32)
+    hot = (np.arange(k) * 9973 + 17) % V
+    lg[np.arange(k), hot] += 5000.0
+    for off in range(64):
+        _, _, gd = sampled_gpu(full_vocab, lg, np.zeros(k, dtype=np.int32), 1.0, 99, off)
+        assert np.array_equal(gd, hot), f"offset {off}"

@@ -653,15 +653,29 @@ def test_sampled_draws_depend_on_seed_offset_and_row_only():
 
 def test_sampled_scores_closed_form():
     """One score written out from the definition: word j % 4 of the Philox block at counter
-    (j / 4, row, offset), u = (x >> 8 + 1/2) / 2^24, score = z / T - log(-log u), in fp32."""
+    (j / 4, row, offset), u = (x >> 9 + 1/2) / 2^23, score = z / T - log(-log u), in fp32."""
     z = np.linspace(-3, 3, 11).astype(np.float32)
     T, seed, offset, row = 0.8, 0x1234567890ABCDEF, 0x0000000100000002, 3
     sc = oracle.sample_scores(z, T, seed, offset, row)
     for j in range(11):
         x = oracle.philox4x32_10([j // 4, row, offset & 0xFFFFFFFF, offset >> 32], [seed & 0xFFFFFFFF, seed >> 32])[j % 4]
-        u = ((int(x) >> 8) + 0.5) / 2.0 ** 24
+        u = ((int(x) >> 9) + 0.5) / 2.0 ** 23
         expect = float(z[j]) / T - math.log(-math.log(u))
         assert abs(float(sc[j]) - expect) < 1e-5 * max(1.0, abs(expect))
+
+
+def test_gumbel_noise_is_finite_at_the_extreme_words():
+    """Every generator word gives a finite noise: u stays inside (0, 1) after the fp32 conversion
+    (the largest word must not round to u = 1, where -log(-log u) is infinite and that entry would
+    win every draw), and the noise grows with the word."""
+    words = [0, 1, 511, 512, 2 ** 31, 0xFFFFFDFF, 0xFFFFFE00, 0xFFFFFFFE, 0xFFFFFFFF]
+    g = [oracle.gumbel_of_word(x) for x in words]
+    assert all(math.isfinite(v) for v in g), g
+    assert g == sorted(g)
+    assert g[-1] < 17.0 and g[0] > -3.0                  # u in [2^-24, 1 - 2^-24]
+    for x in (0, 0xFFFFFFFF):
+        u = ((x >> 9) + 0.5) / 2.0 ** 23
+        assert abs(oracle.gumbel_of_word(x) + math.log(-math.log(u))) < 1e-5 * 17
 
 
 def test_sampled_small_temperature_is_greedy():
