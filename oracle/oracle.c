@@ -117,19 +117,22 @@ static void q4_1_matmul(const uint8_t* img, int n_out, int n_in, const double* x
     int nb = n_in / Q4_1_BLOCK;
 #pragma omp parallel for schedule(static)
     for (int n = 0; n < n_out; n++) {
-        double acc[64];
+        double acc[64];   /* rows in groups of 64; each output still sums blocks and elements in order */
         double w[Q4_1_BLOCK];
-        for (int r = 0; r < m; r++) acc[r] = 0.0;
-        for (int b = 0; b < nb; b++) {
-            q4_1_block(img + ((size_t)n * nb + b) * Q4_1_BYTES, w);
-            for (int r = 0; r < m; r++) {
-                const double* xr = x + (size_t)r * n_in + (size_t)b * Q4_1_BLOCK;
-                double a = acc[r];
-                for (int j = 0; j < Q4_1_BLOCK; j++) a += w[j] * xr[j];
-                acc[r] = a;
+        for (int r0 = 0; r0 < m; r0 += 64) {
+            const int mr = m - r0 < 64 ? m - r0 : 64;
+            for (int r = 0; r < mr; r++) acc[r] = 0.0;
+            for (int b = 0; b < nb; b++) {
+                q4_1_block(img + ((size_t)n * nb + b) * Q4_1_BYTES, w);
+                for (int r = 0; r < mr; r++) {
+                    const double* xr = x + (size_t)(r0 + r) * n_in + (size_t)b * Q4_1_BLOCK;
+                    double a = acc[r];
+                    for (int j = 0; j < Q4_1_BLOCK; j++) a += w[j] * xr[j];
+                    acc[r] = a;
+                }
             }
+            for (int r = 0; r < mr; r++) y[(size_t)(r0 + r) * n_out + n] = acc[r];
         }
-        for (int r = 0; r < m; r++) y[(size_t)r * n_out + n] = acc[r];
     }
 }
 
