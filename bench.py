@@ -172,6 +172,56 @@ def run_loop(args):
     print(json.dumps(res), flush=True)
 
 
+def run_prefill(args):
+    """Chunked prefill: args.prefill prompt tokens on top of args.ctx cached positions, in batched
+    passes of up to 16 rows (one pass over the weights per chunk), the head on the last chunk only;
+    the context is restored from a snapshot before every timed run."""
+    import torch
+    from block_verify_forward_amd import bvf, synth
+
+    threads = min(16, os.cpu_count() or 8)
+    m = synth.target_model(max_ctx=args.ctx + args.prefill + 64, n_layers=args.layers, vocab=args.vocab)
+    w = build_weights(m, args.seed, threads)
+    kv = synth.make_kv(m, args.ctx, args.seed, threads=threads)
+    g = bvf.Model(m)
+    g.load_weights(w)
+    g.set_context(kv, args.ctx)
+    toks = torch.from_numpy(synth.tokens(args.seed, "bench.prefill", args.prefill, m.vocab)).cuda()
+    last = torch.empty(m.vocab, dtype=torch.float32, device="cuda")
+    snap = g.snapshot_take()
+    for _ in range(max(1, args.warmup // 2)):
+        g.prefill(toks, last)
+        g.restore(snap)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.prefill(toks, last)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        assert g.positions_held() == args.ctx + args.prefill
+        g.restore(snap)
+    ms = float(np.median(times))
+    res = {
+        "metric": "chunked prefill tokens/s (16-row batched passes)",
+        "value": round(args.prefill / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": "q4_1 weights, bf16 x bf16 -> fp32 MFMA",
+        "data": f"synthetic (seeded draws, seed {args.seed})",
+        "config": {"workload": f"prefill of {args.prefill} tokens on {args.ctx} cached positions, target {m.n_layers} "
+                               f"layers hidden {m.hidden} Q4_1, chunks of 16 rows"},
+        "ms": round(ms, 3),
+        "chunks": (args.prefill + 15) // 16,
+        "ms_per_chunk": round(ms / ((args.prefill + 15) // 16), 4),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +232,8 @@ def main():
     ap.add_argument("--layers", type=int, default=42, help="decoder layers (42 = the workload)")
     ap.add_argument("--vocab", type=int, default=262144)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="instead of the verify step: chunked prefill of this many prompt tokens")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: the step (or the loop) uses the sampled accept at this temperature instead of greedy")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
@@ -205,6 +257,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     if args.loop > 0:
         return run_loop(args)
+    if args.prefill > 0:
+        return run_prefill(args)
     threads = min(16, os.cpu_count() or 8)
     m = synth.target_model(max_ctx=args.ctx + 64, n_layers=args.layers, vocab=args.vocab)
     t0 = time.time()

@@ -58,6 +58,7 @@ SIGNATURES = {
     "bvf_verify_batch": (_I32, [_P, _P, _I32, _P, _P]),
     "bvf_set_graph_mode": (_I32, [_P, _I32]),
     "bvf_accept_greedy": (_I32, [_P, _P, _I32, _P, _P, _P]),
+    "bvf_prefill": (_I32, [_P, _P, _I32, _P]),
     "bvf_accept_sampled": (_I32, [_P, _P, _I32, _P, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, _P, _P, _P]),
     "bvf_steer_logits": (_I32, [_P, _P, _I32, _P, _P]),
     "bvf_commit_verify_rows": (_I32, [_P, _I32]),
@@ -225,6 +226,10 @@ class Model:
 
     def set_graph_mode(self, on: bool):
         _check(lib().bvf_set_graph_mode(self.h, 1 if on else 0))
+
+    def prefill(self, d_tokens, d_last_logits=None):
+        _check(lib().bvf_prefill(self.h, _ptr(d_tokens), int(d_tokens.numel()),
+                                 None if d_last_logits is None else _ptr(d_last_logits)))
 
     def accept_greedy(self, d_logits_all, d_tokens, d_out_tokens, d_n_accepted):
         _check(lib().bvf_accept_greedy(self.h, _ptr(d_logits_all), int(d_tokens.numel()), _ptr(d_tokens),

@@ -633,6 +633,31 @@ bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, fl
     return ok();
 }
 
+bvf_status bvf_prefill(bvf_model* m, const int32_t* d_tokens, int32_t n, float* d_last_logits) {
+    if (!m || !d_tokens) return fail(BVF_E_INVALID, "NULL argument");
+    if (is_draft(m->d)) return fail(BVF_E_INVALID, "prefill on a draft model");
+    if (n < 1) return fail(BVF_E_INVALID, "n = %d < 1", n);
+    if (m->pending >= 0) return fail(BVF_E_STATE, "a verify of %d rows is pending: commit it first", m->pending);
+    if (m->held + n > m->d.max_ctx)
+        return fail(BVF_E_CAPACITY, "%lld held + %d rows > max_ctx %d", (long long)m->held, n, m->d.max_ctx);
+    bvf_status s = check_loaded(m);
+    if (s) return s;
+    const int H = m->d.hidden, V = m->d.vocab;
+    for (int off = 0; off < n; off += kMaxRows) {
+        const int c = std::min(kMaxRows, n - off);
+        const int P = (int)m->held;
+        HIP_TRY(launch_embed(d_tokens + off, -1, c, m->embed, V, H, 1.0f, m->x, m->ss_x, m->st));
+        for (int l = 0; l < m->d.n_layers; ++l) HIP_TRY(run_layer(m, l, m->x, c, P, nullptr, 0));
+        m->held += c;
+        if (off + c == n && d_last_logits) {
+            HIP_TRY(launch_head(m, nullptr, c, m->logits_tmp, m->st, m, m->x, m->final_norm));
+            HIP_TRY(hipMemcpyAsync(d_last_logits, m->logits_tmp + (size_t)(c - 1) * V, (size_t)V * 4,
+                                   hipMemcpyDeviceToDevice, m->st));
+        }
+    }
+    return ok();
+}
+
 bvf_status bvf_set_graph_mode(bvf_model* m, int32_t on) {
     if (!m) return fail(BVF_E_INVALID, "model is NULL");
     if (on != 0 && on != 1) return fail(BVF_E_INVALID, "graph mode must be 0 or 1");

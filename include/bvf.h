@@ -141,6 +141,16 @@ bvf_status bvf_positions_held(const bvf_model* m, int64_t* h_out);
 bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, float* d_logits_all,
                             uint16_t* d_taps);
 
+/* Chunked prefill ([PR2303] "What changes": the batched body; "Proof": the state test's chunk arms):
+ * the n tokens d_tokens[0..n) at positions P .. P+n-1 (P = positions held) go through every layer
+ * in chunks of up to 16 rows, each chunk one batched pass over the packed weights, and are kept
+ * (positions held = P + n; no commit needed). The head runs once, on the last chunk; d_last_logits
+ * [vocab] fp32 (NULL allowed) receives the last row's logits. With bvf_snapshot_take /
+ * bvf_restore this is a prefix cache: prefill a shared prefix once, snapshot, and restore it before
+ * each continuation. Refuses n < 1 (BVF_E_INVALID), P + n > max_ctx (BVF_E_CAPACITY) and a pending
+ * verify (BVF_E_STATE: commit it first); a refusal changes nothing. */
+bvf_status bvf_prefill(bvf_model* m, const int32_t* d_tokens, int32_t n, float* d_last_logits);
+
 /* Graph replay of bvf_verify_batch (1) or direct launches (0, the default). With 1 the pass is
  * captured once into a HIP graph (on a private stream) and replayed on the model's stream; the
  * capture is reused while positions held, k and the three buffer pointers stay the same, and is

@@ -1,0 +1,130 @@
+"""Chunked prefill on the GPU against the oracle, and snapshot/restore as a prefix cache.
+
+The prefill runs the batched body in chunks of up to 16 rows and keeps every row; the oracle runs
+the same rows as one batched verify plus commit (its batched verify equals sequential steps bit for
+bit). Compared: positions held and plane floats exactly; the last row's logits and the logits of a
+verify that follows, within the stack bar (2e-3, or three times the oracle's own spread under
+fp32-level perturbation of its inputs, as for the verify)."""
+import numpy as np
+import pytest
+
+import oracle
+from block_verify_forward_amd import bvf, synth
+from tests.test_gpu_parity import dev, embed_rows, host, logits_bar
+from tests.util import rel_l1
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+P0 = 24
+
+
+@pytest.fixture(scope="module")
+def setup():
+    m = synth.tiny_two_width_model(max_ctx=256)
+    w = synth.make_weights(m)
+    kv = synth.make_kv(m, P0)
+    return m, w, kv
+
+
+def gpu_model(m, w, kv):
+    g = bvf.Model(m)
+    g.load_weights(w)
+    g.set_context(kv, P0)
+    return g
+
+
+@pytest.mark.parametrize("n", [1, 16, 37, 100])
+def test_prefill_matches_oracle(setup, n):
+    m, w, kv = setup
+    g = gpu_model(m, w, kv)
+    toks = synth.tokens(0, f"prefill.{n}", n, m.vocab)
+    last = torch.empty(m.vocab, dtype=torch.float32, device="cuda")
+    g.prefill(dev(toks), last)
+    o = oracle.Model(m, w)
+    o.set_kv(kv, P0)
+    rlg = o.verify_batch(toks)
+    o.commit_verify_rows(n)
+    assert g.positions_held() == o.held() == P0 + n
+    assert np.array_equal(g.plane_floats(), o.plane_floats())
+    err = rel_l1(host(last)[None, :], rlg[-1:])
+
+    def run_prefill_oracle(arrs):
+        x = oracle.Model(m, w)
+        x.set_kv(arrs[1:], P0)
+        return x.verify_embedded(arrs[0])[-1:]
+
+    tol = logits_bar(err, run_prefill_oracle, [embed_rows(w, toks)] + kv)
+    print(f"prefill {n}: last-row logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    assert err < tol
+    # the context the prefill left: a verify of 8 rows on top of it
+    vt = synth.tokens(1, f"prefill.next.{n}", 8, m.vocab)
+    lg = torch.empty((8, m.vocab), dtype=torch.float32, device="cuda")
+    g.verify_batch(dev(vt), lg, None)
+    rv = o.verify_batch(vt)
+    err = rel_l1(host(lg), rv)
+
+    def run_oracle(arrs):
+        x = oracle.Model(m, w)
+        x.set_kv(arrs[1:], P0)
+        x.verify_batch(toks)
+        x.commit_verify_rows(n)
+        return x.verify_embedded(arrs[0])
+
+    tol = logits_bar(err, run_oracle, [embed_rows(w, vt)] + kv)
+    print(f"prefill {n}: next verify logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    assert err < tol
+
+
+def test_prefill_as_prefix_cache(setup):
+    """Prefill a 40-token prefix once, snapshot; per continuation: restore, prefill the suffix,
+    verify. Each equals a model that prefilled prefix + suffix from the start within the stack bar
+    (the two chunkings group rows differently, so the GEMM plans differ), and the counts are exact."""
+    m, w, kv = setup
+    prefix = synth.tokens(0, "prefix", 40, m.vocab)
+    cache = gpu_model(m, w, kv)
+    cache.prefill(dev(prefix))
+    snap = cache.snapshot_take()
+    held0 = cache.positions_held()
+    lg = torch.empty((4, m.vocab), dtype=torch.float32, device="cuda")
+    lg2 = torch.empty((4, m.vocab), dtype=torch.float32, device="cuda")
+    for j, ns in enumerate([5, 19, 33]):
+        suffix = synth.tokens(j, "suffix", ns, m.vocab)
+        cache.restore(snap)
+        assert cache.positions_held() == held0 == P0 + 40
+        cache.prefill(dev(suffix))
+        vt = synth.tokens(j, "cont", 4, m.vocab)
+        cache.verify_batch(dev(vt), lg, None)
+        cold = gpu_model(m, w, kv)
+        cold.prefill(dev(np.concatenate([prefix, suffix]).astype(np.int32)))
+        cold.verify_batch(dev(vt), lg2, None)
+        assert cache.positions_held() == cold.positions_held() == P0 + 40 + ns + 4
+        assert np.array_equal(cache.plane_floats(), cold.plane_floats())
+        err = rel_l1(host(lg), host(lg2))
+
+        def run_oracle(arrs, suffix=suffix):
+            x = oracle.Model(m, w)
+            x.set_kv(arrs[1:], P0)
+            x.verify_batch(np.concatenate([prefix, suffix]).astype(np.int32))
+            x.commit_verify_rows(40 + len(suffix))
+            return x.verify_embedded(arrs[0])
+
+        tol = logits_bar(err, run_oracle, [embed_rows(w, vt)] + kv)
+        print(f"prefix cache, suffix {ns}: rel-L1 {err:.2e} (bar {tol:.2e})")
+        assert err < tol
+        cache.commit_verify_rows(0)
+
+
+def test_prefill_refusals(setup):
+    m, w, kv = setup
+    g = gpu_model(m, w, kv)
+    toks = synth.tokens(0, "prefill.refuse", 8, m.vocab)
+    lg = torch.empty((8, m.vocab), dtype=torch.float32, device="cuda")
+    g.verify_batch(dev(toks), lg, None)
+    with pytest.raises(bvf.BvfError):          # a verify is pending
+        g.prefill(dev(toks))
+    g.commit_verify_rows(8)
+    big = np.zeros(m.max_ctx, dtype=np.int32)
+    with pytest.raises(bvf.BvfError):          # beyond max_ctx
+        g.prefill(dev(big))
+    assert g.positions_held() == P0 + 8       # refusals change nothing
