@@ -61,6 +61,11 @@ struct KArgs {
     int S, sb_per_split, n_tiles, n_cols;
     int ring_slots;   // LDS slots per wave ring (R)
     int KS;           // K parts per tile inside a workgroup (waves per tile)
+    int T;            // tiles per workgroup item (waves / KS)
+    // host-computed reciprocals, so the kernel divides without an integer-division sequence:
+    // n / KS = (n * mag_ks) >> 16 for n < 4096, n / stride = (n * mag_stride) >> 32 for n < 65536
+    uint32_t mag_ks;
+    uint64_t mag_stride;
     int half;   // STORE on a gate|up image: -1 all 16 columns, 0 the gate half, 1 the up half
     // RMSNorm folded into the staging of A (xsrc != nullptr): A = bf16(x * rinv * gain) with
     // rinv = 1 / sqrt(sum(ss_in[m][0 .. n_ss)) / K + eps)
@@ -335,8 +340,8 @@ __device__ __forceinline__ floatx4 splitk_sum(const KArgs& a, int tile, int lane
     return acc;
 }
 
-// Workgroup b of W = blockDim / 64 waves: split b % S (cross-workgroup K split), index u = b / S
-// among the U = grid / S workgroups of that split. The W waves are T = W / KS tiles times KS parts
+// Workgroup (u, split) of the grid U x S and W = blockDim / 64 waves: split = the cross-workgroup
+// K split, u = its index among the U workgroups of that split. The W waves are T = W / KS tiles times KS parts
 // of the split's K range (wave w: tile slot w / KS, part w % KS). Item i of the workgroup covers
 // tiles (u + i U) T + 0 .. T - 1; the KS partial tiles of an item are summed in LDS in part order.
 // Rows >= M of the MFMA tile read arbitrary LDS data: they only feed output rows that are never
@@ -352,15 +357,15 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: loop control stays scalar
     const int nw = blockDim.x >> 6;
     const int nthr = blockDim.x;
-    const int KS = a.KS, T = nw / KS;
-    const int ts = wave / KS, kp = wave - ts * KS;
+    const int KS = a.KS, T = a.T;
+    const int ts = (int)(((uint32_t)wave * a.mag_ks) >> 16), kp = wave - ts * KS;
     const int S = a.S;
-    const int split = blockIdx.x % S;
-    const int u = blockIdx.x / S;
-    const int U = gridDim.x / S;
+    const int split = blockIdx.y;
+    const int u = blockIdx.x;
+    const int U = gridDim.x;
     const int g0 = split * a.sb_per_split;
     const int nsb = min(a.G, g0 + a.sb_per_split) - g0;
-    const int spk = (nsb + KS - 1) / KS;
+    const int spk = (int)(((uint32_t)(nsb + KS - 1) * a.mag_ks) >> 16);
     const int kb0 = min(nsb, kp * spk), nkp = min(nsb, kb0 + spk) - kb0;   // this wave's superblocks
     const int lds_ld = a.sb_per_split * kSuper + 8;
     uint8_t* ring = lds_raw + (size_t)wave * a.ring_slots * SLOT;
@@ -370,17 +375,21 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
 
     const int first = u * T;            // first tile of item 0
     const int stride = U * T;           // tiles between items
-    const int items = first < a.n_tiles ? (a.n_tiles - 1 - first) / stride + 1 : 0;   // uniform in the workgroup
+    auto div_stride = [&](int n) { return (int)(((uint64_t)(uint32_t)n * a.mag_stride) >> 32); };
+    const int items = first < a.n_tiles ? div_stride(a.n_tiles - 1 - first) + 1 : 0;   // uniform in the workgroup
     // this wave's valid items: tile = first + i stride + ts < n_tiles
-    const int my_items = first + ts < a.n_tiles ? (a.n_tiles - 1 - first - ts) / stride + 1 : 0;
+    const int my_items = first + ts < a.n_tiles ? div_stride(a.n_tiles - 1 - first - ts) + 1 : 0;
     const int total = my_items * nkp;   // superblocks this wave streams
 
     // bf16 activation rows: direct global->LDS copies (1 KB = 4 superblocks of one row per
     // instruction), issued before the ring so the wave's first wait covers them
     const int chunks = (nsb + 3) / 4;
     if (!a.xsrc) {
-        for (int i = wave; i < a.M * chunks; i += nw) {
-            const int m = i / chunks, q = i - m * chunks;
+        int m = 0, q = wave;   // copy i = m chunks + q, i = wave, wave + nw, ...
+        while (q >= chunks) { q -= chunks; ++m; }
+        for (; m < a.M; q += nw) {
+            while (q >= chunks) { q -= chunks; ++m; }
+            if (m >= a.M) break;
             const int e = q * 512 + lane * 8;   // element offset in the K range
             if (e < nsb * kSuper)
                 __builtin_amdgcn_global_load_lds((const void*)(a.A + (size_t)m * a.lda + (size_t)g0 * kSuper + e),
@@ -590,6 +599,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
 
 template <int FMT, int EPI, int R>
 hipError_t launch_r(const KArgs& k, int grid, int waves, size_t lds, hipStream_t st) {
+    const dim3 g2((unsigned)(grid / k.S), (unsigned)k.S);   // U workgroups per split, S splits
     static bool attr_set = false;   // raise the dynamic LDS limit once per instantiation
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)k_gemm<FMT, EPI, R>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -597,7 +607,7 @@ hipError_t launch_r(const KArgs& k, int grid, int waves, size_t lds, hipStream_t
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemm<FMT, EPI, R>), dim3(grid), dim3(64 * waves), lds, st, k);
+    hipLaunchKernelGGL((k_gemm<FMT, EPI, R>), g2, dim3(64 * waves), lds, st, k);
     return hipGetLastError();
 }
 
@@ -746,6 +756,13 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
     k.sb_per_split = p.sb_per_split;
     k.ring_slots = p.ring_slots;
     k.KS = p.KS;
+    k.T = p.waves / p.KS;
+    k.mag_ks = (uint32_t)((65536u + p.KS - 1) / p.KS);
+    {
+        const uint64_t stride = (uint64_t)(p.grid / p.S) * k.T;
+        if (L.n_run_tiles >= 65536 || stride >= 65536 || p.waves > 16) return hipErrorInvalidValue;
+        k.mag_stride = ((1ull << 32) + stride - 1) / stride;
+    }
     k.n_tiles = L.n_run_tiles;
     k.n_cols = L.n_run_tiles * kTile;
     k.half = L.half;
