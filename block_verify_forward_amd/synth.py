@@ -63,6 +63,7 @@ class Model:
     rms_eps: float = 1.0e-6
     block_causal: int = 1     # 1: verify block (causal); 0: draft block (all block rows see each other)
     draft_window: int = 0     # draft only: context rows visible to the block (0 = all)
+    kv_bf16: int = 0          # 1: K/V planes stored in bf16 (a memory variant; the default planes are fp32)
 
     def kv_width(self, l: int) -> int:
         L = self.layers[l]

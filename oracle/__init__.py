@@ -49,6 +49,7 @@ def lib() -> ctypes.CDLL:
             "orc_set_layer": (None, [P, I] + [P] * 11),
             "orc_set_globals": (None, [P, P, P, P, P]),
             "orc_set_kv": (I, [P, I, P, L64]),
+            "orc_set_kv_bf16": (None, [P, I]),
             "orc_set_held": (None, [P, L64]),
             "orc_positions_held": (L64, [P]),
             "orc_plane": (ctypes.POINTER(ctypes.c_float), [P, I]),
@@ -211,6 +212,8 @@ class Model:
         self.h = lib().orc_model_new(m.n_layers, m.hidden, m.n_q_heads, m.vocab, m.max_ctx, m.qk_norm,
                                      m.rope_base, m.rms_eps, m.block_causal, m.draft_window,
                                      _p(fields), _p(taps), len(m.tap_layers))
+        if getattr(m, "kv_bf16", 0):
+            lib().orc_set_kv_bf16(self.h, 1)
         for l, d in enumerate(weights["layers"]):
             g = lambda k: _p(d[k]) if k in d else None
             lib().orc_set_layer(self.h, l, g("q"), g("k"), g("v"), g("o"), g("gate"), g("up"), g("down"),

@@ -244,6 +244,7 @@ typedef struct orc_model {
     float** plane;   /* own planes: [max_ctx][2][w] fp32 (K then V); NULL on a shared layer */
     long held;       /* positions held on every own plane */
     long pending;    /* rows appended by the last verify and not yet committed; -1 = none */
+    int kv_bf16;     /* planes stored in bf16: every K/V value is rounded (from fp32, RNE) when stored */
 } orc_model;
 
 static long kv_width(const orc_model* md, int l) {
@@ -306,9 +307,19 @@ void orc_set_globals(orc_model* md, const uint16_t* embed, const uint16_t* final
 }
 
 /* Cached context: every own plane gets `positions` rows [positions][2][w_l]. */
+/* bf16 K/V planes (a memory variant of the planes the pages keep as floats, [PR2303] "What changes"
+ * item 1): the stored value is the fp32 value rounded to bf16 (RNE); everything else is unchanged. */
+void orc_set_kv_bf16(orc_model* md, int on) { md->kv_bf16 = on; }
+
+static float store_kv(const orc_model* md, double v) {
+    const float f = (float)v;
+    return md->kv_bf16 ? (float)round_bf16((double)f) : f;
+}
+
 int orc_set_kv(orc_model* md, int l, const float* kv, long positions) {
     if (l < 0 || l >= md->n_layers || !md->plane[l] || positions > md->max_ctx) return 1;
-    memcpy(md->plane[l], kv, sizeof(float) * (size_t)positions * 2 * kv_width(md, l));
+    const size_t n = (size_t)positions * 2 * kv_width(md, l);
+    for (size_t i = 0; i < n; i++) md->plane[l][i] = store_kv(md, kv[i]);
     return 0;
 }
 
@@ -452,8 +463,8 @@ static void target_layer(orc_model* md, int l, int m, double* x, const long* pos
                 }
                 rope(kh, hd, p, md->rope_base);
                 for (int i = 0; i < hd; i++) {
-                    row[g * hd + i] = (float)kh[i];
-                    row[w + g * hd + i] = (float)vx[(size_t)r * kvd + (size_t)g * hd + i];
+                    row[g * hd + i] = store_kv(md, kh[i]);
+                    row[w + g * hd + i] = store_kv(md, vx[(size_t)r * kvd + (size_t)g * hd + i]);
                 }
             }
         }
@@ -793,8 +804,8 @@ int orc_draft_append(orc_model* dr, const uint16_t* taps, int n) {
                 }
                 rope(kh, hd, p, dr->rope_base);
                 for (int i = 0; i < hd; i++) {
-                    row[g * hd + i] = (float)kh[i];
-                    row[w + g * hd + i] = (float)round_f32(vx[(size_t)r * kvd + (size_t)g * hd + i]);
+                    row[g * hd + i] = store_kv(dr, kh[i]);
+                    row[w + g * hd + i] = store_kv(dr, round_f32(vx[(size_t)r * kvd + (size_t)g * hd + i]));
                 }
             }
         }
@@ -876,9 +887,9 @@ static int draft_block_x(orc_model* dr, const orc_model* target, int B, double* 
                     memcpy(kh, t, sizeof(double) * hd);
                 }
                 rope(kh, hd, p, dr->rope_base);
-                for (int i = 0; i < hd; i++) {
-                    kh[i] = round_f32(kh[i]);
-                    vx[(size_t)r * kvd + (size_t)g * hd + i] = round_f32(vx[(size_t)r * kvd + (size_t)g * hd + i]);
+                for (int i = 0; i < hd; i++) {   /* the block's rows are read as stored rows are */
+                    kh[i] = store_kv(dr, kh[i]);
+                    vx[(size_t)r * kvd + (size_t)g * hd + i] = store_kv(dr, round_f32(vx[(size_t)r * kvd + (size_t)g * hd + i]));
                 }
             }
         }

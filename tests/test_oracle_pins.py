@@ -707,3 +707,60 @@ def test_sampled_accept_with_concentrated_rows():
         assert (a, em.tolist()) == (ga, gem.tolist())
         assert a == min(mism, k - 1)
         assert em.tolist() == target[:a] + [target[a]]
+
+
+# ------------------------------------------------------------------------------------------
+# bf16 K/V planes (memory variant)
+# ------------------------------------------------------------------------------------------
+def _bf16_model(m):
+    import dataclasses
+    return dataclasses.replace(m, kv_bf16=1)
+
+
+def test_bf16_planes_round_to_nearest_even_on_store():
+    """Cached rows are stored rounded to bf16 (RNE from fp32): 1 + 2^-10 -> 1; the tie 1 + 2^-8
+    -> 1 (even); the tie 1 + 3 2^-8 -> 1 + 2^-6 (even); -2.75 stays (exact)."""
+    m = _bf16_model(synth.tiny_model(max_ctx=8))
+    o = oracle.Model(m, zero_weights(m))
+    kv = np.zeros((2, 2, m.kv_width(0)), dtype=np.float32)
+    vals = [1 + 2 ** -10, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -2.75]
+    kv[0, 0, :4] = vals
+    o.set_kv([kv], 2)
+    got = o.plane(0, 2)[0, 0, :4].tolist()
+    assert got == [1.0, 1.0, 1 + 2 ** -6, -2.75]
+
+
+def test_bf16_planes_single_key_returns_rounded_value():
+    """One visible key: attention returns its value row as stored, i.e. bf16(v)."""
+    m = _bf16_model(synth.tiny_model(max_ctx=8))
+    om = oracle.Model(m, zero_weights(m))
+    kv = np.zeros((1, 2, m.kv_width(0)), dtype=np.float32)
+    kv[0, 1, :] = 1 + 2 ** -10                                # V row
+    om.set_kv([kv], 1)
+    out = om.attend(0, np.ones(256, dtype=np.float32), 0)
+    assert np.all(out == 1.0)
+
+
+def test_bf16_planes_appended_rows_are_the_fp32_rows_rounded():
+    """A verify on bf16 planes stores each new K/V value as bf16 of the value the fp32 planes
+    store (same weights, same rows); the cached rows stay bf16 of their input."""
+    m32 = synth.tiny_two_width_model(max_ctx=64)
+    m16 = _bf16_model(m32)
+    w = synth.make_weights(m32)
+    kv = synth.make_kv(m32, 10)
+    toks = synth.tokens(0, "pins.bf16kv", 5, m32.vocab)
+    a, b = oracle.Model(m32, w), oracle.Model(m16, w)
+    a.set_kv(kv, 10)
+    b.set_kv(kv, 10)
+    a.verify_batch(toks)
+    b.verify_batch(toks)
+    r16 = lambda x: synth.bf16_to_f32(synth.bf16_bits(x.astype(np.float64)))
+    for l in range(m32.n_layers):
+        if not m32.own(l):
+            continue
+        pa, pb = a.plane(l, 15), b.plane(l, 15)
+        assert np.array_equal(pb[:10], r16(pa[:10]))
+        # layer 0's new rows see identical inputs on both models; later layers' inputs differ
+        if l == 0:
+            assert np.array_equal(pb[10:], r16(pa[10:]))
+        assert np.array_equal(pb, r16(pb))
