@@ -52,6 +52,12 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def planes(m, args):
+    """The model with bf16 K/V planes when --kv-bf16 is given (fp32 planes otherwise)."""
+    import dataclasses
+    return dataclasses.replace(m, kv_bf16=1) if args.kv_bf16 else m
+
+
 def build_weights(m, seed: int, threads: int):
     from block_verify_forward_amd import synth
     return synth.make_weights(m, seed, threads=threads)
@@ -117,8 +123,8 @@ def run_loop(args):
 
     threads = min(16, os.cpu_count() or 8)
     max_ctx = args.ctx + args.loop + 64
-    m = synth.target_model(max_ctx=max_ctx, n_layers=args.layers, vocab=args.vocab)
-    dm = synth.draft_model(max_ctx=max_ctx)
+    m = planes(synth.target_model(max_ctx=max_ctx, n_layers=args.layers, vocab=args.vocab), args)
+    dm = planes(synth.draft_model(max_ctx=max_ctx), args)
     t0 = time.time()
     w = synth.make_weights(m, args.seed, threads=threads)
     dw = synth.make_weights(dm, args.seed, threads=threads)
@@ -162,7 +168,8 @@ def run_loop(args):
         "vs_baseline": None,
         "data": f"synthetic (seeded draws, seed {args.seed}); acceptance steered: truncated geometric p=0.8467",
         "config": {"workload": f"speculative loop: target {m.n_layers} layers hidden {m.hidden} Q4_1, draft 5 layers "
-                               f"hidden 2560, block 8, {args.ctx} cached positions, {args.loop} tokens"},
+                               f"hidden 2560, block 8, {args.ctx} cached positions, {args.loop} tokens",
+                   "kv_planes": "bf16" if args.kv_bf16 else "fp32"},
         "tokens": len(toks),
         "rounds": rounds,
         "tokens_per_target_pass": round(len(toks) / rounds, 3),
@@ -180,7 +187,7 @@ def run_prefill(args):
     from block_verify_forward_amd import bvf, synth
 
     threads = min(16, os.cpu_count() or 8)
-    m = synth.target_model(max_ctx=args.ctx + args.prefill + 64, n_layers=args.layers, vocab=args.vocab)
+    m = planes(synth.target_model(max_ctx=args.ctx + args.prefill + 64, n_layers=args.layers, vocab=args.vocab), args)
     w = build_weights(m, args.seed, threads)
     kv = synth.make_kv(m, args.ctx, args.seed, threads=threads)
     g = bvf.Model(m)
@@ -214,7 +221,8 @@ def run_prefill(args):
         "dtype": "q4_1 weights, bf16 x bf16 -> fp32 MFMA",
         "data": f"synthetic (seeded draws, seed {args.seed})",
         "config": {"workload": f"prefill of {args.prefill} tokens on {args.ctx} cached positions, target {m.n_layers} "
-                               f"layers hidden {m.hidden} Q4_1, chunks of 16 rows"},
+                               f"layers hidden {m.hidden} Q4_1, chunks of 16 rows",
+                   "kv_planes": "bf16" if args.kv_bf16 else "fp32"},
         "ms": round(ms, 3),
         "chunks": (args.prefill + 15) // 16,
         "ms_per_chunk": round(ms / ((args.prefill + 15) // 16), 4),
@@ -238,6 +246,7 @@ def main():
                     help="> 0: the step (or the loop) uses the sampled accept at this temperature instead of greedy")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-bf16", action="store_true", help="K/V planes hold bf16 values (half the plane bytes)")
     ap.add_argument("--no-graph", action="store_true", help="direct launches instead of the captured pass")
     ap.add_argument("--loop", type=int, default=0,
                     help="instead of the verify step: the speculative loop (draft block of 8 + batched verify + "
@@ -248,7 +257,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: this benchmark runs the verify pass on one GPU only; "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
+              "--gpus above 1 is not supported", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -260,7 +269,7 @@ def main():
     if args.prefill > 0:
         return run_prefill(args)
     threads = min(16, os.cpu_count() or 8)
-    m = synth.target_model(max_ctx=args.ctx + 64, n_layers=args.layers, vocab=args.vocab)
+    m = planes(synth.target_model(max_ctx=args.ctx + 64, n_layers=args.layers, vocab=args.vocab), args)
     t0 = time.time()
     w = build_weights(m, args.seed, threads)
     kv = synth.make_kv(m, args.ctx, args.seed)
@@ -366,7 +375,8 @@ def main():
         "config": {"workload": f"target-shaped verify: {m.n_layers} layers, hidden {H}, Q4_1, head {V}x{H} bf16, "
                                f"{args.ctx} cached positions, k={k}",
                    "k": k, "cached_positions": args.ctx, "layers": m.n_layers, "vocab": V,
-                   "accept": "greedy" if args.temperature <= 0 else f"sampled, T={args.temperature}"},
+                   "accept": "greedy" if args.temperature <= 0 else f"sampled, T={args.temperature}",
+                   "kv_planes": "bf16" if args.kv_bf16 else "fp32"},
         "q4_1_weight_stream_gbs": round(q4_gbs, 1),
         "q4_1_weight_stream_frac_of_peak": round(q4_gbs / HBM_PEAK_GBS, 4),
         "q4_1_bytes_per_pass": q4_bytes,

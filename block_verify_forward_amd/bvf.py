@@ -38,7 +38,7 @@ class ModelDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
                 ("block_causal", ctypes.c_int32), ("draft_window", ctypes.c_int32), ("n_taps", ctypes.c_int32),
                 ("tap_layers", ctypes.POINTER(ctypes.c_int32)), ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float), ("layers", ctypes.POINTER(LayerDesc))]
+                ("rms_eps", ctypes.c_float), ("layers", ctypes.POINTER(LayerDesc)), ("kv_bf16", ctypes.c_int32)]
 
 
 # exported symbol -> (restype, argtypes); the list is the header's declarations
@@ -51,6 +51,7 @@ SIGNATURES = {
     "bvf_load_q4_1": (_I32, [_P, _I32, _I32, _P, _SZ, _I32, _I32]),
     "bvf_load_bf16": (_I32, [_P, _I32, _I32, _P, _SZ]),
     "bvf_set_kv": (_I32, [_P, _I32, _P, _I64]),
+    "bvf_get_kv": (_I32, [_P, _I32, _P, _I64]),
     "bvf_set_positions": (_I32, [_P, _I64]),
     "bvf_kv_widths": (_I32, [_P, _P, _I32]),
     "bvf_plane_floats": (_I32, [_P, _P, _I32]),
@@ -121,7 +122,7 @@ def make_desc(m) -> tuple:
     vocab = m.vocab
     d = ModelDesc(m.n_layers, m.hidden, m.n_q_heads, vocab, m.max_ctx, m.qk_norm, m.block_causal, m.draft_window,
                   len(m.tap_layers), ctypes.cast(taps, ctypes.POINTER(ctypes.c_int32)), m.rope_base, m.rms_eps,
-                  ctypes.cast(layers, ctypes.POINTER(LayerDesc)))
+                  ctypes.cast(layers, ctypes.POINTER(LayerDesc)), int(getattr(m, "kv_bf16", 0)))
     return d, layers, taps
 
 
@@ -193,6 +194,12 @@ class Model:
     def set_kv(self, layer: int, kv: np.ndarray, positions: int):
         kv = np.ascontiguousarray(kv[:positions], dtype=np.float32)
         _check(lib().bvf_set_kv(self.h, layer, _host(kv), positions))
+
+    def get_kv(self, layer: int, positions: int) -> np.ndarray:
+        """The first `positions` rows of layer's own plane, [positions, 2, w] fp32."""
+        out = np.empty((positions, 2, self.kv_widths()[layer]), dtype=np.float32)
+        _check(lib().bvf_get_kv(self.h, layer, _host(out), positions))
+        return out
 
     def set_positions(self, positions: int):
         _check(lib().bvf_set_positions(self.h, positions))

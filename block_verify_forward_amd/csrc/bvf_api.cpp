@@ -58,7 +58,7 @@ struct Layer {
     int qd = 0, kvd = 0;   // q width, own k/v width (0 on a shared layer)
     Mat qkv, o, gu, down;
     uint16_t *attn_norm = nullptr, *mlp_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
-    float* plane = nullptr;   // own plane [max_ctx][2][w]
+    void* plane = nullptr;    // own plane [max_ctx][2][w] of fp32 or bf16 values (kv_bf16)
     const float2* rope = nullptr;
     unsigned loaded = 0;      // bit i: matrix i; bits 8..11: norms
 };
@@ -121,6 +121,7 @@ struct bvf_snapshot {
     int n_layers = 0;
     int64_t held = 0;
     int device = 0;
+    int kv_elem = 4;   // bytes per stored K/V value
     std::vector<int64_t> per;
     std::vector<int> shared;
     std::vector<float*> data;
@@ -145,6 +146,7 @@ bvf_status check_desc(const bvf_model_desc* d) {
     if (d->n_taps > 0 && !d->tap_layers && !is_draft(*d)) return fail(BVF_E_INVALID, "tap_layers is NULL");
     if (is_draft(*d) && d->n_taps < 1) return fail(BVF_E_INVALID, "a draft needs n_taps >= 1 (fc input rows)");
     if (d->draft_window < 0) return fail(BVF_E_INVALID, "draft_window < 0");
+    if (d->kv_bf16 != 0 && d->kv_bf16 != 1) return fail(BVF_E_INVALID, "kv_bf16 must be 0 or 1");
     if (!is_draft(*d))
         for (int t = 0; t < d->n_taps; ++t)
             if (d->tap_layers[t] < 0 || d->tap_layers[t] >= d->n_layers)
@@ -211,7 +213,7 @@ size_t layout(bvf_model* m, uint8_t* base) {
         L.mlp_norm = (uint16_t*)take((size_t)H * 2);
         L.q_norm = (uint16_t*)take((size_t)hd * 2);
         L.k_norm = (uint16_t*)take((size_t)hd * 2);
-        L.plane = own ? (float*)take((size_t)d.max_ctx * 2 * L.w * 4) : nullptr;
+        L.plane = own ? (void*)take((size_t)d.max_ctx * 2 * L.w * (d.kv_bf16 ? 2 : 4)) : nullptr;
         m->hd_max = std::max(m->hd_max, hd);
         m->qd_max = std::max(m->qd_max, L.qd);
         m->nqkv_max = std::max(m->nqkv_max, L.qd + 2 * L.kvd);
@@ -391,6 +393,7 @@ hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps
     if ((e = launch_gemm(g, st)) != hipSuccess) return e;
     Attn at = attn_for(m, L, k);
     at.plane = L.plane ? L.plane : m->L[L.d.kv_owner].plane;
+    at.kv_bf16 = m->d.kv_bf16;
     at.own = L.plane != nullptr;
     at.causal = 1; at.pos0 = P; at.window = L.d.attn == BVF_ATTN_SLIDING ? L.d.window : 0;
     at.np0 = P; at.np1 = P + k; at.sp = P; at.r_lo = 0; at.r_hi = 0;
@@ -535,8 +538,42 @@ bvf_status bvf_set_kv(bvf_model* m, int32_t layer, const float* h_kv, int64_t po
     Layer& L = m->L[layer];
     if (!L.plane) return fail(BVF_E_INVALID, "layer %d is KV-shared: it holds no plane", layer);
     if (positions < 0 || positions > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions %lld > max_ctx", (long long)positions);
-    HIP_TRY(hipMemcpyAsync(L.plane, h_kv, (size_t)positions * 2 * L.w * 4, hipMemcpyHostToDevice, m->st));
+    const size_t n = (size_t)positions * 2 * L.w;
+    if (!m->d.kv_bf16) {
+        HIP_TRY(hipMemcpyAsync(L.plane, h_kv, n * 4, hipMemcpyHostToDevice, m->st));
+        HIP_TRY(hipStreamSynchronize(m->st));
+        return ok();
+    }
+    std::vector<uint16_t> b(n);   // bf16 planes: each value rounded to nearest even (NaN kept quiet)
+    for (size_t i = 0; i < n; ++i) {
+        uint32_t u;
+        std::memcpy(&u, &h_kv[i], 4);
+        b[i] = (u & 0x7fffffffu) > 0x7f800000u ? (uint16_t)((u >> 16) | 0x40u)
+                                                : (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
     HIP_TRY(hipStreamSynchronize(m->st));
+    HIP_TRY(hipMemcpy(L.plane, b.data(), n * 2, hipMemcpyHostToDevice));
+    return ok();
+}
+
+bvf_status bvf_get_kv(const bvf_model* m, int32_t layer, float* h_kv, int64_t positions) {
+    if (!m || !h_kv) return fail(BVF_E_INVALID, "NULL argument");
+    if (layer < 0 || layer >= m->d.n_layers) return fail(BVF_E_INVALID, "layer %d out of range", layer);
+    const Layer& L = m->L[layer];
+    if (!L.plane) return fail(BVF_E_INVALID, "layer %d is KV-shared: it holds no plane", layer);
+    if (positions < 0 || positions > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions %lld > max_ctx", (long long)positions);
+    const size_t n = (size_t)positions * 2 * L.w;
+    HIP_TRY(hipStreamSynchronize(m->st));
+    if (!m->d.kv_bf16) {
+        HIP_TRY(hipMemcpy(h_kv, L.plane, n * 4, hipMemcpyDeviceToHost));
+        return ok();
+    }
+    std::vector<uint16_t> b(n);
+    HIP_TRY(hipMemcpy(b.data(), L.plane, n * 2, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t u = (uint32_t)b[i] << 16;
+        std::memcpy(&h_kv[i], &u, 4);
+    }
     return ok();
 }
 
@@ -717,6 +754,7 @@ bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out) {
     s->n_layers = m->d.n_layers;
     s->held = m->held;
     s->device = m->device;
+    s->kv_elem = m->d.kv_bf16 ? 2 : 4;
     for (int l = 0; l < m->d.n_layers; ++l) {
         s->per.push_back(m->L[l].w);
         s->shared.push_back(m->L[l].plane ? 0 : 1);
@@ -724,7 +762,7 @@ bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out) {
     }
     for (int l = 0; l < m->d.n_layers; ++l) {
         if (s->shared[l] || s->held == 0) continue;
-        const size_t bytes = (size_t)bvf_cut_floats(s->per.data(), s->n_layers, l, s->held) * 4;
+        const size_t bytes = (size_t)bvf_cut_floats(s->per.data(), s->n_layers, l, s->held) * s->kv_elem;
         hipError_t e = hipMalloc((void**)&s->data[l], bytes);
         if (e == hipSuccess) e = hipMemcpyAsync(s->data[l], m->L[l].plane, bytes, hipMemcpyDeviceToDevice, m->st);
         if (e != hipSuccess) {
@@ -751,9 +789,11 @@ bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s) {
         if (s->shared[l] != (m->L[l].plane ? 0 : 1)) return fail(BVF_E_INVALID, "layer %d: shared/own mismatch", l);
     }
     if (s->held > m->d.max_ctx) return fail(BVF_E_CAPACITY, "snapshot holds more positions than max_ctx");
+    if (s->kv_elem != (m->d.kv_bf16 ? 2 : 4)) return fail(BVF_E_INVALID, "snapshot of %s planes, model of %s planes",
+                                                           s->kv_elem == 2 ? "bf16" : "fp32", m->d.kv_bf16 ? "bf16" : "fp32");
     for (int l = 0; l < m->d.n_layers; ++l) {
         if (s->shared[l] || !s->data[l]) continue;
-        const size_t bytes = (size_t)bvf_cut_floats(s->per.data(), s->n_layers, l, s->held) * 4;
+        const size_t bytes = (size_t)bvf_cut_floats(s->per.data(), s->n_layers, l, s->held) * s->kv_elem;
         HIP_TRY(hipMemcpyAsync(m->L[l].plane, s->data[l], bytes, hipMemcpyDeviceToDevice, m->st));
     }
     HIP_TRY(hipStreamSynchronize(m->st));
@@ -826,7 +866,7 @@ bvf_status bvf_draft_block_forward(bvf_model* dr, const bvf_model* tg, const uin
             ra.pos0 = s_old; ra.pos1 = s_old;
             ra.Hq = dr->d.n_q_heads; ra.nkv = L.d.n_kv_heads; ra.hd = L.d.head_dim; ra.own = 1;
             ra.qk_norm = dr->d.qk_norm; ra.q_norm = L.q_norm; ra.k_norm = L.k_norm; ra.eps = dr->d.rms_eps;
-            ra.rope = L.rope; ra.plane = L.plane; ra.w = L.w; ra.q_out = dr->qbuf;
+            ra.rope = L.rope; ra.plane = L.plane; ra.kv_bf16 = dr->d.kv_bf16; ra.w = L.w; ra.q_out = dr->qbuf;
             HIP_TRY(launch_rope_append(ra, st));
         }
         dr->held = s;
@@ -844,7 +884,7 @@ bvf_status bvf_draft_block_forward(bvf_model* dr, const bvf_model* tg, const uin
         // block rows 0..B-1 at s .. s+B-1 and context rows B.. at s_old .. s-1 are appended; the
         // block sees the context window and all block rows
         Attn at = attn_for(dr, L, B);
-        at.plane = L.plane; at.own = 1;
+        at.plane = L.plane; at.kv_bf16 = dr->d.kv_bf16; at.own = 1;
         at.causal = 0; at.pos0 = s_new; at.ctx_lo = ctx_lo; at.ctx_hi = s_new + B - 1;
         at.np0 = s_old; at.np1 = s_new + B; at.sp = s_new; at.r_lo = B; at.r_hi = 0;
         HIP_TRY(launch_attention(at, st));

@@ -108,7 +108,8 @@ struct RopeAppend {
     const uint16_t* k_norm = nullptr;
     float eps = 0.f;
     const float2* rope = nullptr;  // [max_ctx][hd / 2] (cos, sin)
-    float* plane = nullptr;        // own plane [max_ctx][2][w]
+    void* plane = nullptr;         // own plane [max_ctx][2][w], fp32 or (kv_bf16) bf16 values
+    int kv_bf16 = 0;
     int w = 0;
     float* q_out = nullptr;        // [rows_q][Hq][hd]
 };
@@ -123,7 +124,8 @@ struct Attn {
     int qk_norm = 0;
     float eps = 0.f;
     const float2* rope = nullptr;
-    float* plane = nullptr;      // [max_ctx][2][w] (own or owner's)
+    void* plane = nullptr;       // [max_ctx][2][w] (own or owner's), fp32 or (kv_bf16) bf16 values
+    int kv_bf16 = 0;
     int w = 0, own = 0;
     int M = 0, Hq = 0, nkv = 0, hd = 0;
     int causal = 1;              // 1: row m at pos0 + m sees [max(0, pos0 + m - window + 1), pos0 + m]

@@ -28,6 +28,33 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier over LDS traffic only: this wave's LDS reads and writes are complete, then
+// s_barrier. (__syncthreads also waits for every outstanding global load, which would wait for the
+// next sub-chunk's K/V copies.)
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void wait_lds() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// 4-byte LDS read that the compiler's wait-count insertion does not see (it would otherwise wait
+// for outstanding global->LDS copies into other arrays); the caller calls wait_lds() before using
+// the value.
+__device__ __forceinline__ float lds_read_f32_untracked(const float* p) {
+    float v;
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
 // Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15) without LDS traffic: quad
 // swaps, then the half-row and row mirrors; every lane ends with the same bits.
 template <int CTRL>
@@ -227,7 +254,8 @@ __global__ __launch_bounds__(64) void k_rope_append(RopeAppend a) {
     const int hd = a.hd, h2 = hd / 2;
     const int p = row < a.split_row ? a.pos0 + row : a.pos1 + (row - a.split_row);
     const float* src;
-    float* dst;
+    float* dst = nullptr;        // q heads, or a K row of an fp32 plane
+    uint16_t* dst16 = nullptr;   // a K row of a bf16 plane
     const uint16_t* gain;
     const int qd = a.Hq * hd, kvd = a.nkv * hd;
     if (head < a.Hq) {
@@ -239,11 +267,18 @@ __global__ __launch_bounds__(64) void k_rope_append(RopeAppend a) {
         if (!a.own || row >= a.rows) return;
         const int gh = head - a.Hq;
         src = a.qkv + (size_t)row * a.ldq + qd + gh * hd;
-        float* prow = a.plane + (size_t)p * 2 * a.w;
-        dst = prow + gh * hd;
         gain = a.k_norm;
         const float* vs = a.qkv + (size_t)row * a.ldq + qd + kvd + gh * hd;
-        for (int i = lane; i < hd; i += 64) prow[a.w + gh * hd + i] = vs[i];
+        const size_t off = (size_t)p * 2 * a.w;
+        if (a.kv_bf16) {
+            uint16_t* prow = (uint16_t*)a.plane + off;
+            dst16 = prow + gh * hd;
+            for (int i = lane; i < hd; i += 64) prow[a.w + gh * hd + i] = f32_to_bf16(vs[i]);
+        } else {
+            float* prow = (float*)a.plane + off;
+            dst = prow + gh * hd;
+            for (int i = lane; i < hd; i += 64) prow[a.w + gh * hd + i] = vs[i];
+        }
     }
     float lo[4], hi[4];
     float ss = 0.f;
@@ -268,8 +303,14 @@ __global__ __launch_bounds__(64) void k_rope_append(RopeAppend a) {
             x1 *= bf16_to_f32(gain[i + h2]);
         }
         const float2 cs = rt[i];
-        dst[i] = x0 * cs.x - x1 * cs.y;
-        dst[i + h2] = x0 * cs.y + x1 * cs.x;
+        const float y0 = x0 * cs.x - x1 * cs.y, y1 = x0 * cs.y + x1 * cs.x;
+        if (dst16) {
+            dst16[i] = f32_to_bf16(y0);
+            dst16[i + h2] = f32_to_bf16(y1);
+        } else {
+            dst[i] = y0;
+            dst[i + h2] = y1;
+        }
     }
 }
 
@@ -299,7 +340,8 @@ struct AttnK {
     int qk_norm;
     float eps;
     const float2* rope;      // [max_ctx][hd / 2]
-    float* plane;            // own or owner's plane [max_ctx][2][w]
+    void* plane;             // own or owner's plane [max_ctx][2][w], fp32 or (kv_bf16) bf16 values
+    int kv_bf16;
     int w, own;
     int M, Hq, nkv, Hg, NQ, n_qt;
     int causal, pos0, window, ctx_lo, ctx_hi;
@@ -333,17 +375,53 @@ __device__ __forceinline__ float head_ss(const AttnK& a, int r, int c0, int hd) 
 template <int HD>
 constexpr int attn_ck() { return 4096 / HD > 16 ? 4096 / HD : 16; }
 
-template <int HD>
+// Tile element of the K/V planes: fp32, or (KVB) bf16 values widened exactly where they are read.
+template <bool KVB> struct KVElem { using T = float; };
+template <> struct KVElem<true> { using T = uint16_t; };
+
+template <int N>
+__device__ __forceinline__ void store_bf16_vec(uint16_t* p, const float* v) {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 2; i += 4) *(uint4*)(p + 2 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+    } else if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 2; i += 2) *(uint2*)(p + 2 * i) = make_uint2(w[i], w[i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) *(uint32_t*)(p + 2 * i) = w[i];
+    }
+}
+
+// One workgroup per (key chunk, KV head, tile of 16 query vectors). The chunk's keys go through LDS
+// in sub-chunks of CK keys, in two stages: the copies of sub-chunk i + 1 are in flight while
+// sub-chunk i is scored and weighted. The two stages are distinct LDS arrays, so the compiler's
+// wait-count insertion sees that reads of one stage do not depend on copies into the other.
+// KVB: the planes hold bf16 values; the tiles keep them as bf16 and the reads widen them (exact),
+// and new rows are written rounded to the plane and the tile, so every K/V value the scores and
+// PV see is the stored one.
+template <int HD, bool KVB>
 __global__ __launch_bounds__(256) void k_attention(AttnK a) {
+    using TT = typename KVElem<KVB>::T;
     constexpr int CK = attn_ck<HD>();    // keys per sub-chunk
     constexpr int KB = CK / 16;          // 16-key blocks per sub-chunk
     constexpr int DW = HD / 4;           // dims owned by each wave (scores over them, then O for them)
     constexpr int H2 = HD / 2;
     constexpr int PPT = H2 / 16;         // rotate-half pairs per thread (16 threads per vector)
-    constexpr int LD = HD + 4;           // padded LDS row (float4 reads of 16 rows hit distinct banks)
-    constexpr int UPR = HD / 4;          // 16-byte units per K or V row
-    __shared__ __attribute__((aligned(16))) float Ks[CK][LD];
-    __shared__ __attribute__((aligned(16))) float Vs[CK][LD];
+    constexpr int EPU = 16 / (int)sizeof(TT);   // values per 16-byte copy unit
+    constexpr int UPR = HD / EPU;               // copy units per K or V row
+    // padded rows: K rows shift by 16 bytes (the 16 rows of a score read hit distinct banks), V rows
+    // by 64 bytes (fp32) or 32 bytes (bf16) (the 4 rows x 16 dims of a PV read hit distinct banks)
+    constexpr int LDK = HD + 16 / (int)sizeof(TT);
+    constexpr int LDV = HD + (KVB ? 16 : 16);
+    constexpr int LD = HD + 4;           // query rows
+    __shared__ __attribute__((aligned(16))) TT K0[CK][LDK];
+    __shared__ __attribute__((aligned(16))) TT V0[CK][LDV];
+    __shared__ __attribute__((aligned(16))) TT K1[CK][LDK];
+    __shared__ __attribute__((aligned(16))) TT V1[CK][LDV];
     __shared__ __attribute__((aligned(16))) float Qs[16][LD];
     __shared__ float Sp[4][16][CK + 1];   // per-wave partial scores (over the wave's dims)
     __shared__ float Ps[4][16][CK + 1];   // per-wave probabilities
@@ -360,7 +438,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 
     // K and V rows of a sub-chunk: direct global->LDS copies, one row (UPR 16-byte units) per
     // instruction, a fixed number per wave; rows past c1 repeat row c0 (finite; masked below)
-    auto issue_kv = [&](int c0) {
+    auto issue_kv = [&](TT (*Kt)[LDK], TT (*Vt)[LDV], int c0) __attribute__((always_inline)) {
         const int c1 = min(wk1, c0 + CK);
         constexpr int ipr = (UPR + 63) / 64;   // instructions per row
         static_assert((2 * CK * ipr) % 4 == 0, "K/V copies split evenly over the 4 waves");
@@ -372,9 +450,10 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             const int unit = part * 64 + lane;
             const int key = c0 + kk < c1 ? c0 + kk : c0;
             if (UPR >= 64 || unit < UPR) {
-                const float* srcp = a.plane + (size_t)key * prow + (size_t)kv * a.w + g * HD + unit * 4;
-                float* dst = (kv ? &Vs[kk][0] : &Ks[kk][0]) + part * 256;
-                __builtin_amdgcn_global_load_lds((const void*)srcp, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+                const size_t e = (size_t)key * prow + (size_t)kv * a.w + g * HD + unit * EPU;
+                const void* src = (const TT*)a.plane + e;
+                void* dst = (kv ? &Vt[kk][0] : &Kt[kk][0]) + part * 64 * EPU;
+                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
             }
         }
     };
@@ -384,7 +463,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     const int ri = tid >> 4, jr = tid & 15;
     float kr0[PPT], kr1[PPT], vr0[PPT], vr1[PPT], ssr = 0.f;
     float2 csr[PPT];
-    auto load_row = [&](int p) {
+    auto load_row = [&](int p) __attribute__((always_inline)) {
         const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
         const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
         const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
@@ -395,16 +474,19 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         load_vec<PPT>(vr0, vs + d0);
         load_vec<PPT>(vr1, vs + d0 + H2);
         load_vec<2 * PPT>((float*)csr, (const float*)(rt + d0));
+        // the first term is taken as is (an add to 0 would make the compiler wait for the load here)
         ssr = 0.f;
         if (a.qk_norm) {
+            const float* ssp = a.ss + (size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + jr;
+            if (jr < HD / 16) ssr = ssp[0];
 #pragma unroll
-            for (int u = 0; u < (HD / 16 + 15) / 16; ++u)
-                if (jr + 16 * u < HD / 16) ssr += a.ss[(size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + jr + 16 * u];
+            for (int u = 1; u < (HD / 16 + 15) / 16; ++u)
+                if (jr + 16 * u < HD / 16) ssr += ssp[16 * u];
         }
     };
-    auto store_row = [&](int p, int c0) {
+    auto store_row = [&](int p, int c0, TT (*Kt)[LDK], TT (*Vt)[LDV]) __attribute__((always_inline)) {
         const float inv = a.qk_norm ? 1.0f / sqrtf(row16_sum(ssr) / (float)HD + a.eps) : 1.f;
-        float* dst = a.plane + (size_t)p * prow + g * HD;
+        const size_t prow_off = (size_t)p * prow + g * HD;
         const int kk = p - c0;
         const int d0 = jr * PPT;
         float gk0[PPT], gk1[PPT], k0[PPT], k1[PPT];
@@ -421,14 +503,26 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             k0[i] = y0 * csr[i].x - y1 * csr[i].y;
             k1[i] = y0 * csr[i].y + y1 * csr[i].x;
         }
-        store_vec<PPT>(dst + d0, k0);
-        store_vec<PPT>(dst + d0 + H2, k1);
-        store_vec<PPT>(dst + a.w + d0, vr0);
-        store_vec<PPT>(dst + a.w + d0 + H2, vr1);
-        store_vec<PPT>(&Ks[kk][d0], k0);
-        store_vec<PPT>(&Ks[kk][d0 + H2], k1);
-        store_vec<PPT>(&Vs[kk][d0], vr0);
-        store_vec<PPT>(&Vs[kk][d0 + H2], vr1);
+        TT* dst = (TT*)a.plane + prow_off;
+        if constexpr (KVB) {   // the plane and the tile take the same rounded values
+            store_bf16_vec<PPT>(dst + d0, k0);
+            store_bf16_vec<PPT>(dst + d0 + H2, k1);
+            store_bf16_vec<PPT>(dst + a.w + d0, vr0);
+            store_bf16_vec<PPT>(dst + a.w + d0 + H2, vr1);
+            store_bf16_vec<PPT>(&Kt[kk][d0], k0);
+            store_bf16_vec<PPT>(&Kt[kk][d0 + H2], k1);
+            store_bf16_vec<PPT>(&Vt[kk][d0], vr0);
+            store_bf16_vec<PPT>(&Vt[kk][d0 + H2], vr1);
+        } else {
+            store_vec<PPT>(dst + d0, k0);
+            store_vec<PPT>(dst + d0 + H2, k1);
+            store_vec<PPT>(dst + a.w + d0, vr0);
+            store_vec<PPT>(dst + a.w + d0 + H2, vr1);
+            store_vec<PPT>(&Kt[kk][d0], k0);
+            store_vec<PPT>(&Kt[kk][d0 + H2], k1);
+            store_vec<PPT>(&Vt[kk][d0], vr0);
+            store_vec<PPT>(&Vt[kk][d0 + H2], vr1);
+        }
     };
     auto new_rows = [&](int c0, int& p_lo, int& p_hi) {
         const int c1 = min(wk1, c0 + CK);
@@ -471,7 +565,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         if (p_lo + ri < p_hi) load_row(p_lo + ri);
         asm volatile("" ::: "memory");   // these loads leave before the K/V copies
         __builtin_amdgcn_sched_barrier(0);
-        if (wk0 < wk1) issue_kv(wk0);
+        if (wk0 < wk1) issue_kv(K0, V0, wk0);
         const float inv = a.qk_norm ? 1.0f / sqrtf(row16_sum(ssq) / (float)HD + a.eps) : 1.f;
         float q0[PPT], q1[PPT];
 #pragma unroll
@@ -500,24 +594,33 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
 
-    for (int c0 = wk0; c0 < wk1; c0 += CK) {
+    // one sub-chunk [c0, c0 + CK) from stage (Kc, Vc); the next one's copies go to (Kn, Vn)
+    auto sub_chunk = [&](int c0, TT (*Kc)[LDK], TT (*Vc)[LDV], TT (*Kn)[LDK], TT (*Vn)[LDV]) __attribute__((always_inline)) {
         const int c1 = min(wk1, c0 + CK);
-        // 2. the sub-chunk's K/V copies (and its first new rows, loaded before them) have landed;
-        //    own layers then write the new rows, normalised and rotated, into LDS and the plane
+        // 2. this sub-chunk's K/V copies (and its first new rows, loaded before them) have landed,
+        //    and every wave is past the previous sub-chunk (whose stage the next copies overwrite)
         int p_lo, p_hi;
         new_rows(c0, p_lo, p_hi);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();   // the K/V copies of every wave (and, the first time, the queries) are in LDS
+        __syncthreads();
+        // 3. own layers write the new rows, normalised and rotated, into the stage and the plane
+        //    (the 16-thread groups are whole, so the row sums in store_row stay inside live groups)
         if (p_lo < p_hi) {
-            // the 16-thread groups are whole, so the row sums in store_row stay inside live groups
-            if (p_lo + ri < p_hi) store_row(p_lo + ri, c0);
+            if (p_lo + ri < p_hi) store_row(p_lo + ri, c0, Kc, Vc);
             for (int pr = p_lo + 16; pr < p_hi; pr += 16)
                 if (pr + ri < p_hi) {
                     load_row(pr + ri);
-                    store_row(pr + ri, c0);
+                    store_row(pr + ri, c0, Kc, Vc);
                 }
-            __syncthreads();
         }
+        // the next sub-chunk's new-row loads and copies go out before this one is computed
+        if (c0 + CK < wk1) {
+            int n_lo, n_hi;
+            new_rows(c0 + CK, n_lo, n_hi);
+            if (n_lo + ri < n_hi) load_row(n_lo + ri);
+            issue_kv(Kn, Vn, c0 + CK);
+        }
+        if (p_lo < p_hi) lds_barrier();   // the new rows are in the stage (the copies stay in flight)
 
         // 4. partial scores over this wave's dims: S[qv][key] for the CK keys
         floatx4 sacc[KB];
@@ -529,7 +632,16 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             const float4 qa = *(const float4*)&Qs[col][d];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const float4 kv4 = *(const float4*)&Ks[kb * 16 + col][d];
+                float4 kv4;
+                if constexpr (KVB) {
+                    const uint2 b = *(const uint2*)&Kc[kb * 16 + col][d];
+                    kv4.x = __builtin_bit_cast(float, b.x << 16);
+                    kv4.y = __builtin_bit_cast(float, b.x & 0xffff0000u);
+                    kv4.z = __builtin_bit_cast(float, b.y << 16);
+                    kv4.w = __builtin_bit_cast(float, b.y & 0xffff0000u);
+                } else {
+                    kv4 = *(const float4*)&Kc[kb * 16 + col][d];
+                }
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, kv4.x, sacc[kb], 0, 0, 0);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, kv4.y, sacc[kb], 0, 0, 0);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.z, kv4.z, sacc[kb], 0, 0, 0);
@@ -540,38 +652,53 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) Sp[wave][4 * grp + r][kb * 16 + col] = sacc[kb][r];
-        __syncthreads();
+        lds_barrier();
 
         // 5. softmax update over the sub-chunk (every wave for all 16 vectors; the sums over the
-        //    four waves' dims are taken in wave order), probabilities into this wave's LDS slice
+        //    four waves' dims are taken in wave order), probabilities into this wave's LDS slice.
+        //    The partial scores are read untracked: the compiler would otherwise wait for the next
+        //    sub-chunk's copies before these reads.
+        constexpr int RB = KB == 1 ? 4 : 1;   // vectors whose partial scores are read in one batch
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int qvl = 4 * grp + r;
-            float sv[KB];
-            float mx = -INFINITY;
+        for (int r0 = 0; r0 < 4; r0 += RB) {
+            float spv[RB][KB][4];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const int key = c0 + kb * 16 + col;
-                const float sum = ((Sp[0][qvl][kb * 16 + col] + Sp[1][qvl][kb * 16 + col]) + Sp[2][qvl][kb * 16 + col]) +
-                                  Sp[3][qvl][kb * 16 + col];
-                sv[kb] = (key < c1 && key >= lo_r[r] && key <= hi_r[r]) ? sum * scale : -INFINITY;
-                mx = fmaxf(mx, sv[kb]);
+            for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        spv[rr][kb][w] = lds_read_f32_untracked(&Sp[w][4 * grp + r0 + rr][kb * 16 + col]);
+            wait_lds();
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+                const int r = r0 + rr;
+                const int qvl = 4 * grp + r;
+                float sv[KB];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int key = c0 + kb * 16 + col;
+                    const float sum = ((spv[rr][kb][0] + spv[rr][kb][1]) + spv[rr][kb][2]) + spv[rr][kb][3];
+                    sv[kb] = (key < c1 && key >= lo_r[r] && key <= hi_r[r]) ? sum * scale : -INFINITY;
+                    mx = fmaxf(mx, sv[kb]);
+                }
+                mx = row16_max(mx);
+                const float m_new = fmaxf(m_run[r], mx);
+                const float alpha = (m_run[r] == -INFINITY) ? 0.f : expf(m_run[r] - m_new);
+                float ps = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const float pv = (sv[kb] == -INFINITY) ? 0.f : expf(sv[kb] - m_new);
+                    ps += pv;
+                    Ps[wave][qvl][kb * 16 + col] = pv;
+                }
+                ps = row16_sum(ps);
+                l_run[r] = l_run[r] * alpha + ps;
+                m_run[r] = m_new;
+#pragma unroll
+                for (int d = 0; d < NDT; ++d) o[d][r] *= alpha;
             }
-            mx = row16_max(mx);
-            const float m_new = fmaxf(m_run[r], mx);
-            const float alpha = (m_run[r] == -INFINITY) ? 0.f : expf(m_run[r] - m_new);
-            float ps = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float pv = (sv[kb] == -INFINITY) ? 0.f : expf(sv[kb] - m_new);
-                ps += pv;
-                Ps[wave][qvl][kb * 16 + col] = pv;
-            }
-            ps = row16_sum(ps);
-            l_run[r] = l_run[r] * alpha + ps;
-            m_run[r] = m_new;
-#pragma unroll
-            for (int d = 0; d < NDT; ++d) o[d][r] *= alpha;
         }
         wave_sync();
 
@@ -580,16 +707,17 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         for (int st = 0; st < CK / 4; ++st) {
             const float pa = Ps[wave][col][4 * st + grp];
 #pragma unroll
-            for (int d = 0; d < NDT; ++d)
-                o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vs[4 * st + grp][wave * DW + 16 * d + col], o[d], 0, 0, 0);
+            for (int d = 0; d < NDT; ++d) {
+                float vb;
+                if constexpr (KVB) vb = bf16_to_f32(Vc[4 * st + grp][wave * DW + 16 * d + col]);
+                else vb = Vc[4 * st + grp][wave * DW + 16 * d + col];
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o[d], 0, 0, 0);
+            }
         }
-        __syncthreads();   // every wave is done with Ks, Vs before the next sub-chunk's copies
-        if (c0 + CK < wk1) {
-            int n_lo, n_hi;
-            new_rows(c0 + CK, n_lo, n_hi);
-            if (n_lo + ri < n_hi) load_row(n_lo + ri);
-            issue_kv(c0 + CK);
-        }
+    };
+    for (int c0 = wk0; c0 < wk1; c0 += 2 * CK) {
+        sub_chunk(c0, K0, V0, K1, V1);
+        if (c0 + CK < wk1) sub_chunk(c0 + CK, K1, V1, K0, V0);
     }
 
     // 7. this workgroup's partial: unnormalised O (each wave its dims), the running max and sum
@@ -878,6 +1006,7 @@ AttnK make_attn(const Attn& x) {
     a.eps = x.eps;
     a.rope = x.rope;
     a.plane = x.plane;
+    a.kv_bf16 = x.kv_bf16;
     a.w = x.w;
     a.own = x.own;
     a.M = x.M;
@@ -939,15 +1068,18 @@ hipError_t launch_attention(const Attn& x, hipStream_t st) {
     const int cgrid = a.n_qt * a.nkv * 16 * (x.hd / 64);
     switch (x.hd) {
         case 64:
-            hipLaunchKernelGGL(k_attention<64>, dim3(grid), dim3(256), 0, st, a);
+            if (a.kv_bf16) hipLaunchKernelGGL((k_attention<64, true>), dim3(grid), dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((k_attention<64, false>), dim3(grid), dim3(256), 0, st, a);
             hipLaunchKernelGGL(k_attn_combine<64>, dim3(cgrid), dim3(256), 0, st, a);
             break;
         case 128:
-            hipLaunchKernelGGL(k_attention<128>, dim3(grid), dim3(256), 0, st, a);
+            if (a.kv_bf16) hipLaunchKernelGGL((k_attention<128, true>), dim3(grid), dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((k_attention<128, false>), dim3(grid), dim3(256), 0, st, a);
             hipLaunchKernelGGL(k_attn_combine<128>, dim3(cgrid), dim3(256), 0, st, a);
             break;
         case 256:
-            hipLaunchKernelGGL(k_attention<256>, dim3(grid), dim3(256), 0, st, a);
+            if (a.kv_bf16) hipLaunchKernelGGL((k_attention<256, true>), dim3(grid), dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((k_attention<256, false>), dim3(grid), dim3(256), 0, st, a);
             hipLaunchKernelGGL(k_attn_combine<256>, dim3(cgrid), dim3(256), 0, st, a);
             break;
         default: return hipErrorInvalidValue;

@@ -88,6 +88,10 @@ typedef struct {
     float rope_base;       /* rotate-half RoPE, pairs (i, i + head_dim/2), angle p * base^(-2i/hd) */
     float rms_eps;         /* RMSNorm: x / sqrt(mean(x^2) + eps) * gain */
     const bvf_layer_desc* layers;
+    int32_t kv_bf16;       /* 0: K/V planes hold fp32 values (the pages' floats); 1: a memory variant
+                              holding bf16 values, every stored K/V value (cached by bvf_set_kv, appended
+                              by a pass, or a draft block's own rows) rounded from fp32 to nearest even.
+                              Counts (plane_floats, cut_floats) are in values either way. */
 } bvf_model_desc;
 
 typedef struct bvf_model bvf_model;
@@ -124,6 +128,12 @@ bvf_status bvf_load_bf16(bvf_model* m, int32_t tensor, int32_t layer, const uint
  * bvf_set_positions then fixes the count. Refused on a shared layer. */
 bvf_status bvf_set_kv(bvf_model* m, int32_t layer, const float* h_kv, int64_t positions);
 bvf_status bvf_set_positions(bvf_model* m, int64_t positions);
+/* Read back the first `positions` rows of an own plane into h_kv [positions][2][w] fp32, in the
+ * layout bvf_set_kv takes (bf16 planes are widened exactly). Waits for the model's stream. Rows at
+ * or beyond the held count hold whatever the last pass or set_kv left there. Refused on a shared
+ * layer; positions > max_ctx is BVF_E_CAPACITY. */
+bvf_status bvf_get_kv(const bvf_model* m, int32_t layer, float* h_kv, int64_t positions);
+
 
 /* Per-layer KV bookkeeping [PR2303, "What changes" item 1]. kv_widths: w of each layer (a shared
  * layer reports its owner's width). plane_floats: floats held by each layer's own plane (held
