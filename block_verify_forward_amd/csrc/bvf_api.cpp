@@ -373,6 +373,7 @@ Attn attn_for(const bvf_model* m, const Layer& L, int rows) {
     at.rope = L.rope; at.w = L.w;
     at.M = rows; at.Hq = m->d.n_q_heads; at.nkv = L.d.n_kv_heads; at.hd = L.d.head_dim;
     at.out = m->obuf; at.part = m->attn_part; at.part_floats = m->attn_part_floats;
+    at.n_cu = m->n_cu;
     at.counters = m->counters; at.n_counters = kCounters;
     return at;
 }

@@ -139,6 +139,7 @@ struct Attn {
     size_t part_floats = 0;
     int* counters = nullptr;     // zero between launches
     int n_counters = 0;
+    int n_cu = 256;              // compute units of the device (chunk planning)
 };
 size_t attn_part_floats_needed(const Attn& a);
 hipError_t launch_attention(const Attn& a, hipStream_t st);

@@ -347,6 +347,7 @@ struct AttnK {
     int causal, pos0, window, ctx_lo, ctx_hi;
     int np0, np1, sp, r_lo, r_hi;   // new rows: positions [np0, np1); row of p: p < sp ? r_lo + p - np0 : r_hi + p - sp
     int key_lo, n_keys, spw, n_chunks;   // keys [key_lo, key_lo + n_keys); spw sub-chunks per workgroup
+    int nst;                 // LDS stages of the kernel (1: spw == 1)
     float* part;             // [n_qt][nkv][n_chunks][16][hd + 2] partials
     int* counters;           // [n_qt * nkv]
     uint16_t* out;           // [M][Hq * hd] bf16
@@ -370,10 +371,13 @@ __device__ __forceinline__ float head_ss(const AttnK& a, int r, int c0, int hd) 
     return q;
 }
 
-// Keys per sub-chunk: the K and V tiles of a sub-chunk take 16 KB each in LDS (16 keys at hd 256:
-// small chunks spread the K/V reads over many compute units), at least one 16-key MFMA block.
-template <int HD>
-constexpr int attn_ck() { return 4096 / HD > 16 ? 4096 / HD : 16; }
+// Keys per sub-chunk: the K and V tiles of a sub-chunk take 16 KB each in LDS with fp32 planes (16
+// keys at hd 256: small chunks spread the K/V reads over many compute units), at least one 16-key
+// MFMA block. With two stages and bf16 planes at hd >= 128 a sub-chunk takes twice the keys in the
+// same bytes, so a workgroup that streams many sub-chunks keeps as many bytes in flight.
+__host__ __device__ constexpr int attn_ck(int hd, bool kvb, int nst) {
+    return (kvb && nst == 2 && hd >= 128 ? 2 : 1) * (4096 / hd > 16 ? 4096 / hd : 16);
+}
 
 // Tile element of the K/V planes: fp32, or (KVB) bf16 values widened exactly where they are read.
 template <bool KVB> struct KVElem { using T = float; };
@@ -397,16 +401,18 @@ __device__ __forceinline__ void store_bf16_vec(uint16_t* p, const float* v) {
 }
 
 // One workgroup per (key chunk, KV head, tile of 16 query vectors). The chunk's keys go through LDS
-// in sub-chunks of CK keys, in two stages: the copies of sub-chunk i + 1 are in flight while
-// sub-chunk i is scored and weighted. The two stages are distinct LDS arrays, so the compiler's
+// in sub-chunks of CK keys. NST = 2: two stages, the copies of sub-chunk i + 1 are in flight while
+// sub-chunk i is scored and weighted; the stages are distinct LDS arrays, so the compiler's
 // wait-count insertion sees that reads of one stage do not depend on copies into the other.
+// NST = 1: one sub-chunk per workgroup, one stage (half the LDS, twice the workgroups per CU).
 // KVB: the planes hold bf16 values; the tiles keep them as bf16 and the reads widen them (exact),
 // and new rows are written rounded to the plane and the tile, so every K/V value the scores and
 // PV see is the stored one.
-template <int HD, bool KVB>
+template <int HD, bool KVB, int NST>
 __global__ __launch_bounds__(256) void k_attention(AttnK a) {
+    static_assert(NST == 1 || NST == 2, "one or two stages");
     using TT = typename KVElem<KVB>::T;
-    constexpr int CK = attn_ck<HD>();    // keys per sub-chunk
+    constexpr int CK = attn_ck(HD, KVB, NST);   // keys per sub-chunk
     constexpr int KB = CK / 16;          // 16-key blocks per sub-chunk
     constexpr int DW = HD / 4;           // dims owned by each wave (scores over them, then O for them)
     constexpr int H2 = HD / 2;
@@ -420,8 +426,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     constexpr int LD = HD + 4;           // query rows
     __shared__ __attribute__((aligned(16))) TT K0[CK][LDK];
     __shared__ __attribute__((aligned(16))) TT V0[CK][LDV];
-    __shared__ __attribute__((aligned(16))) TT K1[CK][LDK];
-    __shared__ __attribute__((aligned(16))) TT V1[CK][LDV];
+    __shared__ __attribute__((aligned(16))) TT K1[NST == 2 ? CK : 1][LDK];
+    __shared__ __attribute__((aligned(16))) TT V1[NST == 2 ? CK : 1][LDV];
     __shared__ __attribute__((aligned(16))) float Qs[16][LD];
     __shared__ float Sp[4][16][CK + 1];   // per-wave partial scores (over the wave's dims)
     __shared__ float Ps[4][16][CK + 1];   // per-wave probabilities
@@ -715,9 +721,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             }
         }
     };
-    for (int c0 = wk0; c0 < wk1; c0 += 2 * CK) {
-        sub_chunk(c0, K0, V0, K1, V1);
-        if (c0 + CK < wk1) sub_chunk(c0 + CK, K1, V1, K0, V0);
+    if constexpr (NST == 2) {
+        for (int c0 = wk0; c0 < wk1; c0 += 2 * CK) {
+            sub_chunk(c0, K0, V0, K1, V1);
+            if (c0 + CK < wk1) sub_chunk(c0 + CK, K1, V1, K0, V0);
+        }
+    } else if (wk0 < wk1) {
+        sub_chunk(wk0, K0, V0, K0, V0);   // the only sub-chunk: no next copies are issued
     }
 
     // 7. this workgroup's partial: unnormalised O (each wave its dims), the running max and sum
@@ -736,15 +746,15 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 }
 
 // Merge of the chunks of one (q tile, KV head): one 256-thread block per (query vector, 64 dims).
-// Wave w takes the chunks [w q, (w + 1) q), q = ceil(n_chunks / 4), lane = dim: every value load of
-// the block goes out at once, before the chunk maxima are known. The chunk weights e^(m_c - M) and
-// the denominator are summed in chunk order, and so are the four waves' partial numerators.
+// Wave w takes the chunks [w q, (w + 1) q), q = ceil(n_chunks / 4) <= 32: lane d loads its dim of
+// every chunk, lane j the running maximum and sum of chunk w q + j, all in one round of loads. The
+// chunk weights are computed once per chunk (lane j) and broadcast from it. Every sum runs in a
+// fixed order (butterfly over the lanes, chunks in order, then the waves in order).
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnK a) {
-    constexpr int MAXC = kAttnMaxChunks;
-    constexpr int QMAX = MAXC / 4;   // chunks per wave at most
-    __shared__ float wgt[MAXC], lsum[MAXC], mxw[4], numw[4][64];
-    __shared__ float inv_den;
+    constexpr int QMAX = kAttnMaxChunks / 4;   // chunks per wave at most
+    static_assert(QMAX <= 64, "one lane per chunk of a wave");
+    __shared__ float mxw[4], denw[4], numw[4][64];
     const int dgroups = HD / 64;
     const int dg = blockIdx.x % dgroups;
     const int qvl = (blockIdx.x / dgroups) % 16;
@@ -752,51 +762,44 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnK a) {
     const int g = tile % a.nkv, qt = tile / a.nkv;
     const int qv = qt * 16 + qvl;
     if (qv >= a.NQ) return;   // uniform in the block
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nc = a.n_chunks;
     const int q = (nc + 3) / 4;
     const size_t cstride = (size_t)16 * (HD + 2);
     const float* base = a.part + (size_t)tile * nc * cstride + (size_t)qvl * (HD + 2);
     const int d = dg * 64 + lane;
-    // this thread's values (chunks of its wave, dim d), then the chunk statistics
+    const int cw = wave * q;                              // this wave's first chunk
+    const int nw = max(0, min(q, nc - cw));               // and its number of chunks
     float v[QMAX];
 #pragma unroll
-    for (int i = 0; i < QMAX; ++i) {
-        const int c = wave * q + i;
-        v[i] = (i < q && c < nc) ? base[(size_t)c * cstride + d] : 0.f;
-    }
-    const bool has = tid < nc;
-    const float m_c = has ? base[(size_t)tid * cstride + HD] : -INFINITY;
-    const float l_c = has ? base[(size_t)tid * cstride + HD + 1] : 0.f;
-    float mx = m_c;
+    for (int i = 0; i < QMAX; ++i) v[i] = i < nw ? base[(size_t)(cw + i) * cstride + d] : 0.f;
+    const bool lj = lane < nw;
+    const float* pj = base + (size_t)(cw + (lj ? lane : 0)) * cstride + HD;
+    const float mj = lj ? pj[0] : -INFINITY;
+    const float sj = lj ? pj[1] : 0.f;
+    float mx = mj;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     if (lane == 0) mxw[wave] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(mxw[0], mxw[1]), fmaxf(mxw[2], mxw[3]));
-    if (tid < MAXC) {
-        const float e = (!has || m_c == -INFINITY) ? 0.f : expf(m_c - mx);
-        wgt[tid] = e;
-        lsum[tid] = e * l_c;
-    }
-    __syncthreads();
-    if (tid == 0) {   // the denominator in chunk order
-        float den = 0.f;
-        for (int c = 0; c < nc; ++c) den += lsum[c];
-        inv_den = 1.0f / den;
-    }
+    const float ej = mj == -INFINITY ? 0.f : expf(mj - mx);
+    float den = ej * sj;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o);
     float num = 0.f;
 #pragma unroll
-    for (int i = 0; i < QMAX; ++i) {
-        const int c = wave * q + i;
-        if (i < q && c < nc) num += wgt[c] * v[i];
-    }
+    for (int i = 0; i < QMAX; ++i)
+        if (i < nw) num += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ej), i)) * v[i];
     numw[wave][lane] = num;
+    if (lane == 0) denw[wave] = den;
     __syncthreads();
     if (wave == 0) {
         const float t = ((numw[0][lane] + numw[1][lane]) + numw[2][lane]) + numw[3][lane];
-        const int m = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
-        a.out[(size_t)m * a.Hq * HD + (size_t)h * HD + d] = f32_to_bf16(t * inv_den);
+        const float dn = ((denw[0] + denw[1]) + denw[2]) + denw[3];
+        const int mm = qv / a.Hg, h = g * a.Hg + qv % a.Hg;
+        a.out[(size_t)mm * a.Hq * HD + (size_t)h * HD + d] = f32_to_bf16(t / dn);
     }
 }
 
@@ -1040,14 +1043,25 @@ AttnK make_attn(const Attn& x) {
     }
     a.key_lo = lo;
     a.n_keys = hi - lo + 1;
-    // sub-chunks of attn_ck<hd> keys per workgroup: enough workgroups to spread the keys, few enough
-    // chunks for the merge (at most kAttnMaxChunks)
-    const int ck = std::max(16, 4096 / x.hd);
-    const int subs = (a.n_keys + ck - 1) / ck;
-    int spw = 1;
-    while (spw < 4096 && ((long)((subs + spw - 1) / spw) * a.n_qt * a.nkv > 768 || (subs + spw - 1) / spw > kAttnMaxChunks)) spw *= 2;
-    a.spw = spw;
-    a.n_chunks = (subs + spw - 1) / spw;
+    // One sub-chunk per workgroup (one LDS stage, two workgroups per compute unit) while that takes
+    // at most kAttnMaxChunks chunks and 768 workgroups. Longer key ranges: workgroups of spw
+    // sub-chunks through two stages; their LDS leaves one workgroup per compute unit, so the chunks
+    // are planned to run in a single round of at most n_cu workgroups.
+    const int tiles = a.n_qt * a.nkv;
+    const int ck1 = attn_ck(x.hd, x.kv_bf16 != 0, 1);
+    const int subs1 = (a.n_keys + ck1 - 1) / ck1;
+    if (subs1 <= kAttnMaxChunks && (long)subs1 * tiles <= 768) {
+        a.nst = 1;
+        a.spw = 1;
+        a.n_chunks = subs1;
+    } else {
+        a.nst = 2;
+        const int ck2 = attn_ck(x.hd, x.kv_bf16 != 0, 2);
+        const int subs = (a.n_keys + ck2 - 1) / ck2;
+        const int nch = std::max(1, std::min(kAttnMaxChunks, x.n_cu / tiles));
+        a.spw = (subs + nch - 1) / nch;
+        a.n_chunks = (subs + a.spw - 1) / a.spw;
+    }
     a.part = x.part;
     a.counters = x.counters;
     a.out = x.out;
@@ -1060,6 +1074,21 @@ size_t attn_part_floats_needed(const Attn& x) {
     return (size_t)a.n_qt * a.nkv * a.n_chunks * 16 * (x.hd + 2);
 }
 
+namespace {
+// one stage when every workgroup takes a single sub-chunk (spw == 1), two otherwise
+template <int HD>
+void launch_attn(const AttnK& a, int grid, int cgrid, hipStream_t st) {
+    if (a.nst == 2) {
+        if (a.kv_bf16) hipLaunchKernelGGL((k_attention<HD, true, 2>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_attention<HD, false, 2>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+        if (a.kv_bf16) hipLaunchKernelGGL((k_attention<HD, true, 1>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_attention<HD, false, 1>), dim3(grid), dim3(256), 0, st, a);
+    }
+    hipLaunchKernelGGL(k_attn_combine<HD>, dim3(cgrid), dim3(256), 0, st, a);
+}
+}  // namespace
+
 hipError_t launch_attention(const Attn& x, hipStream_t st) {
     const AttnK a = make_attn(x);
     if (attn_part_floats_needed(x) > x.part_floats || a.n_qt * a.nkv > x.n_counters) return hipErrorInvalidValue;
@@ -1067,21 +1096,9 @@ hipError_t launch_attention(const Attn& x, hipStream_t st) {
     const int grid = a.n_chunks * a.nkv * a.n_qt;
     const int cgrid = a.n_qt * a.nkv * 16 * (x.hd / 64);
     switch (x.hd) {
-        case 64:
-            if (a.kv_bf16) hipLaunchKernelGGL((k_attention<64, true>), dim3(grid), dim3(256), 0, st, a);
-            else hipLaunchKernelGGL((k_attention<64, false>), dim3(grid), dim3(256), 0, st, a);
-            hipLaunchKernelGGL(k_attn_combine<64>, dim3(cgrid), dim3(256), 0, st, a);
-            break;
-        case 128:
-            if (a.kv_bf16) hipLaunchKernelGGL((k_attention<128, true>), dim3(grid), dim3(256), 0, st, a);
-            else hipLaunchKernelGGL((k_attention<128, false>), dim3(grid), dim3(256), 0, st, a);
-            hipLaunchKernelGGL(k_attn_combine<128>, dim3(cgrid), dim3(256), 0, st, a);
-            break;
-        case 256:
-            if (a.kv_bf16) hipLaunchKernelGGL((k_attention<256, true>), dim3(grid), dim3(256), 0, st, a);
-            else hipLaunchKernelGGL((k_attention<256, false>), dim3(grid), dim3(256), 0, st, a);
-            hipLaunchKernelGGL(k_attn_combine<256>, dim3(cgrid), dim3(256), 0, st, a);
-            break;
+        case 64: launch_attn<64>(a, grid, cgrid, st); break;
+        case 128: launch_attn<128>(a, grid, cgrid, st); break;
+        case 256: launch_attn<256>(a, grid, cgrid, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
