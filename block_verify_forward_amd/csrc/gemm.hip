@@ -647,7 +647,6 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
     const double hbm = 5.5e12, lat = 1.5e-6, per_sb = 0.25e-6, l2_round = 0.8e-6, handoff = 3.0e-6, per_split = 0.25e-6,
                  reduce = 0.3e-6;
     const bool norm = L.xsrc != nullptr;
-    const bool long_stream = L.fmt == W_Q4_1 && (long)tiles * G >= 48L * cus;
     double best_t = 1e30;
     auto consider = [&](int Se, int sb, int W, int KS, int R, int ipw, bool forced) {
         const int T = W / KS;
@@ -691,10 +690,11 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
                 if (W % KS) continue;
                 for (int R : {8, 4, 2}) {
                     if (L.fmt == W_BF16 && R == 8) continue;
-                    // long Q4_1 streams (>= 48 superblocks per compute unit) take at least 8 waves
-                    // with rings of 4: measured on MI355X, the extra waves hide the per-superblock
-                    // latency better than deeper rings (which the estimate below does not model)
-                    if (long_stream && (W < 8 || R != 4)) continue;
+                    // Q4_1 rings hold 2 superblocks: measured on MI355X over every forced plan of the
+                    // verify pass's GEMM shapes (q|k|v, o, gate|up, down at k = 8), the best plans
+                    // all take rings of 2 and spend the LDS on more waves per workgroup (the
+                    // estimate below does not model the ring depth well enough to choose it)
+                    if (L.fmt == W_Q4_1 && R != 2) continue;
                     // the fewest items per workgroup for which the grid is resident
                     for (int ipw = 1; ipw <= tiles && (Se == 1 || ipw <= 32); ++ipw)
                         if (consider(Se, sb, W, KS, R, ipw, false)) break;
@@ -712,7 +712,6 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
 
 // Plans depend only on the launch's shape; the search runs once per shape.
 static GemmPlan cached_plan(const GemmLaunch& L) {
-    if (L.force_S > 0) return plan_gemm(L);
     static std::mutex mu;
     static std::unordered_map<uint64_t, GemmPlan> cache;
     uint64_t key = (uint64_t)L.n_run_tiles;
@@ -722,6 +721,7 @@ static GemmPlan cached_plan(const GemmLaunch& L) {
     key = key * 4099u + (uint64_t)L.n_cu;
     key = key * 1000003u + (uint64_t)(L.partial_floats >> 10);
     key = key * 65537u + (uint64_t)L.n_counters;
+    key = key * 1000003u + (uint64_t)(((L.force_S * 17 + L.force_R) * 17 + L.force_ipw) * 17 + L.force_W) * 17 + (uint64_t)L.force_KS;
     std::lock_guard<std::mutex> lock(mu);
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
