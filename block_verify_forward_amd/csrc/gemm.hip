@@ -701,6 +701,21 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
                 }
             }
     }
+    // Long K streams staged by copy (the down projections, K >= 64 superblocks): measured on MI355X
+    // by the plan sweep at 1, 8 and 16 rows, the best plans split K into parts of about 27
+    // superblocks and run 12 waves per workgroup, T tiles x 12 / T parts, with about one workgroup
+    // per compute unit; the estimate above does not find them, so they are taken when they fit.
+    if (L.fmt == W_Q4_1 && !norm && G >= 64 && L.force_S <= 0) {
+        const int sb = 27, Se = (G + sb - 1) / sb;
+        if ((size_t)Se * M * tiles * kTile <= L.partial_floats && tiles <= L.n_counters) {
+            for (int T : {1, 2, 3, 4, 6, 12}) {
+                const int U = (tiles + T - 1) / T;
+                if ((long)Se * U > cus) continue;
+                consider(Se, sb, 12, 12 / T, 2, 1, true);
+                break;
+            }
+        }
+    }
     if (L.force_S > 0 && L.force_R > 0 && L.force_ipw > 0 && L.force_W > 0 && L.force_KS > 0 && L.force_W % L.force_KS == 0) {
         const int sb = (G + L.force_S - 1) / L.force_S;
         const int Se = (G + sb - 1) / sb;
