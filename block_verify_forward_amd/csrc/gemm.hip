@@ -716,6 +716,11 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
             }
         }
     }
+    // Many tiles over a short K range with the RMSNorm folded in (gate|up of the double-wide
+    // layers, >= 8 tiles per compute unit): measured best with one item of T = tiles / n_cu tiles
+    // per workgroup and one K part per wave (W = T), one workgroup per compute unit.
+    if (L.fmt == W_Q4_1 && norm && L.force_S <= 0 && tiles % cus == 0 && tiles / cus >= 8 && tiles / cus <= 16)
+        consider(1, G, tiles / cus, 1, 2, 1, true);
     if (L.force_S > 0 && L.force_R > 0 && L.force_ipw > 0 && L.force_W > 0 && L.force_KS > 0 && L.force_W % L.force_KS == 0) {
         const int sb = (G + L.force_S - 1) / L.force_S;
         const int Se = (G + sb - 1) / sb;
