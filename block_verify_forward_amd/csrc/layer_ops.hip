@@ -824,7 +824,30 @@ __global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict_
     const float* lr = logits + (size_t)row * V;
     float bv = 0.f;
     int bi = -1;
-    for (int i = lo + threadIdx.x; i < hi; i += 256) better(bv, bi, lr[i], i);
+    // the span's 16 values per thread are loaded in one round (four 16-byte loads, coalesced over
+    // the block) before any comparison; "better" is a total order, so the visiting order does not
+    // change the result. A span that ends early or an unaligned row takes the scalar path.
+    constexpr int kVec = kArgmaxSpan / 1024;   // 16-byte loads per thread
+    const bool vec_ok = ((V & 3) == 0) && (((uintptr_t)lr & 15) == 0);
+    float4 v4[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        const int i0 = lo + j * 1024 + (int)threadIdx.x * 4;
+        if (vec_ok && i0 + 3 < hi) v4[j] = *(const float4*)(lr + i0);
+    }
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        const int i0 = lo + j * 1024 + (int)threadIdx.x * 4;
+        if (vec_ok && i0 + 3 < hi) {
+            better(bv, bi, v4[j].x, i0);
+            better(bv, bi, v4[j].y, i0 + 1);
+            better(bv, bi, v4[j].z, i0 + 2);
+            better(bv, bi, v4[j].w, i0 + 3);
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (i0 + e < hi) better(bv, bi, lr[i0 + e], i0 + e);
+        }
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const float ov = __shfl_xor(bv, off);
@@ -911,15 +934,22 @@ __global__ __launch_bounds__(256) void k_sample_partial(const float* __restrict_
     }
 }
 
-__global__ __launch_bounds__(64) void k_accept(const float* __restrict__ pv, const int* __restrict__ pi, int nb, int k,
-                                               const int32_t* __restrict__ tokens, int32_t* __restrict__ out_tokens,
-                                               int32_t* __restrict__ n_acc, int32_t* __restrict__ argmax_out) {
+// One wave per row (64 k threads): every row's partials are loaded in the same round.
+__global__ __launch_bounds__(64 * kMaxRows) void k_accept(const float* __restrict__ pv, const int* __restrict__ pi, int nb,
+                                                          int k, const int32_t* __restrict__ tokens,
+                                                          int32_t* __restrict__ out_tokens, int32_t* __restrict__ n_acc,
+                                                          int32_t* __restrict__ argmax_out) {
     __shared__ int y[kMaxRows];
-    const int lane = threadIdx.x;
-    for (int row = 0; row < k; ++row) {
+    const int lane = threadIdx.x & 63;
+    const int row = threadIdx.x >> 6;
+    if (row < k) {
         float bv = 0.f;
         int bi = -1;
-        for (int b = lane; b < nb; b += 64) if (pi[(size_t)row * nb + b] >= 0) better(bv, bi, pv[(size_t)row * nb + b], pi[(size_t)row * nb + b]);
+        for (int b = lane; b < nb; b += 64) {
+            const int i = pi[(size_t)row * nb + b];
+            const float v = pv[(size_t)row * nb + b];
+            if (i >= 0) better(bv, bi, v, i);
+        }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
             const float ov = __shfl_xor(bv, off);
@@ -929,7 +959,7 @@ __global__ __launch_bounds__(64) void k_accept(const float* __restrict__ pv, con
         if (lane == 0) y[row] = bi < 0 ? 0 : bi;
     }
     __syncthreads();
-    if (lane == 0) {
+    if (threadIdx.x == 0) {
         if (argmax_out) for (int r = 0; r < k; ++r) argmax_out[r] = y[r];
         if (tokens) {
             int acc = 0;
@@ -1115,7 +1145,8 @@ hipError_t launch_argmax_accept(const float* logits, int k, int V, const int32_t
         hipLaunchKernelGGL(k_argmax_partial, dim3(nb, k), dim3(256), 0, st, logits, V, nb, part_val, part_idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, st, part_val, part_idx, nb, k, tokens, out_tokens, n_acc,
+    if (k < 1 || k > kMaxRows) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_accept, dim3(1), dim3(64 * k), 0, st, part_val, part_idx, nb, k, tokens, out_tokens, n_acc,
                        argmax_out);
     return hipGetLastError();
 }
