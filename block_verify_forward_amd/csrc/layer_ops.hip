@@ -934,7 +934,7 @@ __global__ __launch_bounds__(256) void k_sample_partial(const float* __restrict_
     }
 }
 
-// One wave per row (64 k threads): every row's partials are loaded in the same round.
+// One wave per row (64 x k threads): every row's partials are loaded in the same round.
 __global__ __launch_bounds__(64 * kMaxRows) void k_accept(const float* __restrict__ pv, const int* __restrict__ pi, int nb,
                                                           int k, const int32_t* __restrict__ tokens,
                                                           int32_t* __restrict__ out_tokens, int32_t* __restrict__ n_acc,
@@ -1139,13 +1139,13 @@ int argmax_blocks(int V) { return (V + kArgmaxSpan - 1) / kArgmaxSpan; }
 hipError_t launch_argmax_accept(const float* logits, int k, int V, const int32_t* tokens, float* part_val, int* part_idx,
                                 int nb, int32_t* out_tokens, int32_t* n_acc, int32_t* argmax_out, hipStream_t st,
                                 const SampleArgs* sample) {
+    if (k < 1 || k > kMaxRows) return hipErrorInvalidValue;
     if (sample)
         hipLaunchKernelGGL(k_sample_partial, dim3(nb, k), dim3(256), 0, st, logits, V, nb, part_val, part_idx, *sample);
     else
         hipLaunchKernelGGL(k_argmax_partial, dim3(nb, k), dim3(256), 0, st, logits, V, nb, part_val, part_idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (k < 1 || k > kMaxRows) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_accept, dim3(1), dim3(64 * k), 0, st, part_val, part_idx, nb, k, tokens, out_tokens, n_acc,
                        argmax_out);
     return hipGetLastError();
