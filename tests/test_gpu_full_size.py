@@ -51,6 +51,24 @@ def test_full_size_gemms(full, layer):
         assert err < GEMM_TOL
 
 
+@pytest.mark.parametrize("rows", [3, 13, 16])
+@pytest.mark.parametrize("layer", [0, 30])
+def test_full_size_gemms_ragged_rows(full, layer, rows):
+    """The gate|up and down matrices of an own (0) and a shared (30) layer at row counts that are
+    not 8 (the planner's split-K and wide-tile plans at ragged M), rel-L1 per row."""
+    m, w, kv, g = full
+    shapes = synth.layer_matrix_shapes(m, layer)
+    for key in ("gate", "up", "down"):
+        n_out, n_in = shapes[key]
+        x = synth.bf16_normal(0, f"full.gemm.ragged.{layer}.{key}.{rows}", (rows, n_in))
+        y = torch.empty((rows, n_out), dtype=torch.float32, device="cuda")
+        g.q4_1_gemm(layer, MAT[key], dev(x), rows, y)
+        ref = oracle.q4_1_matmul(w["layers"][layer][key], n_out, n_in, x)
+        err = rel_l1(host(y), ref)
+        print(f"layer {layer} {key} {n_out}x{n_in}, {rows} rows: rel-L1 {err:.2e}")
+        assert err < GEMM_TOL
+
+
 @pytest.mark.parametrize("k", [8, 1])
 def test_full_size_verify(full, k):
     """The benchmark's step at full size: logits of every row within the stack bar, the taps, the
