@@ -218,7 +218,7 @@ def run_prefill(args):
         "n_gpus": 1,
         "higher_is_better": True,
         "vs_baseline": None,
-        "dtype": "q4_1 weights, bf16 x bf16 -> fp32 MFMA",
+        "dtype": "bf16",
         "data": f"synthetic (seeded draws, seed {args.seed})",
         "config": {"workload": f"prefill of {args.prefill} tokens on {args.ctx} cached positions, target {m.n_layers} "
                                f"layers hidden {m.hidden} Q4_1, chunks of 16 rows",
@@ -370,10 +370,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_1 weights, bf16 x bf16 -> fp32 MFMA",
+        "dtype": "bf16",
         "data": "synthetic (seeded draws, seed 0)",
         "config": {"workload": f"target-shaped verify: {m.n_layers} layers, hidden {H}, Q4_1, head {V}x{H} bf16, "
                                f"{args.ctx} cached positions, k={k}",
+                   "arithmetic": "Q4_1 weights (codes exact in bf16), bf16 x bf16 -> fp32 MFMA, fp32 residual, "
+                                 "norms and softmax",
                    "k": k, "cached_positions": args.ctx, "layers": m.n_layers, "vocab": V,
                    "accept": "greedy" if args.temperature <= 0 else f"sampled, T={args.temperature}",
                    "kv_planes": "bf16" if args.kv_bf16 else "fp32"},
