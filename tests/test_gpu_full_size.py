@@ -69,12 +69,13 @@ def test_full_size_gemms_ragged_rows(full, layer, rows):
         assert err < GEMM_TOL
 
 
-@pytest.mark.parametrize("k", [8, 1])
+@pytest.mark.parametrize("k", [8, 1, 5, 13])
 def test_full_size_verify(full, k):
-    """The benchmark's step at full size: logits of every row within the stack bar, the taps, the
-    greedy tokens where the top-2 margin is clear, the accept decision bit-exact, KV counts."""
+    """The benchmark's step at full size (k = 8, 1) and at ragged row counts (5, 13): logits of every
+    row within the stack bar, the taps, the greedy tokens where the top-2 margin is clear, the
+    accept decision bit-exact, KV counts."""
     m, w, kv, g = full
-    toks = synth.tokens(0, "bench.tokens", 8, m.vocab)[:k]   # the benchmark's rows
+    toks = synth.tokens(0, "bench.tokens", max(8, k), m.vocab)[:k]   # the benchmark's rows first
     lg, taps = run_verify(g, m, toks)
     o = oracle.Model(m, w)
     o.set_kv(kv, P)
