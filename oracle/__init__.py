@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
             "orc_step": (I, [P, I, P, P]),
             "orc_verify_batch": (I, [P, P, I, P, P]),
             "orc_commit_verify_rows": (I, [P, I]),
+            "orc_extend_context": (I, [P, P, L64]),
             "orc_argmax": (I, [P, I]),
             "orc_accept_greedy": (I, [P, I, I, P, P, P]),
             "orc_philox4x32_10": (None, [P, P, P]),
@@ -237,6 +238,15 @@ class Model:
             kv = np.ascontiguousarray(kv[:positions], dtype=np.float32)
             assert lib().orc_set_kv(self.h, l, _p(kv), positions) == 0
         lib().orc_set_held(self.h, positions)
+
+    def extend_context(self, kv_new, n: int) -> int:
+        """Append n positions of K/V rows to every own plane (kv_new[l]: [n][2][w_l] fp32 for an own
+        layer, ignored for a shared one). Returns 0, or 2 (verify pending) / 3 (past max_ctx) with no
+        state change."""
+        parts = [np.ascontiguousarray(kv_new[l][:n], dtype=np.float32).ravel()
+                 for l in range(self.m.n_layers) if self.m.layers[l].kv_owner < 0]
+        flat = np.concatenate(parts) if parts else np.zeros(1, dtype=np.float32)
+        return int(lib().orc_extend_context(self.h, _p(flat), n))
 
     def held(self) -> int:
         return int(lib().orc_positions_held(self.h))

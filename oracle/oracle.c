@@ -599,6 +599,27 @@ int orc_commit_verify_rows(orc_model* md, int n) {
     return 0;
 }
 
+/* extend_context [PR2303, "What changes" item 1: snapshot, restore, the verify rollback and
+ * extend_context counted every layer at NKV * HD; the count is per layer]. Appends n positions of
+ * given K/V rows to every own plane at the held count, each at that layer's own width: kv_all is
+ * the own planes' new rows one after the other in layer order, [n][2][w_l] fp32 each (K already
+ * normalised and rotated, as for a cached context). Shared planes stay empty. positions held += n.
+ * Refused (2, no state change) while a verify is pending; (3) past max_ctx. */
+int orc_extend_context(orc_model* md, const float* kv_all, long n) {
+    if (md->pending >= 0) return 2;
+    if (n < 0 || md->held + n > md->max_ctx) return 3;
+    size_t off = 0;
+    for (int l = 0; l < md->n_layers; l++) {
+        if (!md->plane[l]) continue;
+        const long w = kv_width(md, l);
+        float* dst = md->plane[l] + (size_t)md->held * 2 * w;
+        for (size_t i = 0; i < (size_t)n * 2 * w; i++) dst[i] = store_kv(md, kv_all[off + i]);
+        off += (size_t)n * 2 * w;
+    }
+    md->held += n;
+    return 0;
+}
+
 /* Greedy longest-prefix accept [CARD, "How it is used"; PR2236, the acceptance tool]: row i's
  * greedy token is the first index of the row's maximum (NaN never wins); draft d_m = tokens[m] is
  * kept while it equals the greedy token of row m-1. Emits d_1..d_a and the target's own y_a. */

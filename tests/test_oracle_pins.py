@@ -399,6 +399,40 @@ def test_commit_refusals():
     assert A.commit_verify_rows(1) == 2          # already committed
 
 
+def test_extend_context_per_layer_widths():
+    """extend_context appends each own plane's rows at its own width ([PR2303] "What changes" item 1:
+    the count is per layer): extending 5 cached positions by 3 gives the planes, the counts and the
+    next step of a model that cached all 8 from the start; shared planes stay empty."""
+    m, w, kv8 = _two_width(positions=8)
+    assert len({m.kv_width(l) for l in range(m.n_layers) if m.own(l)}) == 2   # two geometries
+    A = oracle.Model(m, w); A.set_kv(kv8, 5)
+    new = [None if kv is None else kv[5:8] for kv in kv8]
+    assert A.extend_context(new, 3) == 0
+    assert A.held() == 8
+    assert list(A.plane_floats()) == [8 * 2 * m.kv_width(l) if m.own(l) else 0 for l in range(m.n_layers)]
+    B = oracle.Model(m, w); B.set_kv(kv8, 8)
+    for l in range(m.n_layers):
+        if m.own(l):
+            assert np.array_equal(A.plane(l, 8), B.plane(l, 8)), f"plane {l}"
+    assert np.array_equal(A.step(11), B.step(11))
+
+
+def test_extend_context_refusals_leave_state():
+    m, w, kv8 = _two_width(positions=8)
+    A = oracle.Model(m, w); A.set_kv(kv8, 5)
+    new = [None if kv is None else kv[5:8] for kv in kv8]
+    A.verify_batch(np.array([1, 2], dtype=np.int32))
+    before = [A.plane(l, 8) for l in range(m.n_layers) if m.own(l)]
+    assert A.extend_context(new, 3) == 2                 # a verify is pending
+    assert A.held() == 7
+    assert all(np.array_equal(b, A.plane(l, 8)) for b, l in zip(before, [l for l in range(m.n_layers) if m.own(l)]))
+    assert A.commit_verify_rows(0) == 0
+    big = [None if kv is None else np.zeros((m.max_ctx, 2, kv.shape[2]), np.float32) for kv in kv8]
+    assert A.extend_context(big, m.max_ctx - 4) == 3     # past max_ctx
+    assert A.held() == 5
+    assert A.extend_context(new, 0) == 0 and A.held() == 5
+
+
 def test_snapshot_restore_per_layer_widths():
     m, w, kv = _two_width(positions=6)
     A = oracle.Model(m, w); A.set_kv(kv, 6)
