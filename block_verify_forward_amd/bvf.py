@@ -53,6 +53,7 @@ SIGNATURES = {
     "bvf_set_kv": (_I32, [_P, _I32, _P, _I64]),
     "bvf_get_kv": (_I32, [_P, _I32, _P, _I64]),
     "bvf_set_positions": (_I32, [_P, _I64]),
+    "bvf_extend_context": (_I32, [_P, _P, _I64]),
     "bvf_kv_widths": (_I32, [_P, _P, _I32]),
     "bvf_plane_floats": (_I32, [_P, _P, _I32]),
     "bvf_positions_held": (_I32, [_P, _P]),
@@ -203,6 +204,14 @@ class Model:
 
     def set_positions(self, positions: int):
         _check(lib().bvf_set_positions(self.h, positions))
+
+    def extend_context(self, kv_new, n: int):
+        """Append n positions of K/V rows to every own plane (kv_new[l]: [n][2][w_l] fp32 for an own
+        layer, ignored for a shared one); positions held += n."""
+        parts = [np.ascontiguousarray(kv_new[l][:n], dtype=np.float32).ravel()
+                 for l in range(self.m.n_layers) if self.m.layers[l].kv_owner < 0]
+        flat = np.concatenate(parts) if parts else np.zeros(1, dtype=np.float32)
+        _check(lib().bvf_extend_context(self.h, _host(flat), n))
 
     def set_context(self, kv_list, positions: int):
         """set_kv on every own plane, then set_positions."""

@@ -739,6 +739,42 @@ bvf_status bvf_steer_logits(bvf_model* m, float* d_logits_all, int32_t k, const 
     return ok();
 }
 
+bvf_status bvf_extend_context(bvf_model* m, const float* h_kv_all, int64_t n) {
+    if (!m) return fail(BVF_E_INVALID, "model is NULL");
+    if (n < 0) return fail(BVF_E_INVALID, "n = %lld < 0", (long long)n);
+    if (n > 0 && !h_kv_all) return fail(BVF_E_INVALID, "NULL argument");
+    if (m->pending >= 0) return fail(BVF_E_STATE, "extend_context while a verify of %d rows is pending", m->pending);
+    if (m->held + n > m->d.max_ctx)
+        return fail(BVF_E_CAPACITY, "%lld held + %lld rows > max_ctx %d", (long long)m->held, (long long)n, m->d.max_ctx);
+    if (n == 0) return ok();
+    // every own plane takes its n rows at its own width, after the held positions (the rows of the
+    // own layers follow one another in layer order in h_kv_all)
+    HIP_TRY(hipStreamSynchronize(m->st));
+    size_t off = 0;
+    std::vector<uint16_t> b;
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        Layer& L = m->L[l];
+        if (!L.plane) continue;
+        const size_t cnt = (size_t)n * 2 * L.w;
+        const size_t at = (size_t)m->held * 2 * L.w;
+        if (!m->d.kv_bf16) {
+            HIP_TRY(hipMemcpy((float*)L.plane + at, h_kv_all + off, cnt * 4, hipMemcpyHostToDevice));
+        } else {
+            b.resize(cnt);   // bf16 planes: each value rounded to nearest even (NaN kept quiet)
+            for (size_t i = 0; i < cnt; ++i) {
+                uint32_t u;
+                std::memcpy(&u, &h_kv_all[off + i], 4);
+                b[i] = (u & 0x7fffffffu) > 0x7f800000u ? (uint16_t)((u >> 16) | 0x40u)
+                                                        : (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+            }
+            HIP_TRY(hipMemcpy((uint16_t*)L.plane + at, b.data(), cnt * 2, hipMemcpyHostToDevice));
+        }
+        off += cnt;
+    }
+    m->held += n;
+    return ok();
+}
+
 bvf_status bvf_commit_verify_rows(bvf_model* m, int32_t n) {
     if (!m) return fail(BVF_E_INVALID, "model is NULL");
     if (m->pending < 0) return fail(BVF_E_STATE, "commit_verify_rows with no verify pending");

@@ -128,6 +128,15 @@ bvf_status bvf_load_bf16(bvf_model* m, int32_t tensor, int32_t layer, const uint
  * bvf_set_positions then fixes the count. Refused on a shared layer. */
 bvf_status bvf_set_kv(bvf_model* m, int32_t layer, const float* h_kv, int64_t positions);
 bvf_status bvf_set_positions(bvf_model* m, int64_t positions);
+/* extend_context [PR2303, "What changes" item 1: it is one of the operations whose KV count is per
+ * layer]: appends n positions of given K/V rows to every own plane at the held count, each at that
+ * layer's own width w_l, and positions held += n; shared planes stay empty. h_kv_all (host, read
+ * before the call returns) holds the own layers' new rows one after the other in layer order, each
+ * [n][2][w_l] fp32 (K then V per position, K already normalised and rotated, as for bvf_set_kv);
+ * bf16 planes store each value rounded to nearest even. Synchronous with the model's stream.
+ * Refused with no state change: a verify pending (BVF_E_STATE), held + n > max_ctx
+ * (BVF_E_CAPACITY), n < 0 or h_kv_all NULL with n > 0 (BVF_E_INVALID). n = 0 does nothing. */
+bvf_status bvf_extend_context(bvf_model* m, const float* h_kv_all, int64_t n);
 /* Read back the first `positions` rows of an own plane into h_kv [positions][2][w] fp32, in the
  * layout bvf_set_kv takes (bf16 planes are widened exactly). Waits for the model's stream. Rows at
  * or beyond the held count hold whatever the last pass or set_kv left there. Refused on a shared
