@@ -1,5 +1,6 @@
 // Plan sweep of the small-M Q4_1 GEMM: for each GEMM shape of the target-shaped verify pass (q|k|v of
-// a sliding layer, o, gate|up of own and KV-shared layers, down of own and KV-shared layers), times
+// a sliding layer, o, gate|up of own and KV-shared layers, down of own and KV-shared layers) and of
+// the draft's layers (q|k|v, o, gate|up, down), times
 // every forced plan (K splits S, waves W, K parts KS, ring depth R, items per workgroup) that fits
 // the LDS, per launch over enough distinct weight copies that the stream comes from HBM (more bytes
 // than the 256 MB last-level cache), and checks each plan's output against the planner's own plan.
@@ -27,7 +28,10 @@ int main(int argc, char** argv) {
   const int M = argc > 2 ? atoi(argv[2]) : 8;
   std::vector<Cls> cls = {{"qkv_sliding", 160, 20, EPI_STORE, true}, {"o", 160, 16, EPI_RESID, false},
                           {"gu_own", 1280, 20, EPI_SWIGLU, true}, {"gu_shared", 2560, 20, EPI_SWIGLU, true},
-                          {"down_own", 160, 80, EPI_RESID, false}, {"down_shared", 160, 160, EPI_RESID, false}};
+                          {"down_own", 160, 80, EPI_RESID, false}, {"down_shared", 160, 160, EPI_RESID, false},
+                          // the draft's layers (hidden 2560, 32 query / 8 KV heads of 128, FFN 5120)
+                          {"draft_qkv", 384, 20, EPI_STORE, true}, {"draft_o", 160, 32, EPI_RESID, false},
+                          {"draft_gu", 640, 20, EPI_SWIGLU, true}, {"draft_down", 160, 40, EPI_RESID, false}};
   std::string only = argc > 1 && std::string(argv[1]) != "all" ? argv[1] : "";
   const size_t budget = 600ull << 20;   // bytes of weight copies per class
   float* partial; int* counters; CK(hipMalloc(&partial, (16ull << 20) * 4)); CK(hipMalloc(&counters, 16384 * 4));
