@@ -721,6 +721,11 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
     // per workgroup and one K part per wave (W = T), one workgroup per compute unit.
     if (L.fmt == W_Q4_1 && norm && L.force_S <= 0 && tiles % cus == 0 && tiles / cus >= 8 && tiles / cus <= 16)
         consider(1, G, tiles / cus, 1, 2, 1, true);
+    // Between one and two tiles per compute unit with the RMSNorm folded in (the draft's q|k|v):
+    // measured best with two tiles per workgroup, 8 waves in 4 K parts, at most one workgroup per
+    // compute unit (9.4 against 11.1 us for one tile per workgroup of 5 waves).
+    if (L.fmt == W_Q4_1 && norm && L.force_S <= 0 && tiles > cus && tiles <= 2 * cus)
+        consider(1, G, 8, 4, 2, 1, true);
     if (L.force_S > 0 && L.force_R > 0 && L.force_ipw > 0 && L.force_W > 0 && L.force_KS > 0 && L.force_W % L.force_KS == 0) {
         const int sb = (G + L.force_S - 1) / L.force_S;
         const int Se = (G + sb - 1) / sb;
