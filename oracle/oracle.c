@@ -19,8 +19,10 @@
  * SwiGLU product, taps) is bf16, rounded to nearest even. Q4_1 weights are used exactly.
  *
  * Parity status: every function here is pinned by the CPU tests (closed forms, invariants, hand
- * cases, brute force on tiny shapes), except the draft block forward and the full-depth logits,
- * whose values no page prints ("parity unpinned" beyond the invariants the tests list).
+ * cases, brute force on tiny shapes). No page prints values for the full-depth logits or the draft
+ * block; those are pinned by hand cases with closed forms (the q/k path, the draft's fc, hidden
+ * norm, context positions and head rows) and by an independent numpy float64 twin of the verify
+ * and of the draft, which must agree with this file to 1e-12.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -lm. OpenMP only splits independent output
  * features; each output is summed by one thread in index order, so results do not depend on the

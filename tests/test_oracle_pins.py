@@ -541,7 +541,7 @@ def test_speculative_output_equals_plain_greedy():
 
 
 # ------------------------------------------------------------------------------------------
-# draft block forward (parity unpinned beyond these invariants)
+# draft block forward: invariants (closed forms and the numpy twin in test_oracle_pins_paths.py)
 # ------------------------------------------------------------------------------------------
 def _draft_pair(window=0, n_ctx=10):
     tm = synth.tiny_model(max_ctx=64)
