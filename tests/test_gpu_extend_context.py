@@ -58,7 +58,7 @@ def test_extend_context_equals_cached_context(kv_bf16):
         return x.verify_embedded(arrs[0])
 
     err = rel_l1(a, ref)
-    tol = logits_bar(err, run_oracle, [embed_rows(w, toks)] + kv8)
+    tol = logits_bar(err, m, run_oracle, [embed_rows(w, toks)] + kv8, f"extend_context kv_bf16={kv_bf16}")
     assert err < tol, f"rel-L1 {err:.2e} >= {tol:.2e}"
     A.commit_verify_rows(2)
     assert A.positions_held() == 10

@@ -87,12 +87,24 @@ def test_full_size_verify(full, k):
         return x.verify_embedded(arrs[0])
 
     err = rel_l1(lg, rlg)
-    tol = logits_bar(err, run_oracle, [embed_rows(w, toks)] + kv)
-    print(f"full-size k={k}: logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, m, run_oracle, [embed_rows(w, toks)] + kv, f"full-size verify k={k}")
     assert err < tol
     compare_taps(taps, rtaps, tol)
     assert g.positions_held() == o.held() == P + k
     assert np.array_equal(g.plane_floats(), o.plane_floats())
+    # the fp32 K/V rows this verify appended, element by element against the oracle's planes: the
+    # cached rows untouched, layer 0's rows to the GEMM's accumulation order (its input rows are
+    # the embedding rows on both sides), deeper layers within the logits bar (their inputs carry
+    # the stack's rounding differences); K and V rows compared separately
+    for l in range(m.n_layers):
+        if not m.own(l):
+            continue
+        gp, op = g.get_kv(l, P + k).astype(np.float64), o.plane(l, P + k).astype(np.float64)
+        assert np.array_equal(gp[:P], op[:P]), f"layer {l}: cached rows changed"
+        kv_err = rel_l1(gp[P:].reshape(2 * k, -1), op[P:].reshape(2 * k, -1))
+        bar = GEMM_TOL if l == 0 else tol
+        print(f"layer {l}: appended K/V rows rel-L1 {kv_err:.2e} (bar {bar:.1e})")
+        assert kv_err < bar, f"layer {l}"
     for i in range(k):
         top2 = np.sort(rlg[i])[-2:]
         if top2[1] - top2[0] > 0.02 * np.sqrt(np.mean(rlg[i].astype(np.float64) ** 2)):
@@ -175,7 +187,7 @@ def test_full_size_draft_block(full, n_new):
     rp, rlg = run_oracle([x0] + kvd)
     glg = host(lg)
     err = rel_l1(glg, rlg)
-    tol = logits_bar(err, lambda a: run_oracle(a)[1], [x0] + kvd)
+    tol = logits_bar(err, dm, lambda a: run_oracle(a)[1], [x0] + kvd, f"full-size draft block n_new={n_new}")
     print(f"full-size draft n_new={n_new}: logits rel-L1 {err:.2e} (bar {tol:.2e})")
     assert err < tol
     gp = host(props)

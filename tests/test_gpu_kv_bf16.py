@@ -15,8 +15,7 @@ import pytest
 
 import oracle
 from block_verify_forward_amd import bvf, synth
-from tests.test_gpu_parity import compare_taps, dev, embed_rows, host, logits_bar, ragged_model, run_verify, \
-    stack_tol
+from tests.test_gpu_parity import compare_taps, dev, embed_rows, host, logits_bar, ragged_model, run_verify
 from tests.util import rel_l1
 
 torch = pytest.importorskip("torch")
@@ -146,8 +145,7 @@ def test_verify_parity_kv_bf16(mk, P, k):
         return x.verify_embedded(arrs[0])
 
     err = rel_l1(lg, rlg)
-    tol = logits_bar(err, run_oracle, [embed_rows(w, toks)] + kv)
-    print(f"logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, m, run_oracle, [embed_rows(w, toks)] + kv, f"bf16 planes verify P={P} k={k}")
     assert err < tol
     if m.tap_layers:
         compare_taps(taps, rtaps, tol)
@@ -185,7 +183,8 @@ def test_commit_then_next_pass_kv_bf16(n):
         return x.verify_embedded(arrs[0])
 
     arrs = [embed_rows(w, nxt)] + kv
-    assert rel_l1(lg, run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+    err = rel_l1(lg, run_oracle(arrs))
+    assert err < logits_bar(err, m, run_oracle, arrs, f"bf16 planes commit({n}), next pass")
 
 
 def test_snapshot_restore_kv_bf16():
@@ -211,7 +210,8 @@ def test_snapshot_restore_kv_bf16():
         return x.verify_embedded(arrs[0])
 
     arrs = [embed_rows(w, toks)] + kv
-    assert rel_l1(lg, run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+    err = rel_l1(lg, run_oracle(arrs))
+    assert err < logits_bar(err, m, run_oracle, arrs, "bf16 planes, after snapshot restore")
     g.commit_verify_rows(0)
     m32 = dataclasses.replace(m, kv_bf16=0)
     g32, _, _, _ = build_pair(m32, 18)
@@ -264,8 +264,7 @@ def test_draft_block_kv_bf16(window, n_ctx, n_new, block):
     rp, rlg = run_oracle([x0] + kvd, held)
     glg = host(lg)
     err = rel_l1(glg, rlg)
-    tol = logits_bar(err, lambda a: run_oracle(a)[1], [x0] + kvd)
-    print(f"draft logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, dm, lambda a: run_oracle(a)[1], [x0] + kvd, f"bf16 planes draft w={window} ctx={n_ctx} new={n_new} B={block}")
     assert err < tol
     check_planes(D, held[0], dm, n_ctx, n_new, tol)
     gp = host(props)
@@ -295,8 +294,7 @@ def test_full_size_verify_kv_bf16():
         return x.verify_embedded(arrs[0])
 
     err = rel_l1(lg, rlg)
-    tol = logits_bar(err, run_oracle, [embed_rows(w, toks)] + kv)
-    print(f"full-size bf16 planes: logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, m, run_oracle, [embed_rows(w, toks)] + kv, "full-size verify, bf16 planes")
     assert err < tol
     compare_taps(taps, rtaps, tol)
     check_planes(g, o, m, P, k, tol)
@@ -343,8 +341,7 @@ def test_full_size_draft_block_kv_bf16():
     held = []
     rp, rlg = run_oracle([x0] + kvd, held)
     err = rel_l1(host(lg), rlg)
-    tol = logits_bar(err, lambda a: run_oracle(a)[1], [x0] + kvd)
-    print(f"full-size draft, bf16 planes: logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, dm, lambda a: run_oracle(a)[1], [x0] + kvd, "full-size draft block, bf16 planes")
     assert err < tol
     check_planes(D, held[0], dm, P, n_new, tol)
     gp = host(props)

@@ -49,8 +49,7 @@ def test_long_context_verify(ctx, k):
         return x.verify_embedded(arrs[0])
 
     err = rel_l1(lg, rlg)
-    tol = logits_bar(err, run_oracle, [embed_rows(w, toks)] + kv)
-    print(f"P={P} k={k}: logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, m, run_oracle, [embed_rows(w, toks)] + kv, f"target P={P} k={k}")
     assert err < tol
     compare_taps(taps, rtaps, tol)
     assert g.positions_held() == o.held() == P + k
@@ -112,8 +111,7 @@ def test_long_context_tiny_stack(kv_bf16):
         return x.verify_embedded(arrs[0])
 
     err = rel_l1(lg, rlg)
-    tol = logits_bar(err, run_oracle, [embed_rows(w, toks)] + kv)
-    print(f"tiny stack at {P}, bf16 planes {kv_bf16}: logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, m, run_oracle, [embed_rows(w, toks)] + kv, f"tiny stack at {P}, bf16 planes {kv_bf16}")
     assert err < tol
     compare_taps(taps, rtaps, tol)
     assert g.positions_held() == o.held() == P + k
@@ -152,8 +150,7 @@ def test_long_context_draft_block(kv_bf16):
 
     rp, rlg = run_oracle([x0] + kvd)
     err = rel_l1(host(lg), rlg)
-    tol = logits_bar(err, lambda a: run_oracle(a)[1], [x0] + kvd)
-    print(f"draft over {P} context rows, bf16 planes {kv_bf16}: logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, dm, lambda a: run_oracle(a)[1], [x0] + kvd, f"draft over {P} context rows, bf16 planes {kv_bf16}")
     assert err < tol
     gp = host(props)
     for i in range(block - 1):

@@ -20,16 +20,32 @@ GEMM_TOL = 2e-5           # rel-L1 per row of a single GEMM (fp32 vs fp64 accumu
 
 
 def stack_tol(run_oracle, arrays):
-    """Whole-stack logits bar: the 2e-3 bar, or three times the oracle's own spread under
-    fp32-level perturbation of its inputs when one bf16 rounding flip already moves a row by more
-    (stacks of several layers with these weight distributions). run_oracle(arrays) -> logits."""
+    """Three times the oracle's own spread under fp32-level perturbation of its inputs, never below
+    2e-3 (the bar of the tiny multi-layer stacks, see stack_bar). run_oracle(arrays) -> logits."""
     return max(LOGIT_TOL, 3.0 * noise_floor(run_oracle, arrays))
 
 
-def logits_bar(err, run_oracle, arrays):
-    """The bar for a whole-stack logits error: 2e-3 when the error is already inside it (the bar
-    is never below 2e-3, so the oracle's spread need not be measured), else stack_tol."""
-    return LOGIT_TOL if err < LOGIT_TOL else stack_tol(run_oracle, arrays)
+# Models whose logits take the fixed 2e-3 bar: the single-layer decoder of config 1 (and any
+# single-layer model), the target-shaped stack of configs 3 and 4, and the full-size draft.
+FIXED_BAR_MODELS = ("target", "draft")
+
+
+def logits_bar(err, m, run_oracle, arrays, label=""):
+    """The logits bar of one comparison, printed with the error.
+
+    Fixed 2e-3 (rel-L1 per row) for config 1, the target-shaped stack and the full-size draft.
+    Documented exception, the tiny multi-layer stacks (the 6-layer two-width miniature, the
+    3-layer ragged model, the 2-layer tiny draft): there a single bf16 rounding flip of an attention
+    output or SwiGLU product between two correct fp32 summation orders moves a row by about 1e-3
+    with these weight distributions, and flips add up over the layers; their bar is
+    max(2e-3, 3 x the oracle's own spread under a 1e-5 relative input perturbation), and the spread
+    is printed with every comparison."""
+    if m.n_layers == 1 or m.name in FIXED_BAR_MODELS:
+        print(f"[bar] {m.name} {label}: logits rel-L1 {err:.2e}, fixed bar {LOGIT_TOL:.1e}")
+        return LOGIT_TOL
+    tol = stack_tol(run_oracle, arrays)
+    print(f"[bar] {m.name} {label}: logits rel-L1 {err:.2e}, stack bar {tol:.2e}")
+    return tol
 
 
 def embed_rows(w, toks):
@@ -158,8 +174,7 @@ def test_verify_parity(mk, P, k):
         return x.verify_embedded(arrs[0])
 
     err = rel_l1(lg, rlg)
-    tol = logits_bar(err, run_oracle, [embed_rows(w, toks)] + kv)
-    print(f"logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, m, run_oracle, [embed_rows(w, toks)] + kv, f"verify P={P} k={k}")
     assert err < tol
     if m.tap_layers:
         compare_taps(taps, rtaps, tol)
@@ -309,7 +324,8 @@ def test_commit_worked_case_and_next_step():
         return x.verify_embedded(arrs[0])
 
     arrs = [embed_rows(w, nxt)] + kv
-    assert rel_l1(lg, run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+    err = rel_l1(lg, run_oracle(arrs))
+    assert err < logits_bar(err, m, run_oracle, arrs, "commit worked case, next pass")
 
 
 @pytest.mark.parametrize("n", range(0, 9))
@@ -331,7 +347,8 @@ def test_commit_every_n(n):
         return x.verify_embedded(arrs[0])
 
     arrs = [embed_rows(w, nxt)] + kv
-    assert rel_l1(lg, run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+    err = rel_l1(lg, run_oracle(arrs))
+    assert err < logits_bar(err, m, run_oracle, arrs, f"commit({n}), next pass")
 
 
 def test_commit_refusals_leave_state_unchanged():
@@ -382,13 +399,35 @@ def test_snapshot_restore_per_layer_widths():
         return x.verify_embedded(arrs[0])
 
     arrs = [embed_rows(w, toks)] + kv
-    assert rel_l1(lg, run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+    err = rel_l1(lg, run_oracle(arrs))
+    assert err < logits_bar(err, m, run_oracle, arrs, "after snapshot restore")
     # a snapshot of another geometry is refused
     m2 = synth.tiny_model(max_ctx=m.max_ctx)
     g2 = bvf.Model(m2)
     with pytest.raises(bvf.BvfError) as e:
         g2.restore(snap)
     assert e.value.status == bvf.BVF_E_INVALID
+
+
+def test_snapshot_refused_while_a_verify_is_pending():
+    """Both sides refuse a snapshot between a verify and its commit, with no state change; the
+    commit that follows cuts the verify's rows on both (3 held + 4 verified, commit 2 -> 5)."""
+    m = synth.tiny_two_width_model()
+    g, o, w, kv = build_pair(m, 3)
+    toks = synth.tokens(0, "snap.pending", 4, m.vocab)
+    run_verify(g, m, toks, with_taps=False)
+    o.verify_batch(toks)
+    with pytest.raises(bvf.BvfError) as e:
+        g.snapshot_take()
+    assert e.value.status == bvf.BVF_E_STATE
+    with pytest.raises(RuntimeError):
+        o.snapshot()
+    assert g.positions_held() == o.held() == 7
+    g.commit_verify_rows(2)
+    assert o.commit_verify_rows(2) == 0
+    assert g.positions_held() == o.held() == 5
+    assert np.array_equal(g.plane_floats(), o.plane_floats())
+    assert np.array_equal(g.snapshot_take().floats(), o.snapshot().floats())
 
 
 def test_shared_layers_read_owner_planes():
@@ -411,8 +450,9 @@ def test_shared_layers_read_owner_planes():
         return x.verify_embedded(arrs[0])
 
     arrs = [embed_rows(w, toks)] + kv2
-    tol = stack_tol(run_oracle, arrs)
-    assert rel_l1(lg1, run_oracle(arrs)) < tol
+    err = rel_l1(lg1, run_oracle(arrs))
+    tol = logits_bar(err, m, run_oracle, arrs, "shared layers, perturbed owner plane")
+    assert err < tol
     assert rel_l1(lg1, lg0) > 3 * tol
 
 
@@ -454,8 +494,8 @@ def test_draft_block_parity(window, n_ctx, n_new, block):
 
     rp, rlg = run_oracle([x0] + kvd)
     glg = host(lg)
-    err, tol = rel_l1(glg, rlg), stack_tol(lambda a: run_oracle(a)[1], [x0] + kvd)
-    print(f"draft logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    err = rel_l1(glg, rlg)
+    tol = logits_bar(err, dm, lambda a: run_oracle(a)[1], [x0] + kvd, f"draft block w={window} ctx={n_ctx} new={n_new} B={block}")
     assert err < tol
     gp = host(props)
     for i in range(block - 1):
@@ -490,7 +530,8 @@ def test_draft_append_only_then_block():
         return oracle.draft_block_embedded(Do, To, arrs[0])[1]
 
     arrs = [embed_rows(tw, [5] + [tm.vocab - 1] * 7)]
-    assert rel_l1(host(lg), run_oracle(arrs)) < stack_tol(run_oracle, arrs)
+    err = rel_l1(host(lg), run_oracle(arrs))
+    assert err < logits_bar(err, dm, run_oracle, arrs, "draft append-only then block")
 
 
 # ------------------------------------------------------------------------------------------

@@ -54,8 +54,7 @@ def test_prefill_matches_oracle(setup, n):
         x.set_kv(arrs[1:], P0)
         return x.verify_embedded(arrs[0])[-1:]
 
-    tol = logits_bar(err, run_prefill_oracle, [embed_rows(w, toks)] + kv)
-    print(f"prefill {n}: last-row logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, m, run_prefill_oracle, [embed_rows(w, toks)] + kv, f"prefill {n}: last row")
     assert err < tol
     # the context the prefill left: a verify of 8 rows on top of it
     vt = synth.tokens(1, f"prefill.next.{n}", 8, m.vocab)
@@ -71,8 +70,7 @@ def test_prefill_matches_oracle(setup, n):
         x.commit_verify_rows(n)
         return x.verify_embedded(arrs[0])
 
-    tol = logits_bar(err, run_oracle, [embed_rows(w, vt)] + kv)
-    print(f"prefill {n}: next verify logits rel-L1 {err:.2e} (bar {tol:.2e})")
+    tol = logits_bar(err, m, run_oracle, [embed_rows(w, vt)] + kv, f"prefill {n}: next verify")
     assert err < tol
 
 
@@ -109,8 +107,7 @@ def test_prefill_as_prefix_cache(setup):
             x.commit_verify_rows(40 + len(suffix))
             return x.verify_embedded(arrs[0])
 
-        tol = logits_bar(err, run_oracle, [embed_rows(w, vt)] + kv)
-        print(f"prefix cache, suffix {ns}: rel-L1 {err:.2e} (bar {tol:.2e})")
+        tol = logits_bar(err, m, run_oracle, [embed_rows(w, vt)] + kv, f"prefix cache vs cold, suffix {ns}")
         assert err < tol
         cache.commit_verify_rows(0)
 
