@@ -787,6 +787,8 @@ bvf_status bvf_commit_verify_rows(bvf_model* m, int32_t n) {
 bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out) {
     if (!m || !out) return fail(BVF_E_INVALID, "NULL argument");
     *out = nullptr;
+    if (m->pending >= 0)
+        return fail(BVF_E_STATE, "snapshot while a verify of %d rows is pending: commit it first", m->pending);
     bvf_snapshot* s = new bvf_snapshot;
     s->n_layers = m->d.n_layers;
     s->held = m->held;
@@ -812,7 +814,6 @@ bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out) {
         bvf_snapshot_free(s);
         return fail(BVF_E_DEVICE, "snapshot: %s", hipGetErrorString(e));
     }
-    m->pending = -1;
     *out = s;
     return ok();
 }
@@ -859,7 +860,7 @@ bvf_status bvf_draft_block_forward(bvf_model* dr, const bvf_model* tg, const uin
     if (block != 0 && (!d_last_token || !d_proposals)) return fail(BVF_E_INVALID, "NULL argument");
     if (!is_draft(dr->d)) return fail(BVF_E_INVALID, "the first model is not a draft");
     if (is_draft(tg->d)) return fail(BVF_E_INVALID, "the second model is not a verify (target) model");
-    if (tg->d.hidden != dr->d.hidden) return fail(BVF_E_INVALID, "the target is %d wide and the draft %d: not a pair", tg->d.hidden, dr->d.hidden);
+    if (tg->d.hidden != dr->d.hidden) return fail(BVF_E_INVALID, "draft hidden size %d differs from the target's %d", dr->d.hidden, tg->d.hidden);
     if (block != 0 && (block < 2 || block > kMaxRows)) return fail(BVF_E_INVALID, "block %d not 0 or in [2, %d]", block, kMaxRows);
     if (n_new < 0 || n_new + block > kMaxRows) return fail(BVF_E_INVALID, "n_new %d + block %d > %d", n_new, block, kMaxRows);
     if (block == 0 && n_new == 0) return ok();

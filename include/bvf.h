@@ -209,8 +209,10 @@ bvf_status bvf_commit_verify_rows(bvf_model* m, int32_t n);
 
 /* Snapshot / restore of the held prefix of every own plane at its own width; shared planes stay
  * empty [PR2303, "What changes" item 1]. The library allocates and owns the snapshot's device copy
- * until bvf_snapshot_free. Restore refuses a snapshot whose layer count or widths differ. Both clear
- * a pending verify. snapshot_floats: floats kept per layer (0 on shared layers). */
+ * until bvf_snapshot_free. A snapshot is of committed state: snapshot_take is refused with
+ * BVF_E_STATE (no state change) while a verify is pending, and leaves the model unchanged
+ * otherwise. Restore refuses a snapshot whose layer count or widths differ, and clears a pending
+ * verify. snapshot_floats: floats kept per layer (0 on shared layers). */
 bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out);
 bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s);
 bvf_status bvf_snapshot_floats(const bvf_snapshot* s, int64_t* h_out, int32_t n);

@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "orc_draft_append": (I, [P, P, I]),
             "orc_draft_block": (I, [P, P, I, I, D, I, P, P]),
             "orc_threads": (I, []),
+            "orc_set_threads": (None, [I]),
             "orc_attend": (None, [P, I, P, L64, P]),
             "orc_layer_forward": (None, [P, I, I, P, P, P]),
             "orc_verify_embedded": (I, [P, P, I, P, P]),
@@ -96,6 +97,11 @@ def _p(a: Optional[np.ndarray]):
 
 def threads() -> int:
     return int(lib().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (results do not depend on it)."""
+    lib().orc_set_threads(int(n))
 
 
 # ---- kernels as functions -------------------------------------------------------------------
@@ -300,7 +306,12 @@ class Model:
         return int(lib().orc_commit_verify_rows(self.h, n))
 
     def snapshot(self):
-        return Snapshot(lib().orc_snapshot_take(self.h), self.m.n_layers)
+        """Snapshot of the committed state; refused (RuntimeError, no state change) while a verify
+        is pending."""
+        h = lib().orc_snapshot_take(self.h)
+        if not h:
+            raise RuntimeError("oracle snapshot: a verify is pending")
+        return Snapshot(h, self.m.n_layers)
 
     def restore(self, snap) -> int:
         return int(lib().orc_snapshot_restore(self.h, snap.h))

@@ -736,7 +736,10 @@ typedef struct orc_snapshot {
     float** data;    /* held x 2 x per[l] floats of each own plane; NULL on a shared plane */
 } orc_snapshot;
 
+/* A snapshot is taken of committed state only: while a verify is pending (its rows not yet cut by
+ * commit_verify_rows) it is refused (NULL) and nothing changes. */
 orc_snapshot* orc_snapshot_take(const orc_model* md) {
+    if (md->pending >= 0) return NULL;
     orc_snapshot* s = calloc(1, sizeof(orc_snapshot));
     s->n_layers = md->n_layers;
     s->held = md->held;
@@ -982,5 +985,14 @@ int orc_threads(void) {
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Threads of the OpenMP loops (the results do not depend on it); for timing at one core. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

@@ -798,3 +798,19 @@ def test_bf16_planes_appended_rows_are_the_fp32_rows_rounded():
         if l == 0:
             assert np.array_equal(pb[10:], r16(pa[10:]))
         assert np.array_equal(pb, r16(pb))
+
+
+def test_snapshot_refused_while_a_verify_is_pending():
+    """A snapshot is of committed state: between a verify and its commit it is refused and nothing
+    changes, so the commit that follows still cuts the verify's rows (3 held + 4 verified,
+    commit 2 -> 5 held, engine PR #2303 "Proof")."""
+    m, w, kv = _two_width(positions=3)
+    A = oracle.Model(m, w)
+    A.set_kv(kv, 3)
+    A.verify_batch(synth.tokens(0, "pin.snap.pending", 4, m.vocab))
+    with pytest.raises(RuntimeError):
+        A.snapshot()
+    assert A.held() == 7
+    assert A.commit_verify_rows(2) == 0 and A.held() == 5
+    snap = A.snapshot()
+    assert snap.floats() == [5 * 2 * m.kv_width(l) if m.own(l) else 0 for l in range(m.n_layers)]
