@@ -300,10 +300,10 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
     }
 }
 
-// Split-K: every wave stores its partial tile at device scope (sc1) as soon as the tile's K range
-// is done. After its whole stream the wave waits until its stores are performed, bumps the arrival
-// counter of each of its tiles, and for the tiles where it arrived last reads the S partials at
-// device scope and sums them in split order. No fence flushes a cache.
+// Split-K: every wave stores its partial tile at device scope as soon as the tile's K range is
+// done. After its whole stream the wave releases its stores at device scope, bumps the arrival
+// counter of each of its tiles, and for the tiles where it arrived last acquires at device scope
+// and reads the S partials, summed in split order.
 __device__ __forceinline__ void splitk_store(const KArgs& a, const floatx4& acc, int tile, int split, int lane) {
     const int c = lane & 15, sub = lane >> 4;
     const int n = tile * kTile + c;
@@ -581,13 +581,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
         // a single item's residual rows are loaded now, in the shadow of the stores and the arrival
         floatx4 y_pre = {0.f, 0.f, 0.f, 0.f};
         if (EPI == EPI_RESID && my_items == 1) y_pre = load_resid_rows(a, first + ts, lane);
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are performed
+        // release at device scope: the partial stores of every lane of this wave are visible to the
+        // other workgroups before the arrival (the wave executes the fence before lane 0's atomic)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         if (lane == 0) {
             for (int it = 0; it < my_items; ++it)
                 if (__hip_atomic_fetch_add(&a.counters[first + it * stride + ts], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1)
                     last |= 1u << it;
         }
         last = __shfl(last, 0);
+        // acquire at device scope: the last arriver reads the partials the other splits released
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         for (int it = 0; it < my_items; ++it) {
             if (!((last >> it) & 1u)) continue;
             const int tile = first + it * stride + ts;
