@@ -107,8 +107,53 @@ def cpu_baseline(m, w, kv, ctx, toks, budget_s: float):
         dt = ds * synth.q4_1_bytes(m) / synth.q4_1_bytes(ms)
         sample = (f"first {n_s} layers + head of the workload, k={k}, timed {ds:.1f} s; pass time scaled by "
                   f"Q4_1 bytes to {m.n_layers} layers")
+    one = cpu_one_core(m, w, kv, ctx, toks)
     return {"value": round(k / dt, 4), "unit": "verified rows/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds_per_pass": round(dt, 3)}
+            "sample": sample, "seconds_per_pass": round(dt, 3), "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "one_core": one}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_one_core(m, w, kv, ctx, toks):
+    """The oracle on one thread: a 1-layer and a 2-layer prefix of the workload (each with the
+    head) give the time of layer 0, of layer 1 and of the head; the pass time is the head plus every
+    layer scaled by its Q4_1 bytes from the measured layer of the same kind."""
+    import dataclasses
+    import oracle
+    from block_verify_forward_amd import synth
+    k = len(toks)
+    all_threads = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        def prefix(n):
+            mp = dataclasses.replace(m, n_layers=n, layers=m.layers[:n], tap_layers=())
+            wp = {"layers": w["layers"][:n], "embed": w["embed"], "final_norm": w["final_norm"]}
+            o = oracle.Model(mp, wp)
+            o.set_kv(kv[:n], ctx)
+            t = time.perf_counter()
+            o.verify_batch(toks)
+            return time.perf_counter() - t, mp
+        t1, m1 = prefix(1)
+        t2, m2 = prefix(2)
+    finally:
+        oracle.set_threads(all_threads)
+    t_layer1 = max(t2 - t1, 1e-9)
+    t_head = max(t1 - t_layer1, 0.0)
+    b1 = synth.q4_1_bytes(m2) - synth.q4_1_bytes(m1)
+    dt = t_head + t_layer1 * synth.q4_1_bytes(m) / b1
+    return {"value": round(k / dt, 4), "unit": "verified rows/s", "cores": 1, "seconds_per_pass": round(dt, 2),
+            "sample": f"layers 0 and 1 plus the head at one thread ({t1 + t2:.1f} s); the pass is the head "
+                      f"({t_head:.2f} s) plus {m.n_layers} layers scaled by Q4_1 bytes from layer 1 ({t_layer1:.2f} s)"}
 
 
 def run_loop(args):
