@@ -300,10 +300,11 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
     }
 }
 
-// Split-K: every wave stores its partial tile at device scope as soon as the tile's K range is
-// done. After its whole stream the wave releases its stores at device scope, bumps the arrival
-// counter of each of its tiles, and for the tiles where it arrived last acquires at device scope
-// and reads the S partials, summed in split order.
+// Split-K: every wave stores its partial tile at device scope (sc1) as soon as the tile's K range
+// is done. After its whole stream the wave waits until its stores are performed, bumps the arrival
+// counter of each of its tiles, and for the tiles where it arrived last reads the S partials at
+// device scope and sums them in split order (the hardware guarantee this relies on is stated at
+// the hand-off).
 __device__ __forceinline__ void splitk_store(const KArgs& a, const floatx4& acc, int tile, int split, int lane) {
     const int c = lane & 15, sub = lane >> 4;
     const int n = tile * kTile + c;
@@ -581,17 +582,28 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
         // a single item's residual rows are loaded now, in the shadow of the stores and the arrival
         floatx4 y_pre = {0.f, 0.f, 0.f, 0.f};
         if (EPI == EPI_RESID && my_items == 1) y_pre = load_resid_rows(a, first + ts, lane);
-        // release at device scope: the partial stores of every lane of this wave are visible to the
-        // other workgroups before the arrival (the wave executes the fence before lane 0's atomic)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // The hand-off relies on what gfx950 does with device-scope (sc1) relaxed atomics, not on
+        // release/acquire fences: agent-scope release/acquire fences write back and invalidate the
+        // whole L2 of the XCD (buffer_wbl2 / buffer_inv), which made each down launch 5 us slower.
+        //  - the partial stores and loads are device-scope atomics, coherent across the XCDs (the
+        //    compiler emits them with the sc1 scope bit; each location has one modification order
+        //    at device scope), so no L2 writeback or invalidation is needed for them;
+        //  - s_waitcnt 0 waits until every store of the wave is acknowledged as performed, before
+        //    the arrival atomic is issued (the compiler barriers keep the compiler from moving
+        //    memory operations across it);
+        //  - the last arriver issues its partial loads (device-scope atomic loads, read at the
+        //    coherence point) only after its arrival returned S - 1, i.e. after every other split's
+        //    arrival, each of which followed that split's performed stores.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
         if (lane == 0) {
             for (int it = 0; it < my_items; ++it)
                 if (__hip_atomic_fetch_add(&a.counters[first + it * stride + ts], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1)
                     last |= 1u << it;
         }
         last = __shfl(last, 0);
-        // acquire at device scope: the last arriver reads the partials the other splits released
-        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        asm volatile("" ::: "memory");
         for (int it = 0; it < my_items; ++it) {
             if (!((last >> it) & 1u)) continue;
             const int tile = first + it * stride + ts;
