@@ -64,6 +64,7 @@ class Model:
     block_causal: int = 1     # 1: verify block (causal); 0: draft block (all block rows see each other)
     draft_window: int = 0     # draft only: context rows visible to the block (0 = all)
     kv_bf16: int = 0          # 1: K/V planes stored in bf16 (a memory variant; the default planes are fp32)
+    ple_dim: int = 0          # per-layer embedding width (Gemma4-style PLE); 0 = none
 
     def kv_width(self, l: int) -> int:
         L = self.layers[l]
@@ -234,6 +235,9 @@ def layer_matrix_shapes(m: Model, l: int) -> Dict[str, tuple]:
         s["k"] = (kvd, H)
         s["v"] = (kvd, H)
     s.update({"o": (H, qd), "gate": (L.ffn, H), "up": (L.ffn, H), "down": (H, L.ffn)})
+    if getattr(m, "ple_dim", 0):
+        s["ple_gate"] = (m.ple_dim, H)
+        s["ple_proj"] = (H, m.ple_dim)
     return s
 
 
@@ -251,6 +255,8 @@ def make_weights(m: Model, seed: int = 0, with_head: bool = True, threads: int =
         d["mlp_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.mlp_norm", (m.hidden,), 0.5, 1.5)
         d["q_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.q_norm", (hd,), 0.5, 1.5)
         d["k_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.k_norm", (hd,), 0.5, 1.5)
+        if getattr(m, "ple_dim", 0):
+            d["layer_scalar"] = bf16_uniform(seed, f"{m.name}.L{l}.layer_scalar", (1,), 0.5, 1.5)
         return d
 
     if threads > 1:
@@ -261,6 +267,8 @@ def make_weights(m: Model, seed: int = 0, with_head: bool = True, threads: int =
         out = {"layers": [layer(l) for l in range(m.n_layers)]}
     if with_head and m.vocab > 0 and m.block_causal == 1:
         out["embed"] = embedding_table(seed, m, max(threads, 8))
+    if getattr(m, "ple_dim", 0):
+        out["ple_table"] = ple_table(seed, m, max(threads, 8))
     out["final_norm"] = bf16_uniform(seed, f"{m.name}.final_norm", (m.hidden,), 0.5, 1.5)
     if m.block_causal == 0:
         T = len(m.tap_layers)
@@ -285,6 +293,22 @@ def embedding_table(seed: int, m: Model, threads: int = 8) -> np.ndarray:
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(one, blocks))
+    return out
+
+
+def ple_table(seed: int, m: Model, threads: int = 8) -> np.ndarray:
+    """The per-layer input table [V, n_layers * ple_dim] bf16, N(0,1): row block b (16384 rows) is
+    drawn from the sub-stream '<model>.ple.<b>'."""
+    from concurrent.futures import ThreadPoolExecutor
+    w = m.n_layers * m.ple_dim
+    out = np.empty((m.vocab, w), dtype=np.uint16)
+
+    def one(r0):
+        r1 = min(m.vocab, r0 + EMBED_ROWS_PER_STREAM)
+        out[r0:r1] = bf16_normal(seed, f"{m.name}.ple.{r0 // EMBED_ROWS_PER_STREAM}", (r1 - r0, w))
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, range(0, m.vocab, EMBED_ROWS_PER_STREAM)))
     return out
 
 

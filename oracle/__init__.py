@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
             "orc_model_new": (P, [I, I, I, I, L64, I, D, D, I, I, P, P, I]),
             "orc_model_free": (None, [P]),
             "orc_set_layer": (None, [P, I] + [P] * 11),
+            "orc_set_ple": (None, [P, I, P]),
+            "orc_set_layer_ple": (None, [P, I, P, P, P]),
             "orc_set_globals": (None, [P, P, P, P, P]),
             "orc_set_kv": (I, [P, I, P, L64]),
             "orc_set_kv_bf16": (None, [P, I]),
@@ -76,7 +78,7 @@ def lib() -> ctypes.CDLL:
             "orc_threads": (I, []),
             "orc_set_threads": (None, [I]),
             "orc_attend": (None, [P, I, P, L64, P]),
-            "orc_layer_forward": (None, [P, I, I, P, P, P]),
+            "orc_layer_forward": (I, [P, I, I, P, P, P]),
             "orc_verify_embedded": (I, [P, P, I, P, P]),
             "orc_draft_block_embedded": (I, [P, P, I, P, P, P]),
         }
@@ -227,6 +229,10 @@ class Model:
                                 g("attn_norm"), g("mlp_norm"), g("q_norm"), g("k_norm"))
         lib().orc_set_globals(self.h, _p(weights.get("embed")), _p(weights.get("final_norm")),
                               _p(weights.get("fc")), _p(weights.get("hidden_norm")))
+        if getattr(m, "ple_dim", 0):
+            lib().orc_set_ple(self.h, m.ple_dim, _p(weights["ple_table"]))
+            for l, d in enumerate(weights["layers"]):
+                lib().orc_set_layer_ple(self.h, l, _p(d["ple_gate"]), _p(d["ple_proj"]), _p(d["layer_scalar"]))
 
     def __del__(self):
         try:
@@ -299,7 +305,7 @@ class Model:
         taps = np.empty((k, len(self.m.tap_layers), self.m.hidden), dtype=np.uint16) if with_taps else None
         rc = lib().orc_verify_embedded(self.h, _p(x0), k, _p(lg), _p(taps))
         if rc:
-            raise RuntimeError(f"oracle verify: status {rc}")
+            raise RuntimeError(f"oracle verify: status {rc}" + (" (injected rows on a PLE model)" if rc == 4 else ""))
         return (lg, taps) if with_taps else lg
 
     def commit_verify_rows(self, n: int) -> int:
@@ -327,7 +333,9 @@ class Model:
         x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, self.m.hidden)
         pos = np.ascontiguousarray(pos, dtype=np.int64)
         out = np.empty_like(x)
-        lib().orc_layer_forward(self.h, l, x.shape[0], _p(x), _p(pos), _p(out))
+        rc = lib().orc_layer_forward(self.h, l, x.shape[0], _p(x), _p(pos), _p(out))
+        if rc:
+            raise RuntimeError(f"oracle layer forward: status {rc}" + (" (injected rows on a PLE model)" if rc == 4 else ""))
         return out
 
     # draft

@@ -233,6 +233,8 @@ typedef struct {
 typedef struct {
     const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
     const uint16_t *attn_norm, *mlp_norm, *q_norm, *k_norm;
+    const uint8_t *ple_gate, *ple_proj;   /* per-layer embedding gate [ple_dim][H], projection [H][ple_dim] */
+    const uint16_t* layer_scalar;         /* one bf16 value */
 } orc_layer_w;
 
 typedef struct orc_model {
@@ -247,6 +249,8 @@ typedef struct orc_model {
     long held;       /* positions held on every own plane */
     long pending;    /* rows appended by the last verify and not yet committed; -1 = none */
     int kv_bf16;     /* planes stored in bf16: every K/V value is rounded (from fp32, RNE) when stored */
+    int ple_dim;     /* per-layer embedding width (0: the model has none) */
+    const uint16_t* ple_table;   /* [vocab][n_layers][ple_dim] bf16 per-layer inputs, indexed by token */
 } orc_model;
 
 static long kv_width(const orc_model* md, int l) {
@@ -297,7 +301,19 @@ void orc_set_layer(orc_model* md, int l, const uint8_t* wq, const uint8_t* wk, c
                    const uint8_t* wo, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
                    const uint16_t* attn_norm, const uint16_t* mlp_norm, const uint16_t* q_norm,
                    const uint16_t* k_norm) {
-    md->W[l] = (orc_layer_w){wq, wk, wv, wo, wg, wu, wd, attn_norm, mlp_norm, q_norm, k_norm};
+    md->W[l] = (orc_layer_w){wq, wk, wv, wo, wg, wu, wd, attn_norm, mlp_norm, q_norm, k_norm, NULL, NULL, NULL};
+}
+
+/* Per-layer embeddings (PLE) [PR2303, "What changes": the batched body builds every row's per-layer
+ * inputs and runs the PLE gate and projection as M-row GEMMs, then the layer scalar]. */
+void orc_set_ple(orc_model* md, int ple_dim, const uint16_t* table) {
+    md->ple_dim = ple_dim;
+    md->ple_table = table;
+}
+void orc_set_layer_ple(orc_model* md, int l, const uint8_t* gate, const uint8_t* proj, const uint16_t* scalar) {
+    md->W[l].ple_gate = gate;
+    md->W[l].ple_proj = proj;
+    md->W[l].layer_scalar = scalar;
 }
 
 void orc_set_globals(orc_model* md, const uint16_t* embed, const uint16_t* final_norm,
@@ -413,7 +429,7 @@ void orc_attend(const orc_model* md, int l, const float* q_in, long p, double* o
  * through the attention half (append at pos[r], then attend over j <= pos[r]), so a batch of rows
  * computes exactly what the same rows do as sequential single steps [PR2303, "Proof": k batched
  * rows bit-identical to k sequential steps]. */
-static void target_layer(orc_model* md, int l, int m, double* x, const long* pos) {
+static void target_layer(orc_model* md, int l, int m, double* x, const long* pos, const int* tokens) {
     const orc_layer_desc* Ld = &md->L[l];
     const orc_layer_w* W = &md->W[l];
     const int H = md->hidden, hd = Ld->head_dim, Hq = md->n_q_heads;
@@ -491,16 +507,38 @@ static void target_layer(orc_model* md, int l, int m, double* x, const long* pos
     q4_1_matmul(W->wd, H, F, gg, m, y);
     for (size_t i = 0; i < (size_t)m * H; i++) x[i] = round_f32(x[i] + round_f32(y[i]));
 
+    /* PLE tail: the gate reads the layer's output rows, u = Wg . bf16(x); the per-layer input p of the
+     * row's token (row l of its table entry) multiplies silu(u); the projection adds Wp . bf16(silu(u) p)
+     * to the residual stream, which the layer scalar then scales. */
+    if (md->ple_dim > 0) {
+        const int D = md->ple_dim;
+        double* u = malloc(sizeof(double) * (size_t)m * D);
+        for (size_t i = 0; i < (size_t)m * H; i++) a[i] = round_bf16(x[i]);
+        q4_1_matmul(W->ple_gate, D, H, a, m, u);
+        for (int r = 0; r < m; r++) {
+            const uint16_t* p = md->ple_table + ((size_t)tokens[r] * md->n_layers + l) * D;
+            for (int j = 0; j < D; j++)
+                u[(size_t)r * D + j] = round_bf16(silu(round_f32(u[(size_t)r * D + j])) * bf16_to_double(p[j]));
+        }
+        q4_1_matmul(W->ple_proj, H, D, u, m, y);
+        const double sc = bf16_to_double(W->layer_scalar[0]);
+        for (size_t i = 0; i < (size_t)m * H; i++) x[i] = round_f32(round_f32(x[i] + round_f32(y[i])) * sc);
+        free(u);
+    }
+
     free(a); free(q); free(kx); free(vx); free(o); free(y); free(t); free(gg); free(uu);
 }
 
-/* Test hook: one layer over m rows at positions pos (appends on an own layer like a verify). */
-void orc_layer_forward(orc_model* md, int l, int m, const float* x_in, const long* pos, float* x_out) {
+/* Test hook: one layer over m rows at positions pos (appends on an own layer like a verify).
+ * Refused (4) on a PLE model: injected rows carry no token ids for the per-layer inputs. */
+int orc_layer_forward(orc_model* md, int l, int m, const float* x_in, const long* pos, float* x_out) {
+    if (md->ple_dim > 0) return 4;
     double* x = malloc(sizeof(double) * (size_t)m * md->hidden);
     for (size_t i = 0; i < (size_t)m * md->hidden; i++) x[i] = x_in[i];
-    target_layer(md, l, m, x, pos);
+    target_layer(md, l, m, x, pos, NULL);
     for (size_t i = 0; i < (size_t)m * md->hidden; i++) x_out[i] = (float)x[i];
     free(x);
+    return 0;
 }
 
 /* logits[r] = Head . bf16(rmsnorm(x[r]) * g_final); the head is the tied bf16 embedding table. */
@@ -521,12 +559,13 @@ static void head_logits(const orc_model* target, const uint16_t* final_norm, int
 
 /* Run rows x0 [m][H] (fp32 residual rows) through every layer in layer-major order.
  * taps: [m][n_taps][H] bf16 or NULL ([CARD, "Taps" row]: zero-based layer outputs). */
-static void forward_x(orc_model* md, const double* x0, int m, const long* pos, float* logits, uint16_t* taps) {
+static void forward_x(orc_model* md, const double* x0, int m, const long* pos, const int* tokens, float* logits,
+                      uint16_t* taps) {
     const int H = md->hidden;
     double* x = malloc(sizeof(double) * (size_t)m * H);
     memcpy(x, x0, sizeof(double) * (size_t)m * H);
     for (int l = 0; l < md->n_layers; l++) {
-        target_layer(md, l, m, x, pos);
+        target_layer(md, l, m, x, pos, tokens);
         for (int ti = 0; ti < md->n_taps; ti++) {
             if (md->tap_layers[ti] != l || !taps) continue;
             for (int r = 0; r < m; r++)
@@ -545,7 +584,7 @@ static void forward_rows(orc_model* md, const int* tokens, int m, const long* po
     double* x = malloc(sizeof(double) * (size_t)m * H);
     for (int r = 0; r < m; r++)
         for (int i = 0; i < H; i++) x[(size_t)r * H + i] = bf16_to_double(md->embed[(size_t)tokens[r] * H + i]);
-    forward_x(md, x, m, pos, logits, taps);
+    forward_x(md, x, m, pos, tokens, logits, taps);
     free(x);
 }
 
@@ -553,12 +592,13 @@ static void forward_rows(orc_model* md, const int* tokens, int m, const long* po
  * injected-embedding form of a batch). Test hook: it lets a test perturb the entry rows. */
 int orc_verify_embedded(orc_model* md, const float* x0, int k, float* logits_all, uint16_t* taps) {
     if (k < 1) return 1;
+    if (md->ple_dim > 0) return 4;   /* injected rows carry no token ids for the per-layer inputs [PR2303] */
     if (md->held + k > md->max_ctx) return 3;
     long* pos = malloc(sizeof(long) * k);
     double* x = malloc(sizeof(double) * (size_t)k * md->hidden);
     for (int r = 0; r < k; r++) pos[r] = md->held + r;
     for (size_t i = 0; i < (size_t)k * md->hidden; i++) x[i] = x0[i];
-    forward_x(md, x, k, pos, logits_all, taps);
+    forward_x(md, x, k, pos, NULL, logits_all, taps);
     free(pos);
     free(x);
     md->held += k;

@@ -70,7 +70,8 @@ class Twin:
         self.W = []
         for l in range(m.n_layers):
             d = weights["layers"][l]
-            self.W.append({key: q4_1_weights(d[key]) for key in ("q", "k", "v", "o", "gate", "up", "down") if key in d})
+            self.W.append({key: q4_1_weights(d[key]) for key in ("q", "k", "v", "o", "gate", "up", "down", "ple_gate",
+                                                                  "ple_proj") if key in d})
         self.E = bf16_values(weights["embed"])
         self.planes = [None] * m.n_layers
         self.held = 0
@@ -121,12 +122,24 @@ class Twin:
         gg = f32(b @ W["gate"].T)
         uu = f32(b @ W["up"].T)
         mm = bf16(gg / (1.0 + np.exp(-gg)) * uu)
-        return f32(x + f32(mm @ W["down"].T))
+        x = f32(x + f32(mm @ W["down"].T))
+        if getattr(m, "ple_dim", 0):
+            # per-layer embeddings: the gate reads bf16 of the layer's output, the row's per-layer
+            # input (layer l of its token's table row) multiplies silu of it, the projection adds
+            # to the residual stream, and the layer scalar scales the result
+            D = m.ple_dim
+            u = f32(bf16(x) @ W["ple_gate"].T)
+            p = bf16_values(self.w["ple_table"][self.tokens])[:, l * D:(l + 1) * D]
+            h = bf16(u / (1.0 + np.exp(-u)) * p)
+            s = float(bf16_values(d["layer_scalar"])[0])
+            x = f32(f32(x + f32(h @ W["ple_proj"].T)) * s)
+        return x
 
     def verify_batch(self, tokens):
         """Logits [k][V] (fp32 values as float64) of a verify of the tokens at the held positions;
         the k rows stay appended."""
         tokens = np.asarray(tokens)
+        self.tokens = tokens
         pos = [self.held + r for r in range(len(tokens))]
         x = self.E[tokens].copy()
         for l in range(self.m.n_layers):

@@ -291,3 +291,80 @@ def test_numpy_twin_agrees_with_oracle_on_the_draft(window):
     assert rel_l1(got, ref) <= 1e-12
     for l in range(dm.n_layers):
         assert np.abs(D.plane(l, 10).astype(np.float64) - twin.planes[l][:10]).max() <= 1e-12
+
+
+# ------------------------------------------------------------------------------------------
+# per-layer embeddings (PLE): per-row inputs by token id, gate and projection, layer scalar
+# ------------------------------------------------------------------------------------------
+def _ple_model(n_layers=2, taps=(0, 1)):
+    import dataclasses
+    m = dataclasses.replace(synth.tiny_model(max_ctx=16, n_layers=n_layers), ple_dim=128, name="tinyple",
+                            tap_layers=taps)
+    return m
+
+
+def test_ple_tail_closed_form():
+    """Two layers, every attention and MLP matrix zero, so each layer's residual input passes
+    unchanged to its PLE tail. Layer 0's PLE matrices are zero too: x1 = fp32(x0 s0). Layer 1's
+    gate has one entry (row 5, column 7) = 2 and its projection one entry (row 9, column 5) = 3:
+    u5 = 2 bf16(x1[7]), h5 = bf16(silu(u5) p), p = the per-layer input of the row's token for
+    layer 1 at element 5, and x2 = fp32(fp32(x1 + 3 h5 e9) s1). The taps after layers 0 and 1 are
+    bf16(x1) and bf16(x2); two rows with different tokens."""
+    m = _ple_model()
+    w = zero_weights(m)
+    H, D = 256, 128
+    w["ple_table"] = synth.bf16_normal(0, "pin.ple.table", (m.vocab, m.n_layers * D))
+    for l in range(2):
+        w["layers"][l]["layer_scalar"] = _bits([1.25 if l == 0 else 0.75])
+        w["layers"][l]["ple_gate"] = zero_q4(D, H)
+        w["layers"][l]["ple_proj"] = zero_q4(H, D)
+    w["layers"][1]["ple_gate"] = _q4_from_entries(D, H, {(5, 7): 2.0})
+    w["layers"][1]["ple_proj"] = _q4_from_entries(H, D, {(9, 5): 3.0})
+    om = oracle.Model(m, w)
+    om.set_kv([np.zeros((0, 2, 64), dtype=np.float32)] * 2, 0)
+    toks = np.array([11, 500], dtype=np.int32)
+    _, taps = om.verify_batch(toks, with_taps=True)
+    E = synth.bf16_to_f32(w["embed"]).astype(np.float64)
+    P = synth.bf16_to_f32(w["ple_table"]).astype(np.float64)
+    for r, t in enumerate(toks):
+        x1 = np.float32(E[t] * 1.25).astype(np.float64)
+        u5 = _f32(2.0 * _bf16(x1[7]))
+        h5 = _bf16(u5 / (1.0 + math.exp(-u5)) * P[t, 1 * D + 5])
+        x2 = x1.copy()
+        x2[9] = _f32(x1[9] + _f32(3.0 * h5))
+        x2 = np.float32(x2 * 0.75).astype(np.float64)
+        assert np.array_equal(synth.bf16_to_f32(taps[r, 0]).astype(np.float64), synth.bf16_to_f32(synth.bf16_bits(x1)))
+        assert np.array_equal(synth.bf16_to_f32(taps[r, 1]).astype(np.float64), synth.bf16_to_f32(synth.bf16_bits(x2)))
+    assert h5 != 0.0
+
+
+def test_ple_batched_equals_sequential_and_injected_rows_refused():
+    """With PLE the k batched rows still equal k sequential steps bit for bit; a verify of injected
+    rows, and a single layer fed injected rows, are refused (the per-layer inputs need token ids)."""
+    import dataclasses
+    m = dataclasses.replace(synth.tiny_two_width_model(), ple_dim=128, name="tiny2wple")
+    w = synth.make_weights(m, 0)
+    kv = synth.make_kv(m, 10, 0)
+    toks = synth.tokens(0, "pin.ple.seq", 5, m.vocab)
+    A = oracle.Model(m, w); A.set_kv(kv, 10)
+    B = oracle.Model(m, w); B.set_kv(kv, 10)
+    la = A.verify_batch(toks)
+    lb = np.stack([B.step(int(t)) for t in toks])
+    assert np.array_equal(la, lb)
+    with pytest.raises(RuntimeError):
+        A.verify_embedded(np.zeros((2, m.hidden), dtype=np.float32))
+    with pytest.raises(RuntimeError):
+        A.layer_forward(0, np.zeros((2, m.hidden), dtype=np.float32), [15, 16])
+
+
+def test_numpy_twin_agrees_with_oracle_with_ple():
+    """The two-width miniature with per-layer embeddings (width 128): numpy twin and C oracle agree
+    to 1e-12 on the logits."""
+    import dataclasses
+    m = dataclasses.replace(synth.tiny_two_width_model(), ple_dim=128, name="tiny2wple")
+    w = synth.make_weights(m, 0)
+    kv = synth.make_kv(m, 21, 0)
+    toks = synth.tokens(0, "twin.ple.tokens", 8, m.vocab)
+    om = oracle.Model(m, w); om.set_kv(kv, 21)
+    tw = Twin(m, w); tw.set_kv(kv, 21)
+    assert rel_l1(tw.verify_batch(toks), om.verify_batch(toks)) <= 1e-12
