@@ -60,6 +60,7 @@ SIGNATURES = {
     "bvf_verify_batch": (_I32, [_P, _P, _I32, _P, _P]),
     "bvf_set_graph_mode": (_I32, [_P, _I32]),
     "bvf_accept_greedy": (_I32, [_P, _P, _I32, _P, _P, _P]),
+    "bvf_accept_greedy_static": (_I32, [_P, _I32, _I32, _P, _P, _P, _P]),
     "bvf_prefill": (_I32, [_P, _P, _I32, _P]),
     "bvf_accept_sampled": (_I32, [_P, _P, _I32, _P, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, _P, _P, _P]),
     "bvf_steer_logits": (_I32, [_P, _P, _I32, _P, _P]),
@@ -138,6 +139,17 @@ def arena_bytes(m) -> int:
 def cut_floats(per: Sequence[int], plane: int, positions: int) -> int:
     a = np.ascontiguousarray(per, dtype=np.int64)
     return int(lib().bvf_cut_floats(_host(a), len(a), plane, positions))
+
+
+def accept_greedy_static(d_logits_all, d_tokens, d_out_tokens, d_n_accepted, stream=None):
+    """The greedy accept with no model and no allocation (bvf_accept_greedy_static): logits
+    [k][vocab] fp32, tokens [k] int32, out tokens [k] int32, n_accepted [1] int32, all on the device;
+    enqueued on stream (a torch stream; None: the current torch stream)."""
+    import torch
+    k, vocab = int(d_logits_all.shape[0]), int(d_logits_all.shape[1])
+    st = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib().bvf_accept_greedy_static(_ptr(d_logits_all), k, vocab, _ptr(d_tokens), _ptr(d_out_tokens),
+                                          _ptr(d_n_accepted), st.cuda_stream))
 
 
 class Model:

@@ -713,6 +713,23 @@ bvf_status bvf_accept_greedy(bvf_model* m, const float* d_logits_all, int32_t k,
     return ok();
 }
 
+bvf_status bvf_accept_greedy_static(const float* d_logits_all, int32_t k, int32_t vocab, const int32_t* d_tokens,
+                                    int32_t* d_out_tokens, int32_t* d_n_accepted, void* hip_stream) {
+    if (!d_logits_all || !d_tokens || !d_out_tokens || !d_n_accepted) return fail(BVF_E_INVALID, "NULL argument");
+    if (k < 1 || k > kMaxRows) return fail(BVF_E_INVALID, "k = %d outside [1, %d]", k, kMaxRows);
+    if (vocab < 1 || vocab > kStaticAcceptMaxVocab)
+        return fail(BVF_E_CAPACITY, "vocab %d outside [1, %d] (the static scratch holds %d spans of 4096 per row)", vocab,
+                    kStaticAcceptMaxVocab, kStaticAcceptBlocks);
+    int device = -1;
+    HIP_TRY(hipGetDevice(&device));
+    float* pv = nullptr;
+    int* pi = nullptr;
+    HIP_TRY(static_accept_scratch(device, &pv, &pi));
+    HIP_TRY(launch_argmax_accept(d_logits_all, k, vocab, d_tokens, pv, pi, argmax_blocks(vocab), d_out_tokens,
+                                 d_n_accepted, nullptr, (hipStream_t)hip_stream));
+    return ok();
+}
+
 bvf_status bvf_accept_sampled(bvf_model* m, const float* d_logits_all, int32_t k, const int32_t* d_tokens, float temperature,
                               uint64_t seed, uint64_t offset, int32_t* d_out_tokens, int32_t* d_n_accepted,
                               int32_t* d_draws) {

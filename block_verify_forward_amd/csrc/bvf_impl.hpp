@@ -153,6 +153,15 @@ hipError_t launch_argmax_accept(const float* logits, int k, int V, const int32_t
                                 int* part_idx, int nb, int32_t* out_tokens, int32_t* n_acc, int32_t* argmax_out,
                                 hipStream_t st, const SampleArgs* sample = nullptr);
 int argmax_blocks(int V);
+
+// The allocation-free greedy accept keeps its argmax partials in a file-scope device array of the
+// library (one per GPU): at most kMaxRows rows of at most kStaticAcceptBlocks spans of 4096 logits,
+// i.e. a vocabulary of up to kStaticAcceptMaxVocab entries.
+constexpr int kStaticAcceptBlocks = 256;
+constexpr int kStaticAcceptMaxVocab = kStaticAcceptBlocks * 4096;
+constexpr size_t kStaticAcceptScratchBytes = (size_t)kMaxRows * kStaticAcceptBlocks * 8;
+// Device address of this device's array (hipGetSymbolAddress once per device, the device current).
+hipError_t static_accept_scratch(int device, float** part_val, int** part_idx);
 hipError_t launch_steer(float* logits, int k, int V, const int32_t* tok, const float* add, hipStream_t st);
 
 }  // namespace bvf

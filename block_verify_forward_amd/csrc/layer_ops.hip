@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 namespace bvf {
 namespace {
@@ -1149,6 +1150,39 @@ hipError_t launch_argmax_accept(const float* logits, int k, int V, const int32_t
     hipLaunchKernelGGL(k_accept, dim3(1), dim3(64 * k), 0, st, part_val, part_idx, nb, k, tokens, out_tokens, n_acc,
                        argmax_out);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Argmax partials of the allocation-free greedy accept: one file-scope device array per GPU,
+// [kMaxRows][kStaticAcceptBlocks] values then as many indices. Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device address): each device's
+// address comes from hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------------------------
+__device__ __align__(256) uint8_t scratch[kStaticAcceptScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_accept_scratch(int device, float** part_val, int** part_idx) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device) return hipErrorInvalidDevice;   // the caller makes the device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = p;
+    }
+    *part_val = (float*)g_scratch_ptr[device];
+    *part_idx = (int*)((uint8_t*)g_scratch_ptr[device] + (size_t)kMaxRows * kStaticAcceptBlocks * sizeof(float));
+    return hipSuccess;
 }
 
 hipError_t launch_steer(float* logits, int k, int V, const int32_t* tok, const float* add, hipStream_t st) {

@@ -184,6 +184,18 @@ bvf_status bvf_set_graph_mode(bvf_model* m, int32_t on);
 bvf_status bvf_accept_greedy(bvf_model* m, const float* d_logits_all, int32_t k, const int32_t* d_tokens,
                              int32_t* d_out_tokens, int32_t* d_n_accepted);
 
+/* The greedy accept of bvf_accept_greedy without a model and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). d_logits_all [k][vocab] fp32, d_tokens [k], d_out_tokens [k] and
+ * d_n_accepted [1] are device buffers the caller owns; the work is enqueued on hip_stream (NULL:
+ * the null stream). The argmax partials live in a fixed device array of the library, one per GPU
+ * (16 x 256 x 8 bytes, held until the process ends): k <= 16 and vocab <= 1048576, else
+ * BVF_E_INVALID / BVF_E_CAPACITY before anything is enqueued. The first call on a device looks up
+ * that device's array (the device must be current). Calls on one GPU share the array: calls that
+ * overlap on one GPU (other streams, other threads) race; calls on one stream do not. */
+bvf_status bvf_accept_greedy_static(const float* d_logits_all, int32_t k, int32_t vocab, const int32_t* d_tokens,
+                                    int32_t* d_out_tokens, int32_t* d_n_accepted, void* hip_stream);
+
 /* Sampled accept at temperature T > 0 ([CARD], "How it is used": with a sampler every position is
  * sampled and compared with the draft, so the output follows the target's distribution). Row i's
  * draw y_i is the first index of the maximum of fmaf(z_ij, 1/T, -log(-log u_ij)) in fp32 (the
