@@ -19,7 +19,10 @@ BVF_OK, BVF_E_INVALID, BVF_E_STATE, BVF_E_CAPACITY, BVF_E_DEVICE = range(5)
 ATTN_SLIDING, ATTN_FULL = 0, 1
 Q, K, V, O, GATE, UP, DOWN = range(7)
 EMBED, FINAL_NORM, ATTN_NORM, MLP_NORM, Q_NORM, K_NORM, FC, HIDDEN_NORM = range(8)
-MATRIX_IDS = {"q": Q, "k": K, "v": V, "o": O, "gate": GATE, "up": UP, "down": DOWN}
+PLE_GATE, PLE_PROJ = 7, 8
+PLE_TABLE, LAYER_SCALAR = 8, 9
+MATRIX_IDS = {"q": Q, "k": K, "v": V, "o": O, "gate": GATE, "up": UP, "down": DOWN, "ple_gate": PLE_GATE,
+              "ple_proj": PLE_PROJ}
 
 
 class BvfError(RuntimeError):
@@ -38,7 +41,8 @@ class ModelDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
                 ("block_causal", ctypes.c_int32), ("draft_window", ctypes.c_int32), ("n_taps", ctypes.c_int32),
                 ("tap_layers", ctypes.POINTER(ctypes.c_int32)), ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float), ("layers", ctypes.POINTER(LayerDesc)), ("kv_bf16", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("layers", ctypes.POINTER(LayerDesc)), ("kv_bf16", ctypes.c_int32),
+                ("ple_dim", ctypes.c_int32)]
 
 
 # exported symbol -> (restype, argtypes); the list is the header's declarations
@@ -124,7 +128,8 @@ def make_desc(m) -> tuple:
     vocab = m.vocab
     d = ModelDesc(m.n_layers, m.hidden, m.n_q_heads, vocab, m.max_ctx, m.qk_norm, m.block_causal, m.draft_window,
                   len(m.tap_layers), ctypes.cast(taps, ctypes.POINTER(ctypes.c_int32)), m.rope_base, m.rms_eps,
-                  ctypes.cast(layers, ctypes.POINTER(LayerDesc)), int(getattr(m, "kv_bf16", 0)))
+                  ctypes.cast(layers, ctypes.POINTER(LayerDesc)), int(getattr(m, "kv_bf16", 0)),
+                  int(getattr(m, "ple_dim", 0)))
     return d, layers, taps
 
 
@@ -197,6 +202,10 @@ class Model:
             self.load_bf16(MLP_NORM, l, d["mlp_norm"])
             self.load_bf16(Q_NORM, l, d["q_norm"])
             self.load_bf16(K_NORM, l, d["k_norm"])
+            if "layer_scalar" in d:
+                self.load_bf16(LAYER_SCALAR, l, d["layer_scalar"])
+        if "ple_table" in w:
+            self.load_bf16(PLE_TABLE, 0, w["ple_table"])
         if "embed" in w:
             self.load_bf16(EMBED, 0, w["embed"])
         self.load_bf16(FINAL_NORM, 0, w["final_norm"])

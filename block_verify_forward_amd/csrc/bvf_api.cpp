@@ -57,11 +57,14 @@ struct Layer {
     int w = 0;             // KV width (own or owner's)
     int qd = 0, kvd = 0;   // q width, own k/v width (0 on a shared layer)
     Mat qkv, o, gu, down;
+    Mat ple_gate, ple_proj;   // per-layer embedding gate [ple_dim][H] and projection [H][ple_dim] (ple_dim > 0)
     uint16_t *attn_norm = nullptr, *mlp_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
+    uint16_t* layer_scalar = nullptr;   // one bf16 value (ple_dim > 0)
     void* plane = nullptr;    // own plane [max_ctx][2][w] of fp32 or bf16 values (kv_bf16)
     const float2* rope = nullptr;
-    unsigned loaded = 0;      // bit i: matrix i; bits 8..11: norms
+    unsigned loaded = 0;      // bit i: matrix i; bits 16..20: norms and the layer scalar
 };
+constexpr int kNormBit = 16;   // per-layer bf16 tensor bits start here (matrix ids take bits 0..8)
 
 }  // namespace
 
@@ -76,6 +79,8 @@ struct bvf_model {
     uint8_t* arena = nullptr;
     size_t arena_bytes = 0;
     uint16_t *embed = nullptr, *final_norm = nullptr, *fc = nullptr, *hidden_norm = nullptr;
+    uint16_t* ple_table = nullptr;   // [vocab][n_layers * ple_dim] (ple_dim > 0)
+    uint16_t* pbuf = nullptr;        // [16][ple_dim] bf16 gated per-layer inputs (the projection's rows)
     unsigned loaded = 0;     // bit t: bf16 tensor t (model-wide)
     // scratch
     float* x = nullptr;
@@ -147,6 +152,9 @@ bvf_status check_desc(const bvf_model_desc* d) {
     if (is_draft(*d) && d->n_taps < 1) return fail(BVF_E_INVALID, "a draft needs n_taps >= 1 (fc input rows)");
     if (d->draft_window < 0) return fail(BVF_E_INVALID, "draft_window < 0");
     if (d->kv_bf16 != 0 && d->kv_bf16 != 1) return fail(BVF_E_INVALID, "kv_bf16 must be 0 or 1");
+    if (d->ple_dim < 0 || d->ple_dim % 128 || d->ple_dim > 4096)
+        return fail(BVF_E_INVALID, "ple_dim %d is not 0 or a multiple of 128 up to 4096", d->ple_dim);
+    if (d->ple_dim > 0 && is_draft(*d)) return fail(BVF_E_INVALID, "per-layer embeddings exist on a verify model only");
     if (!is_draft(*d))
         for (int t = 0; t < d->n_taps; ++t)
             if (d->tap_layers[t] < 0 || d->tap_layers[t] >= d->n_layers)
@@ -209,6 +217,11 @@ size_t layout(bvf_model* m, uint8_t* base) {
         mat(L.o, H, L.qd);
         mat(L.gu, 2 * L.d.ffn, H);
         mat(L.down, H, L.d.ffn);
+        if (d.ple_dim > 0) {
+            mat(L.ple_gate, d.ple_dim, H);
+            mat(L.ple_proj, H, d.ple_dim);
+            L.layer_scalar = (uint16_t*)take(2);
+        }
         L.attn_norm = (uint16_t*)take((size_t)H * 2);
         L.mlp_norm = (uint16_t*)take((size_t)H * 2);
         L.q_norm = (uint16_t*)take((size_t)hd * 2);
@@ -219,11 +232,14 @@ size_t layout(bvf_model* m, uint8_t* base) {
         m->nqkv_max = std::max(m->nqkv_max, L.qd + 2 * L.kvd);
         m->ffn_max = std::max(m->ffn_max, L.d.ffn);
         // largest canonical image one load call brings in (Q, K, V, O, GATE, UP, DOWN separately)
-        for (size_t elems : {(size_t)L.qd * H, (size_t)L.kvd * H, (size_t)H * L.qd, (size_t)L.d.ffn * H})
+        for (size_t elems : {(size_t)L.qd * H, (size_t)L.kvd * H, (size_t)H * L.qd, (size_t)L.d.ffn * H,
+                             (size_t)d.ple_dim * H})
             staging = std::max(staging, elems / 32 * 20);
     }
     m->embed = d.vocab > 0 && !is_draft(d) ? (uint16_t*)take((size_t)d.vocab * H * 2) : nullptr;
     m->final_norm = (uint16_t*)take((size_t)H * 2);
+    m->ple_table = d.ple_dim > 0 ? (uint16_t*)take((size_t)d.vocab * d.n_layers * d.ple_dim * 2) : nullptr;
+    m->pbuf = d.ple_dim > 0 ? (uint16_t*)take((size_t)kMaxRows * d.ple_dim * 2) : nullptr;
     if (is_draft(d)) {
         m->fc = (uint16_t*)take((size_t)H * d.n_taps * H * 2);
         m->hidden_norm = (uint16_t*)take((size_t)H * 2);
@@ -293,6 +309,11 @@ bvf_status matrix_run(const bvf_model* m, int layer, int matrix, Run& r) {
         case BVF_GATE: r = {&L.gu, 0, 1, L.d.ffn, 1, 0}; break;
         case BVF_UP: r = {&L.gu, 0, 1, L.d.ffn, 2, 0}; break;
         case BVF_DOWN: r = {&L.down, 0, 1, m->d.hidden, 0, 0}; break;
+        case BVF_PLE_GATE:
+        case BVF_PLE_PROJ:
+            if (m->d.ple_dim == 0) return fail(BVF_E_INVALID, "the model has no per-layer embeddings");
+            r = matrix == BVF_PLE_GATE ? Run{&L.ple_gate, 0, 1, m->d.ple_dim, 0, 0} : Run{&L.ple_proj, 0, 1, m->d.hidden, 0, 0};
+            break;
         default: return fail(BVF_E_INVALID, "matrix id %d", matrix);
     }
     return BVF_OK;
@@ -302,8 +323,9 @@ unsigned layer_needs(const bvf_model* m, int l) {
     const Layer& L = m->L[l];
     unsigned need = (1u << BVF_Q) | (1u << BVF_O) | (1u << BVF_GATE) | (1u << BVF_UP) | (1u << BVF_DOWN);
     if (L.kvd) need |= (1u << BVF_K) | (1u << BVF_V);
-    need |= (1u << (8 + 0)) | (1u << (8 + 1));          // attn_norm, mlp_norm
-    if (m->d.qk_norm) need |= (1u << (8 + 2)) | (1u << (8 + 3));
+    need |= (1u << (kNormBit + 0)) | (1u << (kNormBit + 1));          // attn_norm, mlp_norm
+    if (m->d.qk_norm) need |= (1u << (kNormBit + 2)) | (1u << (kNormBit + 3));
+    if (m->d.ple_dim > 0) need |= (1u << BVF_PLE_GATE) | (1u << BVF_PLE_PROJ) | (1u << (kNormBit + 4));
     return need;
 }
 
@@ -314,6 +336,7 @@ bvf_status check_loaded(const bvf_model* m) {
     }
     unsigned need = 1u << BVF_FINAL_NORM;
     if (!is_draft(m->d)) need |= 1u << BVF_EMBED;
+    if (m->d.ple_dim > 0) need |= 1u << BVF_PLE_TABLE;
     else need |= (1u << BVF_FC) | (1u << BVF_HIDDEN_NORM);
     if ((m->loaded & need) != need) return fail(BVF_E_STATE, "model-wide weights not all loaded");
     return BVF_OK;
@@ -383,7 +406,11 @@ Attn attn_for(const bvf_model* m, const Layer& L, int rows) {
 // KV-shared layer reads its owner's plane. The input rows' RMSNorms run inside the GEMMs' staging
 // from the per-tile sums of squares in ss_x (written by the previous layer's down projection, or
 // the embedding); the layer leaves ss_x for the next one. taps (optional): bf16 copy of the output.
-hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps, int ldt) {
+// On a model with per-layer embeddings the layer ends with the PLE tail ([PR2303] "What changes":
+// the PLE gate and projection as M-row GEMMs, then the layer scalar): the down projection leaves
+// bf16(x) in act, the gate GEMM writes h = bf16(silu(Wg . act) * p) (p gathered by the rows'
+// tokens), and the projection GEMM adds Wp . h to x and scales by the layer scalar.
+hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps, int ldt, const int32_t* tokens) {
     Layer& L = m->L[l];
     const int H = m->d.hidden;
     hipStream_t st = m->st;
@@ -408,6 +435,17 @@ hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps
     if ((e = launch_gemm(g, st)) != hipSuccess) return e;
     g = gemm_for(m, L.down, EPI_RESID);
     g.A = m->mbuf; g.lda = L.d.ffn; g.M = k; g.y = x; g.ldy = H; g.ss_out = m->ss_x;
+    g.taps = taps; g.ldt = ldt;
+    if (m->d.ple_dim == 0) return launch_gemm(g, st);
+    const int D = m->d.ple_dim;
+    g.taps = m->act; g.ldt = H; g.ss_out = nullptr;
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+    g = gemm_for(m, L.ple_gate, EPI_PLE);
+    g.A = m->act; g.lda = H; g.M = k; g.out = m->pbuf; g.ldo = D;
+    g.tokens = tokens; g.ple = m->ple_table + (size_t)l * D; g.ple_ld = m->d.n_layers * D; g.vocab = m->d.vocab;
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+    g = gemm_for(m, L.ple_proj, EPI_RESID);
+    g.A = m->pbuf; g.lda = D; g.M = k; g.y = x; g.ldy = H; g.ss_out = m->ss_x; g.rscale = L.layer_scalar;
     g.taps = taps; g.ldt = ldt;
     return launch_gemm(g, st);
 }
@@ -499,11 +537,12 @@ bvf_status bvf_load_bf16(bvf_model* m, int32_t tensor, int32_t layer, const uint
         if (layer < 0 || layer >= m->d.n_layers) return fail(BVF_E_INVALID, "layer %d out of range", layer);
         Layer& L = m->L[layer];
         const int hd = L.d.head_dim;
-        uint16_t* ptrs[4] = {L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm};
-        size_t sizes[4] = {(size_t)H, (size_t)H, (size_t)hd, (size_t)hd};
+        if (which == 4 && !L.layer_scalar) return fail(BVF_E_INVALID, "the model has no per-layer embeddings");
+        uint16_t* ptrs[5] = {L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm, L.layer_scalar};
+        size_t sizes[5] = {(size_t)H, (size_t)H, (size_t)hd, (size_t)hd, 1};
         dst = ptrs[which];
         want = sizes[which];
-        bit = 8 + which;
+        bit = kNormBit + which;
         return BVF_OK;
     };
     bvf_status s = BVF_OK;
@@ -522,6 +561,10 @@ bvf_status bvf_load_bf16(bvf_model* m, int32_t tensor, int32_t layer, const uint
         case BVF_HIDDEN_NORM:
             if (!is_draft(m->d)) return fail(BVF_E_INVALID, "hidden norm exists on a draft only");
             dst = m->hidden_norm; want = H; break;
+        case BVF_PLE_TABLE:
+            if (m->d.ple_dim == 0) return fail(BVF_E_INVALID, "the model has no per-layer embeddings");
+            dst = m->ple_table; want = (size_t)m->d.vocab * m->d.n_layers * m->d.ple_dim; break;
+        case BVF_LAYER_SCALAR: s = per_layer(4); break;
         default: return fail(BVF_E_INVALID, "tensor id %d", tensor);
     }
     if (s) return s;
@@ -620,7 +663,7 @@ hipError_t enqueue_verify(bvf_model* m, hipStream_t st, const int32_t* d_tokens,
         if (d_taps)
             for (int t = 0; t < T; ++t)
                 if (m->taps[t] == l) taps_l = d_taps + (size_t)t * H;
-        e = run_layer(m, l, m->x, k, P, taps_l, T * H);
+        e = run_layer(m, l, m->x, k, P, taps_l, T * H, d_tokens);
     }
     if (e == hipSuccess) e = launch_head(m, nullptr, k, d_logits_all, st, m, m->x, m->final_norm);
     m->st = saved;
@@ -685,7 +728,7 @@ bvf_status bvf_prefill(bvf_model* m, const int32_t* d_tokens, int32_t n, float* 
         const int c = std::min(kMaxRows, n - off);
         const int P = (int)m->held;
         HIP_TRY(launch_embed(d_tokens + off, -1, c, m->embed, V, H, 1.0f, m->x, m->ss_x, m->st));
-        for (int l = 0; l < m->d.n_layers; ++l) HIP_TRY(run_layer(m, l, m->x, c, P, nullptr, 0));
+        for (int l = 0; l < m->d.n_layers; ++l) HIP_TRY(run_layer(m, l, m->x, c, P, nullptr, 0, d_tokens + off));
         m->held += c;
         if (off + c == n && d_last_logits) {
             HIP_TRY(launch_head(m, nullptr, c, m->logits_tmp, m->st, m, m->x, m->final_norm));
@@ -996,11 +1039,13 @@ bvf_status bvf_layer_forward(bvf_model* m, int32_t layer, float* d_x, int32_t ro
     if (is_draft(m->d)) return fail(BVF_E_INVALID, "layer_forward runs verify layers");
     if (layer < 0 || layer >= m->d.n_layers) return fail(BVF_E_INVALID, "layer %d out of range", layer);
     if (rows < 1 || rows > kMaxRows) return fail(BVF_E_INVALID, "rows %d outside [1, %d]", rows, kMaxRows);
+    if (m->d.ple_dim > 0)
+        return fail(BVF_E_INVALID, "injected rows on a model with per-layer embeddings: its per-layer inputs need token ids");
     if (m->held + rows > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions would exceed max_ctx");
     bvf_status s = check_loaded(m);
     if (s) return s;
     HIP_TRY(launch_sumsq(d_x, m->d.hidden, rows, m->d.hidden, m->ss_x, m->st));
-    HIP_TRY(run_layer(m, layer, d_x, rows, (int)m->held, nullptr, 0));
+    HIP_TRY(run_layer(m, layer, d_x, rows, (int)m->held, nullptr, 0, nullptr));
     return ok();
 }
 
@@ -1061,7 +1106,8 @@ bvf_status bvf_pass_bytes(const bvf_model* m, int64_t* q4, int64_t* head) {
     if (!m || !q4 || !head) return fail(BVF_E_INVALID, "NULL argument");
     int64_t b = 0;
     for (const Layer& L : m->L)
-        for (const Mat* M : {&L.qkv, &L.o, &L.gu, &L.down}) b += (int64_t)M->w.n_tiles * M->w.G * (1024 + 256);
+        for (const Mat* M : {&L.qkv, &L.o, &L.gu, &L.down, &L.ple_gate, &L.ple_proj})
+            b += (int64_t)M->w.n_tiles * M->w.G * (1024 + 256);
     *q4 = b;
     *head = is_draft(m->d) ? 0 : (int64_t)m->d.vocab * m->d.hidden * 2;
     return ok();

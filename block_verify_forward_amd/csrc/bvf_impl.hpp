@@ -28,7 +28,7 @@ struct WMat {
     int K = 0;
 };
 
-enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PLE = 3 };
 enum WFmt : int { W_Q4_1 = 0, W_BF16 = 1 };
 
 // One GEMM launch: y[m][n] (+)= sum_k A[m][k] W[n][k] over the tiles tile0 + i * tile_stride,
@@ -60,6 +60,12 @@ struct GemmLaunch {
     const uint16_t* gain = nullptr;
     float eps = 0.f;
     float* ss_out = nullptr;     // STORE/RESID: per (row, output tile) sums of squares [M][n_run_tiles]
+    const uint16_t* rscale = nullptr;   // RESID: y = (y + W.A) * bf16 scalar (nullptr: no scale)
+    // PLE: out[m * ldo + n] = bf16(silu(W.A) * bf16 ple[clamp(tokens[m]) * ple_ld + n])
+    const int32_t* tokens = nullptr;
+    const uint16_t* ple = nullptr;
+    int ple_ld = 0;
+    int vocab = 0;
     int n_cu = 0;                // compute units of the device (0: 256)
     int force_S = 0, force_R = 0, force_ipw = 0, force_W = 0, force_KS = 0;   // a fixed plan (all > 0), else the planner's
 };

@@ -76,6 +76,10 @@ struct KArgs {
     const uint16_t* gain;
     float eps;
     float* ss_out;   // STORE / RESID: per row and 16-column tile, the sum of squares of the outputs
+    const uint16_t* rscale;   // RESID: the updated rows are scaled by this bf16 value (nullptr: not)
+    const int32_t* tokens;    // PLE: row m multiplies by the bf16 ple[clamp(tokens[m]) * ple_ld + n]
+    const uint16_t* ple;
+    int ple_ld, vocab;
 };
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32; NaN stays a NaN)
@@ -250,6 +254,20 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
                                          bool have_pre = false, floatx4 y_pre = {0.f, 0.f, 0.f, 0.f}) {
     const int c = lane & 15, sub = lane >> 4;
     const int n = tile * kTile + c;
+    if constexpr (EPI == EPI_PLE) {
+        // the per-layer embedding gate: silu of the GEMM output times the row's per-layer input
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * sub + r;
+            if (m >= a.M) continue;
+            int t = a.tokens[m];
+            t = t < 0 ? 0 : (t >= a.vocab ? a.vocab - 1 : t);
+            const float p = __builtin_bit_cast(float, (uint32_t)a.ple[(size_t)t * a.ple_ld + n] << 16);
+            const float g = acc[r];
+            a.out[(size_t)m * a.ldo + n] = f32_to_bf16(g / (1.0f + expf(-g)) * p);
+        }
+        return;
+    }
     if constexpr (EPI == EPI_SWIGLU) {
         // a gate|up tile holds gate columns in lanes c < 8 and the matching up columns in c + 8
         floatx4 up;
@@ -281,7 +299,8 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
                 a.y[(size_t)m * a.ldy + tile * 8 + (c & 7)] = acc[r];
             }
         } else {
-            const float v = (have_pre ? y_pre[r] : a.y[(size_t)m * a.ldy + n]) + acc[r];
+            float v = (have_pre ? y_pre[r] : a.y[(size_t)m * a.ldy + n]) + acc[r];
+            if (a.rscale) v *= __builtin_bit_cast(float, (uint32_t)a.rscale[0] << 16);
             vout[r] = v;
             a.y[(size_t)m * a.ldy + n] = v;
             if (a.taps) a.taps[(size_t)m * a.ldt + n] = f32_to_bf16(v);
@@ -814,11 +833,18 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
     k.gain = L.gain;
     k.eps = L.eps;
     k.ss_out = L.ss_out;
+    k.rscale = L.rscale;
+    k.tokens = L.tokens;
+    k.ple = L.ple;
+    k.ple_ld = L.ple_ld;
+    k.vocab = L.vocab;
+    if (L.epi == EPI_PLE && (!L.tokens || !L.ple || L.vocab < 1 || !L.out)) return hipErrorInvalidValue;
     if (L.fmt == W_Q4_1) {
         switch (L.epi) {
             case EPI_STORE: return launch_fe<W_Q4_1, EPI_STORE>(p.R, k, p.grid, p.waves, p.lds, st);
             case EPI_RESID: return launch_fe<W_Q4_1, EPI_RESID>(p.R, k, p.grid, p.waves, p.lds, st);
             case EPI_SWIGLU: return launch_fe<W_Q4_1, EPI_SWIGLU>(p.R, k, p.grid, p.waves, p.lds, st);
+            case EPI_PLE: return launch_fe<W_Q4_1, EPI_PLE>(p.R, k, p.grid, p.waves, p.lds, st);
         }
     } else if (L.epi == EPI_STORE) {
         return launch_fe<W_BF16, EPI_STORE>(p.R, k, p.grid, p.waves, p.lds, st);

@@ -511,20 +511,26 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             k1[i] = y0 * csr[i].y + y1 * csr[i].x;
         }
         TT* dst = (TT*)a.plane + prow_off;
+        // every query tile of the chunk computes the rows for its own stage; tile 0 writes the plane
+        const bool to_plane = qt == 0;
         if constexpr (KVB) {   // the plane and the tile take the same rounded values
-            store_bf16_vec<PPT>(dst + d0, k0);
-            store_bf16_vec<PPT>(dst + d0 + H2, k1);
-            store_bf16_vec<PPT>(dst + a.w + d0, vr0);
-            store_bf16_vec<PPT>(dst + a.w + d0 + H2, vr1);
+            if (to_plane) {
+                store_bf16_vec<PPT>(dst + d0, k0);
+                store_bf16_vec<PPT>(dst + d0 + H2, k1);
+                store_bf16_vec<PPT>(dst + a.w + d0, vr0);
+                store_bf16_vec<PPT>(dst + a.w + d0 + H2, vr1);
+            }
             store_bf16_vec<PPT>(&Kt[kk][d0], k0);
             store_bf16_vec<PPT>(&Kt[kk][d0 + H2], k1);
             store_bf16_vec<PPT>(&Vt[kk][d0], vr0);
             store_bf16_vec<PPT>(&Vt[kk][d0 + H2], vr1);
         } else {
-            store_vec<PPT>(dst + d0, k0);
-            store_vec<PPT>(dst + d0 + H2, k1);
-            store_vec<PPT>(dst + a.w + d0, vr0);
-            store_vec<PPT>(dst + a.w + d0 + H2, vr1);
+            if (to_plane) {
+                store_vec<PPT>(dst + d0, k0);
+                store_vec<PPT>(dst + d0 + H2, k1);
+                store_vec<PPT>(dst + a.w + d0, vr0);
+                store_vec<PPT>(dst + a.w + d0 + H2, vr1);
+            }
             store_vec<PPT>(&Kt[kk][d0], k0);
             store_vec<PPT>(&Kt[kk][d0 + H2], k1);
             store_vec<PPT>(&Vt[kk][d0], vr0);

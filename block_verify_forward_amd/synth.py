@@ -249,7 +249,14 @@ def make_weights(m: Model, seed: int = 0, with_head: bool = True, threads: int =
     def layer(l):
         d = {}
         for key, (n_out, n_in) in layer_matrix_shapes(m, l).items():
-            d[key] = q4_1_image(seed, f"{m.name}.L{l}.{key}", n_out, n_in)
+            if key.startswith("ple_"):
+                # per-layer embedding gate and projection: a tenth of the layer matrices' scale and
+                # minimum, so the tail's contribution stays a few percent of the residual stream
+                # (with the layer matrices' ranges the unnormalised gate input grows x about 3x per
+                # layer and the stream overflows fp32 within 42 layers)
+                d[key] = q4_1_image(seed, f"{m.name}.L{l}.{key}", n_out, n_in, 0.0002, 0.002, -0.015, 0.0)
+            else:
+                d[key] = q4_1_image(seed, f"{m.name}.L{l}.{key}", n_out, n_in)
         hd = m.layers[l].head_dim
         d["attn_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.attn_norm", (m.hidden,), 0.5, 1.5)
         d["mlp_norm"] = bf16_uniform(seed, f"{m.name}.L{l}.mlp_norm", (m.hidden,), 0.5, 1.5)

@@ -48,7 +48,9 @@ enum { BVF_ATTN_SLIDING = 0, BVF_ATTN_FULL = 1 };
 
 /* Q4_1 matrices of a layer. The library fuses Q|K|V into one packed matrix and interleaves GATE and
  * UP by 16-column tiles; each load call fills its part of the packed image. */
-enum { BVF_Q = 0, BVF_K = 1, BVF_V = 2, BVF_O = 3, BVF_GATE = 4, BVF_UP = 5, BVF_DOWN = 6 };
+enum { BVF_Q = 0, BVF_K = 1, BVF_V = 2, BVF_O = 3, BVF_GATE = 4, BVF_UP = 5, BVF_DOWN = 6,
+       BVF_PLE_GATE = 7,   /* per-layer embedding gate [ple_dim][hidden] (models with ple_dim > 0) */
+       BVF_PLE_PROJ = 8 }; /* per-layer embedding projection [hidden][ple_dim] */
 
 /* bf16 tensors. */
 enum {
@@ -59,7 +61,9 @@ enum {
     BVF_Q_NORM = 4,      /* per layer [head_dim] */
     BVF_K_NORM = 5,      /* per layer [head_dim] */
     BVF_FC = 6,          /* draft only: [hidden][n_taps * hidden], fuses the tapped target rows */
-    BVF_HIDDEN_NORM = 7  /* draft only: [hidden], RMSNorm gain applied after fc */
+    BVF_HIDDEN_NORM = 7, /* draft only: [hidden], RMSNorm gain applied after fc */
+    BVF_PLE_TABLE = 8,   /* ple_dim > 0: [vocab][n_layers * ple_dim] per-layer inputs, row = token id */
+    BVF_LAYER_SCALAR = 9 /* ple_dim > 0: per layer [1], the factor applied to the layer's output */
 };
 
 typedef struct {
@@ -92,6 +96,13 @@ typedef struct {
                               holding bf16 values, every stored K/V value (cached by bvf_set_kv, appended
                               by a pass, or a draft block's own rows) rounded from fp32 to nearest even.
                               Counts (plane_floats, cut_floats) are in values either way. */
+    int32_t ple_dim;       /* 0, or the per-layer embedding width (multiple of 128, verify models only).
+                              After its MLP every layer runs the PLE tail [PR2303, "What changes": the
+                              per-layer inputs of every row, the PLE gate and projection as M-row GEMMs,
+                              then the layer scalar]: u = Wg . bf16(x) [ple_dim], h = bf16(silu(u) * p)
+                              with p = row l of the per-layer input table entry of the row's token,
+                              x = (x + Wp . h) * s_l. The per-layer inputs need token ids, so calls that
+                              take injected rows (bvf_layer_forward) are refused on such a model. */
 } bvf_model_desc;
 
 typedef struct bvf_model bvf_model;
