@@ -65,6 +65,7 @@ class Model:
     draft_window: int = 0     # draft only: context rows visible to the block (0 = all)
     kv_bf16: int = 0          # 1: K/V planes stored in bf16 (a memory variant; the default planes are fp32)
     ple_dim: int = 0          # per-layer embedding width (Gemma4-style PLE); 0 = none
+    kv_ring: int = 0          # 1: sliding planes of a verify model are rings of window + 16 position slots
 
     def kv_width(self, l: int) -> int:
         L = self.layers[l]

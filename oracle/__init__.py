@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
             "orc_set_globals": (None, [P, P, P, P, P]),
             "orc_set_kv": (I, [P, I, P, L64]),
             "orc_set_kv_bf16": (None, [P, I]),
+            "orc_set_kv_ring": (None, [P, I]),
+            "orc_plane_capacity": (L64, [P, I]),
             "orc_set_held": (None, [P, L64]),
             "orc_positions_held": (L64, [P]),
             "orc_plane": (ctypes.POINTER(ctypes.c_float), [P, I]),
@@ -223,6 +225,8 @@ class Model:
                                      _p(fields), _p(taps), len(m.tap_layers))
         if getattr(m, "kv_bf16", 0):
             lib().orc_set_kv_bf16(self.h, 1)
+        if getattr(m, "kv_ring", 0):
+            lib().orc_set_kv_ring(self.h, 1)
         for l, d in enumerate(weights["layers"]):
             g = lambda k: _p(d[k]) if k in d else None
             lib().orc_set_layer(self.h, l, g("q"), g("k"), g("v"), g("o"), g("gate"), g("up"), g("down"),
@@ -273,10 +277,23 @@ class Model:
         lib().orc_plane_floats(self.h, _p(out))
         return out
 
+    def capacity(self, l: int) -> int:
+        """Positions the plane of layer l holds at most (ring planes: window + 16)."""
+        return int(lib().orc_plane_capacity(self.h, l))
+
     def plane(self, l: int, positions: int) -> np.ndarray:
+        """Rows of positions 0 .. positions - 1 of layer l's plane [positions][2][w]; on a ring plane
+        the positions older than its capacity are no longer held and read as NaN."""
         w = self.m.kv_width(l)
+        cap = self.capacity(l)
         ptr = lib().orc_plane(self.h, l)
-        return np.ctypeslib.as_array(ptr, shape=(self.m.max_ctx, 2, w))[:positions].copy()
+        arr = np.ctypeslib.as_array(ptr, shape=(cap, 2, w))
+        if cap >= self.m.max_ctx:
+            return arr[:positions].copy()
+        out = np.full((positions, 2, w), np.nan, dtype=np.float32)
+        for p in range(max(0, positions - cap), positions):
+            out[p] = arr[p % cap]
+        return out
 
     # forward
     def step(self, token: int, with_taps: bool = False):

@@ -249,12 +249,36 @@ typedef struct orc_model {
     long held;       /* positions held on every own plane */
     long pending;    /* rows appended by the last verify and not yet committed; -1 = none */
     int kv_bf16;     /* planes stored in bf16: every K/V value is rounded (from fp32, RNE) when stored */
+    int kv_ring;     /* sliding layers of a verify model keep window + RING_SLACK position slots (ring) */
     int ple_dim;     /* per-layer embedding width (0: the model has none) */
     const uint16_t* ple_table;   /* [vocab][n_layers][ple_dim] bf16 per-layer inputs, indexed by token */
 } orc_model;
 
 static long kv_width(const orc_model* md, int l) {
     return (long)md->L[l].n_kv_heads * md->L[l].head_dim;
+}
+
+/* Ring planes (a memory variant [PR2303, "What changes" item 1 keeps the per-layer cut semantics]):
+ * a sliding layer of a verify model needs at most the last `window` positions plus the rows of the
+ * batch in flight, so its plane can hold window + RING_SLACK position slots with position p in slot
+ * p mod capacity. RING_SLACK is the most rows one pass appends (16): a pass appending rows
+ * P..P+k-1 overwrites positions older than P - window + 1, which no row of the pass and no row
+ * after a rollback to P + n (n >= 0) can see. Other planes hold every position (capacity max_ctx). */
+#define RING_SLACK 16
+static long plane_cap(const orc_model* md, int l) {
+    const orc_layer_desc* L = &md->L[l];
+    if (md->kv_ring && md->block_causal && L->attn == 0 && L->window > 0 && (long)L->window + RING_SLACK < md->max_ctx)
+        return (long)L->window + RING_SLACK;
+    return md->max_ctx;
+}
+static float* plane_row(const orc_model* md, int l, long p) {
+    return md->plane[l] + (size_t)(p % plane_cap(md, l)) * 2 * kv_width(md, l);
+}
+/* Positions a plane holds: every held position on a linear plane; on a ring plane the last
+ * `window` of them (older slots may already carry rows of a pass that a commit cut back). */
+static long plane_positions(const orc_model* md, int l, long held) {
+    const long c = plane_cap(md, l) < md->max_ctx ? md->L[l].window : held;
+    return held < c ? held : c;
 }
 
 orc_model* orc_model_new(int n_layers, int hidden, int n_q_heads, int vocab, long max_ctx, int qk_norm,
@@ -329,6 +353,17 @@ void orc_set_globals(orc_model* md, const uint16_t* embed, const uint16_t* final
  * item 1): the stored value is the fp32 value rounded to bf16 (RNE); everything else is unchanged. */
 void orc_set_kv_bf16(orc_model* md, int on) { md->kv_bf16 = on; }
 
+/* Ring planes on (before any K/V is set): the sliding planes shrink to their ring capacity. */
+void orc_set_kv_ring(orc_model* md, int on) {
+    md->kv_ring = on;
+    for (int l = 0; l < md->n_layers; l++) {
+        if (!md->plane[l]) continue;
+        free(md->plane[l]);
+        md->plane[l] = calloc((size_t)plane_cap(md, l) * 2 * kv_width(md, l), sizeof(float));
+    }
+}
+long orc_plane_capacity(const orc_model* md, int l) { return plane_cap(md, l); }
+
 static float store_kv(const orc_model* md, double v) {
     const float f = (float)v;
     return md->kv_bf16 ? (float)round_bf16((double)f) : f;
@@ -336,8 +371,12 @@ static float store_kv(const orc_model* md, double v) {
 
 int orc_set_kv(orc_model* md, int l, const float* kv, long positions) {
     if (l < 0 || l >= md->n_layers || !md->plane[l] || positions > md->max_ctx) return 1;
-    const size_t n = (size_t)positions * 2 * kv_width(md, l);
-    for (size_t i = 0; i < n; i++) md->plane[l][i] = store_kv(md, kv[i]);
+    const long w = kv_width(md, l);
+    const long keep = positions < plane_cap(md, l) ? positions : plane_cap(md, l);
+    for (long p = positions - keep; p < positions; p++) {
+        float* row = plane_row(md, l, p);
+        for (long i = 0; i < 2 * w; i++) row[i] = store_kv(md, kv[(size_t)p * 2 * w + i]);
+    }
     return 0;
 }
 
@@ -362,7 +401,7 @@ void orc_kv_widths(const orc_model* md, long* out) {
 /* Floats held per plane: held positions x 2 x w_l on an own plane; 0 on a shared plane. */
 void orc_plane_floats(const orc_model* md, long* out) {
     for (int l = 0; l < md->n_layers; l++)
-        out[l] = md->L[l].kv_owner < 0 ? md->held * 2 * kv_width(md, l) : 0;
+        out[l] = md->L[l].kv_owner < 0 ? plane_positions(md, l, md->held) * 2 * kv_width(md, l) : 0;
 }
 
 /* Per-plane cut with the extrapolation rule of [PR2303, review "VERDICT at 4d10370: READY"]: plane i
@@ -385,7 +424,6 @@ static void attend_row(const orc_model* md, int l, const double* q, long p, doub
     const int src = Ld->kv_owner < 0 ? l : Ld->kv_owner;
     const long w = kv_width(md, src);
     const int group = Hq / nkv;
-    const float* P = md->plane[src];
     long lo = 0;
     if (Ld->attn == 0 && Ld->window > 0 && p - Ld->window + 1 > 0) lo = p - Ld->window + 1;
     const long nk = p - lo + 1;
@@ -395,7 +433,7 @@ static void attend_row(const orc_model* md, int l, const double* q, long p, doub
         const double* qh = q + (size_t)h * hd;
         double mx = -INFINITY;
         for (long j = lo; j <= p; j++) {
-            const float* kj = P + (size_t)j * 2 * w + (size_t)g * hd;
+            const float* kj = plane_row(md, src, j) + (size_t)g * hd;
             double s = 0.0;
             for (int i = 0; i < hd; i++) s += qh[i] * kj[i];
             s /= sqrt((double)hd);
@@ -409,7 +447,7 @@ static void attend_row(const orc_model* md, int l, const double* q, long p, doub
         }
         for (int i = 0; i < hd; i++) {
             double acc = 0.0;
-            for (long j = lo; j <= p; j++) acc += sc[j - lo] * P[(size_t)j * 2 * w + w + (size_t)g * hd + i];
+            for (long j = lo; j <= p; j++) acc += sc[j - lo] * plane_row(md, src, j)[w + (size_t)g * hd + i];
             out[(size_t)h * hd + i] = acc / z;
         }
     }
@@ -472,7 +510,7 @@ static void target_layer(orc_model* md, int l, int m, double* x, const long* pos
             for (int i = 0; i < hd; i++) qh[i] = round_f32(qh[i]);
         }
         if (own) {
-            float* row = md->plane[l] + (size_t)p * 2 * w;
+            float* row = plane_row(md, l, p);
             for (int g = 0; g < nkv; g++) {
                 double* kh = kx + (size_t)r * kvd + (size_t)g * hd;
                 if (md->qk_norm) {
@@ -654,8 +692,10 @@ int orc_extend_context(orc_model* md, const float* kv_all, long n) {
     for (int l = 0; l < md->n_layers; l++) {
         if (!md->plane[l]) continue;
         const long w = kv_width(md, l);
-        float* dst = md->plane[l] + (size_t)md->held * 2 * w;
-        for (size_t i = 0; i < (size_t)n * 2 * w; i++) dst[i] = store_kv(md, kv_all[off + i]);
+        for (long r = 0; r < n; r++) {
+            float* dst = plane_row(md, l, md->held + r);
+            for (long i = 0; i < 2 * w; i++) dst[i] = store_kv(md, kv_all[off + (size_t)r * 2 * w + i]);
+        }
         off += (size_t)n * 2 * w;
     }
     md->held += n;
@@ -772,8 +812,10 @@ typedef struct orc_snapshot {
     int n_layers;
     long held;
     long* per;       /* width of each plane (shared: the owner's) */
+    long* cap;       /* position capacity of each plane (ring planes: window + RING_SLACK) */
+    long* kept;      /* positions kept of each plane: held, or on a ring plane the last min(held, window) */
     int* shared;
-    float** data;    /* held x 2 x per[l] floats of each own plane; NULL on a shared plane */
+    float** data;    /* kept x 2 x per[l] floats of each own plane, in position order; NULL on a shared plane */
 } orc_snapshot;
 
 /* A snapshot is taken of committed state only: while a verify is pending (its rows not yet cut by
@@ -784,21 +826,27 @@ orc_snapshot* orc_snapshot_take(const orc_model* md) {
     s->n_layers = md->n_layers;
     s->held = md->held;
     s->per = calloc((size_t)md->n_layers, sizeof(long));
+    s->cap = calloc((size_t)md->n_layers, sizeof(long));
+    s->kept = calloc((size_t)md->n_layers, sizeof(long));
     s->shared = calloc((size_t)md->n_layers, sizeof(int));
     s->data = calloc((size_t)md->n_layers, sizeof(float*));
     orc_kv_widths(md, s->per);
     for (int l = 0; l < md->n_layers; l++) {
         s->shared[l] = md->L[l].kv_owner >= 0;
+        s->cap[l] = plane_cap(md, s->shared[l] ? md->L[l].kv_owner : l);
         if (s->shared[l]) continue;
-        long nf = orc_cut_floats(s->per, md->n_layers, l, md->held);
+        s->kept[l] = plane_positions(md, l, md->held);
+        const long nf = orc_cut_floats(s->per, md->n_layers, l, s->kept[l]);
         s->data[l] = malloc(sizeof(float) * (size_t)(nf > 0 ? nf : 1));
-        memcpy(s->data[l], md->plane[l], sizeof(float) * (size_t)nf);
+        const long row = 2 * s->per[l];
+        for (long i = 0; i < s->kept[l]; i++)
+            memcpy(s->data[l] + (size_t)i * row, plane_row(md, l, md->held - s->kept[l] + i), sizeof(float) * (size_t)row);
     }
     return s;
 }
 
 long orc_snapshot_floats(const orc_snapshot* s, int l) {
-    return s->shared[l] ? 0 : orc_cut_floats(s->per, s->n_layers, l, s->held);
+    return s->shared[l] ? 0 : orc_cut_floats(s->per, s->n_layers, l, s->kept[l]);
 }
 
 int orc_snapshot_restore(orc_model* md, const orc_snapshot* s) {
@@ -806,10 +854,13 @@ int orc_snapshot_restore(orc_model* md, const orc_snapshot* s) {
     long* w = calloc((size_t)md->n_layers, sizeof(long));
     orc_kv_widths(md, w);
     for (int l = 0; l < md->n_layers; l++)
-        if (w[l] != s->per[l] || s->shared[l] != (md->L[l].kv_owner >= 0)) { free(w); return 1; }
+        if (w[l] != s->per[l] || s->shared[l] != (md->L[l].kv_owner >= 0) ||
+            s->cap[l] != plane_cap(md, s->shared[l] ? md->L[l].kv_owner : l)) { free(w); return 1; }
     for (int l = 0; l < md->n_layers; l++) {
         if (s->shared[l]) continue;
-        memcpy(md->plane[l], s->data[l], sizeof(float) * (size_t)orc_cut_floats(w, md->n_layers, l, s->held));
+        const long row = 2 * w[l];
+        for (long i = 0; i < s->kept[l]; i++)
+            memcpy(plane_row(md, l, s->held - s->kept[l] + i), s->data[l] + (size_t)i * row, sizeof(float) * (size_t)row);
     }
     free(w);
     md->held = s->held;
@@ -822,6 +873,8 @@ void orc_snapshot_free(orc_snapshot* s) {
     for (int l = 0; l < s->n_layers; l++) free(s->data[l]);
     free(s->data);
     free(s->per);
+    free(s->cap);
+    free(s->kept);
     free(s->shared);
     free(s);
 }

@@ -368,3 +368,56 @@ def test_numpy_twin_agrees_with_oracle_with_ple():
     om = oracle.Model(m, w); om.set_kv(kv, 21)
     tw = Twin(m, w); tw.set_kv(kv, 21)
     assert rel_l1(tw.verify_batch(toks), om.verify_batch(toks)) <= 1e-12
+
+
+# ------------------------------------------------------------------------------------------
+# ring planes: sliding planes of window + 16 position slots behave as the linear planes
+# ------------------------------------------------------------------------------------------
+def test_ring_planes_equal_linear_planes_over_a_state_sequence():
+    """The two-width miniature (sliding window 16 -> ring of 32 slots; full and shared layers
+    unchanged), once with linear planes and once with rings: through set_kv of 45 positions, verifies
+    of 8, 5, 16 and 4 rows with commits of 3, 5, 0 and 4 rows, an extend_context of 7 rows, a
+    snapshot and a restore, every verify's logits are bit-identical, the held positions agree, ring
+    planes count the last min(held, window) positions at their width (engine PR #2303 "What changes"
+    item 1: the count is per layer; older slots may carry rows a commit cut back), and the rows a
+    ring holds equal the linear plane's rows."""
+    import dataclasses
+    base = synth.tiny_two_width_model()
+    ring = dataclasses.replace(base, kv_ring=1)
+    w = synth.make_weights(base, 0)
+    kv = synth.make_kv(base, 45, 0)
+    kv_new = synth.make_kv(base, 7, 1)
+    L = oracle.Model(base, w); L.set_kv(kv, 45)
+    R = oracle.Model(ring, w); R.set_kv(kv, 45)
+    caps = [R.capacity(l) if base.own(l) else 0 for l in range(base.n_layers)]
+    assert caps == [32 if (base.own(l) and base.layers[l].attn == synth.ATTN_SLIDING) else
+                    (base.max_ctx if base.own(l) else 0) for l in range(base.n_layers)]
+
+    keep = [base.layers[l].window if caps[l] == 32 else base.max_ctx for l in range(base.n_layers)]
+
+    def counts(held):
+        return [min(held, keep[l]) * 2 * base.kv_width(l) if base.own(l) else 0 for l in range(base.n_layers)]
+
+    def step(k, n, tag):
+        toks = synth.tokens(0, f"pin.ring.{tag}", k, base.vocab)
+        assert np.array_equal(L.verify_batch(toks), R.verify_batch(toks)), tag
+        assert L.commit_verify_rows(n) == 0 and R.commit_verify_rows(n) == 0
+        assert L.held() == R.held()
+        assert list(R.plane_floats()) == counts(R.held())
+        for l in range(base.n_layers):
+            if base.own(l):
+                h = R.held()
+                lo = max(0, h - keep[l])
+                assert np.array_equal(R.plane(l, h)[lo:], L.plane(l, h)[lo:]), (tag, l)
+
+    step(8, 3, "a")
+    step(5, 5, "b")
+    assert L.extend_context(kv_new, 7) == 0 and R.extend_context(kv_new, 7) == 0
+    snap_l, snap_r = L.snapshot(), R.snapshot()
+    assert snap_r.floats() == counts(R.held())
+    step(16, 0, "c")
+    assert L.restore(snap_l) == 0 and R.restore(snap_r) == 0
+    step(4, 4, "d")
+    assert L.held() == 45 + 3 + 5 + 7 + 4
+    # a ring snapshot does not restore into a linear model (different plane capacities)
+    assert L.restore(snap_r) != 0
