@@ -42,7 +42,7 @@ class ModelDesc(ctypes.Structure):
                 ("block_causal", ctypes.c_int32), ("draft_window", ctypes.c_int32), ("n_taps", ctypes.c_int32),
                 ("tap_layers", ctypes.POINTER(ctypes.c_int32)), ("rope_base", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("layers", ctypes.POINTER(LayerDesc)), ("kv_bf16", ctypes.c_int32),
-                ("ple_dim", ctypes.c_int32)]
+                ("ple_dim", ctypes.c_int32), ("kv_ring", ctypes.c_int32)]
 
 
 # exported symbol -> (restype, argtypes); the list is the header's declarations
@@ -129,7 +129,7 @@ def make_desc(m) -> tuple:
     d = ModelDesc(m.n_layers, m.hidden, m.n_q_heads, vocab, m.max_ctx, m.qk_norm, m.block_causal, m.draft_window,
                   len(m.tap_layers), ctypes.cast(taps, ctypes.POINTER(ctypes.c_int32)), m.rope_base, m.rms_eps,
                   ctypes.cast(layers, ctypes.POINTER(LayerDesc)), int(getattr(m, "kv_bf16", 0)),
-                  int(getattr(m, "ple_dim", 0)))
+                  int(getattr(m, "ple_dim", 0)), int(getattr(m, "kv_ring", 0)))
     return d, layers, taps
 
 

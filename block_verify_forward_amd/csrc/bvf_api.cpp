@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <string>
 #include <vector>
 
@@ -60,11 +61,43 @@ struct Layer {
     Mat ple_gate, ple_proj;   // per-layer embedding gate [ple_dim][H] and projection [H][ple_dim] (ple_dim > 0)
     uint16_t *attn_norm = nullptr, *mlp_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
     uint16_t* layer_scalar = nullptr;   // one bf16 value (ple_dim > 0)
-    void* plane = nullptr;    // own plane [max_ctx][2][w] of fp32 or bf16 values (kv_bf16)
+    void* plane = nullptr;    // own plane [cap][2][w] of fp32 or bf16 values (kv_bf16)
+    int cap = 0;              // position slots of the own plane: max_ctx, or window + kRingSlack (ring)
+    bool ring = false;        // position p lives in slot p mod cap
     const float2* rope = nullptr;
     unsigned loaded = 0;      // bit i: matrix i; bits 16..20: norms and the layer scalar
 };
 constexpr int kNormBit = 16;   // per-layer bf16 tensor bits start here (matrix ids take bits 0..8)
+// Ring planes: the most rows one pass appends; a pass appending rows P..P+k-1 into a ring of
+// window + kRingSlack slots overwrites only positions older than P - window + 1.
+constexpr int kRingSlack = kMaxRows;
+
+// Positions a plane holds at `held` positions: all of them, or on a ring the last `window`.
+int64_t plane_keep(const Layer& L, int64_t held) { return L.ring ? std::min<int64_t>(held, L.d.window) : held; }
+
+// Calls f(slot, first, count) for the runs of consecutive slots that positions [p0, p1) of a plane
+// occupy (one run on a linear plane; up to two per pass round the ring); first = p - p0.
+template <class F>
+hipError_t for_slot_runs(const Layer& L, int64_t p0, int64_t p1, F f) {
+    for (int64_t p = p0; p < p1;) {
+        const int64_t slot = p % L.cap;
+        const int64_t n = std::min<int64_t>(p1 - p, L.cap - slot);
+        hipError_t e = f(slot, p - p0, n);
+        if (e != hipSuccess) return e;
+        p += n;
+    }
+    return hipSuccess;
+}
+
+// bf16 bits of fp32 values, rounded to nearest even (NaN kept quiet)
+void round_to_bf16(const float* src, size_t n, std::vector<uint16_t>& out) {
+    out.resize(n);
+    for (size_t i = 0; i < n; ++i) {
+        uint32_t u;
+        std::memcpy(&u, &src[i], 4);
+        out[i] = (u & 0x7fffffffu) > 0x7f800000u ? (uint16_t)((u >> 16) | 0x40u) : (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+}
 
 }  // namespace
 
@@ -129,7 +162,9 @@ struct bvf_snapshot {
     int kv_elem = 4;   // bytes per stored K/V value
     std::vector<int64_t> per;
     std::vector<int> shared;
-    std::vector<float*> data;
+    std::vector<int> cap;        // position slots of each own plane (ring planes: window + 16)
+    std::vector<int64_t> kept;   // positions kept of each own plane (ring planes: the last min(held, window))
+    std::vector<float*> data;    // kept rows of each own plane, in position order
 };
 
 namespace {
@@ -155,6 +190,8 @@ bvf_status check_desc(const bvf_model_desc* d) {
     if (d->ple_dim < 0 || d->ple_dim % 128 || d->ple_dim > 4096)
         return fail(BVF_E_INVALID, "ple_dim %d is not 0 or a multiple of 128 up to 4096", d->ple_dim);
     if (d->ple_dim > 0 && is_draft(*d)) return fail(BVF_E_INVALID, "per-layer embeddings exist on a verify model only");
+    if (d->kv_ring != 0 && d->kv_ring != 1) return fail(BVF_E_INVALID, "kv_ring must be 0 or 1");
+    if (d->kv_ring && is_draft(*d)) return fail(BVF_E_INVALID, "ring planes exist on a verify model only");
     if (!is_draft(*d))
         for (int t = 0; t < d->n_taps; ++t)
             if (d->tap_layers[t] < 0 || d->tap_layers[t] >= d->n_layers)
@@ -226,7 +263,10 @@ size_t layout(bvf_model* m, uint8_t* base) {
         L.mlp_norm = (uint16_t*)take((size_t)H * 2);
         L.q_norm = (uint16_t*)take((size_t)hd * 2);
         L.k_norm = (uint16_t*)take((size_t)hd * 2);
-        L.plane = own ? (void*)take((size_t)d.max_ctx * 2 * L.w * (d.kv_bf16 ? 2 : 4)) : nullptr;
+        L.ring = own && d.kv_ring && L.d.attn == BVF_ATTN_SLIDING && L.d.window > 0 &&
+                 L.d.window + kRingSlack < d.max_ctx;
+        L.cap = L.ring ? L.d.window + kRingSlack : d.max_ctx;
+        L.plane = own ? (void*)take((size_t)L.cap * 2 * L.w * (d.kv_bf16 ? 2 : 4)) : nullptr;
         m->hd_max = std::max(m->hd_max, hd);
         m->qd_max = std::max(m->qd_max, L.qd);
         m->nqkv_max = std::max(m->nqkv_max, L.qd + 2 * L.kvd);
@@ -336,8 +376,8 @@ bvf_status check_loaded(const bvf_model* m) {
     }
     unsigned need = 1u << BVF_FINAL_NORM;
     if (!is_draft(m->d)) need |= 1u << BVF_EMBED;
-    if (m->d.ple_dim > 0) need |= 1u << BVF_PLE_TABLE;
     else need |= (1u << BVF_FC) | (1u << BVF_HIDDEN_NORM);
+    if (m->d.ple_dim > 0) need |= 1u << BVF_PLE_TABLE;
     if ((m->loaded & need) != need) return fail(BVF_E_STATE, "model-wide weights not all loaded");
     return BVF_OK;
 }
@@ -421,6 +461,10 @@ hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps
     if ((e = launch_gemm(g, st)) != hipSuccess) return e;
     Attn at = attn_for(m, L, k);
     at.plane = L.plane ? L.plane : m->L[L.d.kv_owner].plane;
+    {
+        const Layer& src = L.plane ? L : m->L[L.d.kv_owner];
+        at.ring_cap = src.ring ? src.cap : 0;
+    }
     at.kv_bf16 = m->d.kv_bf16;
     at.own = L.plane != nullptr;
     at.causal = 1; at.pos0 = P; at.window = L.d.attn == BVF_ATTN_SLIDING ? L.d.window : 0;
@@ -582,21 +626,16 @@ bvf_status bvf_set_kv(bvf_model* m, int32_t layer, const float* h_kv, int64_t po
     Layer& L = m->L[layer];
     if (!L.plane) return fail(BVF_E_INVALID, "layer %d is KV-shared: it holds no plane", layer);
     if (positions < 0 || positions > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions %lld > max_ctx", (long long)positions);
-    const size_t n = (size_t)positions * 2 * L.w;
-    if (!m->d.kv_bf16) {
-        HIP_TRY(hipMemcpyAsync(L.plane, h_kv, n * 4, hipMemcpyHostToDevice, m->st));
-        HIP_TRY(hipStreamSynchronize(m->st));
-        return ok();
-    }
-    std::vector<uint16_t> b(n);   // bf16 planes: each value rounded to nearest even (NaN kept quiet)
-    for (size_t i = 0; i < n; ++i) {
-        uint32_t u;
-        std::memcpy(&u, &h_kv[i], 4);
-        b[i] = (u & 0x7fffffffu) > 0x7f800000u ? (uint16_t)((u >> 16) | 0x40u)
-                                                : (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-    }
+    // a ring plane takes the last cap positions (older ones would be overwritten at once)
+    const int64_t p0 = std::max<int64_t>(0, positions - L.cap);
+    const size_t row = (size_t)2 * L.w, eb = m->d.kv_bf16 ? 2 : 4;
+    std::vector<uint16_t> b;
+    if (m->d.kv_bf16) round_to_bf16(h_kv + (size_t)p0 * row, (size_t)(positions - p0) * row, b);
     HIP_TRY(hipStreamSynchronize(m->st));
-    HIP_TRY(hipMemcpy(L.plane, b.data(), n * 2, hipMemcpyHostToDevice));
+    HIP_TRY(for_slot_runs(L, p0, positions, [&](int64_t slot, int64_t first, int64_t n) {
+        const void* src = m->d.kv_bf16 ? (const void*)(b.data() + (size_t)first * row) : (const void*)(h_kv + (size_t)(p0 + first) * row);
+        return hipMemcpy((uint8_t*)L.plane + (size_t)slot * row * eb, src, (size_t)n * row * eb, hipMemcpyHostToDevice);
+    }));
     return ok();
 }
 
@@ -606,17 +645,19 @@ bvf_status bvf_get_kv(const bvf_model* m, int32_t layer, float* h_kv, int64_t po
     const Layer& L = m->L[layer];
     if (!L.plane) return fail(BVF_E_INVALID, "layer %d is KV-shared: it holds no plane", layer);
     if (positions < 0 || positions > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions %lld > max_ctx", (long long)positions);
-    const size_t n = (size_t)positions * 2 * L.w;
+    const size_t row = (size_t)2 * L.w, eb = m->d.kv_bf16 ? 2 : 4;
+    const int64_t p0 = positions - plane_keep(L, positions);   // older rows of a ring read as NaN
+    const float qnan = std::numeric_limits<float>::quiet_NaN();
+    std::fill(h_kv, h_kv + (size_t)p0 * row, qnan);
+    std::vector<uint16_t> b(m->d.kv_bf16 ? (size_t)(positions - p0) * row : 0);
     HIP_TRY(hipStreamSynchronize(m->st));
-    if (!m->d.kv_bf16) {
-        HIP_TRY(hipMemcpy(h_kv, L.plane, n * 4, hipMemcpyDeviceToHost));
-        return ok();
-    }
-    std::vector<uint16_t> b(n);
-    HIP_TRY(hipMemcpy(b.data(), L.plane, n * 2, hipMemcpyDeviceToHost));
-    for (size_t i = 0; i < n; ++i) {
+    HIP_TRY(for_slot_runs(L, p0, positions, [&](int64_t slot, int64_t first, int64_t n) {
+        void* dst = m->d.kv_bf16 ? (void*)(b.data() + (size_t)first * row) : (void*)(h_kv + (size_t)(p0 + first) * row);
+        return hipMemcpy(dst, (const uint8_t*)L.plane + (size_t)slot * row * eb, (size_t)n * row * eb, hipMemcpyDeviceToHost);
+    }));
+    for (size_t i = 0; i < b.size(); ++i) {
         const uint32_t u = (uint32_t)b[i] << 16;
-        std::memcpy(&h_kv[i], &u, 4);
+        std::memcpy(&h_kv[(size_t)p0 * row + i], &u, 4);
     }
     return ok();
 }
@@ -637,7 +678,7 @@ bvf_status bvf_kv_widths(const bvf_model* m, int64_t* out, int32_t n) {
 
 bvf_status bvf_plane_floats(const bvf_model* m, int64_t* out, int32_t n) {
     if (!m || !out || n != m->d.n_layers) return fail(BVF_E_INVALID, "need an array of n_layers entries");
-    for (int l = 0; l < n; ++l) out[l] = m->L[l].plane ? m->held * 2 * m->L[l].w : 0;
+    for (int l = 0; l < n; ++l) out[l] = m->L[l].plane ? plane_keep(m->L[l], m->held) * 2 * m->L[l].w : 0;
     return ok();
 }
 
@@ -815,21 +856,16 @@ bvf_status bvf_extend_context(bvf_model* m, const float* h_kv_all, int64_t n) {
     for (int l = 0; l < m->d.n_layers; ++l) {
         Layer& L = m->L[l];
         if (!L.plane) continue;
-        const size_t cnt = (size_t)n * 2 * L.w;
-        const size_t at = (size_t)m->held * 2 * L.w;
-        if (!m->d.kv_bf16) {
-            HIP_TRY(hipMemcpy((float*)L.plane + at, h_kv_all + off, cnt * 4, hipMemcpyHostToDevice));
-        } else {
-            b.resize(cnt);   // bf16 planes: each value rounded to nearest even (NaN kept quiet)
-            for (size_t i = 0; i < cnt; ++i) {
-                uint32_t u;
-                std::memcpy(&u, &h_kv_all[off + i], 4);
-                b[i] = (u & 0x7fffffffu) > 0x7f800000u ? (uint16_t)((u >> 16) | 0x40u)
-                                                        : (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-            }
-            HIP_TRY(hipMemcpy((uint16_t*)L.plane + at, b.data(), cnt * 2, hipMemcpyHostToDevice));
-        }
-        off += cnt;
+        const size_t row = (size_t)2 * L.w, eb = m->d.kv_bf16 ? 2 : 4;
+        // positions held .. held + n - 1 go to their slots; on a ring only the last cap of them stay
+        const int64_t q0 = m->held + std::max<int64_t>(0, n - L.cap), q1 = m->held + n;
+        const float* src = h_kv_all + off + (size_t)(q0 - m->held) * row;
+        if (m->d.kv_bf16) round_to_bf16(src, (size_t)(q1 - q0) * row, b);   // bf16 planes: RNE, NaN kept quiet
+        HIP_TRY(for_slot_runs(L, q0, q1, [&](int64_t slot, int64_t first, int64_t cnt) {
+            const void* from = m->d.kv_bf16 ? (const void*)(b.data() + (size_t)first * row) : (const void*)(src + (size_t)first * row);
+            return hipMemcpy((uint8_t*)L.plane + (size_t)slot * row * eb, from, (size_t)cnt * row * eb, hipMemcpyHostToDevice);
+        }));
+        off += (size_t)n * row;
     }
     m->held += n;
     return ok();
@@ -855,15 +891,23 @@ bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out) {
     s->device = m->device;
     s->kv_elem = m->d.kv_bf16 ? 2 : 4;
     for (int l = 0; l < m->d.n_layers; ++l) {
-        s->per.push_back(m->L[l].w);
-        s->shared.push_back(m->L[l].plane ? 0 : 1);
+        const Layer& L = m->L[l];
+        s->per.push_back(L.w);
+        s->shared.push_back(L.plane ? 0 : 1);
+        s->cap.push_back(L.plane ? L.cap : 0);
+        s->kept.push_back(L.plane ? plane_keep(L, m->held) : 0);
         s->data.push_back(nullptr);
     }
     for (int l = 0; l < m->d.n_layers; ++l) {
-        if (s->shared[l] || s->held == 0) continue;
-        const size_t bytes = (size_t)bvf_cut_floats(s->per.data(), s->n_layers, l, s->held) * s->kv_elem;
-        hipError_t e = hipMalloc((void**)&s->data[l], bytes);
-        if (e == hipSuccess) e = hipMemcpyAsync(s->data[l], m->L[l].plane, bytes, hipMemcpyDeviceToDevice, m->st);
+        if (s->shared[l] || s->kept[l] == 0) continue;
+        const Layer& L = m->L[l];
+        const size_t row = (size_t)2 * L.w * s->kv_elem;
+        hipError_t e = hipMalloc((void**)&s->data[l], (size_t)s->kept[l] * row);
+        if (e == hipSuccess)
+            e = for_slot_runs(L, s->held - s->kept[l], s->held, [&](int64_t slot, int64_t first, int64_t n) {
+                return hipMemcpyAsync((uint8_t*)s->data[l] + (size_t)first * row, (const uint8_t*)L.plane + (size_t)slot * row,
+                                      (size_t)n * row, hipMemcpyDeviceToDevice, m->st);
+            });
         if (e != hipSuccess) {
             bvf_snapshot_free(s);
             return fail(BVF_E_DEVICE, "snapshot: %s", hipGetErrorString(e));
@@ -885,14 +929,21 @@ bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s) {
     for (int l = 0; l < m->d.n_layers; ++l) {
         if (s->per[l] != m->L[l].w) return fail(BVF_E_INVALID, "layer %d: snapshot width %lld, model %d", l, (long long)s->per[l], m->L[l].w);
         if (s->shared[l] != (m->L[l].plane ? 0 : 1)) return fail(BVF_E_INVALID, "layer %d: shared/own mismatch", l);
+        if (s->cap[l] != (m->L[l].plane ? m->L[l].cap : 0))
+            return fail(BVF_E_INVALID, "layer %d: snapshot plane of %d positions, model plane of %d (ring and linear planes differ)",
+                        l, s->cap[l], m->L[l].plane ? m->L[l].cap : 0);
     }
     if (s->held > m->d.max_ctx) return fail(BVF_E_CAPACITY, "snapshot holds more positions than max_ctx");
     if (s->kv_elem != (m->d.kv_bf16 ? 2 : 4)) return fail(BVF_E_INVALID, "snapshot of %s planes, model of %s planes",
                                                            s->kv_elem == 2 ? "bf16" : "fp32", m->d.kv_bf16 ? "bf16" : "fp32");
     for (int l = 0; l < m->d.n_layers; ++l) {
         if (s->shared[l] || !s->data[l]) continue;
-        const size_t bytes = (size_t)bvf_cut_floats(s->per.data(), s->n_layers, l, s->held) * s->kv_elem;
-        HIP_TRY(hipMemcpyAsync(m->L[l].plane, s->data[l], bytes, hipMemcpyDeviceToDevice, m->st));
+        const Layer& L = m->L[l];
+        const size_t row = (size_t)2 * L.w * s->kv_elem;
+        HIP_TRY(for_slot_runs(L, s->held - s->kept[l], s->held, [&](int64_t slot, int64_t first, int64_t n) {
+            return hipMemcpyAsync((uint8_t*)L.plane + (size_t)slot * row, (const uint8_t*)s->data[l] + (size_t)first * row,
+                                  (size_t)n * row, hipMemcpyDeviceToDevice, m->st);
+        }));
     }
     HIP_TRY(hipStreamSynchronize(m->st));
     m->held = s->held;
@@ -902,7 +953,7 @@ bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s) {
 
 bvf_status bvf_snapshot_floats(const bvf_snapshot* s, int64_t* out, int32_t n) {
     if (!s || !out || n != s->n_layers) return fail(BVF_E_INVALID, "need an array of n_layers entries");
-    for (int l = 0; l < n; ++l) out[l] = s->shared[l] ? 0 : bvf_cut_floats(s->per.data(), s->n_layers, l, s->held);
+    for (int l = 0; l < n; ++l) out[l] = s->shared[l] ? 0 : bvf_cut_floats(s->per.data(), s->n_layers, l, s->kept[l]);
     return ok();
 }
 

@@ -132,6 +132,7 @@ struct Attn {
     const float2* rope = nullptr;
     void* plane = nullptr;       // [max_ctx][2][w] (own or owner's), fp32 or (kv_bf16) bf16 values
     int kv_bf16 = 0;
+    int ring_cap = 0;            // > 0: the plane is a ring of ring_cap slots, position p in slot p mod ring_cap
     int w = 0, own = 0;
     int M = 0, Hq = 0, nkv = 0, hd = 0;
     int causal = 1;              // 1: row m at pos0 + m sees [max(0, pos0 + m - window + 1), pos0 + m]

@@ -343,6 +343,7 @@ struct AttnK {
     const float2* rope;      // [max_ctx][hd / 2]
     void* plane;             // own or owner's plane [max_ctx][2][w], fp32 or (kv_bf16) bf16 values
     int kv_bf16;
+    int ring_cap;            // > 0: ring plane of ring_cap slots (position p in slot p mod ring_cap)
     int w, own;
     int M, Hq, nkv, Hg, NQ, n_qt;
     int causal, pos0, window, ctx_lo, ctx_hi;
@@ -353,6 +354,9 @@ struct AttnK {
     int* counters;           // [n_qt * nkv]
     uint16_t* out;           // [M][Hq * hd] bf16
 };
+
+// Plane slot of position p: p itself, or p mod the ring's capacity on a ring plane.
+__device__ __forceinline__ int kv_slot(const AttnK& a, int p) { return a.ring_cap > 0 ? p % a.ring_cap : p; }
 
 __device__ __forceinline__ void row_range(const AttnK& a, int m, int& lo, int& hi) {
     if (a.causal) {
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             const int unit = part * 64 + lane;
             const int key = c0 + kk < c1 ? c0 + kk : c0;
             if (UPR >= 64 || unit < UPR) {
-                const size_t e = (size_t)key * prow + (size_t)kv * a.w + g * HD + unit * EPU;
+                const size_t e = (size_t)kv_slot(a, key) * prow + (size_t)kv * a.w + g * HD + unit * EPU;
                 const void* src = (const TT*)a.plane + e;
                 void* dst = (kv ? &Vt[kk][0] : &Kt[kk][0]) + part * 64 * EPU;
                 __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -493,7 +497,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     };
     auto store_row = [&](int p, int c0, TT (*Kt)[LDK], TT (*Vt)[LDV]) __attribute__((always_inline)) {
         const float inv = a.qk_norm ? 1.0f / sqrtf(row16_sum(ssr) / (float)HD + a.eps) : 1.f;
-        const size_t prow_off = (size_t)p * prow + g * HD;
+        const size_t prow_off = (size_t)kv_slot(a, p) * prow + g * HD;
         const int kk = p - c0;
         const int d0 = jr * PPT;
         float gk0[PPT], gk1[PPT], k0[PPT], k1[PPT];
@@ -1047,6 +1051,7 @@ AttnK make_attn(const Attn& x) {
     a.rope = x.rope;
     a.plane = x.plane;
     a.kv_bf16 = x.kv_bf16;
+    a.ring_cap = x.ring_cap;
     a.w = x.w;
     a.own = x.own;
     a.M = x.M;

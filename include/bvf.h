@@ -103,6 +103,13 @@ typedef struct {
                               with p = row l of the per-layer input table entry of the row's token,
                               x = (x + Wp . h) * s_l. The per-layer inputs need token ids, so calls that
                               take injected rows (bvf_layer_forward) are refused on such a model. */
+    int32_t kv_ring;       /* 0: linear planes (every position held). 1: a memory variant for verify
+                              models: each own sliding layer with a window keeps a ring of window + 16
+                              position slots, position p in slot p mod (window + 16); the 16 spare
+                              slots take a pass's rows, so rows a commit cuts back never overwrite a
+                              key that a later row can see. Such a plane holds, counts, snapshots and
+                              returns (bvf_get_kv) the last min(held, window) positions; older rows
+                              read as NaN. Cuts stay per layer [PR2303, "What changes" item 1]. */
 } bvf_model_desc;
 
 typedef struct bvf_model bvf_model;
