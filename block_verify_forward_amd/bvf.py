@@ -63,6 +63,7 @@ SIGNATURES = {
     "bvf_positions_held": (_I32, [_P, _P]),
     "bvf_verify_batch": (_I32, [_P, _P, _I32, _P, _P]),
     "bvf_set_graph_mode": (_I32, [_P, _I32]),
+    "bvf_graph_captures": (_I32, [_P, _P]),
     "bvf_accept_greedy": (_I32, [_P, _P, _I32, _P, _P, _P]),
     "bvf_accept_greedy_static": (_I32, [_P, _I32, _I32, _P, _P, _P, _P]),
     "bvf_prefill": (_I32, [_P, _P, _I32, _P]),
@@ -263,6 +264,11 @@ class Model:
 
     def set_graph_mode(self, on: bool):
         _check(lib().bvf_set_graph_mode(self.h, 1 if on else 0))
+
+    def graph_captures(self) -> int:
+        out = np.zeros(1, dtype=np.int64)
+        _check(lib().bvf_graph_captures(self.h, _host(out)))
+        return int(out[0])
 
     def prefill(self, d_tokens, d_last_logits=None):
         _check(lib().bvf_prefill(self.h, _ptr(d_tokens), int(d_tokens.numel()),

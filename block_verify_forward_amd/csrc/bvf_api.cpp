@@ -142,11 +142,14 @@ struct bvf_model {
     int64_t held = 0;
     int32_t pending = -1;
     // graph replay of the verify pass: captured on cap_st, launched on st; valid for one
-    // (positions held, k, tokens, logits, taps) key
+    // (plan bound, k, tokens, logits, taps) key. The captured attention reads the positions held
+    // from dpos, which a one-thread kernel sets before each replay.
     int use_graph = 0;
     hipStream_t cap_st = nullptr;
     hipGraphExec_t gexec = nullptr;
-    int64_t g_P = -1;
+    int64_t* dpos = nullptr;
+    int64_t g_plan = -1;
+    int64_t n_captures = 0;
     int32_t g_k = 0;
     const void *g_tok = nullptr, *g_lg = nullptr, *g_taps = nullptr;
     ~bvf_model() {
@@ -303,6 +306,7 @@ size_t layout(bvf_model* m, uint8_t* base) {
     m->fcout = (float*)take((size_t)kMaxRows * H * 4);
     m->partial = (float*)take(kPartialFloats * 4);
     m->counters = (int*)take((size_t)kCounters * 4);
+    m->dpos = (int64_t*)take(8);
     // attention partials: at most max(384, Hq * (max_ctx / 4096 + 2)) workgroups of 16 rows
     // attention partials: (query tiles x KV heads) <= n_q_heads at 16 rows, up to kAttnMaxChunks chunks each
     m->attn_part_floats = (size_t)d.n_q_heads * kAttnMaxChunks * 16 * (m->hd_max + 2);
@@ -450,7 +454,18 @@ Attn attn_for(const bvf_model* m, const Layer& L, int rows) {
 // the PLE gate and projection as M-row GEMMs, then the layer scalar): the down projection leaves
 // bf16(x) in act, the gate GEMM writes h = bf16(silu(Wg . act) * p) (p gathered by the rows'
 // tokens), and the projection GEMM adds Wp . h to x and scales by the layer scalar.
-hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps, int ldt, const int32_t* tokens) {
+// Causal passes plan their attention for a bound on the positions held: the last position of the
+// 256-position span that holds P (at most max_ctx - k). Direct launches and graph replays at any P
+// of one span then run the same chunk plan and agree bit for bit, and one captured pass serves the
+// whole span.
+constexpr int kPlanSpan = 256;
+int plan_bound(const bvf_model* m, int64_t P, int k) {
+    return (int)std::min<int64_t>(m->d.max_ctx - k, P | (kPlanSpan - 1));
+}
+
+// dpos (optional): the positions held are read from device memory at run time (captured passes).
+hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps, int ldt, const int32_t* tokens,
+                     const int64_t* dpos = nullptr) {
     Layer& L = m->L[l];
     const int H = m->d.hidden;
     hipStream_t st = m->st;
@@ -469,6 +484,8 @@ hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps
     at.own = L.plane != nullptr;
     at.causal = 1; at.pos0 = P; at.window = L.d.attn == BVF_ATTN_SLIDING ? L.d.window : 0;
     at.np0 = P; at.np1 = P + k; at.sp = P; at.r_lo = 0; at.r_hi = 0;
+    at.pos_plan = plan_bound(m, P, k);
+    at.dpos = dpos;
     if ((e = launch_attention(at, st)) != hipSuccess) return e;
     g = gemm_for(m, L.o, EPI_RESID);
     g.A = m->obuf; g.lda = L.qd; g.M = k; g.y = x; g.ldy = H; g.ss_out = m->ss_x;
@@ -691,9 +708,9 @@ bvf_status bvf_positions_held(const bvf_model* m, int64_t* out) {
 }  // extern "C"
 
 namespace {
-// The verify pass's launches on stream st (positions P .. P + k - 1).
+// The verify pass's launches on stream st (positions P .. P + k - 1; with dpos, P read from there).
 hipError_t enqueue_verify(bvf_model* m, hipStream_t st, const int32_t* d_tokens, int k, float* d_logits_all,
-                          uint16_t* d_taps) {
+                          uint16_t* d_taps, const int64_t* dpos) {
     const int H = m->d.hidden, V = m->d.vocab, P = (int)m->held;
     const int T = (int)m->taps.size();
     hipStream_t saved = m->st;
@@ -704,7 +721,7 @@ hipError_t enqueue_verify(bvf_model* m, hipStream_t st, const int32_t* d_tokens,
         if (d_taps)
             for (int t = 0; t < T; ++t)
                 if (m->taps[t] == l) taps_l = d_taps + (size_t)t * H;
-        e = run_layer(m, l, m->x, k, P, taps_l, T * H, d_tokens);
+        e = run_layer(m, l, m->x, k, P, taps_l, T * H, d_tokens, dpos);
     }
     if (e == hipSuccess) e = launch_head(m, nullptr, k, d_logits_all, st, m, m->x, m->final_norm);
     m->st = saved;
@@ -723,9 +740,10 @@ bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, fl
     bvf_status s = check_loaded(m);
     if (s) return s;
     if (!m->use_graph) {
-        HIP_TRY(enqueue_verify(m, m->st, d_tokens, k, d_logits_all, d_taps));
+        HIP_TRY(enqueue_verify(m, m->st, d_tokens, k, d_logits_all, d_taps, nullptr));
     } else {
-        if (!m->gexec || m->g_P != m->held || m->g_k != k || m->g_tok != d_tokens || m->g_lg != d_logits_all ||
+        const int64_t plan = plan_bound(m, m->held, k);
+        if (!m->gexec || m->g_plan != plan || m->g_k != k || m->g_tok != d_tokens || m->g_lg != d_logits_all ||
             m->g_taps != d_taps) {
             if (m->gexec) {
                 HIP_TRY(hipGraphExecDestroy(m->gexec));
@@ -734,7 +752,7 @@ bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, fl
             if (!m->cap_st) HIP_TRY(hipStreamCreateWithFlags(&m->cap_st, hipStreamNonBlocking));
             hipGraph_t graph = nullptr;
             HIP_TRY(hipStreamBeginCapture(m->cap_st, hipStreamCaptureModeThreadLocal));
-            hipError_t e = enqueue_verify(m, m->cap_st, d_tokens, k, d_logits_all, d_taps);
+            hipError_t e = enqueue_verify(m, m->cap_st, d_tokens, k, d_logits_all, d_taps, m->dpos);
             hipError_t e2 = hipStreamEndCapture(m->cap_st, &graph);
             if (e != hipSuccess || e2 != hipSuccess) {
                 if (graph) (void)hipGraphDestroy(graph);
@@ -746,8 +764,10 @@ bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, fl
                 m->gexec = nullptr;
                 return fail(BVF_E_DEVICE, "graph instantiate: %s", hipGetErrorString(e));
             }
-            m->g_P = m->held; m->g_k = k; m->g_tok = d_tokens; m->g_lg = d_logits_all; m->g_taps = d_taps;
+            m->g_plan = plan; m->g_k = k;
+            ++m->n_captures; m->g_tok = d_tokens; m->g_lg = d_logits_all; m->g_taps = d_taps;
         }
+        HIP_TRY(launch_set_i64(m->dpos, m->held, m->st));
         HIP_TRY(hipGraphLaunch(m->gexec, m->st));
     }
     m->held += k;
@@ -784,6 +804,12 @@ bvf_status bvf_set_graph_mode(bvf_model* m, int32_t on) {
     if (!m) return fail(BVF_E_INVALID, "model is NULL");
     if (on != 0 && on != 1) return fail(BVF_E_INVALID, "graph mode must be 0 or 1");
     m->use_graph = on;
+    return ok();
+}
+
+bvf_status bvf_graph_captures(const bvf_model* m, int64_t* out) {
+    if (!m || !out) return fail(BVF_E_INVALID, "NULL argument");
+    *out = m->n_captures;
     return ok();
 }
 

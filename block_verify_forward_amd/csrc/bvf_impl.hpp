@@ -147,8 +147,15 @@ struct Attn {
     int* counters = nullptr;     // zero between launches
     int n_counters = 0;
     int n_cu = 256;              // compute units of the device (chunk planning)
+    // causal passes: the key chunks are planned for rows at pos_plan .. pos_plan + M - 1 (pos_plan >=
+    // pos0), so passes at positions up to pos_plan share one launch configuration; 0: at pos0
+    int pos_plan = 0;
+    // causal passes replayed from a graph: the positions held P are read from *dpos at run time and
+    // the rows sit at P .. P + M - 1 (pos0, the new rows and the key range follow from P)
+    const int64_t* dpos = nullptr;
 };
 size_t attn_part_floats_needed(const Attn& a);
+hipError_t launch_set_i64(int64_t* dst, int64_t v, hipStream_t st);
 hipError_t launch_attention(const Attn& a, hipStream_t st);
 
 // Sampled draws instead of the argmax: 1/T (fp32), Philox key (seed) and counter offset words.

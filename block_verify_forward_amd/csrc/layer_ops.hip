@@ -350,10 +350,26 @@ struct AttnK {
     int np0, np1, sp, r_lo, r_hi;   // new rows: positions [np0, np1); row of p: p < sp ? r_lo + p - np0 : r_hi + p - sp
     int key_lo, n_keys, spw, n_chunks;   // keys [key_lo, key_lo + n_keys); spw sub-chunks per workgroup
     int nst;                 // LDS stages of the kernel (1: spw == 1)
+    const int64_t* dpos;     // causal graph replays: positions held read here (see bind_positions)
     float* part;             // [n_qt][nkv][n_chunks][16][hd + 2] partials
     int* counters;           // [n_qt * nkv]
     uint16_t* out;           // [M][Hq * hd] bf16
 };
+
+// A causal pass captured in a graph reads the positions held P from device memory: its rows sit at
+// P .. P + M - 1, an own layer appends them, and row m sees [max(0, P + m - window + 1), P + m].
+__device__ __forceinline__ void bind_positions(AttnK& a) {
+    const int P = (int)*a.dpos;
+    a.pos0 = P;
+    a.np0 = P;
+    a.np1 = P + a.M;
+    a.sp = P;
+    const int lo = (a.window > 0 && P - a.window + 1 > 0) ? P - a.window + 1 : 0;
+    a.key_lo = lo;
+    a.n_keys = P + a.M - lo;
+}
+
+__global__ void k_set_i64(int64_t* dst, int64_t v) { *dst = v; }
 
 // Plane slot of position p: p itself, or p mod the ring's capacity on a ring plane.
 __device__ __forceinline__ int kv_slot(const AttnK& a, int p) { return a.ring_cap > 0 ? p % a.ring_cap : p; }
@@ -436,6 +452,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     __shared__ __attribute__((aligned(16))) float Qs[16][LD];
     __shared__ float Sp[4][16][CK + 1];   // per-wave partial scores (over the wave's dims)
     __shared__ float Ps[4][16][CK + 1];   // per-wave probabilities
+    if (a.dpos) bind_positions(a);
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int chunk = blockIdx.x % a.n_chunks;
@@ -1085,13 +1102,21 @@ AttnK make_attn(const Attn& x) {
     }
     a.key_lo = lo;
     a.n_keys = hi - lo + 1;
+    a.dpos = x.dpos;
+    // the plan covers the keys of rows at pos_plan when given (a bound shared by passes at lower
+    // positions: a later pass there leaves trailing chunks empty)
+    int plan_keys = a.n_keys;
+    if (x.causal && x.pos_plan > x.pos0) {
+        const int plo = (x.window > 0 && x.pos_plan - x.window + 1 > 0) ? x.pos_plan - x.window + 1 : 0;
+        plan_keys = std::max(plan_keys, x.pos_plan + x.M - plo);
+    }
     // One sub-chunk per workgroup (one LDS stage, two workgroups per compute unit) while that takes
     // at most kAttnMaxChunks chunks and 768 workgroups. Longer key ranges: workgroups of spw
     // sub-chunks through two stages; their LDS leaves one workgroup per compute unit, so the chunks
     // are planned to run in a single round of at most n_cu workgroups.
     const int tiles = a.n_qt * a.nkv;
     const int ck1 = attn_ck(x.hd, x.kv_bf16 != 0, 1);
-    const int subs1 = (a.n_keys + ck1 - 1) / ck1;
+    const int subs1 = (plan_keys + ck1 - 1) / ck1;
     if (subs1 <= kAttnMaxChunks && (long)subs1 * tiles <= 768) {
         a.nst = 1;
         a.spw = 1;
@@ -1099,7 +1124,7 @@ AttnK make_attn(const Attn& x) {
     } else {
         a.nst = 2;
         const int ck2 = attn_ck(x.hd, x.kv_bf16 != 0, 2);
-        const int subs = (a.n_keys + ck2 - 1) / ck2;
+        const int subs = (plan_keys + ck2 - 1) / ck2;
         const int nch = std::max(1, std::min(kAttnMaxChunks, x.n_cu / tiles));
         a.spw = (subs + nch - 1) / nch;
         a.n_chunks = (subs + a.spw - 1) / a.spw;
@@ -1194,6 +1219,11 @@ hipError_t static_accept_scratch(int device, float** part_val, int** part_idx) {
     *part_val = (float*)g_scratch_ptr[device];
     *part_idx = (int*)((uint8_t*)g_scratch_ptr[device] + (size_t)kMaxRows * kStaticAcceptBlocks * sizeof(float));
     return hipSuccess;
+}
+
+hipError_t launch_set_i64(int64_t* dst, int64_t v, hipStream_t st) {
+    hipLaunchKernelGGL(k_set_i64, dim3(1), dim3(1), 0, st, dst, v);
+    return hipGetLastError();
 }
 
 hipError_t launch_steer(float* logits, int k, int V, const int32_t* tok, const float* add, hipStream_t st) {

@@ -190,9 +190,14 @@ bvf_status bvf_prefill(bvf_model* m, const int32_t* d_tokens, int32_t n, float* 
 
 /* Graph replay of bvf_verify_batch (1) or direct launches (0, the default). With 1 the pass is
  * captured once into a HIP graph (on a private stream) and replayed on the model's stream; the
- * capture is reused while positions held, k and the three buffer pointers stay the same, and is
- * taken again when any of them changes. Results are identical in both modes. */
+ * replayed pass reads the positions held from device memory (set by a one-thread kernel launched
+ * before each replay), so the capture serves every position of a 256-position span (P with the same
+ * P / 256, below max_ctx - k) while k and the three buffer pointers stay the same; it is taken again
+ * when any of them changes. Both modes plan the attention for the span's last position, so their
+ * results are identical bit for bit. */
 bvf_status bvf_set_graph_mode(bvf_model* m, int32_t on);
+/* Number of verify-pass graph captures the model has taken so far (h_out[0]). */
+bvf_status bvf_graph_captures(const bvf_model* m, int64_t* h_out);
 
 /* Greedy longest-prefix accept ([CARD], "How it is used"; [PR2236], the acceptance tool): y_i is the
  * first index of the maximum of row i of d_logits_all [k][vocab] (NaN never wins); the drafts are

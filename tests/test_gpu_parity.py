@@ -539,7 +539,7 @@ def test_draft_append_only_then_block():
 # ------------------------------------------------------------------------------------------
 def test_graph_replay_matches_direct_launches():
     """The captured pass replays bit-identically to direct launches, over several replays with
-    other device work in between, and is re-captured when the positions held change."""
+    other device work in between, and at other positions held."""
     m = synth.tiny_two_width_model()
     g, o, w, kv = build_pair(m, 20)
     toks = dev(synth.tokens(0, "graph.toks", 8, m.vocab))
@@ -558,12 +558,68 @@ def test_graph_replay_matches_direct_launches():
         assert np.array_equal(host(lg), ref), f"replay {rep}"
         g.q4_1_gemm(0, bvf.Q, x, 8, y[:, :256])      # eager work between replays
         torch.cuda.synchronize()
-    # new positions: the graph is captured again and still matches direct launches
+    assert g.graph_captures() == 1
+    # new positions (same 256-position span): the capture is replayed and still matches direct launches
     g.verify_batch(toks, lg, None)
     g.commit_verify_rows(3)
     g.verify_batch(toks, lg, None)
     got = host(lg)
     g.commit_verify_rows(0)
+    assert g.graph_captures() == 1
     g.set_graph_mode(False)
     g.verify_batch(toks, lg, None)
     assert np.array_equal(host(lg), got)
+
+
+def test_graph_serves_a_position_span_across_rounds():
+    """A loop-shaped sequence on the two-width miniature (max_ctx 600): verifies of 8 rows with
+    commits of 1..8 rows from 200 cached positions past 256 and 512. The graph model (positions read
+    from device memory at replay) and a direct-launch twin give bit-identical logits and taps at every
+    round, the graph is captured once per 256-position span (3 captures), the planes agree, and the
+    last round's logits agree with the oracle replaying the same sequence."""
+    m = synth.tiny_two_width_model(max_ctx=600)
+    P = 200
+    gd, o, w, kv = build_pair(m, P)
+    gg = bvf.Model(m)
+    gg.load_weights(w)
+    gg.set_context(kv, P)
+    gg.set_graph_mode(True)
+    T = len(m.tap_layers)
+    buf = lambda: (torch.empty((8, m.vocab), dtype=torch.float32, device="cuda"),
+                   torch.empty((8, T, m.hidden), dtype=torch.int16, device="cuda"))
+    (lgd, tpd), (lgg, tpg) = buf(), buf()
+    toks = torch.empty(8, dtype=torch.int32, device="cuda")
+    commits = [int(c) for c in synth.accept_lengths(0, 200, max_a=7) + 1]
+    seq = []
+    r = 0
+    while gd.positions_held() + 8 <= 530:
+        t = synth.tokens(r, "graph.span", 8, m.vocab)
+        toks.copy_(torch.from_numpy(t))
+        gd.verify_batch(toks, lgd, tpd)
+        gg.verify_batch(toks, lgg, tpg)
+        a, b = host(lgd), host(lgg)
+        assert np.array_equal(a, b), f"round {r} at {gd.positions_held() - 8}"
+        assert np.array_equal(host(tpd), host(tpg)), f"round {r} taps"
+        n = commits[r]
+        gd.commit_verify_rows(n)
+        gg.commit_verify_rows(n)
+        seq.append((t, n))
+        r += 1
+    held = gg.positions_held()
+    print(f"[graph span] {r} rounds, positions {P} -> {held}, captures {gg.graph_captures()}", flush=True)
+    assert held > 512 and gg.graph_captures() == 3
+    assert np.array_equal(gg.plane_floats(), gd.plane_floats())
+    for l in range(m.n_layers):
+        if m.own(l):
+            assert np.array_equal(gg.get_kv(l, held), gd.get_kv(l, held)), f"layer {l} plane"
+
+    def run(arrs):
+        x = oracle.Model(m, w)
+        x.set_kv(arrs, P)
+        for t, n in seq[:-1]:
+            x.verify_batch(t)
+            assert x.commit_verify_rows(n) == 0
+        return x.verify_batch(seq[-1][0])
+
+    err = rel_l1(b, run(kv))
+    assert err < logits_bar(err, m, run, kv, f"graph replays over {r} rounds, last at {held - seq[-1][1]}")
