@@ -226,8 +226,10 @@ def run_loop(args):
 
 def run_prefill(args):
     """Chunked prefill: args.prefill prompt tokens on top of args.ctx cached positions, in batched
-    passes of up to 16 rows (one pass over the weights per chunk), the head on the last chunk only;
-    the context is restored from a snapshot before every timed run."""
+    passes of up to 64 rows (one pass over the weights per chunk, four 16-row MFMA tiles per weight
+    superblock), the head on the last row only; the context is restored from a snapshot before every
+    timed run. Also times each Q4_1 GEMM class at 64 rows (HIP events over 3 x n_layers launches)
+    and reports its weight-stream GB/s and useful bf16 MFMA TFLOP/s."""
     import torch
     from block_verify_forward_amd import bvf, synth
 
@@ -256,8 +258,20 @@ def run_prefill(args):
         assert g.positions_held() == args.ctx + args.prefill
         g.restore(snap)
     ms = float(np.median(times))
+    chunk = 64
+    n_chunks = (args.prefill + chunk - 1) // chunk
+    cls_ms, cls_bytes = g.time_gemms(chunk, 3)
+    gemm = {}
+    for i, name in enumerate(("qkv", "o", "gate_up", "down")):
+        t = float(cls_ms[i]) * 1e-3
+        flops = 2.0 * chunk * float(cls_bytes[i]) / 0.625   # Q4_1: 0.625 bytes per weight
+        gemm[name] = {"us_per_launch": round(t * 1e6, 2), "gbs": round(float(cls_bytes[i]) / t / 1e9, 1),
+                      "tflops_useful_bf16": round(flops / t / 1e12, 1),
+                      "frac_of_mfma_peak": round(flops / t / 2.5e15, 4)}
+    log(f"per-class GEMM at {chunk} rows: " + ", ".join(f"{k} {v['us_per_launch']} us ({v['gbs']} GB/s, "
+                                                         f"{v['tflops_useful_bf16']} TFLOP/s)" for k, v in gemm.items()))
     res = {
-        "metric": "chunked prefill tokens/s (16-row batched passes)",
+        "metric": "chunked prefill tokens/s (64-row batched passes)",
         "value": round(args.prefill / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -266,11 +280,12 @@ def run_prefill(args):
         "dtype": "bf16",
         "data": f"synthetic (seeded draws, seed {args.seed})",
         "config": {"workload": f"prefill of {args.prefill} tokens on {args.ctx} cached positions, target {m.n_layers} "
-                               f"layers hidden {m.hidden} Q4_1, chunks of 16 rows",
+                               f"layers hidden {m.hidden} Q4_1, chunks of {chunk} rows",
                    "kv_planes": "bf16" if args.kv_bf16 else "fp32"},
         "ms": round(ms, 3),
-        "chunks": (args.prefill + 15) // 16,
-        "ms_per_chunk": round(ms / ((args.prefill + 15) // 16), 4),
+        "chunks": n_chunks,
+        "ms_per_chunk": round(ms / n_chunks, 4),
+        "gemm_64_rows": gemm,
     }
     print(json.dumps(res), flush=True)
 

@@ -138,6 +138,7 @@ struct bvf_model {
     size_t staging_bytes = 0;
     std::vector<std::pair<int, float2*>> rope_tables;
     int hd_max = 0, qd_max = 0, nqkv_max = 0, ffn_max = 0;
+    int row_cap = kMaxRows;    // rows of the activation buffers: prefill chunks on verify models
     // state
     int64_t held = 0;
     int32_t pending = -1;
@@ -234,6 +235,9 @@ size_t layout(bvf_model* m, uint8_t* base) {
     };
     const bvf_model_desc& d = m->d;
     const int H = d.hidden;
+    // verify models run prefill chunks of up to kMaxGemmRows rows through the same buffers
+    const int RC = is_draft(d) ? kMaxRows : kMaxGemmRows;
+    m->row_cap = RC;
     auto mat = [&](Mat& M, int n_out, int K) {
         M.n_out = n_out;
         M.w.n_tiles = n_out / kTile;
@@ -282,7 +286,7 @@ size_t layout(bvf_model* m, uint8_t* base) {
     m->embed = d.vocab > 0 && !is_draft(d) ? (uint16_t*)take((size_t)d.vocab * H * 2) : nullptr;
     m->final_norm = (uint16_t*)take((size_t)H * 2);
     m->ple_table = d.ple_dim > 0 ? (uint16_t*)take((size_t)d.vocab * d.n_layers * d.ple_dim * 2) : nullptr;
-    m->pbuf = d.ple_dim > 0 ? (uint16_t*)take((size_t)kMaxRows * d.ple_dim * 2) : nullptr;
+    m->pbuf = d.ple_dim > 0 ? (uint16_t*)take((size_t)RC * d.ple_dim * 2) : nullptr;
     if (is_draft(d)) {
         m->fc = (uint16_t*)take((size_t)H * d.n_taps * H * 2);
         m->hidden_norm = (uint16_t*)take((size_t)H * 2);
@@ -297,22 +301,22 @@ size_t layout(bvf_model* m, uint8_t* base) {
             m->rope_tables.push_back({hd, (float2*)take((size_t)d.max_ctx * (hd / 2) * sizeof(float2))});
         m->L[l].rope = m->rope_tables[i].second;
     }
-    m->x = (float*)take((size_t)kMaxRows * H * 4);
-    m->act = (uint16_t*)take((size_t)kMaxRows * H * 2);
-    m->qkv = (float*)take((size_t)kMaxRows * m->nqkv_max * 4);
-    m->qbuf = (float*)take((size_t)kMaxRows * m->qd_max * 4);
-    m->obuf = (uint16_t*)take((size_t)kMaxRows * m->qd_max * 2);
-    m->mbuf = (uint16_t*)take((size_t)kMaxRows * m->ffn_max * 2);
-    m->fcout = (float*)take((size_t)kMaxRows * H * 4);
+    m->x = (float*)take((size_t)RC * H * 4);
+    m->act = (uint16_t*)take((size_t)RC * H * 2);
+    m->qkv = (float*)take((size_t)RC * m->nqkv_max * 4);
+    m->qbuf = (float*)take((size_t)RC * m->qd_max * 4);
+    m->obuf = (uint16_t*)take((size_t)RC * m->qd_max * 2);
+    m->mbuf = (uint16_t*)take((size_t)RC * m->ffn_max * 2);
+    m->fcout = (float*)take((size_t)RC * H * 4);
     m->partial = (float*)take(kPartialFloats * 4);
     m->counters = (int*)take((size_t)kCounters * 4);
     m->dpos = (int64_t*)take(8);
-    // attention partials: at most max(384, Hq * (max_ctx / 4096 + 2)) workgroups of 16 rows
-    // attention partials: (query tiles x KV heads) <= n_q_heads at 16 rows, up to kAttnMaxChunks chunks each
-    m->attn_part_floats = (size_t)d.n_q_heads * kAttnMaxChunks * 16 * (m->hd_max + 2);
+    // attention partials: (query tiles x KV heads) <= (RC / 16) n_q_heads at RC rows, up to
+    // kAttnMaxChunks chunks each
+    m->attn_part_floats = (size_t)(RC / 16) * d.n_q_heads * kAttnMaxChunks * 16 * (m->hd_max + 2);
     m->attn_part = (float*)take(m->attn_part_floats * 4);
-    m->ss_x = (float*)take((size_t)kMaxRows * (H / kTile) * 4);
-    m->ss_qkv = (float*)take((size_t)kMaxRows * (m->nqkv_max / kTile) * 4);
+    m->ss_x = (float*)take((size_t)RC * (H / kTile) * 4);
+    m->ss_qkv = (float*)take((size_t)RC * (m->nqkv_max / kTile) * 4);
     const int V = d.vocab;
     m->am_blocks = V > 0 ? argmax_blocks(V) : 1;
     m->am_val = (float*)take((size_t)kMaxRows * m->am_blocks * 4);
@@ -406,7 +410,8 @@ GemmLaunch gemm_for(const bvf_model* m, const Mat& mat, int epi) {
 // xsrc is given, bf16(rmsnorm(xsrc rows) * gain) formed in the GEMM's staging (sums of squares of
 // xsrc in the scratch owner's ss_x).
 hipError_t launch_head(const bvf_model* target, const uint16_t* A, int rows, float* logits, hipStream_t st,
-                       const bvf_model* scratch_owner, const float* xsrc = nullptr, const uint16_t* gain = nullptr) {
+                       const bvf_model* scratch_owner, const float* xsrc = nullptr, const uint16_t* gain = nullptr,
+                       int row0 = 0) {
     GemmLaunch g;
     g.w.codes = (const uint8_t*)target->embed;
     g.w.n_tiles = target->d.vocab / kTile;
@@ -426,7 +431,9 @@ hipError_t launch_head(const bvf_model* target, const uint16_t* A, int rows, flo
     g.n_counters = kCounters;
     g.n_cu = scratch_owner->n_cu;
     if (xsrc) {
-        g.xsrc = xsrc; g.ldx = target->d.hidden; g.ss_in = scratch_owner->ss_x; g.n_ss = target->d.hidden / kTile;
+        // rows row0 .. row0 + rows - 1 of xsrc and of the sums of squares
+        g.xsrc = xsrc + (size_t)row0 * target->d.hidden; g.ldx = target->d.hidden; g.n_ss = target->d.hidden / kTile;
+        g.ss_in = scratch_owner->ss_x + (size_t)row0 * g.n_ss;
         g.gain = gain; g.eps = scratch_owner->d.rms_eps;
     }
     return launch_gemm(g, st);
@@ -785,17 +792,14 @@ bvf_status bvf_prefill(bvf_model* m, const int32_t* d_tokens, int32_t n, float* 
     bvf_status s = check_loaded(m);
     if (s) return s;
     const int H = m->d.hidden, V = m->d.vocab;
-    for (int off = 0; off < n; off += kMaxRows) {
-        const int c = std::min(kMaxRows, n - off);
+    for (int off = 0; off < n; off += m->row_cap) {
+        const int c = std::min(m->row_cap, n - off);
         const int P = (int)m->held;
         HIP_TRY(launch_embed(d_tokens + off, -1, c, m->embed, V, H, 1.0f, m->x, m->ss_x, m->st));
         for (int l = 0; l < m->d.n_layers; ++l) HIP_TRY(run_layer(m, l, m->x, c, P, nullptr, 0, d_tokens + off));
         m->held += c;
-        if (off + c == n && d_last_logits) {
-            HIP_TRY(launch_head(m, nullptr, c, m->logits_tmp, m->st, m, m->x, m->final_norm));
-            HIP_TRY(hipMemcpyAsync(d_last_logits, m->logits_tmp + (size_t)(c - 1) * V, (size_t)V * 4,
-                                   hipMemcpyDeviceToDevice, m->st));
-        }
+        // the head on the last row of the last chunk only
+        if (off + c == n && d_last_logits) HIP_TRY(launch_head(m, nullptr, 1, d_last_logits, m->st, m, m->x, m->final_norm, c - 1));
     }
     return ok();
 }
@@ -1096,7 +1100,7 @@ bvf_status bvf_q4_1_dequant(const bvf_model* m, int32_t layer, int32_t matrix, f
 
 bvf_status bvf_q4_1_gemm(const bvf_model* m, int32_t layer, int32_t matrix, const uint16_t* d_x, int32_t rows, float* d_y) {
     if (!m || !d_x || !d_y) return fail(BVF_E_INVALID, "NULL argument");
-    if (rows < 1 || rows > kMaxRows) return fail(BVF_E_INVALID, "rows %d outside [1, %d]", rows, kMaxRows);
+    if (rows < 1 || rows > m->row_cap) return fail(BVF_E_INVALID, "rows %d outside [1, %d]", rows, m->row_cap);
     Run r;
     bvf_status s = matrix_run(m, layer, matrix, r);
     if (s) return s;
@@ -1115,7 +1119,7 @@ bvf_status bvf_layer_forward(bvf_model* m, int32_t layer, float* d_x, int32_t ro
     if (!m || !d_x) return fail(BVF_E_INVALID, "NULL argument");
     if (is_draft(m->d)) return fail(BVF_E_INVALID, "layer_forward runs verify layers");
     if (layer < 0 || layer >= m->d.n_layers) return fail(BVF_E_INVALID, "layer %d out of range", layer);
-    if (rows < 1 || rows > kMaxRows) return fail(BVF_E_INVALID, "rows %d outside [1, %d]", rows, kMaxRows);
+    if (rows < 1 || rows > m->row_cap) return fail(BVF_E_INVALID, "rows %d outside [1, %d]", rows, m->row_cap);
     if (m->d.ple_dim > 0)
         return fail(BVF_E_INVALID, "injected rows on a model with per-layer embeddings: its per-layer inputs need token ids");
     if (m->held + rows > m->d.max_ctx) return fail(BVF_E_CAPACITY, "positions would exceed max_ctx");
@@ -1129,7 +1133,7 @@ bvf_status bvf_layer_forward(bvf_model* m, int32_t layer, float* d_x, int32_t ro
 bvf_status bvf_time_gemms(bvf_model* m, int32_t rows, int32_t iters, float* h_ms, int64_t* h_bytes) {
     if (!m || !h_ms || !h_bytes) return fail(BVF_E_INVALID, "NULL argument");
     if (is_draft(m->d)) return fail(BVF_E_INVALID, "timing runs the verify model's GEMMs");
-    if (rows < 1 || rows > kMaxRows || iters < 1) return fail(BVF_E_INVALID, "rows in [1, 16], iters >= 1");
+    if (rows < 1 || rows > m->row_cap || iters < 1) return fail(BVF_E_INVALID, "rows in [1, %d], iters >= 1", m->row_cap);
     bvf_status s = check_loaded(m);
     if (s) return s;
     const int H = m->d.hidden;
@@ -1139,6 +1143,11 @@ bvf_status bvf_time_gemms(bvf_model* m, int32_t rows, int32_t iters, float* h_ms
     for (int cls = 0; cls < 5; ++cls) {
         int64_t bytes = 0;
         int launches = 0;
+        if (cls == 4 && rows > kMaxRows) {   // the bf16 head runs at most 16 rows: reported as 0
+            h_ms[cls] = 0.f;
+            h_bytes[cls] = 0;
+            continue;
+        }
         HIP_TRY(hipEventRecord(e0, m->st));
         for (int it = 0; it < iters; ++it) {
             if (cls == 4) {   // the bf16 head

@@ -7,6 +7,9 @@
 namespace bvf {
 
 constexpr int kMaxRows = 16;      // k <= 16 rows per pass: one 16-row MFMA tile
+constexpr int kMaxGemmRows = 64;  // prefill chunks: up to 4 row tiles share each weight pass
+// row tiles of 16 the GEMM kernel runs for M rows: 1, 2 or 4
+constexpr int gemm_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 constexpr int kTile = 16;         // output columns per MFMA tile
 constexpr int kSuper = 128;       // K per superblock = 4 Q4_1 blocks of 32
 constexpr int kAttnMaxChunks = 128;   // key chunks per (query tile, KV head) merged by the combine

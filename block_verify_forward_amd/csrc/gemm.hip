@@ -1,4 +1,5 @@
-// Small-M (k <= 16 rows) weight-streaming GEMM for gfx950, Q4_1 or bf16 weights.
+// Small-M (k <= 16 rows; up to 64 rows for prefill chunks) weight-streaming GEMM for gfx950, Q4_1
+// or bf16 weights.
 //
 // The verify pass is a skinny GEMM over the whole weight image: k <= 16 activation rows against
 // every weight column ([PR2303] "What changes": all k drafted rows go through every layer in one
@@ -25,6 +26,14 @@
 // when requested), then each wave streams its items (tiles wv, wv + WV, ...) through its ring.
 // Split-K partials are summed in a fixed order by the last wave to arrive (integer arrival
 // counter), so results are deterministic.
+//
+// Wider chunks (prefill, [PR2303] "Proof": the chunk arms of the state test): with M up to 64 rows
+// a wave's dequantised superblock feeds MT = 2 or 4 row tiles of 16 (one MFMA per tile and block),
+// so the weight stream and the dequantisation are paid once for all rows and the matrix cores take
+// the extra work. Such workgroups run at most 8 waves (two per SIMD, for the MT accumulators). Their
+// activation rows fill the LDS at a third of K or less, so they split K; the split partials are
+// plain stores, summed in split order by a second, fully parallel kernel that also runs the
+// epilogue (a last arriver would serialise several items' sums per wave).
 #include "bvf_impl.hpp"
 
 #include <algorithm>
@@ -185,45 +194,54 @@ __device__ __forceinline__ void issue_slot(const KArgs& a, int idx, uint8_t* slo
 template <int FMT>
 constexpr int loads_per_slot() { return FMT == W_Q4_1 ? 2 : 4; }
 
-// One superblock from a ring slot. A (this lane's row, 4 blocks of 8 bf16) comes from the LDS
-// copy of the rows; lanes of rows >= M read the zero row.
+// One superblock from a ring slot for MT row tiles. A (this lane's row of tile t, 4 blocks of 8
+// bf16) comes from the LDS copy of the rows at As_k + a_off[t]; lanes of rows >= M read row 0.
 //
 // Q4_1: block j contributes scale_j * C'_j (bf16 MFMA + VALU FMAs) and the min terms of the four
 // blocks are one fp32 MFMA 16x16x4 into accm, fed by the block sums the staging step left in LDS
-// (this lane's value: S[m = lane % 16][j = lane / 16]) and MM[j][c] = min - 16 scale.
-template <int FMT>
-__device__ __forceinline__ void compute_slot(const uint8_t* slot, const uint16_t* As_row, float s_val, int lane,
-                                             floatx4& acc, floatx4& accm) {
+// (this lane's value for tile t: S[m = 16 t + lane % 16][j = lane / 16]) and MM[j][c] = min - 16 scale.
+// The dequantised B operand of a block is built once and used by the MT tiles.
+template <int FMT, int MT>
+__device__ __forceinline__ void compute_slot(const uint8_t* slot, const uint16_t* As_k, const int (&a_off)[MT],
+                                             const float (&s_val)[MT], int lane, floatx4 (&acc)[MT],
+                                             floatx4 (&accm)[MT]) {
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
     const int c = lane & 15, sub = lane >> 4;
-    u32x4 av4[4];
+    u32x4 av4[MT][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) av4[j] = *(const u32x4*)(As_row + j * 32);
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) av4[t][j] = *(const u32x4*)(As_k + a_off[t] + j * 32);
     if constexpr (FMT == W_Q4_1) {
         const u32x4 cw = *(const u32x4*)(slot + lane * 16);
         const u32x4 sm = *(const u32x4*)(slot + 1024 + c * 16);
         const uint32_t smj = *(const uint32_t*)(slot + 1024 + (c * 4 + sub) * 4);   // column c, block sub
         const float mm = fmaf(-16.f, half_lo(smj), half_hi(smj));
-        accm = __builtin_amdgcn_mfma_f32_16x16x4f32(s_val, mm, accm, 0, 0, 0);
-        // block j's MFMA is issued before block j-1's scale FMAs (covers the MFMA latency with two
+#pragma unroll
+        for (int t = 0; t < MT; ++t) accm[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_val[t], mm, accm[t], 0, 0, 0);
+        // block j's MFMAs are issued before block j-1's scale FMAs (covers the MFMA latency with two
         // blocks of results live; the sched barriers keep the scheduler from hoisting all MFMAs)
-        floatx4 cc[2];
+        floatx4 cc[MT][2];
         uint32_t O;   // bf16 pair 16 | 16 with the code bits clear; the nibble lands in mantissa bits 3..6
         asm("v_mov_b32 %0, 0x41804180" : "=v"(O));
         const uint32_t M4 = 0x00780078u;
 #pragma unroll
         for (int j = 0; j < 5; ++j) {
             if (j < 4) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, av4[j]);
                 const uint32_t w = cw[j];
                 const u32x4 b = {and_or(w << 3, M4, O), and_or(w >> 1, M4, O), and_or(w >> 5, M4, O), and_or(w >> 9, M4, O)};
-                cc[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    cc[t][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av4[t][j]),
+                                                                           __builtin_bit_cast(bf16x8, b), zero, 0, 0, 0);
             }
             if (j > 0) {
                 const int jp = j - 1;
                 const float s = half_lo(sm[jp]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = fmaf(s, cc[jp & 1][r], acc[r]);
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(s, cc[t][jp & 1][r], acc[t][r]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -232,25 +250,29 @@ __device__ __forceinline__ void compute_slot(const uint8_t* slot, const uint16_t
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const u32x4 bw = *(const u32x4*)(slot + j * 1024 + lane * 16);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av4[j]), __builtin_bit_cast(bf16x8, bw), acc, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av4[t][j]), __builtin_bit_cast(bf16x8, bw),
+                                                                 acc[t], 0, 0, 0);
         }
     }
 }
 
 // RESID rows of a tile, loaded ahead (the split-K tail issues them before its arrival)
-__device__ __forceinline__ floatx4 load_resid_rows(const KArgs& a, int tile, int lane) {
+__device__ __forceinline__ floatx4 load_resid_rows(const KArgs& a, int tile, int lane, int m0) {
     const int c = lane & 15, sub = lane >> 4;
     floatx4 y;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int m = 4 * sub + r;
+        const int m = m0 + 4 * sub + r;
         y[r] = m < a.M ? a.y[(size_t)m * a.ldy + tile * kTile + c] : 0.f;
     }
     return y;
 }
 
+// Output rows m0 + 4 sub + r of the tile (m0: the row tile's first row).
 template <int EPI>
-__device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int tile, int lane,
+__device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int tile, int lane, int m0,
                                          bool have_pre = false, floatx4 y_pre = {0.f, 0.f, 0.f, 0.f}) {
     const int c = lane & 15, sub = lane >> 4;
     const int n = tile * kTile + c;
@@ -258,7 +280,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
         // the per-layer embedding gate: silu of the GEMM output times the row's per-layer input
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = 4 * sub + r;
+            const int m = m0 + 4 * sub + r;
             if (m >= a.M) continue;
             int t = a.tokens[m];
             t = t < 0 ? 0 : (t >= a.vocab ? a.vocab - 1 : t);
@@ -277,7 +299,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
             const int nh = tile * 8 + c;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = 4 * sub + r;
+                const int m = m0 + 4 * sub + r;
                 if (m >= a.M) continue;
                 const float g = acc[r];
                 a.out[(size_t)m * a.ldo + nh] = f32_to_bf16(g / (1.0f + expf(-g)) * up[r]);
@@ -288,7 +310,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
     float vout[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int m = 4 * sub + r;
+        const int m = m0 + 4 * sub + r;
         vout[r] = 0.f;
         if (m >= a.M) continue;
         if constexpr (EPI == EPI_STORE) {
@@ -313,7 +335,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
             float q = vout[r] * vout[r];
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) q += __shfl_xor(q, o);
-            const int m = 4 * sub + r;
+            const int m = m0 + 4 * sub + r;
             if (c == 0 && m < a.M) a.ss_out[(size_t)m * (a.n_cols / kTile) + tile] = q;
         }
     }
@@ -324,18 +346,18 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const floatx4& acc, int
 // counter of each of its tiles, and for the tiles where it arrived last reads the S partials at
 // device scope and sums them in split order (the hardware guarantee this relies on is stated at
 // the hand-off).
-__device__ __forceinline__ void splitk_store(const KArgs& a, const floatx4& acc, int tile, int split, int lane) {
+__device__ __forceinline__ void splitk_store(const KArgs& a, const floatx4& acc, int tile, int split, int lane, int m0) {
     const int c = lane & 15, sub = lane >> 4;
     const int n = tile * kTile + c;
     float* P = a.partial + (size_t)split * a.M * a.n_cols;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int m = 4 * sub + r;
+        const int m = m0 + 4 * sub + r;
         if (m < a.M) __hip_atomic_store(P + (size_t)m * a.n_cols + n, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-__device__ __forceinline__ floatx4 splitk_sum(const KArgs& a, int tile, int lane) {
+__device__ __forceinline__ floatx4 splitk_sum(const KArgs& a, int tile, int lane, int m0) {
     const int c = lane & 15, sub = lane >> 4;
     const float* base = a.partial + tile * kTile + c;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -345,7 +367,7 @@ __device__ __forceinline__ floatx4 splitk_sum(const KArgs& a, int tile, int lane
         float v[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = 4 * sub + r < a.M ? 4 * sub + r : 0;
+            const int m = m0 + 4 * sub + r < a.M ? m0 + 4 * sub + r : 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 v[r][i] = sp0 + i < a.S
@@ -360,16 +382,63 @@ __device__ __forceinline__ floatx4 splitk_sum(const KArgs& a, int tile, int lane
     return acc;
 }
 
+// Wide chunks: plain stores of a split's partial tile (k_splitk_epilogue reads them after the
+// kernel boundary).
+__device__ __forceinline__ void splitk_store_plain(const KArgs& a, const floatx4& acc, int tile, int split, int lane, int m0) {
+    const int c = lane & 15, sub = lane >> 4;
+    const int n = tile * kTile + c;
+    float* P = a.partial + (size_t)split * a.M * a.n_cols;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 4 * sub + r;
+        if (m < a.M) P[(size_t)m * a.n_cols + n] = acc[r];
+    }
+}
+
+// The S partials of the four rows m0 + 4 sub + r of column tile * 16 + c (this lane), summed in split
+// order; the loads of eight splits go out together.
+__device__ __forceinline__ floatx4 splitk_sum_plain(const KArgs& a, int tile, int lane, int m0) {
+    const int c = lane & 15, sub = lane >> 4;
+    const float* base = a.partial + tile * kTile + c;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < a.S; sp0 += 8) {
+        float v[4][8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 4 * sub + r < a.M ? m0 + 4 * sub + r : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[r][i] = sp0 + i < a.S ? base[((size_t)(sp0 + i) * a.M + m) * a.n_cols] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[r] += v[r][i];
+    }
+    return acc;
+}
+
+// Wide chunks, second kernel: one wave per (column tile, row tile of 16), lanes in the MFMA output
+// layout, so the epilogue is the GEMM's own.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_splitk_epilogue(KArgs a, int n_rt) {
+    const int lane = threadIdx.x & 63;
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= a.n_tiles * n_rt) return;   // uniform in the wave
+    const int tile = wv / n_rt, t = wv - tile * n_rt;
+    epilogue<EPI>(a, splitk_sum_plain(a, tile, lane, 16 * t), tile, lane, 16 * t);
+}
+
 // Workgroup (u, split) of the grid U x S and W = blockDim / 64 waves: split = the cross-workgroup
 // K split, u = its index among the U workgroups of that split. The W waves are T = W / KS tiles times KS parts
 // of the split's K range (wave w: tile slot w / KS, part w % KS). Item i of the workgroup covers
 // tiles (u + i U) T + 0 .. T - 1; the KS partial tiles of an item are summed in LDS in part order.
-// Rows >= M of the MFMA tile read arbitrary LDS data: they only feed output rows that are never
-// stored.
-template <int FMT, int EPI, int R>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemm(KArgs a) {
-    // dynamic LDS: [ring: W waves x ring_slots slots] [Q4_1: block sums S[sb_per_split * 4][16] fp32]
-    //              [A: M rows x lds_ld bf16] [KS > 1: partial tiles W x 64 lanes x 4 fp32]
+// Rows >= M of the MFMA tiles read arbitrary LDS data: they only feed output rows that are never
+// stored. MT row tiles of 16 (M <= 16 MT); MT > 1 workgroups hold at most 8 waves.
+template <int FMT, int EPI, int R, int MT>
+__global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2, 8))) void k_gemm(KArgs a) {
+    // dynamic LDS: [ring: W waves x ring_slots slots] [Q4_1: block sums S[sb_per_split * 4][16 MT] fp32]
+    //              [A: M rows x lds_ld bf16] [KS > 1: partial tiles W x 64 lanes x MT x 4 fp32]
+    constexpr int MP = 16 * MT;   // rows of the block-sum table
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
     constexpr int SLOT = FMT == W_Q4_1 ? kSlotQ4 : kSlotBf16;
     constexpr int LPS = loads_per_slot<FMT>();
@@ -390,7 +459,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     const int lds_ld = a.sb_per_split * kSuper + 8;
     uint8_t* ring = lds_raw + (size_t)wave * a.ring_slots * SLOT;
     float* Ss = (float*)(lds_raw + (size_t)nw * a.ring_slots * SLOT);
-    uint16_t* As = (uint16_t*)((uint8_t*)Ss + (FMT == W_Q4_1 ? (size_t)a.sb_per_split * 64 * 4 : 0));
+    uint16_t* As = (uint16_t*)((uint8_t*)Ss + (FMT == W_Q4_1 ? (size_t)a.sb_per_split * 4 * MP * 4 : 0));
     float* red = (float*)(As + (size_t)a.M * lds_ld);
 
     const int first = u * T;            // first tile of item 0
@@ -419,7 +488,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     // RMSNorm folded in: the loads of the first batch (the sums of squares of the rows, and per
     // thread piece p = 8 elements of K of up to 8 rows plus the gains) are issued before the ring,
     // so they are not queued behind the weight stream
-    __shared__ float rinv_s[kMaxRows];
+    __shared__ float rinv_s[kMaxGemmRows];
     const int pieces = nsb * (kSuper / 8);
     const int p0 = threadIdx.x;
     const int rows0 = min(a.M, 8);
@@ -483,6 +552,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
             q = wave_sum_dpp(q);
             if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
         }
+        // rows past 4 nw (wide chunks): the same sums, loaded now
+        for (int m = wave + 4 * nw; m < a.M; m += nw) {
+            float t4[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int i = lane + 64 * t;
+                t4[t] = i < a.n_ss ? a.ss_in[(size_t)m * a.n_ss + i] : 0.f;
+            }
+            float q = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+            for (int i = lane + 256; i < a.n_ss; i += 64) q += a.ss_in[(size_t)m * a.n_ss + i];
+            q = wave_sum_dpp(q);
+            if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
+        }
         lds_barrier();
         auto convert = [&](int p, int m0, int nrows, const u32x4& gv, const float4 (&xr)[8][2]) {
             float rvs[8];   // the eight rows' factors in registers before any LDS write of the batch
@@ -505,25 +587,28 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
                 if constexpr (FMT == W_Q4_1) {
                     // block sum of the 32 bf16 of block p / 4 (the quad of lanes holding its pieces)
                     const float bs = quad_sum(bf16x8_sum(o));
-                    if ((p & 3) == 0) Ss[(p >> 2) * kTile + m] = bs;
+                    if ((p & 3) == 0) Ss[(p >> 2) * MP + m] = bs;
                 }
             }
         };
+        // work items i = b pieces + p: piece p of the 8-row batch b, spread over all threads. Item
+        // p0 of batch 0, loaded above, is converted outside the loop (so the compiler's wait for
+        // its loads is not merged with the loop's). The four pieces of a block sit in four
+        // consecutive lanes of one iteration (pieces and the thread count are multiples of 4).
+        const int n_items = pieces * ((a.M + 7) >> 3);
         if (p0 < pieces) convert(p0, 0, rows0, gv0, xv);
-        // the remaining batches: rows 8.. of the first pieces, then further pieces
-        for (int p = p0; p < pieces; p += nthr) {
+        for (int i = p0 < pieces ? p0 + nthr : p0; i < n_items; i += nthr) {
+            const int b = i / pieces, p = i - b * pieces;
+            const int m0 = 8 * b, nrows = min(8, a.M - m0);
             const int k0 = g0 * kSuper + p * 8;
             const u32x4 gv = *(const u32x4*)(a.gain + k0);
-            for (int m0 = p == p0 ? 8 : 0; m0 < a.M; m0 += 8) {
-                const int nrows = min(8, a.M - m0);
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int m = m0 + (r < nrows ? r : nrows - 1);
-                    xv[r][0] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0);
-                    xv[r][1] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0 + 4);
-                }
-                convert(p, m0, nrows, gv, xv);
+            for (int r = 0; r < 8; ++r) {
+                const int m = m0 + (r < nrows ? r : nrows - 1);
+                xv[r][0] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0);
+                xv[r][1] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0 + 4);
             }
+            convert(p, m0, nrows, gv, xv);
         }
     } else {
         // this wave's activation copies have landed (they are older than its R ring slots)
@@ -533,18 +618,20 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     if (FMT == W_Q4_1 && !a.xsrc) {
         // block sums S[b][m] = sum of the 32 bf16 of block b of row m < M (the copied rows; the
         // normalised rows got theirs while being converted); the four pieces of a block sit in
-        // four consecutive lanes; eight rows' LDS reads are issued together
-        for (int p = threadIdx.x; p < pieces; p += nthr) {
-            for (int m0 = 0; m0 < a.M; m0 += 8) {
-                u32x4 o[8];
+        // four consecutive lanes; eight rows' LDS reads are issued together; work items as in the
+        // normalised staging (piece p of 8-row batch b)
+        const int n_items = pieces * ((a.M + 7) >> 3);
+        for (int i = threadIdx.x; i < n_items; i += nthr) {
+            const int b = i / pieces, p = i - b * pieces;
+            const int m0 = 8 * b;
+            u32x4 o[8];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) o[r] = lds_read16_untracked(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
-                wait_lds();
+            for (int r = 0; r < 8; ++r) o[r] = lds_read16_untracked(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
+            wait_lds();
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float bs = quad_sum(bf16x8_sum(o[r]));
-                    if (m0 + r < a.M && (p & 3) == 0) Ss[(p >> 2) * kTile + m0 + r] = bs;
-                }
+            for (int r = 0; r < 8; ++r) {
+                const float bs = quad_sum(bf16x8_sum(o[r]));
+                if (m0 + r < a.M && (p & 3) == 0) Ss[(p >> 2) * MP + m0 + r] = bs;
             }
         }
         lds_barrier();
@@ -552,14 +639,20 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
     if (items == 0) return;   // uniform in the workgroup
 
     const int m_a = lane & 15, sub = lane >> 4;
-    const uint16_t* As_row = As + (m_a < a.M ? m_a : 0) * lds_ld + sub * 8 + kb0 * kSuper;
-    const float* Ss_l = Ss + lane + 64 * kb0;   // superblock i of this wave's part: Ss_l[64 i]
+    int a_off[MT];   // this lane's A row in row tile t (rows >= M read row 0)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) a_off[t] = (16 * t + m_a < a.M ? 16 * t + m_a : 0) * lds_ld;
+    const uint16_t* As_k = As + sub * 8 + kb0 * kSuper;
+    // block sum of superblock i of this wave's part for row tile t: Ss_l[4 MP i + 16 t]
+    const float* Ss_l = Ss + m_a + sub * MP + 4 * MP * kb0;
 
     int s_off = 0;   // ring offset of the next slot to use
     uint32_t last = 0;   // split-K: bit i set where this wave arrived last on item i (reducer waves)
     for (int it = 0; it < items; ++it) {
         const int tile = first + it * stride + ts;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f}, accm = {0.f, 0.f, 0.f, 0.f};
+        floatx4 acc[MT], accm[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] = accm[t] = (floatx4){0.f, 0.f, 0.f, 0.f};
         if (it < my_items) {
 #pragma nounroll
             for (int gi = 0; gi < nkp; ++gi) {
@@ -567,7 +660,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
                 // superblock into the slot just used), so the oldest has landed at R - 1 younger
                 wait_vm<LPS * (R - 1)>();
                 uint8_t* slot = ring + s_off;
-                compute_slot<FMT>(slot, As_row + gi * kSuper, FMT == W_Q4_1 ? Ss_l[64 * gi] : 0.f, lane, acc, accm);
+                float s_val[MT];
+#pragma unroll
+                for (int t = 0; t < MT; ++t) s_val[t] = FMT == W_Q4_1 ? Ss_l[4 * MP * gi + 16 * t] : 0.f;
+                compute_slot<FMT, MT>(slot, As_k + gi * kSuper, a_off, s_val, lane, acc, accm);
                 wait_lds();   // the slot's LDS reads have returned before the refill overwrites it
                 const bool real = s_issue < total;
                 issue_slot<FMT>(a, real ? ib : ib_first, slot, lane);
@@ -578,29 +674,37 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
                 }
                 s_off = s_off + SLOT == R * SLOT ? 0 : s_off + SLOT;
             }
-            if constexpr (FMT == W_Q4_1) acc += accm;
+            if constexpr (FMT == W_Q4_1) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[t] += accm[t];
+            }
         }
         if (KS > 1) {
             // the KS parts of each tile meet in LDS; part 0 sums them in part order
-            *(floatx4*)(red + ((size_t)wave * 64 + lane) * 4) = acc;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) *(floatx4*)(red + (((size_t)wave * 64 + lane) * MT + t) * 4) = acc[t];
             lds_barrier();
             if (kp == 0) {
-                for (int q = 1; q < KS; ++q) acc += *(const floatx4*)(red + ((size_t)(wave + q) * 64 + lane) * 4);
+                for (int q = 1; q < KS; ++q)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) acc[t] += *(const floatx4*)(red + (((size_t)(wave + q) * 64 + lane) * MT + t) * 4);
             }
             lds_barrier();
         }
         if (kp != 0 || it >= my_items) continue;
-        if (S == 1) {
-            epilogue<EPI>(a, acc, tile, lane);
-        } else {
-            splitk_store(a, acc, tile, split, lane);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (16 * t >= a.M) break;
+            if (S == 1) epilogue<EPI>(a, acc[t], tile, lane, 16 * t);
+            else if (MT > 1) splitk_store_plain(a, acc[t], tile, split, lane, 16 * t);
+            else splitk_store(a, acc[t], tile, split, lane, 16 * t);
         }
     }
     wait_vm<0>();   // no copy into this wave's ring is left in flight
-    if (S > 1 && kp == 0 && my_items > 0) {
+    if (MT == 1 && S > 1 && kp == 0 && my_items > 0) {
         // a single item's residual rows are loaded now, in the shadow of the stores and the arrival
         floatx4 y_pre = {0.f, 0.f, 0.f, 0.f};
-        if (EPI == EPI_RESID && my_items == 1) y_pre = load_resid_rows(a, first + ts, lane);
+        if (EPI == EPI_RESID && MT == 1 && my_items == 1) y_pre = load_resid_rows(a, first + ts, lane, 0);
         // The hand-off relies on what gfx950 does with device-scope (sc1) relaxed atomics, not on
         // release/acquire fences: agent-scope release/acquire fences write back and invalidate the
         // whole L2 of the XCD (buffer_wbl2 / buffer_inv), which made each down launch 5 us slower.
@@ -626,32 +730,53 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8))) vo
         for (int it = 0; it < my_items; ++it) {
             if (!((last >> it) & 1u)) continue;
             const int tile = first + it * stride + ts;
-            epilogue<EPI>(a, splitk_sum(a, tile, lane), tile, lane, EPI == EPI_RESID && my_items == 1, y_pre);
+            for (int t = 0; t < MT && 16 * t < a.M; ++t)
+                epilogue<EPI>(a, splitk_sum(a, tile, lane, 16 * t), tile, lane, 16 * t,
+                              EPI == EPI_RESID && MT == 1 && my_items == 1, y_pre);
             if (lane == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-template <int FMT, int EPI, int R>
+template <int FMT, int EPI, int R, int MT>
 hipError_t launch_r(const KArgs& k, int grid, int waves, size_t lds, hipStream_t st) {
     const dim3 g2((unsigned)(grid / k.S), (unsigned)k.S);   // U workgroups per split, S splits
+    if (waves * 64 > (MT == 1 ? 1024 : 512)) return hipErrorInvalidValue;
     static bool attr_set = false;   // raise the dynamic LDS limit once per instantiation
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_gemm<FMT, EPI, R>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipError_t e = hipFuncSetAttribute((const void*)k_gemm<FMT, EPI, R, MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)kGemmLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemm<FMT, EPI, R>), g2, dim3(64 * waves), lds, st, k);
+    hipLaunchKernelGGL((k_gemm<FMT, EPI, R, MT>), g2, dim3(64 * waves), lds, st, k);
+    if constexpr (MT > 1) {
+        if (k.S > 1) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int n_rt = (k.M + 15) / 16;
+            const int waves_total = k.n_tiles * n_rt;
+            hipLaunchKernelGGL(k_splitk_epilogue<EPI>, dim3((waves_total + 3) / 4), dim3(256), 0, st, k, n_rt);
+        }
+    }
     return hipGetLastError();
 }
 
+// MT > 1 (wide chunks): Q4_1 only, rings of 2 superblocks (measured on MI355X at 64 rows: rings of
+// 4 leave room for fewer waves and the prefill ran 10% slower)
 template <int FMT, int EPI>
-hipError_t launch_fe(int R, const KArgs& k, int grid, int waves, size_t lds, hipStream_t st) {
-    switch (R) {
-        case 2: return launch_r<FMT, EPI, 2>(k, grid, waves, lds, st);
-        case 4: return launch_r<FMT, EPI, 4>(k, grid, waves, lds, st);
-        case 8: return launch_r<FMT, EPI, 8>(k, grid, waves, lds, st);
+hipError_t launch_fe(int R, int MT, const KArgs& k, int grid, int waves, size_t lds, hipStream_t st) {
+    if (MT == 1) {
+        switch (R) {
+            case 2: return launch_r<FMT, EPI, 2, 1>(k, grid, waves, lds, st);
+            case 4: return launch_r<FMT, EPI, 4, 1>(k, grid, waves, lds, st);
+            case 8: return launch_r<FMT, EPI, 8, 1>(k, grid, waves, lds, st);
+        }
+        return hipErrorInvalidValue;
+    }
+    if constexpr (FMT == W_Q4_1) {
+        if (R == 2 && MT == 2) return launch_r<FMT, EPI, 2, 2>(k, grid, waves, lds, st);
+        if (R == 2 && MT == 4) return launch_r<FMT, EPI, 2, 4>(k, grid, waves, lds, st);
     }
     return hipErrorInvalidValue;
 }
@@ -660,8 +785,9 @@ hipError_t launch_fe(int R, const KArgs& k, int grid, int waves, size_t lds, hip
 
 size_t gemm_lds_bytes(int fmt, int M, int sb, int waves, int ring, int KS) {
     const size_t slot = fmt == W_Q4_1 ? kSlotQ4 : kSlotBf16;
-    return (size_t)waves * ring * slot + (fmt == W_Q4_1 ? (size_t)sb * 256 : 0) + (size_t)M * ((size_t)sb * kSuper + 8) * 2 +
-           (KS > 1 ? (size_t)waves * 1024 : 0);
+    const int mt = gemm_row_tiles(M);
+    return (size_t)waves * ring * slot + (fmt == W_Q4_1 ? (size_t)sb * 4 * 16 * mt * 4 : 0) +
+           (size_t)M * ((size_t)sb * kSuper + 8) * 2 + (KS > 1 ? (size_t)waves * 1024 * mt : 0);
 }
 
 // Plan: choose the cross-workgroup K split S, the waves per workgroup W = T tiles x KS parts, the
@@ -674,6 +800,8 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
     GemmPlan best{};
     best.S = -1;
     const int tiles = L.n_run_tiles, G = L.w.G, M = L.M;
+    const int MT = gemm_row_tiles(M);
+    const int max_waves = MT == 1 ? 16 : 8;
     const int cus = L.n_cu > 0 ? L.n_cu : 256;
     const size_t slot_bytes = L.fmt == W_Q4_1 ? kSlotQ4 : kSlotBf16;
     const double bytes = (double)tiles * G * slot_bytes;
@@ -697,9 +825,15 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
         const double pieces = (double)sb * (kSuper / 8);
         const double staging = norm ? (1.0 + std::ceil(pieces / (64.0 * W)) * std::ceil(M / 8.0)) * l2_round : 0.3e-6;
         const double wsb = (double)ipw * spk;   // superblocks per wave
-        const double stream = lat + std::max({bytes / hbm, wsb * per_sb, std::ceil(wsb / R) * lat});
-        // the split-K hand-off: arrival, then the last arriver's loads of the Se partials
-        const double t = staging + stream + (KS > 1 ? ipw * reduce : 0.0) + (Se > 1 ? handoff + Se * per_split : 0.0);
+        // the dequantisation is shared by the MT row tiles; each adds its MFMAs and scale FMAs
+        const double sb_cost = per_sb * (1.0 + 0.35 * (MT - 1));
+        const double stream = lat + std::max({bytes / hbm, wsb * sb_cost, std::ceil(wsb / R) * lat});
+        // the split-K hand-off: arrival, then the last arriver's loads of the Se partials; wide
+        // chunks: the partials written and read back by the summing kernel, and its launch
+        const double split_t = Se == 1 ? 0.0
+                               : MT == 1 ? handoff + Se * per_split
+                                         : 2.5e-6 + 2.0 * Se * (double)M * tiles * kTile * 4.0 / 4.0e12;
+        const double t = staging + stream + (KS > 1 ? ipw * reduce : 0.0) + split_t;
         if (forced || t < best_t * 0.98) {
             best_t = t;
             best.S = Se;
@@ -720,7 +854,7 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
         prev_sb = sb;
         const int Se = (G + sb - 1) / sb;
         if (Se > 1 && ((size_t)Se * M * tiles * kTile > L.partial_floats || tiles > L.n_counters)) continue;
-        for (int W = 4; W <= 16; ++W)
+        for (int W = 4; W <= max_waves; ++W)
             for (int KS = 1; KS <= W; ++KS) {
                 if (W % KS) continue;
                 for (int R : {8, 4, 2}) {
@@ -740,7 +874,7 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
     // by the plan sweep at 1, 8 and 16 rows, the best plans split K into parts of about 27
     // superblocks and run 12 waves per workgroup, T tiles x 12 / T parts, with about one workgroup
     // per compute unit; the estimate above does not find them, so they are taken when they fit.
-    if (L.fmt == W_Q4_1 && !norm && G >= 64 && L.force_S <= 0) {
+    if (L.fmt == W_Q4_1 && !norm && G >= 64 && L.force_S <= 0 && MT == 1) {
         const int sb = 27, Se = (G + sb - 1) / sb;
         if ((size_t)Se * M * tiles * kTile <= L.partial_floats && tiles <= L.n_counters) {
             for (int T : {1, 2, 3, 4, 6, 12}) {
@@ -754,14 +888,15 @@ GemmPlan plan_gemm(const GemmLaunch& L) {
     // Many tiles over a short K range with the RMSNorm folded in (gate|up of the double-wide
     // layers, >= 8 tiles per compute unit): measured best with one item of T = tiles / n_cu tiles
     // per workgroup and one K part per wave (W = T), one workgroup per compute unit.
-    if (L.fmt == W_Q4_1 && norm && L.force_S <= 0 && tiles % cus == 0 && tiles / cus >= 8 && tiles / cus <= 16)
+    if (L.fmt == W_Q4_1 && norm && L.force_S <= 0 && MT == 1 && tiles % cus == 0 && tiles / cus >= 8 && tiles / cus <= 16)
         consider(1, G, tiles / cus, 1, 2, 1, true);
     // Between one and two tiles per compute unit with the RMSNorm folded in (the draft's q|k|v):
     // measured best with two tiles per workgroup, 8 waves in 4 K parts, at most one workgroup per
     // compute unit (9.4 against 11.1 us for one tile per workgroup of 5 waves).
-    if (L.fmt == W_Q4_1 && norm && L.force_S <= 0 && tiles > cus && tiles <= 2 * cus)
+    if (L.fmt == W_Q4_1 && norm && L.force_S <= 0 && MT == 1 && tiles > cus && tiles <= 2 * cus)
         consider(1, G, 8, 4, 2, 1, true);
-    if (L.force_S > 0 && L.force_R > 0 && L.force_ipw > 0 && L.force_W > 0 && L.force_KS > 0 && L.force_W % L.force_KS == 0) {
+    if (L.force_S > 0 && L.force_R > 0 && L.force_ipw > 0 && L.force_W > 0 && L.force_KS > 0 && L.force_W % L.force_KS == 0 &&
+        L.force_W <= max_waves) {
         const int sb = (G + L.force_S - 1) / L.force_S;
         const int Se = (G + sb - 1) / sb;
         if (Se == 1 || ((size_t)Se * M * tiles * kTile <= L.partial_floats && tiles <= L.n_counters))
@@ -791,7 +926,8 @@ static GemmPlan cached_plan(const GemmLaunch& L) {
 }
 
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
-    if (L.M < 1 || L.M > kMaxRows) return hipErrorInvalidValue;
+    if (L.M < 1 || L.M > kMaxGemmRows || (L.M > kMaxRows && L.fmt != W_Q4_1)) return hipErrorInvalidValue;
+    const int MT = gemm_row_tiles(L.M);
     const GemmPlan p = cached_plan(L);
     if (p.S < 1) return hipErrorInvalidValue;
     KArgs k;
@@ -841,13 +977,13 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
     if (L.epi == EPI_PLE && (!L.tokens || !L.ple || L.vocab < 1 || !L.out)) return hipErrorInvalidValue;
     if (L.fmt == W_Q4_1) {
         switch (L.epi) {
-            case EPI_STORE: return launch_fe<W_Q4_1, EPI_STORE>(p.R, k, p.grid, p.waves, p.lds, st);
-            case EPI_RESID: return launch_fe<W_Q4_1, EPI_RESID>(p.R, k, p.grid, p.waves, p.lds, st);
-            case EPI_SWIGLU: return launch_fe<W_Q4_1, EPI_SWIGLU>(p.R, k, p.grid, p.waves, p.lds, st);
-            case EPI_PLE: return launch_fe<W_Q4_1, EPI_PLE>(p.R, k, p.grid, p.waves, p.lds, st);
+            case EPI_STORE: return launch_fe<W_Q4_1, EPI_STORE>(p.R, MT, k, p.grid, p.waves, p.lds, st);
+            case EPI_RESID: return launch_fe<W_Q4_1, EPI_RESID>(p.R, MT, k, p.grid, p.waves, p.lds, st);
+            case EPI_SWIGLU: return launch_fe<W_Q4_1, EPI_SWIGLU>(p.R, MT, k, p.grid, p.waves, p.lds, st);
+            case EPI_PLE: return launch_fe<W_Q4_1, EPI_PLE>(p.R, MT, k, p.grid, p.waves, p.lds, st);
         }
     } else if (L.epi == EPI_STORE) {
-        return launch_fe<W_BF16, EPI_STORE>(p.R, k, p.grid, p.waves, p.lds, st);
+        return launch_fe<W_BF16, EPI_STORE>(p.R, MT, k, p.grid, p.waves, p.lds, st);
     }
     return hipErrorInvalidValue;
 }

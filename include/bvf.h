@@ -180,9 +180,10 @@ bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, fl
 
 /* Chunked prefill ([PR2303] "What changes": the batched body; "Proof": the state test's chunk arms):
  * the n tokens d_tokens[0..n) at positions P .. P+n-1 (P = positions held) go through every layer
- * in chunks of up to 16 rows, each chunk one batched pass over the packed weights, and are kept
- * (positions held = P + n; no commit needed). The head runs once, on the last chunk; d_last_logits
- * [vocab] fp32 (NULL allowed) receives the last row's logits. With bvf_snapshot_take /
+ * in chunks of up to 64 rows, each chunk one batched pass over the packed weights (every weight
+ * superblock feeds up to four 16-row MFMA tiles), and are kept (positions held = P + n; no commit
+ * needed). The head runs once, on the last row; d_last_logits [vocab] fp32 (NULL allowed) receives
+ * that row's logits. With bvf_snapshot_take /
  * bvf_restore this is a prefix cache: prefill a shared prefix once, snapshot, and restore it before
  * each continuation. Refuses n < 1 (BVF_E_INVALID), P + n > max_ctx (BVF_E_CAPACITY) and a pending
  * verify (BVF_E_STATE: commit it first); a refusal changes nothing. */
@@ -271,18 +272,22 @@ bvf_status bvf_draft_block_forward(bvf_model* draft, const bvf_model* target, co
 /* Dequantised fp32 weights of one loaded Q4_1 matrix, d_w [n_out][n_in]. */
 bvf_status bvf_q4_1_dequant(const bvf_model* m, int32_t layer, int32_t matrix, float* d_w);
 /* d_y [rows][n_out] fp32 = d_x [rows][n_in] bf16 times the matrix (the fused-matrix kernel, run on
- * the one matrix's columns; GATE and UP give their own halves). 1 <= rows <= 16. */
+ * the one matrix's columns; GATE and UP give their own halves). 1 <= rows <= 16 on a draft, <= 64 on
+ * a verify model (the prefill chunk width: 17..64 rows take the kernel's 2 or 4 row-tile form). */
 bvf_status bvf_q4_1_gemm(const bvf_model* m, int32_t layer, int32_t matrix, const uint16_t* d_x, int32_t rows,
                          float* d_y);
 /* One verify layer (the kernels of bvf_verify_batch) over d_x [rows][hidden] fp32, in place, at
- * positions P .. P + rows - 1 (P = positions held). An own layer writes its K/V rows into its plane
- * at those positions; the positions held do not change. For layer-by-layer parity tests. */
+ * positions P .. P + rows - 1 (P = positions held), 1 <= rows <= 64. An own layer writes its K/V rows
+ * into its plane at those positions; the positions held do not change. For layer-by-layer parity
+ * tests. */
 bvf_status bvf_layer_forward(bvf_model* m, int32_t layer, float* d_x, int32_t rows);
 /* Measurement: launches each GEMM class of the verify pass exactly as the pass does (same kernels,
  * plans and epilogues, into the model's scratch) for every layer, `iters` times, between two HIP
  * events recorded on the model's stream, and synchronises. Class 0 = fused q|k|v, 1 = o (+residual),
  * 2 = gate|up (+SwiGLU), 3 = down (+residual), 4 = the bf16 head. h_ms[5]: average milliseconds per
- * launch; h_bytes[5]: average weight bytes streamed per launch. Overwrites the scratch activations. */
+ * launch; h_bytes[5]: average weight bytes streamed per launch. 1 <= rows <= 64; above 16 rows (the
+ * prefill chunk widths) the head is not run and class 4 reports 0. Overwrites the scratch
+ * activations. */
 bvf_status bvf_time_gemms(bvf_model* m, int32_t rows, int32_t iters, float* h_ms, int64_t* h_bytes);
 /* Q4_1 bytes (packed image: 5 bits per weight) and bf16 head bytes one verify pass streams. */
 bvf_status bvf_pass_bytes(const bvf_model* m, int64_t* h_q4_1_bytes, int64_t* h_head_bytes);

@@ -69,6 +69,55 @@ def test_full_size_gemms_ragged_rows(full, layer, rows):
         assert err < GEMM_TOL
 
 
+@pytest.mark.parametrize("rows", [40, 64])
+@pytest.mark.parametrize("layer", [0, 5, 30])
+def test_full_size_gemms_wide_rows(full, layer, rows):
+    """Prefill chunk widths (40 rows: four row tiles, the last partly empty; 64: four full tiles):
+    every matrix of an own sliding (0), own full (5) and shared (30) layer at its real shape, rel-L1
+    per row within fp32 accumulation order."""
+    m, w, kv, g = full
+    for key, (n_out, n_in) in synth.layer_matrix_shapes(m, layer).items():
+        x = synth.bf16_normal(0, f"full.gemm.wide.{layer}.{key}.{rows}", (rows, n_in))
+        y = torch.empty((rows, n_out), dtype=torch.float32, device="cuda")
+        g.q4_1_gemm(layer, MAT[key], dev(x), rows, y)
+        ref = oracle.q4_1_matmul(w["layers"][layer][key], n_out, n_in, x)
+        err = rel_l1(host(y), ref)
+        print(f"layer {layer} {key} {n_out}x{n_in}, {rows} rows: rel-L1 {err:.2e}")
+        assert err < GEMM_TOL
+
+
+def test_full_size_prefill_64(full):
+    """One 64-row prefill chunk at full size on the 1024 cached positions: counts exact, the last
+    row's logits within the fixed 2e-3 bar of the oracle's batched rows, the appended K/V rows of
+    layer 0 to the GEMM's accumulation order and of the other own layers within the logits bar."""
+    m, w, kv, g = full
+    n = 64
+    snap = g.snapshot_take()
+    toks = synth.tokens(0, "full.prefill", n, m.vocab)
+    last = torch.empty(m.vocab, dtype=torch.float32, device="cuda")
+    print(f"[full prefill] {n} rows at {P} cached positions", flush=True)
+    g.prefill(dev(toks), last)
+    o = oracle.Model(m, w)
+    o.set_kv(kv, P)
+    rlg = o.verify_batch(toks)
+    o.commit_verify_rows(n)
+    assert g.positions_held() == o.held() == P + n
+    assert np.array_equal(g.plane_floats(), o.plane_floats())
+    err = rel_l1(host(last)[None, :], rlg[-1:])
+    tol = logits_bar(err, m, None, None, "full-size prefill of 64 rows: last row")
+    assert err < tol
+    for l in range(m.n_layers):
+        if not m.own(l):
+            continue
+        gp, op = g.get_kv(l, P + n).astype(np.float64), o.plane(l, P + n).astype(np.float64)
+        assert np.array_equal(gp[:P], op[:P]), f"layer {l}: cached rows changed"
+        kv_err = rel_l1(gp[P:].reshape(2 * n, -1), op[P:].reshape(2 * n, -1))
+        bar = GEMM_TOL if l == 0 else tol
+        assert kv_err < bar, f"layer {l}: {kv_err:.2e}"
+    g.restore(snap)
+    assert g.positions_held() == P
+
+
 @pytest.mark.parametrize("k", [8, 1, 5, 13])
 def test_full_size_verify(full, k):
     """The benchmark's step at full size (k = 8, 1) and at ragged row counts (5, 13): logits of every

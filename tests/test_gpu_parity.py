@@ -105,7 +105,7 @@ def test_dequant_bit_exact(mk):
             assert np.array_equal(host(out), ref), f"layer {l} {key}"
 
 
-@pytest.mark.parametrize("rows", [1, 3, 8, 16])
+@pytest.mark.parametrize("rows", [1, 3, 8, 16, 17, 32, 45, 64])
 @pytest.mark.parametrize("mk", [synth.tiny_two_width_model, ragged_model])
 def test_q4_1_gemm_parity(mk, rows):
     m = mk()
