@@ -3,16 +3,18 @@ library never imports this file).
 
 usage (from the repository root):
   python profile_summaries.py kernel-trace <rocprofv3 output dir> [kernels per pass, default 256]
-  python profile_summaries.py pmc-traffic <fetch dir> <write dir> <probe MiB> <gate|up bytes> <down bytes>
+  python profile_summaries.py pmc-traffic <fetch dir> <write dir> <probe MiB> <q|k|v bytes> <o bytes> <gate|up bytes> <down bytes>
   python profile_summaries.py mfma <rocprofv3 output dir>
 
 kernel-trace: the per-kernel statistics of a --kernel-trace --stats csv run, then the median of the
   first 7 verify passes (embed ... accept) with every kernel labelled by its place in the layer.
 pmc-traffic: two --pmc runs (FETCH_SIZE, then WRITE_SIZE) of bench.py --no-graph --copy-probe-mib N;
   each counter is scaled by what it reads for the copy probe (torch neg over N MiB: N MiB read, N MiB
-  written); the Q4_1 GEMM dispatches of the verify passes are classed by their place in each layer.
-mfma: a --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_INSTS_VALU_MFMA_MOPS_F32: per Q4_1 GEMM
-  class, the MFMA work per launch (512 flops per MOPS unit, as rocprofv3's MfmaFlops metric counts
+  written); the Q4_1 GEMM dispatches of the verify passes are classed by their place in each layer
+  (the byte arguments: each class's algorithmic bytes per launch, bench.py's gemm_alg_bytes), and
+  the whole Q4_1 stream of a pass (one launch of each class per layer) is summed from the classes.
+mfma: a --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_INSTS_VALU_MFMA_MOPS_F32 (of bench.py, or
+  of bench.py --prefill N for the 64-row chunks): per Q4_1 GEMM class, the MFMA work per launch (512 flops per MOPS unit, as rocprofv3's MfmaFlops metric counts
   it), its rate over the dispatches' durations and the fraction of the 2.5 PFLOP/s dense bf16 peak.
 """
 import collections
@@ -69,7 +71,8 @@ def kernel_trace(ARGV):
 
 def pmc_traffic(ARGV):
     fetch_dir, write_dir, probe_mib = ARGV[1], ARGV[2], int(ARGV[3])
-    alg = {"gate_up": float(ARGV[4]), "down": float(ARGV[5])}   # algorithmic bytes per launch (class average)
+    # algorithmic bytes per launch (class average)
+    alg = {"qkv": float(ARGV[4]), "o": float(ARGV[5]), "gate_up": float(ARGV[6]), "down": float(ARGV[7])}
     def load(d, counter):
         f = glob.glob(f"{d}/**/*counter_collection.csv", recursive=True)[0]
         rows = [r for r in csv.DictReader(open(f)) if r['Counter_Name'] == counter]
@@ -80,18 +83,24 @@ def pmc_traffic(ARGV):
             else: by[did] = [r['Kernel_Name'], float(r['Counter_Value'])]
         return by
     def classify(by):
+        # q|k|v: the store-epilogue GEMM right before an attention; o: the residual GEMM right
+        # before a gate|up; gate|up: the SwiGLU-epilogue GEMM; down: the residual GEMM right after it
         seq = list(by.items())
         cls = collections.defaultdict(list)
         probe = []
-        prev = None
-        for did, (name, v) in seq:
+        for i, (did, (name, v)) in enumerate(seq):
+            nxt = seq[i + 1][1][0] if i + 1 < len(seq) else ''
+            prev = seq[i - 1][1][0] if i > 0 else ''
             if 'elementwise' in name and 'neg' in name.lower() and len(probe) < 3:
                 probe.append(v)
             if 'k_gemm<0, 2,' in name:
                 cls['gate_up'].append(v)
-            elif 'k_gemm<0, 1,' in name and prev is not None and 'k_gemm<0, 2,' in prev:
+            elif 'k_gemm<0, 1,' in name and 'k_gemm<0, 2,' in prev:
                 cls['down'].append(v)
-            prev = name
+            elif 'k_gemm<0, 1,' in name and 'k_gemm<0, 2,' in nxt:
+                cls['o'].append(v)
+            elif 'k_gemm<0, 0,' in name and 'k_attention' in nxt:
+                cls['qkv'].append(v)
         return probe, cls
     out = []
     sh = hashlib.sha256(open('block_verify_forward_amd/csrc/gemm.hip', 'rb').read()).hexdigest()
@@ -104,15 +113,21 @@ def pmc_traffic(ARGV):
         for c, v in cls.items():
             kib = sum(v) / len(v)
             res.setdefault(c, {})[counter] = (len(v), kib, kib * scale * 1024)
-    for c in ("gate_up", "down"):
+    pass_traffic = pass_alg = 0.0
+    for c in ("qkv", "o", "gate_up", "down"):
         f, w = res[c]['FETCH_SIZE'], res[c]['WRITE_SIZE']
         tot = f[2] + w[2]
+        pass_traffic += tot
+        pass_alg += alg[c]
         out.append(f"\n{c} dispatches: {f[0]}")
         out.append(f"  FETCH_SIZE {f[1]:.1f} KiB per dispatch -> {f[2]/1e6:.2f} MB")
         out.append(f"  WRITE_SIZE {w[1]:.1f} KiB per dispatch -> {w[2]/1e6:.2f} MB")
         out.append(f"  algorithmic bytes per launch (class average of the Q4_1 image, 0.625 B per weight): {alg[c]/1e6:.2f} MB")
         out.append(f"  traffic / algorithmic: {tot/alg[c]:.3f}")
         out.append(f"traffic_bytes_per_launch.{c}: {int(tot)}")
+    out.append("\nwhole Q4_1 stream (one launch of each class per layer, averaged over the 4 launches):")
+    out.append(f"  traffic / algorithmic: {pass_traffic / pass_alg:.3f}")
+    out.append(f"traffic_bytes_per_launch.all: {int(pass_traffic / 4)}")
     out.append(f"\ngemm_hip_sha256: {sh}")
     print("\n".join(out))
 
@@ -125,9 +140,16 @@ def mfma(ARGV):
     for r in sorted(csv.DictReader(open(f)), key=lambda r: int(r["Dispatch_Id"])):
         e = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    seq = list(by.values())
+    allseq = list(by.values())
     # the GEMMs of a layer: q|k|v (store epilogue, followed by attention), o (residual, before
-    # gate|up), gate|up (SwiGLU epilogue), down (residual, right after gate|up)
+    # gate|up), gate|up (SwiGLU epilogue), down (residual, right after gate|up). Wide launches
+    # (prefill chunks) are each followed by their split-sum kernel (k_splitk_epilogue): it is
+    # skipped when looking at neighbours, and its duration is reported beside the GEMM's.
+    seq = [e for e in allseq if "k_splitk_epilogue" not in e["name"]]
+    follow = {}
+    for i, e in enumerate(allseq):
+        if "k_gemm" in e["name"] and i + 1 < len(allseq) and "k_splitk_epilogue" in allseq[i + 1]["name"]:
+            follow[id(e)] = allseq[i + 1]["ns"]
     cls = collections.defaultdict(list)
     for i, e in enumerate(seq):
         n = e["name"]
@@ -139,14 +161,18 @@ def mfma(ARGV):
                 cls["o"].append(seq[i - 1])
         elif "k_gemm<0, 0," in n and i + 1 < len(seq) and "k_attention" in seq[i + 1]["name"]:
             cls["q|k|v"].append(e)
-    print(f"{'class':8s} {'dispatches':>10s} {'MFMA GFLOP/launch':>18s} {'TFLOP/s':>9s} {'% of bf16 peak':>15s}")
+    print(f"{'class':8s} {'dispatches':>10s} {'MFMA GFLOP/launch':>18s} {'GEMM us':>8s} {'sum us':>7s} {'TFLOP/s':>9s} {'% of bf16 peak':>15s}")
     for c in ("q|k|v", "o", "gate|up", "down"):
         v = cls[c]
         if not v:
             continue
         fl = sum((e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + e["SQ_INSTS_VALU_MFMA_MOPS_F32"]) * 512 for e in v)
         ns = sum(e["ns"] for e in v)
-        print(f"{c:8s} {len(v):10d} {fl / len(v) / 1e9:18.3f} {fl / ns / 1e3:9.1f} {100 * fl / (ns * 1e-9) / PEAK_BF16:15.2f}")
+        ns_sum = sum(follow.get(id(e), 0) for e in v)
+        print(f"{c:8s} {len(v):10d} {fl / len(v) / 1e9:18.3f} {ns / len(v) / 1e3:8.2f} {ns_sum / len(v) / 1e3:7.2f} "
+              f"{fl / ns / 1e3:9.1f} {100 * fl / (ns * 1e-9) / PEAK_BF16:15.2f}")
+    print("(TFLOP/s: the MFMA work over the GEMM kernel's own duration; 'sum us': the split-sum kernel that follows a wide")
+    print(" launch, 0 where there is none)")
 
 
 if __name__ == "__main__":
