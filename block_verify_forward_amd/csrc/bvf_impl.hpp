@@ -12,7 +12,7 @@ constexpr int kMaxGemmRows = 64;  // prefill chunks: up to 4 row tiles share eac
 constexpr int gemm_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 constexpr int kTile = 16;         // output columns per MFMA tile
 constexpr int kSuper = 128;       // K per superblock = 4 Q4_1 blocks of 32
-constexpr int kAttnMaxChunks = 128;   // key chunks per (query tile, KV head) merged by the combine
+constexpr int kAttnMaxChunks = 256;   // key chunks per (query tile, KV head) merged by the combine
 
 // A packed Q4_1 (or bf16) weight image, column-tiled for the small-M GEMM.
 //   Q4_1: codes  [n_tiles][G][64 lanes][4 x u32]: lane = sub * 16 + c holds, for block j of the

@@ -349,7 +349,6 @@ struct AttnK {
     int causal, pos0, window, ctx_lo, ctx_hi;
     int np0, np1, sp, r_lo, r_hi;   // new rows: positions [np0, np1); row of p: p < sp ? r_lo + p - np0 : r_hi + p - sp
     int key_lo, n_keys, spw, n_chunks;   // keys [key_lo, key_lo + n_keys); spw sub-chunks per workgroup
-    int nst;                 // LDS stages of the kernel (1: spw == 1)
     const int64_t* dpos;     // causal graph replays: positions held read here (see bind_positions)
     float* part;             // [n_qt][nkv][n_chunks][16][hd + 2] partials
     int* counters;           // [n_qt * nkv]
@@ -394,10 +393,14 @@ __device__ __forceinline__ float head_ss(const AttnK& a, int r, int c0, int hd) 
 
 // Keys per sub-chunk: the K and V tiles of a sub-chunk take 16 KB each in LDS with fp32 planes (16
 // keys at hd 256: small chunks spread the K/V reads over many compute units), at least one 16-key
-// MFMA block. With two stages and bf16 planes at hd >= 128 a sub-chunk takes twice the keys in the
-// same bytes, so a workgroup that streams many sub-chunks keeps as many bytes in flight.
-__host__ __device__ constexpr int attn_ck(int hd, bool kvb, int nst) {
-    return (kvb && nst == 2 && hd >= 128 ? 2 : 1) * (4096 / hd > 16 ? 4096 / hd : 16);
+// MFMA block.
+__host__ __device__ constexpr int attn_ck(int hd) { return 4096 / hd > 16 ? 4096 / hd : 16; }
+
+// LDS of k_attention<hd, kvb>: the K and V tiles (padded rows), the query rows, the partial
+// scores and the probabilities (the arrays declared in the kernel).
+constexpr size_t attn_lds_bytes(int hd, bool kvb) {
+    const size_t ck = attn_ck(hd), eb = kvb ? 2 : 4;
+    return ck * (hd + 16 / eb) * eb + ck * (hd + 16) * eb + (size_t)16 * (hd + 4) * 4 + (size_t)2 * 4 * 16 * (ck + 1) * 4;
 }
 
 // Tile element of the K/V planes: fp32, or (KVB) bf16 values widened exactly where they are read.
@@ -421,19 +424,17 @@ __device__ __forceinline__ void store_bf16_vec(uint16_t* p, const float* v) {
     }
 }
 
-// One workgroup per (key chunk, KV head, tile of 16 query vectors). The chunk's keys go through LDS
-// in sub-chunks of CK keys. NST = 2: two stages, the copies of sub-chunk i + 1 are in flight while
-// sub-chunk i is scored and weighted; the stages are distinct LDS arrays, so the compiler's
-// wait-count insertion sees that reads of one stage do not depend on copies into the other.
-// NST = 1: one sub-chunk per workgroup, one stage (half the LDS, twice the workgroups per CU).
+// One workgroup per (key chunk, KV head, tile of 16 query vectors). The chunk's keys go through one
+// LDS stage in sub-chunks of CK keys, one after another; the stage is small enough for two or more
+// workgroups per compute unit, so one workgroup's copies are in flight while another computes (a
+// second stage inside the workgroup left one workgroup per compute unit and ran slower).
 // KVB: the planes hold bf16 values; the tiles keep them as bf16 and the reads widen them (exact),
 // and new rows are written rounded to the plane and the tile, so every K/V value the scores and
 // PV see is the stored one.
-template <int HD, bool KVB, int NST>
+template <int HD, bool KVB>
 __global__ __launch_bounds__(256) void k_attention(AttnK a) {
-    static_assert(NST == 1 || NST == 2, "one or two stages");
     using TT = typename KVElem<KVB>::T;
-    constexpr int CK = attn_ck(HD, KVB, NST);   // keys per sub-chunk
+    constexpr int CK = attn_ck(HD);      // keys per sub-chunk
     constexpr int KB = CK / 16;          // 16-key blocks per sub-chunk
     constexpr int DW = HD / 4;           // dims owned by each wave (scores over them, then O for them)
     constexpr int H2 = HD / 2;
@@ -447,8 +448,6 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     constexpr int LD = HD + 4;           // query rows
     __shared__ __attribute__((aligned(16))) TT K0[CK][LDK];
     __shared__ __attribute__((aligned(16))) TT V0[CK][LDV];
-    __shared__ __attribute__((aligned(16))) TT K1[NST == 2 ? CK : 1][LDK];
-    __shared__ __attribute__((aligned(16))) TT V1[NST == 2 ? CK : 1][LDV];
     __shared__ __attribute__((aligned(16))) float Qs[16][LD];
     __shared__ float Sp[4][16][CK + 1];   // per-wave partial scores (over the wave's dims)
     __shared__ float Ps[4][16][CK + 1];   // per-wave probabilities
@@ -628,11 +627,10 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
 
-    // one sub-chunk [c0, c0 + CK) from stage (Kc, Vc); the next one's copies go to (Kn, Vn)
-    auto sub_chunk = [&](int c0, TT (*Kc)[LDK], TT (*Vc)[LDV], TT (*Kn)[LDK], TT (*Vn)[LDV]) __attribute__((always_inline)) {
+    // one sub-chunk [c0, c0 + CK) from the stage (Kc, Vc)
+    auto sub_chunk = [&](int c0, TT (*Kc)[LDK], TT (*Vc)[LDV]) __attribute__((always_inline)) {
         const int c1 = min(wk1, c0 + CK);
-        // 2. this sub-chunk's K/V copies (and its first new rows, loaded before them) have landed,
-        //    and every wave is past the previous sub-chunk (whose stage the next copies overwrite)
+        // 2. this sub-chunk's K/V copies (and its first new rows, loaded before them) have landed
         int p_lo, p_hi;
         new_rows(c0, p_lo, p_hi);
         __builtin_amdgcn_s_waitcnt(0);
@@ -647,14 +645,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
                     store_row(pr + ri, c0, Kc, Vc);
                 }
         }
-        // the next sub-chunk's new-row loads and copies go out before this one is computed
-        if (c0 + CK < wk1) {
-            int n_lo, n_hi;
-            new_rows(c0 + CK, n_lo, n_hi);
-            if (n_lo + ri < n_hi) load_row(n_lo + ri);
-            issue_kv(Kn, Vn, c0 + CK);
-        }
-        if (p_lo < p_hi) lds_barrier();   // the new rows are in the stage (the copies stay in flight)
+        if (p_lo < p_hi) lds_barrier();   // the new rows are in the stage
 
         // 4. partial scores over this wave's dims: S[qv][key] for the CK keys
         floatx4 sacc[KB];
@@ -749,13 +740,17 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             }
         }
     };
-    if constexpr (NST == 2) {
-        for (int c0 = wk0; c0 < wk1; c0 += 2 * CK) {
-            sub_chunk(c0, K0, V0, K1, V1);
-            if (c0 + CK < wk1) sub_chunk(c0 + CK, K1, V1, K0, V0);
+    // the sub-chunks one after another (the first one's copies went out above); a barrier keeps the
+    // next copies from overwriting the stage before every wave has read it
+    for (int c0 = wk0; c0 < wk1; c0 += CK) {
+        if (c0 != wk0) {
+            __syncthreads();
+            int n_lo, n_hi;
+            new_rows(c0, n_lo, n_hi);
+            if (n_lo + ri < n_hi) load_row(n_lo + ri);
+            issue_kv(K0, V0, c0);
         }
-    } else if (wk0 < wk1) {
-        sub_chunk(wk0, K0, V0, K0, V0);   // the only sub-chunk: no next copies are issued
+        sub_chunk(c0, K0, V0);
     }
 
     // 7. this workgroup's partial: unnormalised O (each wave its dims), the running max and sum
@@ -1110,22 +1105,19 @@ AttnK make_attn(const Attn& x) {
         const int plo = (x.window > 0 && x.pos_plan - x.window + 1 > 0) ? x.pos_plan - x.window + 1 : 0;
         plan_keys = std::max(plan_keys, x.pos_plan + x.M - plo);
     }
-    // One sub-chunk per workgroup (one LDS stage, two workgroups per compute unit) while that takes
-    // at most kAttnMaxChunks chunks and 768 workgroups. Longer key ranges: workgroups of spw
-    // sub-chunks through two stages; their LDS leaves one workgroup per compute unit, so the chunks
-    // are planned to run in a single round of at most n_cu workgroups.
+    // One sub-chunk per workgroup while that takes at most kAttnMaxChunks chunks and 768
+    // workgroups. Longer key ranges: workgroups of spw sub-chunks, planned to run in a single round
+    // of as many workgroups per compute unit as the LDS holds, at most two (the kernel's 164-216
+    // VGPRs leave two waves per SIMD; one workgroup's copies are in flight while another computes).
     const int tiles = a.n_qt * a.nkv;
-    const int ck1 = attn_ck(x.hd, x.kv_bf16 != 0, 1);
-    const int subs1 = (plan_keys + ck1 - 1) / ck1;
-    if (subs1 <= kAttnMaxChunks && (long)subs1 * tiles <= 768) {
-        a.nst = 1;
+    const int ck = attn_ck(x.hd);
+    const int subs = (plan_keys + ck - 1) / ck;
+    if (subs <= kAttnMaxChunks && (long)subs * tiles <= 768) {
         a.spw = 1;
-        a.n_chunks = subs1;
+        a.n_chunks = subs;
     } else {
-        a.nst = 2;
-        const int ck2 = attn_ck(x.hd, x.kv_bf16 != 0, 2);
-        const int subs = (plan_keys + ck2 - 1) / ck2;
-        const int nch = std::max(1, std::min(kAttnMaxChunks, x.n_cu / tiles));
+        const int per_cu = std::max(1, std::min(2, (int)(kLdsPerCu / attn_lds_bytes(x.hd, x.kv_bf16 != 0))));
+        const int nch = std::max(1, std::min(kAttnMaxChunks, per_cu * x.n_cu / tiles));
         a.spw = (subs + nch - 1) / nch;
         a.n_chunks = (subs + a.spw - 1) / a.spw;
     }
@@ -1142,16 +1134,10 @@ size_t attn_part_floats_needed(const Attn& x) {
 }
 
 namespace {
-// one stage when every workgroup takes a single sub-chunk (spw == 1), two otherwise
 template <int HD>
 void launch_attn(const AttnK& a, int grid, int cgrid, hipStream_t st) {
-    if (a.nst == 2) {
-        if (a.kv_bf16) hipLaunchKernelGGL((k_attention<HD, true, 2>), dim3(grid), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((k_attention<HD, false, 2>), dim3(grid), dim3(256), 0, st, a);
-    } else {
-        if (a.kv_bf16) hipLaunchKernelGGL((k_attention<HD, true, 1>), dim3(grid), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((k_attention<HD, false, 1>), dim3(grid), dim3(256), 0, st, a);
-    }
+    if (a.kv_bf16) hipLaunchKernelGGL((k_attention<HD, true>), dim3(grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_attention<HD, false>), dim3(grid), dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_attn_combine<HD>, dim3(cgrid), dim3(256), 0, st, a);
 }
 }  // namespace
