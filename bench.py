@@ -223,6 +223,7 @@ def run_loop(args):
         "tokens_per_target_pass": round(len(toks) / rounds, 3),
         "mean_accepted_drafts": round(float(np.mean(loop.accepted)), 3),
         "ms_per_round": round(ms / rounds, 4),
+        "verify_graph_captures": T.graph_captures(),
     }
     print(json.dumps(res), flush=True)
 
@@ -261,6 +262,21 @@ def run_prefill(args):
         assert g.positions_held() == args.ctx + args.prefill
         g.restore(snap)
     ms = float(np.median(times))
+    # snapshot costs at ctx + prefill positions: a first take allocates, an update and a restore copy
+    g.prefill(toks, last)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    s2 = g.snapshot_take()
+    take_ms = (time.time() - t0) * 1e3
+    t0 = time.time()
+    g.snapshot_update(s2)
+    update_ms = (time.time() - t0) * 1e3
+    t0 = time.time()
+    g.restore(s2)
+    restore_ms = (time.time() - t0) * 1e3
+    snap_mb = float(np.sum(s2.floats())) * (2 if args.kv_bf16 else 4) / 1e6
+    del s2
+    g.restore(snap)
     chunk = 64
     n_chunks = (args.prefill + chunk - 1) // chunk
     cls_ms, cls_bytes = g.time_gemms(chunk, 3)
@@ -289,6 +305,8 @@ def run_prefill(args):
         "chunks": n_chunks,
         "ms_per_chunk": round(ms / n_chunks, 4),
         "gemm_64_rows": gemm,
+        "snapshot_ms": {"positions": args.ctx + args.prefill, "mb": round(snap_mb, 1), "take": round(take_ms, 3),
+                        "update": round(update_ms, 3), "restore": round(restore_ms, 3)},
     }
     print(json.dumps(res), flush=True)
 

@@ -71,6 +71,7 @@ SIGNATURES = {
     "bvf_steer_logits": (_I32, [_P, _P, _I32, _P, _P]),
     "bvf_commit_verify_rows": (_I32, [_P, _I32]),
     "bvf_snapshot_take": (_I32, [_P, ctypes.POINTER(_P)]),
+    "bvf_snapshot_update": (_I32, [_P, _P]),
     "bvf_restore": (_I32, [_P, _P]),
     "bvf_snapshot_floats": (_I32, [_P, _P, _I32]),
     "bvf_snapshot_free": (None, [_P]),
@@ -295,6 +296,9 @@ class Model:
         h = ctypes.c_void_p()
         _check(lib().bvf_snapshot_take(self.h, ctypes.byref(h)))
         return Snapshot(h, self.m.n_layers)
+
+    def snapshot_update(self, snap: "Snapshot"):
+        _check(lib().bvf_snapshot_update(self.h, snap.h))
 
     def restore(self, snap: "Snapshot"):
         _check(lib().bvf_restore(self.h, snap.h))

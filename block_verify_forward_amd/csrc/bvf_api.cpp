@@ -168,6 +168,7 @@ struct bvf_snapshot {
     std::vector<int> shared;
     std::vector<int> cap;        // position slots of each own plane (ring planes: window + 16)
     std::vector<int64_t> kept;   // positions kept of each own plane (ring planes: the last min(held, window))
+    std::vector<int64_t> rows;   // rows allocated for each own plane (>= kept; bvf_snapshot_update reuses them)
     std::vector<float*> data;    // kept rows of each own plane, in position order
 };
 
@@ -926,6 +927,7 @@ bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out) {
         s->shared.push_back(L.plane ? 0 : 1);
         s->cap.push_back(L.plane ? L.cap : 0);
         s->kept.push_back(L.plane ? plane_keep(L, m->held) : 0);
+        s->rows.push_back(s->kept.back());
         s->data.push_back(nullptr);
     }
     for (int l = 0; l < m->d.n_layers; ++l) {
@@ -952,8 +954,10 @@ bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out) {
     return ok();
 }
 
-bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s) {
-    if (!m || !s) return fail(BVF_E_INVALID, "NULL argument");
+namespace {
+// A snapshot fits a model when the layer count, the widths, own/shared, the plane capacities and the
+// stored element size agree.
+bvf_status snapshot_fits(const bvf_model* m, const bvf_snapshot* s) {
     if (s->n_layers != m->d.n_layers)
         return fail(BVF_E_INVALID, "snapshot of %d layers, model of %d", s->n_layers, m->d.n_layers);
     for (int l = 0; l < m->d.n_layers; ++l) {
@@ -963,11 +967,48 @@ bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s) {
             return fail(BVF_E_INVALID, "layer %d: snapshot plane of %d positions, model plane of %d (ring and linear planes differ)",
                         l, s->cap[l], m->L[l].plane ? m->L[l].cap : 0);
     }
-    if (s->held > m->d.max_ctx) return fail(BVF_E_CAPACITY, "snapshot holds more positions than max_ctx");
     if (s->kv_elem != (m->d.kv_bf16 ? 2 : 4)) return fail(BVF_E_INVALID, "snapshot of %s planes, model of %s planes",
                                                            s->kv_elem == 2 ? "bf16" : "fp32", m->d.kv_bf16 ? "bf16" : "fp32");
+    return BVF_OK;
+}
+}  // namespace
+
+bvf_status bvf_snapshot_update(bvf_model* m, bvf_snapshot* s) {
+    if (!m || !s) return fail(BVF_E_INVALID, "NULL argument");
+    if (m->pending >= 0)
+        return fail(BVF_E_STATE, "snapshot while a verify of %d rows is pending: commit it first", m->pending);
+    bvf_status st = snapshot_fits(m, s);
+    if (st) return st;
+    std::vector<int64_t> kept(m->d.n_layers, 0);
     for (int l = 0; l < m->d.n_layers; ++l) {
-        if (s->shared[l] || !s->data[l]) continue;
+        if (!m->L[l].plane) continue;
+        kept[l] = plane_keep(m->L[l], m->held);
+        if (kept[l] > s->rows[l])
+            return fail(BVF_E_CAPACITY, "layer %d: %lld positions to keep, the snapshot holds room for %lld", l,
+                        (long long)kept[l], (long long)s->rows[l]);
+    }
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        if (kept[l] == 0) continue;
+        const Layer& L = m->L[l];
+        const size_t row = (size_t)2 * L.w * s->kv_elem;
+        HIP_TRY(for_slot_runs(L, m->held - kept[l], m->held, [&](int64_t slot, int64_t first, int64_t n) {
+            return hipMemcpyAsync((uint8_t*)s->data[l] + (size_t)first * row, (const uint8_t*)L.plane + (size_t)slot * row,
+                                  (size_t)n * row, hipMemcpyDeviceToDevice, m->st);
+        }));
+    }
+    HIP_TRY(hipStreamSynchronize(m->st));
+    s->held = m->held;
+    s->kept = kept;
+    return ok();
+}
+
+bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s) {
+    if (!m || !s) return fail(BVF_E_INVALID, "NULL argument");
+    bvf_status st = snapshot_fits(m, s);
+    if (st) return st;
+    if (s->held > m->d.max_ctx) return fail(BVF_E_CAPACITY, "snapshot holds more positions than max_ctx");
+    for (int l = 0; l < m->d.n_layers; ++l) {
+        if (s->shared[l] || !s->data[l] || s->kept[l] == 0) continue;
         const Layer& L = m->L[l];
         const size_t row = (size_t)2 * L.w * s->kv_elem;
         HIP_TRY(for_slot_runs(L, s->held - s->kept[l], s->held, [&](int64_t slot, int64_t first, int64_t n) {

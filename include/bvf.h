@@ -250,6 +250,13 @@ bvf_status bvf_commit_verify_rows(bvf_model* m, int32_t n);
  * otherwise. Restore refuses a snapshot whose layer count or widths differ, and clears a pending
  * verify. snapshot_floats: floats kept per layer (0 on shared layers). */
 bvf_status bvf_snapshot_take(bvf_model* m, bvf_snapshot** out);
+/* Re-take a snapshot of the model's committed state into an existing snapshot of the same model
+ * shape (layers, widths, plane capacities, stored element size), allocating nothing: each own
+ * plane's kept rows must fit the rows the snapshot was first taken with, else BVF_E_CAPACITY; a
+ * pending verify is BVF_E_STATE; a shape mismatch BVF_E_INVALID. A refusal leaves the snapshot
+ * unchanged. For prefix caches that refresh their snapshot (a snapshot taken at the largest state
+ * holds any smaller one). */
+bvf_status bvf_snapshot_update(bvf_model* m, bvf_snapshot* s);
 bvf_status bvf_restore(bvf_model* m, const bvf_snapshot* s);
 bvf_status bvf_snapshot_floats(const bvf_snapshot* s, int64_t* h_out, int32_t n);
 void bvf_snapshot_free(bvf_snapshot* s);

@@ -126,3 +126,53 @@ def test_prefill_refusals(setup):
     with pytest.raises(bvf.BvfError):          # beyond max_ctx
         g.prefill(dev(big))
     assert g.positions_held() == P0 + 8       # refusals change nothing
+
+
+def test_snapshot_update_reuses_the_snapshot(setup):
+    """bvf_snapshot_update refreshes a snapshot in place: take one at 24 + 60 positions, prefill 20
+    more, update it at 24 + 80 positions -- refused (more rows than it was taken with, snapshot
+    unchanged) --, restore it, cut back by a verify and commit(0) to a smaller state, update it
+    there, prefill something else, restore: the planes and the next verify equal those of a model
+    that reached the same state directly (bit for bit), counts follow the update; refused while a
+    verify is pending; on ring planes as well."""
+    import dataclasses
+    for ring in (0, 1):
+        m, w, kv = setup
+        m = dataclasses.replace(m, kv_ring=ring)
+        g = gpu_model(m, w, kv)
+        pre = synth.tokens(0, "upd.pre", 60, m.vocab)
+        g.prefill(dev(pre))
+        snap = g.snapshot_take()
+        f60 = snap.floats().copy()
+        g.prefill(dev(synth.tokens(1, "upd.more", 20, m.vocab)))
+        with pytest.raises(bvf.BvfError) as e:            # the full layers' planes outgrew the snapshot
+            g.snapshot_update(snap)
+        assert e.value.status == bvf.BVF_E_CAPACITY
+        assert np.array_equal(snap.floats(), f60)
+        g.restore(snap)
+        assert g.positions_held() == P0 + 60
+        # a smaller committed state: 24 + 45 via a fresh model's prefill of the first 45 tokens
+        ref = gpu_model(m, w, kv)
+        ref.prefill(dev(pre[:45]))
+        small = gpu_model(m, w, kv)
+        small.prefill(dev(pre[:45]))
+        small.snapshot_update(snap)                        # taken by another model of the same shape
+        assert np.array_equal(snap.floats(), small.plane_floats())
+        lg = torch.empty((8, m.vocab), dtype=torch.float32, device="cuda")
+        small.verify_batch(dev(synth.tokens(2, "upd.v", 8, m.vocab)), lg, None)
+        with pytest.raises(bvf.BvfError) as e:             # a verify is pending
+            small.snapshot_update(snap)
+        assert e.value.status == bvf.BVF_E_STATE
+        small.commit_verify_rows(0)
+        g.prefill(dev(synth.tokens(3, "upd.other", 5, m.vocab)))
+        g.restore(snap)
+        assert g.positions_held() == ref.positions_held() == P0 + 45
+        assert np.array_equal(g.plane_floats(), ref.plane_floats())
+        for l in range(m.n_layers):
+            if m.own(l):
+                assert np.array_equal(g.get_kv(l, P0 + 45), ref.get_kv(l, P0 + 45), equal_nan=True), f"ring {ring} layer {l}"
+        vt = synth.tokens(4, "upd.next", 8, m.vocab)
+        a, b = (torch.empty((8, m.vocab), dtype=torch.float32, device="cuda") for _ in range(2))
+        g.verify_batch(dev(vt), a, None)
+        ref.verify_batch(dev(vt), b, None)
+        assert np.array_equal(host(a), host(b))
