@@ -431,7 +431,8 @@ __device__ __forceinline__ void store_bf16_vec(uint16_t* p, const float* v) {
 // KVB: the planes hold bf16 values; the tiles keep them as bf16 and the reads widen them (exact),
 // and new rows are written rounded to the plane and the tile, so every K/V value the scores and
 // PV see is the stored one.
-template <int HD, bool KVB>
+// MULTI: several sub-chunks per workgroup (long key ranges); without it the kernel has no loop.
+template <int HD, bool KVB, bool MULTI>
 __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     using TT = typename KVElem<KVB>::T;
     constexpr int CK = attn_ck(HD);      // keys per sub-chunk
@@ -740,17 +741,21 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             }
         }
     };
-    // the sub-chunks one after another (the first one's copies went out above); a barrier keeps the
-    // next copies from overwriting the stage before every wave has read it
-    for (int c0 = wk0; c0 < wk1; c0 += CK) {
-        if (c0 != wk0) {
-            __syncthreads();
-            int n_lo, n_hi;
-            new_rows(c0, n_lo, n_hi);
-            if (n_lo + ri < n_hi) load_row(n_lo + ri);
-            issue_kv(K0, V0, c0);
+    if constexpr (MULTI) {
+        // the sub-chunks one after another (the first one's copies went out above); a barrier keeps
+        // the next copies from overwriting the stage before every wave has read it
+        for (int c0 = wk0; c0 < wk1; c0 += CK) {
+            if (c0 != wk0) {
+                __syncthreads();
+                int n_lo, n_hi;
+                new_rows(c0, n_lo, n_hi);
+                if (n_lo + ri < n_hi) load_row(n_lo + ri);
+                issue_kv(K0, V0, c0);
+            }
+            sub_chunk(c0, K0, V0);
         }
-        sub_chunk(c0, K0, V0);
+    } else if (wk0 < wk1) {
+        sub_chunk(wk0, K0, V0);   // the only sub-chunk
     }
 
     // 7. this workgroup's partial: unnormalised O (each wave its dims), the running max and sum
@@ -769,13 +774,12 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 }
 
 // Merge of the chunks of one (q tile, KV head): one 256-thread block per (query vector, 64 dims).
-// Wave w takes the chunks [w q, (w + 1) q), q = ceil(n_chunks / 4) <= 32: lane d loads its dim of
+// Wave w takes the chunks [w q, (w + 1) q), q = ceil(n_chunks / 4) <= QMAX: lane d loads its dim of
 // every chunk, lane j the running maximum and sum of chunk w q + j, all in one round of loads. The
 // chunk weights are computed once per chunk (lane j) and broadcast from it. Every sum runs in a
 // fixed order (butterfly over the lanes, chunks in order, then the waves in order).
-template <int HD>
+template <int HD, int QMAX>   // QMAX: chunks per wave at most (32, or 64 for up to kAttnMaxChunks)
 __global__ __launch_bounds__(256) void k_attn_combine(AttnK a) {
-    constexpr int QMAX = kAttnMaxChunks / 4;   // chunks per wave at most
     static_assert(QMAX <= 64, "one lane per chunk of a wave");
     __shared__ float mxw[4], denw[4], numw[4][64];
     const int dgroups = HD / 64;
@@ -1136,9 +1140,16 @@ size_t attn_part_floats_needed(const Attn& x) {
 namespace {
 template <int HD>
 void launch_attn(const AttnK& a, int grid, int cgrid, hipStream_t st) {
-    if (a.kv_bf16) hipLaunchKernelGGL((k_attention<HD, true>), dim3(grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_attention<HD, false>), dim3(grid), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_attn_combine<HD>, dim3(cgrid), dim3(256), 0, st, a);
+    if (a.spw > 1) {
+        if (a.kv_bf16) hipLaunchKernelGGL((k_attention<HD, true, true>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_attention<HD, false, true>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+        if (a.kv_bf16) hipLaunchKernelGGL((k_attention<HD, true, false>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_attention<HD, false, false>), dim3(grid), dim3(256), 0, st, a);
+    }
+    static_assert(kAttnMaxChunks <= 4 * 64, "the combine's wider form takes 64 chunks per wave");
+    if (a.n_chunks <= 128) hipLaunchKernelGGL((k_attn_combine<HD, 32>), dim3(cgrid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_combine<HD, 64>), dim3(cgrid), dim3(256), 0, st, a);
 }
 }  // namespace
 
