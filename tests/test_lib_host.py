@@ -73,3 +73,53 @@ def test_layer_refusals():
     hd[0] = dataclasses.replace(hd[0], head_dim=96)
     with pytest.raises(bvf.BvfError, match="head_dim"):
         bvf.arena_bytes(dataclasses.replace(base, layers=tuple(hd)))
+
+
+def test_arena_bytes_for_the_variants():
+    """Every model shape the tests and the benchmark build: per-layer embeddings, ring planes, bf16
+    planes, the ragged model, the tiny draft; the ring arena is smaller than the linear one."""
+    from tests.test_gpu_parity import ragged_model
+    tgt = synth.target_model(max_ctx=16384 + 64)
+    models = [dataclasses.replace(synth.tiny_model(), ple_dim=128), dataclasses.replace(tgt, ple_dim=256, vocab=16384),
+              dataclasses.replace(tgt, kv_ring=1), dataclasses.replace(tgt, kv_bf16=1),
+              dataclasses.replace(synth.tiny_two_width_model(), kv_ring=1, kv_bf16=1), ragged_model(),
+              synth.tiny_draft_model(), dataclasses.replace(synth.draft_model(), kv_bf16=1)]
+    for m in models:
+        assert bvf.arena_bytes(m) > 0, (m.name, bvf.last_error())
+    assert bvf.arena_bytes(dataclasses.replace(tgt, kv_ring=1)) < bvf.arena_bytes(tgt)
+    assert bvf.arena_bytes(dataclasses.replace(tgt, kv_bf16=1)) < bvf.arena_bytes(tgt)
+
+
+@pytest.mark.parametrize("change, msg", [
+    (dict(ple_dim=100), "ple_dim"),
+    (dict(ple_dim=8192), "ple_dim"),
+    (dict(kv_ring=2), "kv_ring"),
+    (dict(kv_bf16=3), "kv_bf16"),
+    (dict(max_ctx=(1 << 24) + 1), "max_ctx"),
+    (dict(rope_base=0.0), "rope_base"),
+])
+def test_descriptor_refusals_more(change, msg):
+    m = dataclasses.replace(synth.tiny_model(), **change)
+    with pytest.raises(bvf.BvfError) as e:
+        bvf.arena_bytes(m)
+    assert msg in str(e.value)
+
+
+def test_kv_heads_must_divide_the_query_heads():
+    m = synth.tiny_model()
+    m = dataclasses.replace(m, n_q_heads=6, layers=(dataclasses.replace(m.layers[0], n_kv_heads=4),))
+    with pytest.raises(bvf.BvfError, match="does not divide"):
+        bvf.arena_bytes(m)
+
+
+def test_draft_refusals():
+    d = synth.tiny_draft_model()
+    for change, msg in [(dict(ple_dim=128), "verify model only"), (dict(kv_ring=1), "verify model only"),
+                        (dict(tap_layers=()), "n_taps")]:
+        with pytest.raises(bvf.BvfError) as e:
+            bvf.arena_bytes(dataclasses.replace(d, **change))
+        assert msg in str(e.value)
+    shared = list(d.layers)
+    shared[1] = dataclasses.replace(shared[1], kv_owner=0)
+    with pytest.raises(bvf.BvfError, match="cannot share"):
+        bvf.arena_bytes(dataclasses.replace(d, layers=tuple(shared)))
