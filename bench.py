@@ -55,10 +55,17 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def planes(m, args):
-    """The model with bf16 K/V planes when --kv-bf16 is given (fp32 planes otherwise)."""
+def planes(m, args, verify: bool = True):
+    """The model with the memory variants asked for: bf16 K/V planes (--kv-bf16), and on the verify
+    model ring sliding planes (--kv-ring) and per-layer embeddings of width --ple-dim."""
     import dataclasses
-    return dataclasses.replace(m, kv_bf16=1) if args.kv_bf16 else m
+    if args.kv_bf16:
+        m = dataclasses.replace(m, kv_bf16=1)
+    if verify and args.kv_ring:
+        m = dataclasses.replace(m, kv_ring=1)
+    if verify and args.ple_dim:
+        m = dataclasses.replace(m, ple_dim=args.ple_dim)
+    return m
 
 
 def build_weights(m, seed: int, threads: int):
@@ -172,7 +179,7 @@ def run_loop(args):
     threads = min(16, os.cpu_count() or 8)
     max_ctx = args.ctx + args.loop + 64
     m = planes(synth.target_model(max_ctx=max_ctx, n_layers=args.layers, vocab=args.vocab), args)
-    dm = planes(synth.draft_model(max_ctx=max_ctx), args)
+    dm = planes(synth.draft_model(max_ctx=max_ctx), args, verify=False)
     t0 = time.time()
     w = synth.make_weights(m, args.seed, threads=threads)
     dw = synth.make_weights(dm, args.seed, threads=threads)
@@ -217,7 +224,8 @@ def run_loop(args):
         "data": f"synthetic (seeded draws, seed {args.seed}); acceptance steered: truncated geometric p=0.8467",
         "config": {"workload": f"speculative loop: target {m.n_layers} layers hidden {m.hidden} Q4_1, draft 5 layers "
                                f"hidden 2560, block 8, {args.ctx} cached positions, {args.loop} tokens",
-                   "kv_planes": "bf16" if args.kv_bf16 else "fp32"},
+                   "kv_planes": ("bf16" if args.kv_bf16 else "fp32") + (", ring" if args.kv_ring else ""),
+                   "ple_dim": args.ple_dim},
         "tokens": len(toks),
         "rounds": rounds,
         "tokens_per_target_pass": round(len(toks) / rounds, 3),
@@ -300,7 +308,8 @@ def run_prefill(args):
         "data": f"synthetic (seeded draws, seed {args.seed})",
         "config": {"workload": f"prefill of {args.prefill} tokens on {args.ctx} cached positions, target {m.n_layers} "
                                f"layers hidden {m.hidden} Q4_1, chunks of {chunk} rows",
-                   "kv_planes": "bf16" if args.kv_bf16 else "fp32"},
+                   "kv_planes": ("bf16" if args.kv_bf16 else "fp32") + (", ring" if args.kv_ring else ""),
+                   "ple_dim": args.ple_dim},
         "ms": round(ms, 3),
         "chunks": n_chunks,
         "ms_per_chunk": round(ms / n_chunks, 4),
@@ -328,6 +337,10 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-bf16", action="store_true", help="K/V planes hold bf16 values (half the plane bytes)")
+    ap.add_argument("--kv-ring", action="store_true",
+                    help="the verify model's own sliding planes are rings of window + 16 slots")
+    ap.add_argument("--ple-dim", type=int, default=0,
+                    help="> 0: the verify model runs per-layer embeddings of this width (vocab x layers x width table)")
     ap.add_argument("--no-graph", action="store_true", help="direct launches instead of the captured pass")
     ap.add_argument("--loop", type=int, default=0,
                     help="instead of the verify step: the speculative loop (draft block of 8 + batched verify + "
@@ -464,7 +477,8 @@ def main():
                                  "norms and softmax",
                    "k": k, "cached_positions": args.ctx, "layers": m.n_layers, "vocab": V,
                    "accept": "greedy" if args.temperature <= 0 else f"sampled, T={args.temperature}",
-                   "kv_planes": "bf16" if args.kv_bf16 else "fp32"},
+                   "kv_planes": ("bf16" if args.kv_bf16 else "fp32") + (", ring" if args.kv_ring else ""),
+                   "ple_dim": args.ple_dim},
         "q4_1_weight_stream_gbs": round(q4_gbs, 1),
         "q4_1_weight_stream_frac_of_peak": round(q4_gbs / HBM_PEAK_GBS, 4),
         "q4_1_bytes_per_pass": q4_bytes,
