@@ -314,7 +314,7 @@ size_t layout(bvf_model* m, uint8_t* base) {
     m->dpos = (int64_t*)take(8);
     // attention partials: (query tiles x KV heads) <= (RC / 16) n_q_heads at RC rows, up to
     // kAttnMaxChunks chunks each
-    m->attn_part_floats = (size_t)(RC / 16) * d.n_q_heads * kAttnMaxChunks * 16 * (m->hd_max + 2);
+    m->attn_part_floats = (size_t)(RC / 16) * d.n_q_heads * kAttnMaxChunks * 16 * attn_part_ld(m->hd_max);
     m->attn_part = (float*)take(m->attn_part_floats * 4);
     m->ss_x = (float*)take((size_t)RC * (H / kTile) * 4);
     m->ss_qkv = (float*)take((size_t)RC * (m->nqkv_max / kTile) * 4);

@@ -13,6 +13,9 @@ constexpr int gemm_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 constexpr int kTile = 16;         // output columns per MFMA tile
 constexpr int kSuper = 128;       // K per superblock = 4 Q4_1 blocks of 32
 constexpr int kAttnMaxChunks = 256;   // key chunks per (query tile, KV head) merged by the combine
+// floats per query vector in an attention chunk partial: hd values of O, the running maximum and
+// sum, padded so every row starts 16-byte aligned
+__host__ __device__ constexpr int attn_part_ld(int hd) { return hd + 4; }
 
 // A packed Q4_1 (or bf16) weight image, column-tiled for the small-M GEMM.
 //   Q4_1: codes  [n_tiles][G][64 lanes][4 x u32]: lane = sub * 16 + c holds, for block j of the

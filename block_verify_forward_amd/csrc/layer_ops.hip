@@ -40,21 +40,15 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void wait_lds() {
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+// s_waitcnt for at most N vector memory operations of this wave in flight (LDS and scalar counts
+// untouched)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
 }
 
-// 4-byte LDS read that the compiler's wait-count insertion does not see (it would otherwise wait
-// for outstanding global->LDS copies into other arrays); the caller calls wait_lds() before using
-// the value.
-__device__ __forceinline__ float lds_read_f32_untracked(const float* p) {
-    float v;
-    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-    return v;
-}
 
 // Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15) without LDS traffic: quad
 // swaps, then the half-row and row mirrors; every lane ends with the same bits.
@@ -76,6 +70,29 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<0x140>(v);
     return v;
 }
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48) with the
+// row swaps of gfx950: v_permlane16_swap exchanges the odd rows of its first register with the even
+// rows of its second, v_permlane32_swap the upper half of the first with the lower half of the
+// second. Given two copies of a value, each lane then holds its own value and its partner's, in
+// the same order on both partners, so both compute the same bits. The swaps are written as inline
+// asm with both registers as outputs: this compiler's builtins return the first register for both
+// results. The s_nop pairs cover the VALU hazards around the swap.
+__device__ __forceinline__ void swap_rows16(float& x, float& y) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void swap_rows32(float& x, float& y) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ float swap_rows16_max(float v) { float x = v, y = v; swap_rows16(x, y); return fmaxf(x, y); }
+__device__ __forceinline__ float swap_rows32_max(float v) { float x = v, y = v; swap_rows32(x, y); return fmaxf(x, y); }
+__device__ __forceinline__ float swap_rows16_sum(float v) { float x = v, y = v; swap_rows16(x, y); return x + y; }
+__device__ __forceinline__ float swap_rows32_sum(float v) { float x = v, y = v; swap_rows32(x, y); return x + y; }
+__device__ __forceinline__ float rows4_max(float v) { return swap_rows32_max(swap_rows16_max(v)); }
+__device__ __forceinline__ float rows4_sum(float v) { return swap_rows32_sum(swap_rows16_sum(v)); }
+// all 64 lanes: the 16 lanes of each row, then the four rows
+__device__ __forceinline__ float wave64_max(float v) { return rows4_max(row16_max(v)); }
+__device__ __forceinline__ float wave64_sum(float v) { return rows4_sum(row16_sum(v)); }
 
 // N consecutive floats (N a multiple of 4, or 2) through 16- or 8-byte accesses; the addresses are
 // aligned to the access size.
@@ -126,6 +143,36 @@ __device__ __forceinline__ void load_bf16_vec(float* v, const uint16_t* p) {
             v[i] = __builtin_bit_cast(float, w << 16);
             v[i + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
         }
+    }
+}
+
+// N consecutive bf16 (N even; the address aligned to the access) as raw 32-bit pairs, and their widening: a load whose
+// conversion is placed later does not make the wave wait for it at the load site
+template <int N>
+__device__ __forceinline__ void load_bf16_raw(uint32_t* w, const uint16_t* p) {
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 8) {
+            const uint4 t = *(const uint4*)(p + i);
+            w[i / 2] = t.x; w[i / 2 + 1] = t.y; w[i / 2 + 2] = t.z; w[i / 2 + 3] = t.w;
+        }
+    } else if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const uint2 t = *(const uint2*)(p + i);
+            w[i / 2] = t.x; w[i / 2 + 1] = t.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 2) w[i / 2] = *(const uint32_t*)(p + i);
+    }
+}
+template <int N>
+__device__ __forceinline__ void widen_bf16(float* v, const uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
     }
 }
 
@@ -350,7 +397,7 @@ struct AttnK {
     int np0, np1, sp, r_lo, r_hi;   // new rows: positions [np0, np1); row of p: p < sp ? r_lo + p - np0 : r_hi + p - sp
     int key_lo, n_keys, spw, n_chunks;   // keys [key_lo, key_lo + n_keys); spw sub-chunks per workgroup
     const int64_t* dpos;     // causal graph replays: positions held read here (see bind_positions)
-    float* part;             // [n_qt][nkv][n_chunks][16][hd + 2] partials
+    float* part;             // [n_qt][nkv][n_chunks][16][attn_part_ld(hd)] partials: O, then max and sum
     int* counters;           // [n_qt * nkv]
     uint16_t* out;           // [M][Hq * hd] bf16
 };
@@ -396,11 +443,13 @@ __device__ __forceinline__ float head_ss(const AttnK& a, int r, int c0, int hd) 
 // MFMA block.
 __host__ __device__ constexpr int attn_ck(int hd) { return 4096 / hd > 16 ? 4096 / hd : 16; }
 
-// LDS of k_attention<hd, kvb>: the K and V tiles (padded rows), the query rows, the partial
-// scores and the probabilities (the arrays declared in the kernel).
-constexpr size_t attn_lds_bytes(int hd, bool kvb) {
+// LDS of k_attention<hd, kvb, multi>: the K and V tiles (padded rows), the query rows (with multi:
+// the larger of them and a second K/V stage) and the partial scores (the arrays declared in the
+// kernel).
+constexpr size_t attn_lds_bytes(int hd, bool kvb, bool multi) {
     const size_t ck = attn_ck(hd), eb = kvb ? 2 : 4;
-    return ck * (hd + 16 / eb) * eb + ck * (hd + 16) * eb + (size_t)16 * (hd + 4) * 4 + (size_t)2 * 4 * 16 * (ck + 1) * 4;
+    const size_t kv = ck * (hd + 16 / eb) * eb + ck * (hd + 16) * eb, q = (size_t)16 * (hd + 4) * 4;
+    return kv + (multi && kv > q ? kv : q) + (size_t)4 * 16 * (ck + 4) * 4;
 }
 
 // Tile element of the K/V planes: fp32, or (KVB) bf16 values widened exactly where they are read.
@@ -424,14 +473,16 @@ __device__ __forceinline__ void store_bf16_vec(uint16_t* p, const float* v) {
     }
 }
 
-// One workgroup per (key chunk, KV head, tile of 16 query vectors). The chunk's keys go through one
-// LDS stage in sub-chunks of CK keys, one after another; the stage is small enough for two or more
-// workgroups per compute unit, so one workgroup's copies are in flight while another computes (a
-// second stage inside the workgroup left one workgroup per compute unit and ran slower).
+// One workgroup per (key chunk, KV head, tile of 16 query vectors). The chunk's keys go through LDS
+// in sub-chunks of CK keys.
+// MULTI (long key ranges): several sub-chunks per workgroup through two LDS stages, the copies of
+// the next sub-chunk in flight while the current one is computed. The query values are read into
+// registers once, and the space of the query rows then holds the second stage, so a workgroup takes
+// ~73 KB of LDS at head dim 256 with fp32 planes and two workgroups share a compute unit.
+// Without MULTI: one sub-chunk, no loop; its K/V copies are issued before any other load.
 // KVB: the planes hold bf16 values; the tiles keep them as bf16 and the reads widen them (exact),
 // and new rows are written rounded to the plane and the tile, so every K/V value the scores and
 // PV see is the stored one.
-// MULTI: several sub-chunks per workgroup (long key ranges); without it the kernel has no loop.
 template <int HD, bool KVB, bool MULTI>
 __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     using TT = typename KVElem<KVB>::T;
@@ -440,6 +491,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     constexpr int DW = HD / 4;           // dims owned by each wave (scores over them, then O for them)
     constexpr int H2 = HD / 2;
     constexpr int PPT = H2 / 16;         // rotate-half pairs per thread (16 threads per vector)
+    static_assert(HD <= 256, "a head's tile sums of squares: at most one per thread of a vector");
     constexpr int EPU = 16 / (int)sizeof(TT);   // values per 16-byte copy unit
     constexpr int UPR = HD / EPU;               // copy units per K or V row
     // padded rows: K rows shift by 16 bytes (the 16 rows of a score read hit distinct banks), V rows
@@ -447,43 +499,71 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     constexpr int LDK = HD + 16 / (int)sizeof(TT);
     constexpr int LDV = HD + (KVB ? 16 : 16);
     constexpr int LD = HD + 4;           // query rows
+    constexpr size_t KT_BYTES = (size_t)CK * LDK * sizeof(TT), VT_BYTES = (size_t)CK * LDV * sizeof(TT);
+    constexpr size_t Q_BYTES = (size_t)16 * LD * 4;
+    constexpr size_t ST1 = MULTI && KT_BYTES + VT_BYTES > Q_BYTES ? KT_BYTES + VT_BYTES : Q_BYTES;
+    static_assert(KT_BYTES % 16 == 0, "the second stage's V rows start 16-byte aligned");
     __shared__ __attribute__((aligned(16))) TT K0[CK][LDK];
     __shared__ __attribute__((aligned(16))) TT V0[CK][LDV];
-    __shared__ __attribute__((aligned(16))) float Qs[16][LD];
-    __shared__ float Sp[4][16][CK + 1];   // per-wave partial scores (over the wave's dims)
-    __shared__ float Ps[4][16][CK + 1];   // per-wave probabilities
+    // the query rows; with MULTI, after they are read into registers, the second K/V stage
+    __shared__ __attribute__((aligned(16))) uint8_t st1[ST1];
+    __shared__ __attribute__((aligned(16))) float Sp[4][16][CK + 4];   // per-wave partial scores (over the wave's dims)
+    float (*Qs)[LD] = reinterpret_cast<float (*)[LD]>(st1);
+    TT (*K1)[LDK] = reinterpret_cast<TT (*)[LDK]>(st1);
+    TT (*V1)[LDV] = reinterpret_cast<TT (*)[LDV]>(st1 + KT_BYTES);
+    constexpr int NPW = 2 * CK / 4;   // K/V copy instructions per wave per stage
     if (a.dpos) bind_positions(a);
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int chunk = blockIdx.x % a.n_chunks;
-    const int g = (blockIdx.x / a.n_chunks) % a.nkv;
-    const int qt = blockIdx.x / (a.n_chunks * a.nkv);
+    // block order: the query tiles of one (chunk, KV head) pair sit 8 blocks apart, so they run on
+    // the same XCD at about the same time and the second tile's K/V copies find the rows in its L2;
+    // the grid is padded to whole groups of 8 pairs and the padding blocks leave at once
+    const int xl = blockIdx.x % 8, rest = blockIdx.x / 8;
+    const int qt = rest % a.n_qt, pidx = (rest / a.n_qt) * 8 + xl;
+    if (pidx >= a.n_chunks * a.nkv) return;   // uniform in the workgroup
+    const int chunk = pidx % a.n_chunks;
+    const int g = pidx / a.n_chunks;
     const int col = lane & 15, grp = lane >> 4;
     const int qd = a.Hq * HD;
     const size_t prow = (size_t)2 * a.w;
     const int wk0 = a.key_lo + chunk * a.spw * CK;                   // this workgroup's keys [wk0, wk1)
     const int wk1 = min(a.key_lo + a.n_keys, wk0 + a.spw * CK);
 
-    // K and V rows of a sub-chunk: direct global->LDS copies, one row (UPR 16-byte units) per
-    // instruction, a fixed number per wave; rows past c1 repeat row c0 (finite; masked below)
+    // K and V rows of a sub-chunk: direct global->LDS copies, one row (UPR <= 64 16-byte units) per
+    // instruction, CK / 4 rows per wave (rows wave + 4 t); rows past c1 repeat row c0 (finite;
+    // masked below). A sub-chunk past the workgroup's keys (c0 >= wk1: the two-stage loop's last
+    // copies, never read) copies row wk1 - 1 into every row. The ring slot of each row steps by 4
+    // from the first one, so the copies form one straight run of NPW instructions with no branch
+    // between them: the compiler's wait-count analysis then sees the same copies on every path and
+    // needs no wait of its own before the reads of the other stage.
+    static_assert(UPR <= 64, "one copy instruction per row");
     auto issue_kv = [&](TT (*Kt)[LDK], TT (*Vt)[LDV], int c0) __attribute__((always_inline)) {
         const int c1 = min(wk1, c0 + CK);
-        constexpr int ipr = (UPR + 63) / 64;   // instructions per row
-        static_assert((2 * CK * ipr) % 4 == 0, "K/V copies split evenly over the 4 waves");
+        const int cb = c0 < wk1 ? c0 : wk1 - 1;   // the row repeated past c1
+        const int rc = a.ring_cap;
+        const int sb = rc > 0 ? cb % rc : cb;     // its plane slot
+        int sl = rc > 0 ? (cb + wave) % rc : cb + wave;   // slot of row wave (when it is a key)
+        static_assert(CK % 4 == 0, "K (and V) copies split evenly over the 4 waves");
+        int slots[CK / 4];
 #pragma unroll
-        for (int t = 0; t < 2 * CK * ipr / 4; ++t) {
-            const int i = wave + 4 * t;
-            const int kv = i / (CK * ipr), rem = i - kv * CK * ipr;
-            const int kk = rem / ipr, part = rem - kk * ipr;
-            const int unit = part * 64 + lane;
-            const int key = c0 + kk < c1 ? c0 + kk : c0;
-            if (UPR >= 64 || unit < UPR) {
-                const size_t e = (size_t)kv_slot(a, key) * prow + (size_t)kv * a.w + g * HD + unit * EPU;
-                const void* src = (const TT*)a.plane + e;
-                void* dst = (kv ? &Vt[kk][0] : &Kt[kk][0]) + part * 64 * EPU;
-                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-            }
+        for (int t = 0; t < CK / 4; ++t) {
+            slots[t] = c0 + wave + 4 * t < c1 ? sl : sb;
+            sl += 4;
+            sl = rc > 0 && sl >= rc ? sl - rc : sl;   // one wrap: a ring holds at least 4 slots
         }
+        const int unit = lane;
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+            for (int t = 0; t < CK / 4; ++t) {
+                const int kk = wave + 4 * t;
+                if (UPR == 64 || unit < UPR) {
+                    const size_t e = (size_t)slots[t] * prow + (size_t)kv * a.w + g * HD + unit * EPU;
+                    const void* src = (const TT*)a.plane + e;
+                    void* dst = kv ? (void*)&Vt[kk][0] : (void*)&Kt[kk][0];
+                    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+                }
+            }
     };
 
     // new rows of an own layer (16 threads per row): raw K, V, RoPE row and the head's sums of
@@ -491,8 +571,11 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     const int ri = tid >> 4, jr = tid & 15;
     float kr0[PPT], kr1[PPT], vr0[PPT], vr1[PPT], ssr = 0.f;
     float2 csr[PPT];
-    auto load_row = [&](int p) __attribute__((always_inline)) {
-        const int r = p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
+    // has == false: the thread has no row; it loads row 0 at position 0 (readable, unused), so the
+    // loads need no branch (a load under a branch is waited for where the branches join)
+    auto load_row = [&](int p, bool has = true) __attribute__((always_inline)) {
+        const int r = !has ? 0 : p < a.sp ? a.r_lo + (p - a.np0) : a.r_hi + (p - a.sp);
+        if (!has) p = 0;
         const float* ks = a.qkv + (size_t)r * a.ldq + qd + g * HD;
         const float* vs = a.qkv + (size_t)r * a.ldq + qd + a.nkv * HD + g * HD;
         const float2* rt = a.rope + (size_t)p * H2;
@@ -502,18 +585,14 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         load_vec<PPT>(vr0, vs + d0);
         load_vec<PPT>(vr1, vs + d0 + H2);
         load_vec<2 * PPT>((float*)csr, (const float*)(rt + d0));
-        // the first term is taken as is (an add to 0 would make the compiler wait for the load here)
-        ssr = 0.f;
-        if (a.qk_norm) {
-            const float* ssp = a.ss + (size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + jr;
-            if (jr < HD / 16) ssr = ssp[0];
-#pragma unroll
-            for (int u = 1; u < (HD / 16 + 15) / 16; ++u)
-                if (jr + 16 * u < HD / 16) ssr += ssp[16 * u];
-        }
+        // the head's tile sums (one per thread jr < HD / 16), loaded without a branch and selected
+        // where they are used (store_row)
+        ssr = *(a.qk_norm && jr < HD / 16 ? a.ss + (size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + jr
+                                           : (const float*)a.rope);
     };
     auto store_row = [&](int p, int c0, TT (*Kt)[LDK], TT (*Vt)[LDV]) __attribute__((always_inline)) {
-        const float inv = a.qk_norm ? 1.0f / sqrtf(row16_sum(ssr) / (float)HD + a.eps) : 1.f;
+        const float ssv = a.qk_norm && jr < HD / 16 ? ssr : 0.f;
+        const float inv = a.qk_norm ? 1.0f / sqrtf(row16_sum(ssv) / (float)HD + a.eps) : 1.f;
         const size_t prow_off = (size_t)kv_slot(a, p) * prow + g * HD;
         const int kk = p - c0;
         const int d0 = jr * PPT;
@@ -566,8 +645,10 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 
     // 1. the 16 query vectors of the tile: per-head RMSNorm (sums of squares from the q|k|v GEMM's
     //    epilogue) and rotate-half RoPE at the row's position, into LDS; 16 threads per vector.
-    //    Their loads, and those of the first sub-chunk's new rows, go out before the K/V copies
-    //    (a wave's loads return in order).
+    //    Their loads, and (one sub-chunk) those of its new rows, go out before the K/V copies
+    //    (a wave's loads return in order: the query is built while the copies are in flight), and
+    //    nothing waits for a load before the copies are issued: the gains stay raw and the first
+    //    sum-of-squares term is taken as is.
     {
         const int qi = tid >> 4, j = tid & 15;
         const int qv = qt * 16 + qi;
@@ -576,30 +657,37 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         const float* src = a.qkv + (size_t)m * a.ldq + h * HD;
         const float2* rt = a.rope + (size_t)(a.pos0 + m) * H2;
         float x0[PPT], x1[PPT], g0[PPT], g1[PPT];
+        uint32_t gw0[PPT / 2], gw1[PPT / 2];
         float2 cs[PPT];
         const int d0 = j * PPT;   // this thread's PPT consecutive pairs (d0 + i, d0 + i + H2)
         load_vec<PPT>(x0, src + d0);
         load_vec<PPT>(x1, src + d0 + H2);
         load_vec<2 * PPT>((float*)cs, (const float*)(rt + d0));
-        if (a.qk_norm) {
-            load_bf16_vec<PPT>(g0, a.q_norm + d0);
-            load_bf16_vec<PPT>(g1, a.q_norm + d0 + H2);
-        } else {
-#pragma unroll
-            for (int i = 0; i < PPT; ++i) g0[i] = g1[i] = 1.f;
+        // without QK-norm the gain loads read the RoPE table (any HD readable halves; unused)
+        const uint16_t* gsrc = a.qk_norm ? a.q_norm : (const uint16_t*)a.rope;
+        load_bf16_raw<PPT>(gw0, gsrc + d0);
+        load_bf16_raw<PPT>(gw1, gsrc + d0 + H2);
+        // the head's HD / 16 <= 16 tile sums: one per thread j < HD / 16, loaded without a branch
+        // (a load under a branch is waited for where the branches join)
+        const bool has_ss = a.qk_norm && j < HD / 16;
+        const float ssq_raw = *(has_ss ? a.ss + (size_t)m * (a.ldq / 16) + h * (HD / 16) + j : (const float*)a.rope);
+        if constexpr (!MULTI) {
+            // the first sub-chunk's new rows (the two-stage form loads them where it stores them:
+            // only the workgroup that holds the pass's positions has any)
+            int p_lo, p_hi;
+            new_rows(wk0, p_lo, p_hi);
+            load_row(p_lo + ri, p_lo + ri < p_hi);
         }
-        float ssq = 0.f;
-        if (a.qk_norm) {
-#pragma unroll
-            for (int u = 0; u < (HD / 16 + 15) / 16; ++u)
-                if (j + 16 * u < HD / 16) ssq += a.ss[(size_t)m * (a.ldq / 16) + h * (HD / 16) + j + 16 * u];
-        }
-        int p_lo, p_hi;
-        new_rows(wk0, p_lo, p_hi);
-        if (p_lo + ri < p_hi) load_row(p_lo + ri);
         asm volatile("" ::: "memory");   // these loads leave before the K/V copies
         __builtin_amdgcn_sched_barrier(0);
         if (wk0 < wk1) issue_kv(K0, V0, wk0);
+        widen_bf16<PPT>(g0, gw0);
+        widen_bf16<PPT>(g1, gw1);
+        if (!a.qk_norm) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) g0[i] = g1[i] = 1.f;
+        }
+        const float ssq = has_ss ? ssq_raw : 0.f;
         const float inv = a.qk_norm ? 1.0f / sqrtf(row16_sum(ssq) / (float)HD + a.eps) : 1.f;
         float q0[PPT], q1[PPT];
 #pragma unroll
@@ -611,177 +699,196 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         store_vec<PPT>(&Qs[qi][d0], q0);
         store_vec<PPT>(&Qs[qi][d0 + H2], q1);
     }
-
-    int lo_r[4], hi_r[4];
+    // MULTI: this lane's query values for the score MFMAs into registers; then the shared space
+    // takes the second stage's copies
+    float4 qreg[MULTI ? DW / 16 : 1];
+    if constexpr (MULTI) {
+        lds_barrier();   // the query rows are in LDS
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int qv = qt * 16 + 4 * grp + r;
-        if (qv < a.NQ) row_range(a, qv / a.Hg, lo_r[r], hi_r[r]);
-        else { lo_r[r] = 1; hi_r[r] = 0; }
+        for (int t = 0; t < DW / 16; ++t) qreg[t] = *(const float4*)&Qs[col][wave * DW + 16 * t + 4 * grp];
+        lds_barrier();   // every wave has its query values
+        issue_kv(K1, V1, wk0 + CK);
+    }
+
+    // the softmax and O are kept transposed: lane (col, grp) owns query vector col of the tile
+    int lo_q, hi_q;
+    {
+        const int qv = qt * 16 + col;
+        if (qv < a.NQ) row_range(a, qv / a.Hg, lo_q, hi_q);
+        else { lo_q = 1; hi_q = 0; }
     }
     const float scale = 1.0f / sqrtf((float)HD);
     constexpr int NDT = DW / 16;
-    floatx4 o[NDT];
+    floatx4 o[NDT];   // o[d][i] = O[q = col][wave * DW + 16 d + 4 grp + i]
 #pragma unroll
     for (int d = 0; d < NDT; ++d) o[d] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    float m_run[4], l_run[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
+    float m_run = -INFINITY, l_run = 0.f;
+    // score row m of a 16-key block is key 4 (m % 4) + m / 4 of the block, so lane (col, grp) gets
+    // the keys 4 i + grp (i = 0..3): the keys its lane group feeds to PV step i
+    const int krow = 4 * (col & 3) + (col >> 2);
 
-    // one sub-chunk [c0, c0 + CK) from the stage (Kc, Vc)
-    auto sub_chunk = [&](int c0, TT (*Kc)[LDK], TT (*Vc)[LDV]) __attribute__((always_inline)) {
+    // one sub-chunk [c0, c0 + CK) from the stage (Kc, Vc); first: the sub-chunk whose first new rows
+    // were loaded with the query
+    auto sub_chunk = [&](int c0, TT (*Kc)[LDK], TT (*Vc)[LDV], bool first) __attribute__((always_inline)) {
         const int c1 = min(wk1, c0 + CK);
-        // 2. this sub-chunk's K/V copies (and its first new rows, loaded before them) have landed
+        // 2. this sub-chunk's K/V copies (and the loads before them) have landed in every wave. With
+        //    MULTI the other stage's copies were issued after them and are the last NPW loads of the
+        //    wave: a wave's loads land in order, so at most NPW left in flight means these are in.
         int p_lo, p_hi;
         new_rows(c0, p_lo, p_hi);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        if constexpr (MULTI) {
+            wait_vmcnt<NPW>();
+            lds_barrier();
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
         // 3. own layers write the new rows, normalised and rotated, into the stage and the plane
         //    (the 16-thread groups are whole, so the row sums in store_row stay inside live groups)
         if (p_lo < p_hi) {
+            if (!first && p_lo + ri < p_hi) load_row(p_lo + ri);
             if (p_lo + ri < p_hi) store_row(p_lo + ri, c0, Kc, Vc);
             for (int pr = p_lo + 16; pr < p_hi; pr += 16)
                 if (pr + ri < p_hi) {
                     load_row(pr + ri);
                     store_row(pr + ri, c0, Kc, Vc);
                 }
+            // MULTI: the plane writes are complete inside this block, so the compiler needs no
+            // wait where it joins the path without new rows for the registers they read (it would
+            // otherwise wait for the next stage's copies on every sub-chunk); only sub-chunks with
+            // new rows pay for it
+            if constexpr (MULTI) wait_vmcnt<0>();
+            lds_barrier();   // the new rows are in the stage
         }
-        if (p_lo < p_hi) lds_barrier();   // the new rows are in the stage
 
-        // 4. partial scores over this wave's dims: S[qv][key] for the CK keys
+        // 4. partial scores over this wave's dims, transposed (S^T = K Q^T): lane (col, grp) gets
+        //    S[q = col][key 4 i + grp] of each 16-key block
         floatx4 sacc[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) sacc[kb] = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < DW / 16; ++t) {
             const int d = wave * DW + 16 * t + 4 * grp;
-            const float4 qa = *(const float4*)&Qs[col][d];
+            float4 qa;
+            if constexpr (MULTI) qa = qreg[t];
+            else qa = *(const float4*)&Qs[col][d];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 float4 kv4;
                 if constexpr (KVB) {
-                    const uint2 b = *(const uint2*)&Kc[kb * 16 + col][d];
+                    const uint2 b = *(const uint2*)&Kc[kb * 16 + krow][d];
                     kv4.x = __builtin_bit_cast(float, b.x << 16);
                     kv4.y = __builtin_bit_cast(float, b.x & 0xffff0000u);
                     kv4.z = __builtin_bit_cast(float, b.y << 16);
                     kv4.w = __builtin_bit_cast(float, b.y & 0xffff0000u);
                 } else {
-                    kv4 = *(const float4*)&Kc[kb * 16 + col][d];
+                    kv4 = *(const float4*)&Kc[kb * 16 + krow][d];
                 }
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, kv4.x, sacc[kb], 0, 0, 0);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, kv4.y, sacc[kb], 0, 0, 0);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.z, kv4.z, sacc[kb], 0, 0, 0);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.w, kv4.w, sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv4.x, qa.x, sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv4.y, qa.y, sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv4.z, qa.z, sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv4.w, qa.w, sacc[kb], 0, 0, 0);
             }
         }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) *(floatx4*)&Sp[wave][col][kb * 16 + 4 * grp] = sacc[kb];
+        lds_barrier();
+
+        // 5. softmax update for the lane's vector over the sub-chunk (every wave for all 16
+        //    vectors; the sums over the four waves' dims are taken in wave order). The maximum and
+        //    the sum run over the lane's 4 KB keys, then over the four lane groups.
+        float sv[KB][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            floatx4 sp[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) sp[w] = *(const floatx4*)&Sp[w][col][kb * 16 + 4 * grp];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = c0 + kb * 16 + 4 * i + grp;
+                const float sum = ((sp[0][i] + sp[1][i]) + sp[2][i]) + sp[3][i];
+                sv[kb][i] = (key < c1 && key >= lo_q && key <= hi_q) ? sum * scale : -INFINITY;
+                mx = fmaxf(mx, sv[kb][i]);
+            }
+        }
+        mx = rows4_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
+        float ps = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sp[wave][4 * grp + r][kb * 16 + col] = sacc[kb][r];
-        lds_barrier();
-
-        // 5. softmax update over the sub-chunk (every wave for all 16 vectors; the sums over the
-        //    four waves' dims are taken in wave order), probabilities into this wave's LDS slice.
-        //    The partial scores are read untracked: the compiler would otherwise wait for the next
-        //    sub-chunk's copies before these reads.
-        constexpr int RB = KB == 1 ? 4 : 1;   // vectors whose partial scores are read in one batch
-#pragma unroll
-        for (int r0 = 0; r0 < 4; r0 += RB) {
-            float spv[RB][KB][4];
-#pragma unroll
-            for (int rr = 0; rr < RB; ++rr)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        spv[rr][kb][w] = lds_read_f32_untracked(&Sp[w][4 * grp + r0 + rr][kb * 16 + col]);
-            wait_lds();
-#pragma unroll
-            for (int rr = 0; rr < RB; ++rr) {
-                const int r = r0 + rr;
-                const int qvl = 4 * grp + r;
-                float sv[KB];
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const int key = c0 + kb * 16 + col;
-                    const float sum = ((spv[rr][kb][0] + spv[rr][kb][1]) + spv[rr][kb][2]) + spv[rr][kb][3];
-                    sv[kb] = (key < c1 && key >= lo_r[r] && key <= hi_r[r]) ? sum * scale : -INFINITY;
-                    mx = fmaxf(mx, sv[kb]);
-                }
-                mx = row16_max(mx);
-                const float m_new = fmaxf(m_run[r], mx);
-                const float alpha = (m_run[r] == -INFINITY) ? 0.f : expf(m_run[r] - m_new);
-                float ps = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const float pv = (sv[kb] == -INFINITY) ? 0.f : expf(sv[kb] - m_new);
-                    ps += pv;
-                    Ps[wave][qvl][kb * 16 + col] = pv;
-                }
-                ps = row16_sum(ps);
-                l_run[r] = l_run[r] * alpha + ps;
-                m_run[r] = m_new;
-#pragma unroll
-                for (int d = 0; d < NDT; ++d) o[d][r] *= alpha;
+            for (int i = 0; i < 4; ++i) {
+                sv[kb][i] = (sv[kb][i] == -INFINITY) ? 0.f : expf(sv[kb][i] - m_new);
+                ps += sv[kb][i];
             }
-        }
-        wave_sync();
+        ps = rows4_sum(ps);
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+#pragma unroll
+        for (int d = 0; d < NDT; ++d) o[d] *= alpha;
 
-        // 6. O += P V for this wave's dims
+        // 6. O^T += V^T P^T for this wave's dims: step (kb, i) takes the keys kb 16 + 4 i + grp,
+        //    whose probabilities the lane holds
 #pragma unroll
-        for (int st = 0; st < CK / 4; ++st) {
-            const float pa = Ps[wave][col][4 * st + grp];
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int d = 0; d < NDT; ++d) {
-                float vb;
-                if constexpr (KVB) vb = bf16_to_f32(Vc[4 * st + grp][wave * DW + 16 * d + col]);
-                else vb = Vc[4 * st + grp][wave * DW + 16 * d + col];
-                o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o[d], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const int vr = kb * 16 + 4 * i + grp;
+#pragma unroll
+                for (int d = 0; d < NDT; ++d) {
+                    float vb;
+                    if constexpr (KVB) vb = bf16_to_f32(Vc[vr][wave * DW + 16 * d + col]);
+                    else vb = Vc[vr][wave * DW + 16 * d + col];
+                    o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb, sv[kb][i], o[d], 0, 0, 0);
+                }
             }
-        }
     };
     if constexpr (MULTI) {
-        // the sub-chunks one after another (the first one's copies went out above); a barrier keeps
-        // the next copies from overwriting the stage before every wave has read it
-        for (int c0 = wk0; c0 < wk1; c0 += CK) {
-            if (c0 != wk0) {
-                __syncthreads();
-                int n_lo, n_hi;
-                new_rows(c0, n_lo, n_hi);
-                if (n_lo + ri < n_hi) load_row(n_lo + ri);
-                issue_kv(K0, V0, c0);
-            }
-            sub_chunk(c0, K0, V0);
+        // the sub-chunks alternate between the stages (the first two's copies went out above). Each
+        // stage is refilled two sub-chunks ahead after a barrier (every wave has read it), also
+        // past the last sub-chunk, so every stage read follows the same copies on every path; the
+        // stages are named in each call, so the compiler sees that the copies in flight write the
+        // other stage. The copies still in flight at the end are waited for before the exit.
+        for (int c0 = wk0; c0 < wk1; c0 += 2 * CK) {
+            sub_chunk(c0, K0, V0, false);
+            lds_barrier();
+            issue_kv(K0, V0, c0 + 2 * CK);
+            if (c0 + CK < wk1) sub_chunk(c0 + CK, K1, V1, false);
+            lds_barrier();
+            issue_kv(K1, V1, c0 + 3 * CK);
         }
+        wait_vmcnt<0>();
     } else if (wk0 < wk1) {
-        sub_chunk(wk0, K0, V0);   // the only sub-chunk
+        sub_chunk(wk0, K0, V0, true);   // the only sub-chunk
     }
 
     // 7. this workgroup's partial: unnormalised O (each wave its dims), the running max and sum
+    constexpr int PLD = attn_part_ld(HD);
     const size_t tile_base = ((size_t)qt * a.nkv + g) * a.n_chunks;
-    float* part = a.part + (tile_base + chunk) * 16 * (HD + 2);
+    float* part = a.part + (tile_base + chunk) * 16 * PLD + (size_t)col * PLD;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int qvl = 4 * grp + r;
-#pragma unroll
-        for (int d = 0; d < NDT; ++d) part[(size_t)qvl * (HD + 2) + wave * DW + 16 * d + col] = o[d][r];
-        if (wave == 0 && col == 0) {
-            part[(size_t)qvl * (HD + 2) + HD] = m_run[r];
-            part[(size_t)qvl * (HD + 2) + HD + 1] = l_run[r];
-        }
+    for (int d = 0; d < NDT; ++d) *(floatx4*)&part[wave * DW + 16 * d + 4 * grp] = o[d];
+    if (wave == 0 && grp == 0) {
+        part[HD] = m_run;
+        part[HD + 1] = l_run;
     }
 }
 
 // Merge of the chunks of one (q tile, KV head): one 256-thread block per (query vector, 64 dims).
 // Wave w takes the chunks [w q, (w + 1) q), q = ceil(n_chunks / 4) <= QMAX: lane d loads its dim of
-// every chunk, lane j the running maximum and sum of chunk w q + j, all in one round of loads. The
-// chunk weights are computed once per chunk (lane j) and broadcast from it. Every sum runs in a
-// fixed order (butterfly over the lanes, chunks in order, then the waves in order).
+// every chunk, lane j the running maximum and sum of chunk w q + j, and every wave the maxima of all
+// chunks (lane j those of chunks j + 64 u), all in one round of loads, so each wave has the overall
+// maximum without an exchange. Chunk indices past the last chunk are clamped to it for the loads
+// and masked after. The chunk weights are computed once per chunk (lane j) and broadcast from it.
+// Every sum runs in a fixed order (within the 16-lane rows, across the rows, chunks in order, then
+// the waves in order).
 template <int HD, int QMAX>   // QMAX: chunks per wave at most (32, or 64 for up to kAttnMaxChunks)
 __global__ __launch_bounds__(256) void k_attn_combine(AttnK a) {
     static_assert(QMAX <= 64, "one lane per chunk of a wave");
-    __shared__ float mxw[4], denw[4], numw[4][64];
+    constexpr int NU = (4 * QMAX + 63) / 64;   // rounds of 64 chunk maxima
+    __shared__ float denw[4], numw[4][64];
     const int dgroups = HD / 64;
     const int dg = blockIdx.x % dgroups;
     const int qvl = (blockIdx.x / dgroups) % 16;
@@ -793,28 +900,29 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnK a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nc = a.n_chunks;
     const int q = (nc + 3) / 4;
-    const size_t cstride = (size_t)16 * (HD + 2);
-    const float* base = a.part + (size_t)tile * nc * cstride + (size_t)qvl * (HD + 2);
+    constexpr int PLD = attn_part_ld(HD);
+    const size_t cstride = (size_t)16 * PLD;
+    const float* base = a.part + (size_t)tile * nc * cstride + (size_t)qvl * PLD;
     const int d = dg * 64 + lane;
     const int cw = wave * q;                              // this wave's first chunk
     const int nw = max(0, min(q, nc - cw));               // and its number of chunks
     float v[QMAX];
 #pragma unroll
-    for (int i = 0; i < QMAX; ++i) v[i] = i < nw ? base[(size_t)(cw + i) * cstride + d] : 0.f;
+    for (int i = 0; i < QMAX; ++i) v[i] = base[(size_t)min(cw + i, nc - 1) * cstride + d];
+    const float* pj = base + (size_t)min(cw + lane, nc - 1) * cstride + HD;
+    const float mj_raw = pj[0], sj_raw = pj[1];
+    float mu[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) mu[u] = base[(size_t)min(lane + 64 * u, nc - 1) * cstride + HD];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+        if (lane + 64 * u < nc) mx = fmaxf(mx, mu[u]);
+    mx = wave64_max(mx);
     const bool lj = lane < nw;
-    const float* pj = base + (size_t)(cw + (lj ? lane : 0)) * cstride + HD;
-    const float mj = lj ? pj[0] : -INFINITY;
-    const float sj = lj ? pj[1] : 0.f;
-    float mx = mj;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if (lane == 0) mxw[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(mxw[0], mxw[1]), fmaxf(mxw[2], mxw[3]));
+    const float mj = lj ? mj_raw : -INFINITY;
     const float ej = mj == -INFINITY ? 0.f : expf(mj - mx);
-    float den = ej * sj;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o);
+    const float den = wave64_sum(lj ? ej * sj_raw : 0.f);
     float num = 0.f;
 #pragma unroll
     for (int i = 0; i < QMAX; ++i)
@@ -1120,7 +1228,7 @@ AttnK make_attn(const Attn& x) {
         a.spw = 1;
         a.n_chunks = subs;
     } else {
-        const int per_cu = std::max(1, std::min(2, (int)(kLdsPerCu / attn_lds_bytes(x.hd, x.kv_bf16 != 0))));
+        const int per_cu = std::max(1, std::min(2, (int)(kLdsPerCu / attn_lds_bytes(x.hd, x.kv_bf16 != 0, true))));
         const int nch = std::max(1, std::min(kAttnMaxChunks, per_cu * x.n_cu / tiles));
         a.spw = (subs + nch - 1) / nch;
         a.n_chunks = (subs + a.spw - 1) / a.spw;
@@ -1134,7 +1242,7 @@ AttnK make_attn(const Attn& x) {
 
 size_t attn_part_floats_needed(const Attn& x) {
     const AttnK a = make_attn(x);
-    return (size_t)a.n_qt * a.nkv * a.n_chunks * 16 * (x.hd + 2);
+    return (size_t)a.n_qt * a.nkv * a.n_chunks * 16 * attn_part_ld(x.hd);
 }
 
 namespace {
@@ -1157,7 +1265,8 @@ hipError_t launch_attention(const Attn& x, hipStream_t st) {
     const AttnK a = make_attn(x);
     if (attn_part_floats_needed(x) > x.part_floats || a.n_qt * a.nkv > x.n_counters) return hipErrorInvalidValue;
     if (a.n_chunks > kAttnMaxChunks) return hipErrorInvalidValue;
-    const int grid = a.n_chunks * a.nkv * a.n_qt;
+    if (a.ring_cap > 0 && a.ring_cap < 4) return hipErrorInvalidValue;   // the copies step slots by 4
+    const int grid = (a.n_chunks * a.nkv + 7) / 8 * 8 * a.n_qt;
     const int cgrid = a.n_qt * a.nkv * 16 * (x.hd / 64);
     switch (x.hd) {
         case 64: launch_attn<64>(a, grid, cgrid, st); break;
