@@ -676,7 +676,11 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
             // only the workgroup that holds the pass's positions has any)
             int p_lo, p_hi;
             new_rows(wk0, p_lo, p_hi);
-            load_row(p_lo + ri, p_lo + ri < p_hi);
+            // waves without a new row issue nothing; with bf16 planes the loads are issued by every
+            // thread instead (rows of no one read row 0 at position 0), since the compiler would
+            // otherwise round the V rows to bf16 inside the branch and wait for them there
+            if constexpr (KVB) load_row(p_lo + ri, p_lo + ri < p_hi);
+            else if (p_lo + ri < p_hi) load_row(p_lo + ri);
         }
         asm volatile("" ::: "memory");   // these loads leave before the K/V copies
         __builtin_amdgcn_sched_barrier(0);
