@@ -571,6 +571,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
     const int ri = tid >> 4, jr = tid & 15;
     float kr0[PPT], kr1[PPT], vr0[PPT], vr1[PPT], ssr = 0.f;
     float2 csr[PPT];
+    uint32_t gkw0[PPT / 2], gkw1[PPT / 2];   // the K gains, raw (widened in store_row)
     // has == false: the thread has no row; it loads row 0 at position 0 (readable, unused), so the
     // loads need no branch (a load under a branch is waited for where the branches join)
     auto load_row = [&](int p, bool has = true) __attribute__((always_inline)) {
@@ -589,6 +590,11 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         // where they are used (store_row)
         ssr = *(a.qk_norm && jr < HD / 16 ? a.ss + (size_t)r * (a.ldq / 16) + (qd + g * HD) / 16 + jr
                                            : (const float*)a.rope);
+        // the K gains with the row (no round trip of their own in store_row); without QK-norm they
+        // read the RoPE table (unused)
+        const uint16_t* gks = a.qk_norm ? a.k_norm : (const uint16_t*)a.rope;
+        load_bf16_raw<PPT>(gkw0, gks + d0);
+        load_bf16_raw<PPT>(gkw1, gks + d0 + H2);
     };
     auto store_row = [&](int p, int c0, TT (*Kt)[LDK], TT (*Vt)[LDV]) __attribute__((always_inline)) {
         const float ssv = a.qk_norm && jr < HD / 16 ? ssr : 0.f;
@@ -598,8 +604,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         const int d0 = jr * PPT;
         float gk0[PPT], gk1[PPT], k0[PPT], k1[PPT];
         if (a.qk_norm) {
-            load_bf16_vec<PPT>(gk0, a.k_norm + d0);
-            load_bf16_vec<PPT>(gk1, a.k_norm + d0 + H2);
+            widen_bf16<PPT>(gk0, gkw0);
+            widen_bf16<PPT>(gk1, gkw1);
         } else {
 #pragma unroll
             for (int i = 0; i < PPT; ++i) gk0[i] = gk1[i] = 1.f;
@@ -671,14 +677,15 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
         // (a load under a branch is waited for where the branches join)
         const bool has_ss = a.qk_norm && j < HD / 16;
         const float ssq_raw = *(has_ss ? a.ss + (size_t)m * (a.ldq / 16) + h * (HD / 16) + j : (const float*)a.rope);
+        // the first sub-chunk's new rows (the two-stage form loads them where it stores them: only
+        // the workgroup that holds the pass's positions has any). With fp32 planes only waves with
+        // a new row issue the loads; with bf16 planes every thread does (rows of no one read row 0
+        // at position 0), since the compiler would otherwise round the V rows to bf16 inside the
+        // branch and wait for them there, before the copies. (Issuing them after the copies instead
+        // made the query wait for the copies, with the same step time.)
         if constexpr (!MULTI) {
-            // the first sub-chunk's new rows (the two-stage form loads them where it stores them:
-            // only the workgroup that holds the pass's positions has any)
             int p_lo, p_hi;
             new_rows(wk0, p_lo, p_hi);
-            // waves without a new row issue nothing; with bf16 planes the loads are issued by every
-            // thread instead (rows of no one read row 0 at position 0), since the compiler would
-            // otherwise round the V rows to bf16 inside the branch and wait for them there
             if constexpr (KVB) load_row(p_lo + ri, p_lo + ri < p_hi);
             else if (p_lo + ri < p_hi) load_row(p_lo + ri);
         }
@@ -888,7 +895,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnK a) {
 // and masked after. The chunk weights are computed once per chunk (lane j) and broadcast from it.
 // Every sum runs in a fixed order (within the 16-lane rows, across the rows, chunks in order, then
 // the waves in order).
-template <int HD, int QMAX>   // QMAX: chunks per wave at most (32, or 64 for up to kAttnMaxChunks)
+template <int HD, int QMAX>   // QMAX: chunks per wave at most (16, 32, or 64 for up to kAttnMaxChunks)
 __global__ __launch_bounds__(256) void k_attn_combine(AttnK a) {
     static_assert(QMAX <= 64, "one lane per chunk of a wave");
     constexpr int NU = (4 * QMAX + 63) / 64;   // rounds of 64 chunk maxima
@@ -1260,7 +1267,9 @@ void launch_attn(const AttnK& a, int grid, int cgrid, hipStream_t st) {
         else hipLaunchKernelGGL((k_attention<HD, false, false>), dim3(grid), dim3(256), 0, st, a);
     }
     static_assert(kAttnMaxChunks <= 4 * 64, "the combine's wider form takes 64 chunks per wave");
-    if (a.n_chunks <= 128) hipLaunchKernelGGL((k_attn_combine<HD, 32>), dim3(cgrid), dim3(256), 0, st, a);
+    // chunks per wave of the combine: the smallest form that holds them (every form issues QMAX loads)
+    if (a.n_chunks <= 64) hipLaunchKernelGGL((k_attn_combine<HD, 16>), dim3(cgrid), dim3(256), 0, st, a);
+    else if (a.n_chunks <= 128) hipLaunchKernelGGL((k_attn_combine<HD, 32>), dim3(cgrid), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((k_attn_combine<HD, 64>), dim3(cgrid), dim3(256), 0, st, a);
 }
 }  // namespace

@@ -90,9 +90,12 @@ def test_ring_equals_linear_over_a_state_sequence(kv_bf16):
 def test_ring_full_size_4096_equals_linear():
     """Target-shaped stack at 4096 cached positions: ring planes (window 512: 528 slots on the 20
     own sliding layers) against linear planes, k = 8 and k = 16, logits bit-identical, commit counts
-    per layer, and the arena smaller by the planes' difference."""
+    per layer, and the arena smaller by the planes' difference. Then a prefill of 72 tokens (a
+    64-row chunk, whose attention walks several sub-chunks per workgroup through two LDS stages,
+    and an 8-row chunk) on both: last-token logits bit-identical and the window's rows of a ring
+    plane equal to the linear plane's."""
     P = 4096
-    base = synth.target_model(max_ctx=P + 64)
+    base = synth.target_model(max_ctx=P + 128)
     ring = dataclasses.replace(base, kv_ring=1)
     w = synth.make_weights(base, 0, threads=16)
     kv = synth.make_kv(base, P, 0, threads=16)
@@ -113,6 +116,21 @@ def test_ring_full_size_4096_equals_linear():
         want = [_keep(ring, l, P + k // 2) * 2 * ring.kv_width(l) for l in range(ring.n_layers)]
         assert gr.plane_floats().tolist() == want
         gr.set_positions(P)
+    gl.set_positions(P)
+    n = 72
+    toks = torch.from_numpy(synth.tokens(0, "ring.full.prefill", n, base.vocab)).cuda()
+    outs = []
+    for g in (gl, gr):
+        last = torch.empty(base.vocab, dtype=torch.float32, device="cuda")
+        g.prefill(toks, last)
+        torch.cuda.synchronize()
+        outs.append(last.cpu().numpy())
+        assert g.positions_held() == P + n
+    assert np.array_equal(outs[0], outs[1]), "prefill logits"
+    l_ring = next(l for l in range(ring.n_layers) if ring.own(l) and ring.layers[l].attn == synth.ATTN_SLIDING)
+    a, b = gl.get_kv(l_ring, P + n), gr.get_kv(l_ring, P + n)
+    win = ring.layers[l_ring].window
+    assert np.array_equal(a[P + n - win:], b[P + n - win:]), "ring rows after the prefill"
 
 
 def test_ring_refused_on_a_draft():
