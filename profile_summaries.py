@@ -5,6 +5,7 @@ usage (from the repository root):
   python profile_summaries.py kernel-trace <rocprofv3 output dir> [kernels per pass, default 256]
   python profile_summaries.py pmc-traffic <fetch dir> <write dir> <probe MiB> <q|k|v bytes> <o bytes> <gate|up bytes> <down bytes>
   python profile_summaries.py mfma <rocprofv3 output dir>
+  python profile_summaries.py attn-traffic <fetch dir> <write dir> <probe MiB> <one-chunk K/V bytes> <two-stage K/V bytes>
 
 kernel-trace: the per-kernel statistics of a --kernel-trace --stats csv run, then the median of the
   first 7 verify passes (embed ... accept) with every kernel labelled by its place in the layer.
@@ -13,6 +14,11 @@ pmc-traffic: two --pmc runs (FETCH_SIZE, then WRITE_SIZE) of bench.py --no-graph
   written); the Q4_1 GEMM dispatches of the verify passes are classed by their place in each layer
   (the byte arguments: each class's algorithmic bytes per launch, bench.py's gemm_alg_bytes), and
   the whole Q4_1 stream of a pass (one launch of each class per layer) is summed from the classes.
+attn-traffic: two --pmc runs (FETCH_SIZE, then WRITE_SIZE) of bench.py --no-graph --copy-probe-mib N
+  restricted to the attention kernels and the copy probe; each counter scaled by the copy probe as in
+  pmc-traffic; per attention form (one sub-chunk per workgroup, two-stage) and for the combine, the
+  bytes per dispatch against the K/V bytes a launch of that form reads (the byte arguments: rows read
+  x 2 x KV width x element size, one layer of each form at the run's context).
 mfma: a --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_INSTS_VALU_MFMA_MOPS_F32 (of bench.py, or
   of bench.py --prefill N for the 64-row chunks): per Q4_1 GEMM class, the MFMA work per launch (512 flops per MOPS unit, as rocprofv3's MfmaFlops metric counts
   it), its rate over the dispatches' durations and the fraction of the 2.5 PFLOP/s dense bf16 peak.
@@ -175,8 +181,46 @@ def mfma(ARGV):
     print(" launch, 0 where there is none)")
 
 
+def attn_traffic(ARGV):
+    fetch_dir, write_dir, probe_mib = ARGV[1], ARGV[2], int(ARGV[3])
+    alg = {"one sub-chunk": float(ARGV[4]), "two-stage": float(ARGV[5])}
+    def load(d, counter):
+        f = glob.glob(f"{d}/**/*counter_collection.csv", recursive=True)[0]
+        by = collections.OrderedDict()
+        for r in csv.DictReader(open(f)):
+            if r['Counter_Name'] != counter:
+                continue
+            did = int(r['Dispatch_Id'])
+            if did in by: by[did][1] += float(r['Counter_Value'])
+            else: by[did] = [r['Kernel_Name'], float(r['Counter_Value'])]
+        return by
+    def form(name):
+        if 'k_attn_combine' in name: return 'combine'
+        if 'k_attention<' in name: return 'two-stage' if name.split('>')[0].endswith('true') else 'one sub-chunk'
+        return None
+    res = {}
+    for d, counter in [(fetch_dir, 'FETCH_SIZE'), (write_dir, 'WRITE_SIZE')]:
+        by = load(d, counter)
+        probe = [v for n, v in by.values() if 'elementwise' in n and 'neg' in n.lower()][:3]
+        scale = probe_mib * 1024 / (sum(probe) / len(probe))
+        print(f"{counter}: copy probe {sum(probe) / len(probe):.1f} KiB per dispatch ({len(probe)} dispatches) -> scale {scale:.4f}")
+        for n, v in by.values():
+            f = form(n)
+            if f: res.setdefault(f, {}).setdefault(counter, []).append(v * scale * 1024)
+    for f in ('one sub-chunk', 'two-stage', 'combine'):
+        if f not in res: continue
+        fe, wr = res[f]['FETCH_SIZE'], res[f]['WRITE_SIZE']
+        fm, wm = sorted(fe)[len(fe) // 2], sorted(wr)[len(wr) // 2]
+        print(f"\n{f}: {len(fe)} dispatches (median of each counter)")
+        print(f"  FETCH_SIZE -> {fm / 1e6:.2f} MB, WRITE_SIZE -> {wm / 1e6:.2f} MB per dispatch")
+        if f in alg:
+            print(f"  K/V bytes a launch reads: {alg[f] / 1e6:.2f} MB; fetched / K/V: {fm / alg[f]:.3f}")
+    sh = hashlib.sha256(open('block_verify_forward_amd/csrc/layer_ops.hip', 'rb').read()).hexdigest()
+    print(f"\nlayer_ops_hip_sha256: {sh}")
+
+
 if __name__ == "__main__":
-    cmds = {"kernel-trace": kernel_trace, "pmc-traffic": pmc_traffic, "mfma": mfma}
+    cmds = {"kernel-trace": kernel_trace, "pmc-traffic": pmc_traffic, "mfma": mfma, "attn-traffic": attn_traffic}
     if len(sys.argv) < 3 or sys.argv[1] not in cmds:
         sys.exit(__doc__)
     cmds[sys.argv[1]](sys.argv[1:])
