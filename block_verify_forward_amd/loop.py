@@ -4,7 +4,7 @@ verifies [last token, proposals] in one batched pass, the greedy longest-prefix 
 emitted tokens and commit_verify_rows keeps the rows on the accepted path.
 
 Sequencing only: every step runs in the library's kernels on the models' stream; the host reads
-the accepted count (and the emitted tokens, for the record) once per round. The proposals are
+the accepted count and the emitted tokens in one copy per round. The proposals are
 written by the draft straight into the verify's token rows, the last emitted token is copied on the
 device into row 0 of the next round, and the taps of the accepted rows become the draft's next
 context rows without leaving the device.
@@ -40,8 +40,10 @@ class SpecLoop:
         self.toks = torch.zeros(block, dtype=torch.int32, device=dev)            # [last, d_1 .. d_{B-1}]
         self.logits = torch.empty((block, m.vocab), dtype=torch.float32, device=dev)
         self.taps = torch.empty((block, len(m.tap_layers), m.hidden), dtype=torch.int16, device=dev)
-        self.out = torch.zeros(block, dtype=torch.int32, device=dev)
-        self.n_acc = torch.zeros(1, dtype=torch.int32, device=dev)
+        # the emitted tokens and the accepted count side by side, so one copy to the host reads both
+        self.res = torch.zeros(block + 1, dtype=torch.int32, device=dev)
+        self.out = self.res[:block]
+        self.n_acc = self.res[block:]
         self.add = torch.zeros(block - 1, dtype=torch.float32, device=dev)
         self.draws = torch.zeros(block, dtype=torch.int32, device=dev)
         self.temperature = float(temperature)
@@ -73,9 +75,10 @@ class SpecLoop:
         else:
             self.T.accept_greedy(self.logits, self.toks, self.out, self.n_acc)
         self.n_rounds += 1
-        a = int(self.n_acc.item())
+        res = self.res.cpu().numpy()   # one read of the round's results
+        a = int(res[B])
         self.T.commit_verify_rows(a + 1)
-        emitted = self.out[: a + 1].cpu().numpy().tolist()
+        emitted = res[: a + 1].tolist()
         self.toks[0:1].copy_(self.out[a:a + 1])
         self.n_new = a + 1
         return a, emitted
