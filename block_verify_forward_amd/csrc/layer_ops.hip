@@ -278,21 +278,47 @@ __global__ void k_sumsq(const float* __restrict__ x, int ldx, int H, float* __re
 }
 
 // out[r][i] = bf16(x[r][i] / sqrt(mean_i x[r][i]^2 + eps) * g[i]); one workgroup per row.
+// One 256-thread block per row: every float4 of the row is loaded before the sum of squares (rows
+// of up to 8192 values stay in registers, so the output needs no second read of x; longer rows
+// continue in a loop), then bf16(x * inv * gain) is written four values at a time.
+constexpr int kNormPieces = 8;   // float4 pieces per thread held in registers
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int ldx, int H,
                                                  const uint16_t* __restrict__ g, float eps, uint16_t* __restrict__ out,
                                                  int ldo) {
     __shared__ float red[4];
     const int r = blockIdx.x;
     const float* xr = x + (size_t)r * ldx;
+    uint16_t* orow = out + (size_t)r * ldo;
+    float4 v[kNormPieces];
+#pragma unroll
+    for (int j = 0; j < kNormPieces; ++j) {
+        const int i = 4 * threadIdx.x + 1024 * j;
+        v[j] = i < H ? *(const float4*)(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) ss = fmaf(xr[i], xr[i], ss);
+#pragma unroll
+    for (int j = 0; j < kNormPieces; ++j) ss += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
+    for (int i = 4 * threadIdx.x + 1024 * kNormPieces; i < H; i += 1024) {
+        const float4 t = *(const float4*)(xr + i);
+        ss += (t.x * t.x + t.y * t.y) + (t.z * t.z + t.w * t.w);
+    }
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     ss = red[0] + red[1] + red[2] + red[3];
     const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += 256)
-        out[(size_t)r * ldo + i] = f32_to_bf16(xr[i] * inv * bf16_to_f32(g[i]));
+    auto put = [&](int i, const float4& t) {
+        const uint2 gw = *(const uint2*)(g + i);
+        const float g0 = __builtin_bit_cast(float, gw.x << 16), g1 = __builtin_bit_cast(float, gw.x & 0xffff0000u);
+        const float g2 = __builtin_bit_cast(float, gw.y << 16), g3 = __builtin_bit_cast(float, gw.y & 0xffff0000u);
+        *(uint2*)(orow + i) = make_uint2(pack_bf16x2(t.x * inv * g0, t.y * inv * g1), pack_bf16x2(t.z * inv * g2, t.w * inv * g3));
+    };
+#pragma unroll
+    for (int j = 0; j < kNormPieces; ++j) {
+        const int i = 4 * threadIdx.x + 1024 * j;
+        if (i < H) put(i, v[j]);
+    }
+    for (int i = 4 * threadIdx.x + 1024 * kNormPieces; i < H; i += 1024) put(i, *(const float4*)(xr + i));
 }
 
 // One wave per (row, head): per-head RMSNorm (optional), rotate-half RoPE at the row's position;
