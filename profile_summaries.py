@@ -8,7 +8,8 @@ usage (from the repository root):
   python profile_summaries.py attn-traffic <fetch dir> <write dir> <probe MiB> <one-chunk K/V bytes> <two-stage K/V bytes>
 
 kernel-trace: the per-kernel statistics of a --kernel-trace --stats csv run, then the median of the
-  first 7 verify passes (embed ... accept) with every kernel labelled by its place in the layer.
+  first 7 verify passes (embed ... accept) with every kernel labelled by its place in the layer (the
+  statistics alone where the run holds no verify pass, as a prefill run does).
 pmc-traffic: two --pmc runs (FETCH_SIZE, then WRITE_SIZE) of bench.py --no-graph --copy-probe-mib N;
   each counter is scaled by what it reads for the copy probe (torch neg over N MiB: N MiB read, N MiB
   written); the Q4_1 GEMM dispatches of the verify passes are classed by their place in each layer
@@ -35,18 +36,18 @@ def kernel_trace(ARGV):
     stats = glob.glob(f"{d}/**/*kernel_stats.csv", recursive=True)
     trace = glob.glob(f"{d}/**/*kernel_trace.csv", recursive=True)
     rows = list(csv.DictReader(open(stats[0])))
-    print(f"{'kernel':40s} {'calls':>7s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'share %':>8s}")
-    for r in rows:
-        print(f"{r['Name'][:40]:40s} {int(r['Calls']):7d} {float(r['AverageNs'])/1e3:9.2f} {float(r['MinNs'])/1e3:9.2f} {float(r['MaxNs'])/1e3:9.2f} {float(r['Percentage']):8.2f}")
-    tr = list(csv.DictReader(open(trace[0])))
-    tr.sort(key=lambda r: int(r['Start_Timestamp']))
-    names = [r['Kernel_Name'] for r in tr]
     def short(n):
         n = n.replace('void ', '')
         for pre in ('bvf::(anonymous namespace)::', 'bvf::'):
             n = n.replace(pre, '')
         i = n.find('(')
         return n[:i] if i > 0 else n
+    print(f"{'kernel':48s} {'calls':>7s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'share %':>8s}")
+    for r in rows:
+        print(f"{short(r['Name'])[:48]:48s} {int(r['Calls']):7d} {float(r['AverageNs'])/1e3:9.2f} {float(r['MinNs'])/1e3:9.2f} {float(r['MaxNs'])/1e3:9.2f} {float(r['Percentage']):8.2f}")
+    tr = list(csv.DictReader(open(trace[0])))
+    tr.sort(key=lambda r: int(r['Start_Timestamp']))
+    names = [r['Kernel_Name'] for r in tr]
     # last pass: from the last k_embed that is followed by a k_accept before the next k_embed
     emb = [i for i, n in enumerate(names) if 'k_embed' in n]
     passes = []
@@ -57,6 +58,9 @@ def kernel_trace(ARGV):
             passes.append((i, acc[0]))
     want = int(ARGV[2]) if len(ARGV) > 2 else 256
     cands = [p for p in passes if p[1] - p[0] + 1 == want][:7]
+    if not cands:
+        print(f"\nno verify pass of {want} kernels in this trace (a prefill run has none)")
+        return
     dur = lambda p: int(tr[p[1]]['End_Timestamp']) - int(tr[p[0]]['Start_Timestamp'])
     i0, i1 = sorted(cands, key=dur)[len(cands) // 2]   # the median of the k = 8 graph passes
     seg = tr[i0:i1 + 1]
