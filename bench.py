@@ -194,6 +194,7 @@ def run_loop(args):
     D.set_context(kvd, args.ctx)
     if not args.no_graph:
         T.set_graph_mode(True)
+        D.set_graph_mode(True)
     rounds_max = args.loop
     steer = synth.accept_lengths(args.seed, rounds_max, max_a=7)
     loop = SpecLoop(T, D, 8, temperature=args.temperature, seed=args.seed)
@@ -232,6 +233,7 @@ def run_loop(args):
         "mean_accepted_drafts": round(float(np.mean(loop.accepted)), 3),
         "ms_per_round": round(ms / rounds, 4),
         "verify_graph_captures": T.graph_captures(),
+        "draft_graph_captures": D.graph_captures(),
     }
     print(json.dumps(res), flush=True)
 

@@ -153,8 +153,21 @@ struct bvf_model {
     int64_t n_captures = 0;
     int32_t g_k = 0;
     const void *g_tok = nullptr, *g_lg = nullptr, *g_taps = nullptr;
+    // graph replays of the draft block: one capture per context-row count n_new, valid for one key
+    // (the layers' attention plans, block, buffers, embedding scale, mask token, target model); the
+    // captured attention reads the draft's positions held from dpos like the verify pass
+    struct DraftGraph {
+        hipGraphExec_t exec = nullptr;
+        int64_t plan = -1;
+        int32_t block = 0, mask = 0;
+        float scale = 0.f;
+        const void* ptr[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    };
+    DraftGraph dg[kMaxRows + 1];
     ~bvf_model() {
         if (gexec) (void)hipGraphExecDestroy(gexec);
+        for (DraftGraph& g : dg)
+            if (g.exec) (void)hipGraphExecDestroy(g.exec);
         if (cap_st) (void)hipStreamDestroy(cap_st);
     }
 };
@@ -735,6 +748,84 @@ hipError_t enqueue_verify(bvf_model* m, hipStream_t st, const int32_t* d_tokens,
     m->st = saved;
     return e;
 }
+
+// The draft's context rows from their taps: fc ([CARD] "Draft": the tapped target features
+// projected to the hidden size), then RMSNorm with the hidden-norm gain, into the rows of the A
+// buffer that follow the B block rows.
+hipError_t enqueue_draft_fc(bvf_model* dr, const uint16_t* d_new_taps, int n_new, int B, hipStream_t st) {
+    if (n_new == 0) return hipSuccess;
+    const int H = dr->d.hidden, T = dr->d.n_taps;
+    GemmLaunch g;
+    g.w.codes = (const uint8_t*)dr->fc;
+    g.w.n_tiles = H / kTile;
+    g.w.G = T * H / kSuper;
+    g.w.K = T * H;
+    g.fmt = W_BF16;
+    g.epi = EPI_STORE;
+    g.n_run_tiles = g.w.n_tiles;
+    g.A = d_new_taps; g.lda = T * H; g.M = n_new; g.y = dr->fcout; g.ldy = H;
+    g.partial = dr->partial; g.partial_floats = kPartialFloats; g.counters = dr->counters; g.n_counters = kCounters;
+    g.n_cu = dr->n_cu;
+    hipError_t e = launch_gemm(g, st);
+    if (e != hipSuccess) return e;
+    return launch_rmsnorm(dr->fcout, H, n_new, H, dr->hidden_norm, dr->d.rms_eps, dr->act + (size_t)B * H, H, st);
+}
+
+// Attention arguments of draft layer l for a block of B rows after n_new context rows ([CARD]
+// "Draft"; [PR2236] section 2): the block rows 0..B-1 sit at s .. s + B - 1 and the context rows
+// B.. at s_old .. s - 1 (s = s_old + n_new, s_old = the draft's positions held); both are appended,
+// and the block sees the last draft_window context positions and every block row. With dpos the
+// positions held are read from device memory (graph replays).
+Attn draft_attn(bvf_model* dr, int l, int n_new, int B, const int64_t* dpos) {
+    Layer& L = dr->L[l];
+    const int s_old = (int)dr->held, s_new = s_old + n_new;
+    Attn at = attn_for(dr, L, B);
+    at.plane = L.plane; at.kv_bf16 = dr->d.kv_bf16; at.own = 1;
+    at.causal = 0; at.pos0 = s_new;
+    at.ctx_lo = (dr->d.draft_window > 0 && s_new - dr->d.draft_window > 0) ? s_new - dr->d.draft_window : 0;
+    at.ctx_hi = s_new + B - 1;
+    at.np0 = s_old; at.np1 = s_new + B; at.sp = s_new; at.r_lo = B; at.r_hi = 0;
+    at.window = dr->d.draft_window; at.n_ctx = n_new; at.dpos = dpos;
+    return at;
+}
+
+// The draft block's launches on stream st: the context rows (fc), the block rows [last token,
+// mask x (B - 1)] through the draft layers, the final norm and the target's head on rows 1..B-1,
+// their argmax. The attention norm runs as its own kernel (the block's q|k|v also takes the
+// context rows, normalised by fc's hidden norm); the MLP norm is folded into the gate|up GEMM's
+// staging and the final norm into the head's, from the per-tile sums of squares that the o and down
+// GEMMs leave in ss_x.
+hipError_t enqueue_draft(bvf_model* dr, const bvf_model* tg, const uint16_t* d_new_taps, int n_new,
+                         const int32_t* d_last_token, int B, float embedding_scale, int mask_token, int32_t* d_proposals,
+                         float* d_logits, hipStream_t st, const int64_t* dpos) {
+    const int H = dr->d.hidden, V = tg->d.vocab;
+    hipError_t e = enqueue_draft_fc(dr, d_new_taps, n_new, B, st);
+    if (e != hipSuccess) return e;
+    if ((e = launch_embed(d_last_token, mask_token, B, tg->embed, V, H, embedding_scale, dr->x, nullptr, st)) != hipSuccess)
+        return e;
+    for (int l = 0; l < dr->d.n_layers; ++l) {
+        Layer& L = dr->L[l];
+        if ((e = launch_rmsnorm(dr->x, H, B, H, L.attn_norm, dr->d.rms_eps, dr->act, H, st)) != hipSuccess) return e;
+        GemmLaunch g = gemm_for(dr, L.qkv, EPI_STORE);
+        g.A = dr->act; g.lda = H; g.M = B + n_new; g.y = dr->qkv; g.ldy = L.qkv.n_out; g.ss_out = dr->ss_qkv;
+        if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+        if ((e = launch_attention(draft_attn(dr, l, n_new, B, dpos), st)) != hipSuccess) return e;
+        g = gemm_for(dr, L.o, EPI_RESID);
+        g.A = dr->obuf; g.lda = L.qd; g.M = B; g.y = dr->x; g.ldy = H; g.ss_out = dr->ss_x;
+        if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+        g = gemm_for(dr, L.gu, EPI_SWIGLU);
+        g.xsrc = dr->x; g.ldx = H; g.ss_in = dr->ss_x; g.n_ss = H / kTile; g.gain = L.mlp_norm; g.eps = dr->d.rms_eps;
+        g.M = B; g.out = dr->mbuf; g.ldo = L.d.ffn;
+        if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+        g = gemm_for(dr, L.down, EPI_RESID);
+        g.A = dr->mbuf; g.lda = L.d.ffn; g.M = B; g.y = dr->x; g.ldy = H; g.ss_out = dr->ss_x;
+        if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+    }
+    float* logits = d_logits ? d_logits : dr->logits_scratch;
+    if ((e = launch_head(tg, nullptr, B - 1, logits, st, dr, dr->x, dr->final_norm, 1)) != hipSuccess) return e;
+    return launch_argmax_accept(logits, B - 1, V, nullptr, dr->am_val, dr->am_idx, argmax_blocks(V), nullptr, nullptr,
+                                d_proposals, st);
+}
 }  // namespace
 
 extern "C" {
@@ -1055,27 +1146,13 @@ bvf_status bvf_draft_block_forward(bvf_model* dr, const bvf_model* tg, const uin
     bvf_status stt = check_loaded(dr);
     if (stt) return stt;
     if (!(tg->loaded & (1u << BVF_EMBED))) return fail(BVF_E_STATE, "the target's embedding table is not loaded");
-    const int H = dr->d.hidden, T = dr->d.n_taps, B = block;
-    const int s_old = (int)dr->held, s_new = (int)s;
+    const int H = dr->d.hidden, B = block;
+    const int s_old = (int)dr->held;
     hipStream_t st = dr->st;
-    uint16_t* ctx_rows = dr->act + (size_t)B * H;   // context rows c follow the block rows in the A buffer
-    if (n_new > 0) {
-        GemmLaunch g;
-        g.w.codes = (const uint8_t*)dr->fc;
-        g.w.n_tiles = H / kTile;
-        g.w.G = T * H / kSuper;
-        g.w.K = T * H;
-        g.fmt = W_BF16;
-        g.epi = EPI_STORE;
-        g.n_run_tiles = g.w.n_tiles;
-        g.A = d_new_taps; g.lda = T * H; g.M = n_new; g.y = dr->fcout; g.ldy = H;
-        g.partial = dr->partial; g.partial_floats = kPartialFloats; g.counters = dr->counters; g.n_counters = kCounters;
-        g.n_cu = dr->n_cu;
-        HIP_TRY(launch_gemm(g, st));
-        HIP_TRY(launch_rmsnorm(dr->fcout, H, n_new, H, dr->hidden_norm, dr->d.rms_eps, ctx_rows, H, st));
-    }
     if (B == 0) {
         // append only: the context rows' K/V in every draft layer, no block
+        HIP_TRY(enqueue_draft_fc(dr, d_new_taps, n_new, B, st));
+        uint16_t* ctx_rows = dr->act + (size_t)B * H;
         for (int l = 0; l < dr->d.n_layers; ++l) {
             Layer& L = dr->L[l];
             GemmLaunch g = gemm_for(dr, L.qkv, EPI_STORE);
@@ -1092,39 +1169,45 @@ bvf_status bvf_draft_block_forward(bvf_model* dr, const bvf_model* tg, const uin
         dr->held = s;
         return ok();
     }
-    HIP_TRY(launch_embed(d_last_token, mask_token, B, tg->embed, V, H, embedding_scale, dr->x, nullptr, st));
-    const int ctx_lo = (dr->d.draft_window > 0 && s_new - dr->d.draft_window > 0) ? s_new - dr->d.draft_window : 0;
-    for (int l = 0; l < dr->d.n_layers; ++l) {
-        Layer& L = dr->L[l];
-        const int hd = L.d.head_dim;
-        HIP_TRY(launch_rmsnorm(dr->x, H, B, H, L.attn_norm, dr->d.rms_eps, dr->act, H, st));
-        GemmLaunch g = gemm_for(dr, L.qkv, EPI_STORE);
-        g.A = dr->act; g.lda = H; g.M = B + n_new; g.y = dr->qkv; g.ldy = L.qkv.n_out; g.ss_out = dr->ss_qkv;
-        HIP_TRY(launch_gemm(g, st));
-        // block rows 0..B-1 at s .. s+B-1 and context rows B.. at s_old .. s-1 are appended; the
-        // block sees the context window and all block rows
-        Attn at = attn_for(dr, L, B);
-        at.plane = L.plane; at.kv_bf16 = dr->d.kv_bf16; at.own = 1;
-        at.causal = 0; at.pos0 = s_new; at.ctx_lo = ctx_lo; at.ctx_hi = s_new + B - 1;
-        at.np0 = s_old; at.np1 = s_new + B; at.sp = s_new; at.r_lo = B; at.r_hi = 0;
-        HIP_TRY(launch_attention(at, st));
-        g = gemm_for(dr, L.o, EPI_RESID);
-        g.A = dr->obuf; g.lda = L.qd; g.M = B; g.y = dr->x; g.ldy = H;
-        HIP_TRY(launch_gemm(g, st));
-        HIP_TRY(launch_rmsnorm(dr->x, H, B, H, L.mlp_norm, dr->d.rms_eps, dr->act, H, st));
-        g = gemm_for(dr, L.gu, EPI_SWIGLU);
-        g.A = dr->act; g.lda = H; g.M = B; g.out = dr->mbuf; g.ldo = L.d.ffn;
-        HIP_TRY(launch_gemm(g, st));
-        g = gemm_for(dr, L.down, EPI_RESID);
-        g.A = dr->mbuf; g.lda = L.d.ffn; g.M = B; g.y = dr->x; g.ldy = H;
-        HIP_TRY(launch_gemm(g, st));
+    if (!dr->use_graph) {
+        HIP_TRY(enqueue_draft(dr, tg, d_new_taps, n_new, d_last_token, B, embedding_scale, mask_token, d_proposals, d_logits,
+                              st, nullptr));
+    } else {
+        // the layers' attention plans at these positions (a replay runs the plan it was captured with)
+        int64_t plan = 0;
+        for (int l = 0; l < dr->d.n_layers; ++l) plan = plan * 1000003 + attn_plan_key(draft_attn(dr, l, n_new, B, nullptr));
+        const void* ptr[5] = {d_new_taps, d_last_token, d_proposals, d_logits, tg};
+        bvf_model::DraftGraph& G = dr->dg[n_new];
+        bool same = G.exec && G.plan == plan && G.block == B && G.mask == mask_token && G.scale == embedding_scale;
+        for (int i = 0; i < 5 && same; ++i) same = G.ptr[i] == ptr[i];
+        if (!same) {
+            if (G.exec) {
+                HIP_TRY(hipGraphExecDestroy(G.exec));
+                G.exec = nullptr;
+            }
+            if (!dr->cap_st) HIP_TRY(hipStreamCreateWithFlags(&dr->cap_st, hipStreamNonBlocking));
+            hipGraph_t graph = nullptr;
+            HIP_TRY(hipStreamBeginCapture(dr->cap_st, hipStreamCaptureModeThreadLocal));
+            hipError_t e = enqueue_draft(dr, tg, d_new_taps, n_new, d_last_token, B, embedding_scale, mask_token, d_proposals,
+                                         d_logits, dr->cap_st, dr->dpos);
+            hipError_t e2 = hipStreamEndCapture(dr->cap_st, &graph);
+            if (e != hipSuccess || e2 != hipSuccess) {
+                if (graph) (void)hipGraphDestroy(graph);
+                return fail(BVF_E_DEVICE, "graph capture: %s", hipGetErrorString(e != hipSuccess ? e : e2));
+            }
+            e = hipGraphInstantiate(&G.exec, graph, nullptr, nullptr, 0);
+            (void)hipGraphDestroy(graph);
+            if (e != hipSuccess) {
+                G.exec = nullptr;
+                return fail(BVF_E_DEVICE, "graph instantiate: %s", hipGetErrorString(e));
+            }
+            G.plan = plan; G.block = B; G.mask = mask_token; G.scale = embedding_scale;
+            for (int i = 0; i < 5; ++i) G.ptr[i] = ptr[i];
+            ++dr->n_captures;
+        }
+        HIP_TRY(launch_set_i64(dr->dpos, dr->held, st));
+        HIP_TRY(hipGraphLaunch(G.exec, st));
     }
-    // rows 1 .. B-1 through the final norm and the target's head
-    HIP_TRY(launch_rmsnorm(dr->x + H, H, B - 1, H, dr->final_norm, dr->d.rms_eps, dr->act, H, st));
-    float* logits = d_logits ? d_logits : dr->logits_scratch;
-    HIP_TRY(launch_head(tg, dr->act, B - 1, logits, st, dr));
-    HIP_TRY(launch_argmax_accept(logits, B - 1, V, nullptr, dr->am_val, dr->am_idx, argmax_blocks(V), nullptr, nullptr,
-                                 d_proposals, st));
     dr->held = s;
     return ok();
 }

@@ -156,11 +156,16 @@ struct Attn {
     // causal passes: the key chunks are planned for rows at pos_plan .. pos_plan + M - 1 (pos_plan >=
     // pos0), so passes at positions up to pos_plan share one launch configuration; 0: at pos0
     int pos_plan = 0;
-    // causal passes replayed from a graph: the positions held P are read from *dpos at run time and
-    // the rows sit at P .. P + M - 1 (pos0, the new rows and the key range follow from P)
+    // passes replayed from a graph: the positions held P are read from *dpos at run time. Causal:
+    // the rows sit at P .. P + M - 1. Draft block: the n_ctx context rows at P .., the block rows after
+    // them, and window is the draft's context window. pos0, the new rows and the key range follow from P.
     const int64_t* dpos = nullptr;
+    int n_ctx = 0;
 };
 size_t attn_part_floats_needed(const Attn& a);
+// The launch configuration the attention takes for these arguments: chunks and sub-chunks per
+// workgroup (the merge order of the partials follows from it).
+int64_t attn_plan_key(const Attn& a);
 hipError_t launch_set_i64(int64_t* dst, int64_t v, hipStream_t st);
 hipError_t launch_attention(const Attn& a, hipStream_t st);
 

@@ -278,9 +278,9 @@ __global__ void k_sumsq(const float* __restrict__ x, int ldx, int H, float* __re
 }
 
 // out[r][i] = bf16(x[r][i] / sqrt(mean_i x[r][i]^2 + eps) * g[i]); one workgroup per row.
-// One 256-thread block per row: every float4 of the row is loaded before the sum of squares (rows
-// of up to 8192 values stay in registers, so the output needs no second read of x; longer rows
-// continue in a loop), then bf16(x * inv * gain) is written four values at a time.
+// One 256-thread block per row: every float4 of the row and its four gains are loaded before the
+// sum of squares (rows of up to 8192 values stay in registers, so the output needs no second read;
+// longer rows continue in a loop), then bf16(x * inv * gain) is written four values at a time.
 constexpr int kNormPieces = 8;   // float4 pieces per thread held in registers
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int ldx, int H,
                                                  const uint16_t* __restrict__ g, float eps, uint16_t* __restrict__ out,
@@ -290,10 +290,12 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
     const float* xr = x + (size_t)r * ldx;
     uint16_t* orow = out + (size_t)r * ldo;
     float4 v[kNormPieces];
+    uint2 gv[kNormPieces];   // the gains of the same pieces, loaded in the same round
 #pragma unroll
     for (int j = 0; j < kNormPieces; ++j) {
         const int i = 4 * threadIdx.x + 1024 * j;
         v[j] = i < H ? *(const float4*)(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        gv[j] = i < H ? *(const uint2*)(g + i) : make_uint2(0u, 0u);
     }
     float ss = 0.f;
 #pragma unroll
@@ -307,8 +309,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
     __syncthreads();
     ss = red[0] + red[1] + red[2] + red[3];
     const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-    auto put = [&](int i, const float4& t) {
-        const uint2 gw = *(const uint2*)(g + i);
+    auto put = [&](int i, const float4& t, const uint2& gw) {
         const float g0 = __builtin_bit_cast(float, gw.x << 16), g1 = __builtin_bit_cast(float, gw.x & 0xffff0000u);
         const float g2 = __builtin_bit_cast(float, gw.y << 16), g3 = __builtin_bit_cast(float, gw.y & 0xffff0000u);
         *(uint2*)(orow + i) = make_uint2(pack_bf16x2(t.x * inv * g0, t.y * inv * g1), pack_bf16x2(t.z * inv * g2, t.w * inv * g3));
@@ -316,9 +317,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
 #pragma unroll
     for (int j = 0; j < kNormPieces; ++j) {
         const int i = 4 * threadIdx.x + 1024 * j;
-        if (i < H) put(i, v[j]);
+        if (i < H) put(i, v[j], gv[j]);
     }
-    for (int i = 4 * threadIdx.x + 1024 * kNormPieces; i < H; i += 1024) put(i, *(const float4*)(xr + i));
+    for (int i = 4 * threadIdx.x + 1024 * kNormPieces; i < H; i += 1024) put(i, *(const float4*)(xr + i), *(const uint2*)(g + i));
 }
 
 // One wave per (row, head): per-head RMSNorm (optional), rotate-half RoPE at the row's position;
@@ -422,23 +423,41 @@ struct AttnK {
     int causal, pos0, window, ctx_lo, ctx_hi;
     int np0, np1, sp, r_lo, r_hi;   // new rows: positions [np0, np1); row of p: p < sp ? r_lo + p - np0 : r_hi + p - sp
     int key_lo, n_keys, spw, n_chunks;   // keys [key_lo, key_lo + n_keys); spw sub-chunks per workgroup
-    const int64_t* dpos;     // causal graph replays: positions held read here (see bind_positions)
+    const int64_t* dpos;     // graph replays: positions held read here (see bind_positions)
+    int n_ctx;               // draft block replays: context rows appended before the block rows
     float* part;             // [n_qt][nkv][n_chunks][16][attn_part_ld(hd)] partials: O, then max and sum
     int* counters;           // [n_qt * nkv]
     uint16_t* out;           // [M][Hq * hd] bf16
 };
 
-// A causal pass captured in a graph reads the positions held P from device memory: its rows sit at
-// P .. P + M - 1, an own layer appends them, and row m sees [max(0, P + m - window + 1), P + m].
+// A pass captured in a graph reads the positions held P from device memory.
+// Causal: its rows sit at P .. P + M - 1, an own layer appends them, and row m sees
+// [max(0, P + m - window + 1), P + m].
+// Draft block: the n_ctx context rows go to P .. s - 1 (s = P + n_ctx) and the M block rows to
+// s .. s + M - 1; every block row sees [max(0, s - window), s + M - 1] (window: the draft's context
+// window, 0 = all), and the key range also covers the appended context rows.
 __device__ __forceinline__ void bind_positions(AttnK& a) {
     const int P = (int)*a.dpos;
-    a.pos0 = P;
+    if (a.causal) {
+        a.pos0 = P;
+        a.np0 = P;
+        a.np1 = P + a.M;
+        a.sp = P;
+        const int lo = (a.window > 0 && P - a.window + 1 > 0) ? P - a.window + 1 : 0;
+        a.key_lo = lo;
+        a.n_keys = P + a.M - lo;
+        return;
+    }
+    const int s = P + a.n_ctx;
+    a.pos0 = s;
+    a.ctx_lo = (a.window > 0 && s - a.window > 0) ? s - a.window : 0;
+    a.ctx_hi = s + a.M - 1;
     a.np0 = P;
-    a.np1 = P + a.M;
-    a.sp = P;
-    const int lo = (a.window > 0 && P - a.window + 1 > 0) ? P - a.window + 1 : 0;
+    a.np1 = s + a.M;
+    a.sp = s;
+    const int lo = a.own && a.ctx_lo > P ? P : a.ctx_lo;
     a.key_lo = lo;
-    a.n_keys = P + a.M - lo;
+    a.n_keys = s + a.M - lo;
 }
 
 __global__ void k_set_i64(int64_t* dst, int64_t v) { *dst = v; }
@@ -1247,6 +1266,7 @@ AttnK make_attn(const Attn& x) {
     a.key_lo = lo;
     a.n_keys = hi - lo + 1;
     a.dpos = x.dpos;
+    a.n_ctx = x.n_ctx;
     // the plan covers the keys of rows at pos_plan when given (a bound shared by passes at lower
     // positions: a later pass there leaves trailing chunks empty)
     int plan_keys = a.n_keys;
@@ -1280,6 +1300,11 @@ AttnK make_attn(const Attn& x) {
 size_t attn_part_floats_needed(const Attn& x) {
     const AttnK a = make_attn(x);
     return (size_t)a.n_qt * a.nkv * a.n_chunks * 16 * attn_part_ld(x.hd);
+}
+
+int64_t attn_plan_key(const Attn& x) {
+    const AttnK a = make_attn(x);
+    return (int64_t)a.n_chunks * 65536 + a.spw;
 }
 
 namespace {

@@ -189,15 +189,22 @@ bvf_status bvf_verify_batch(bvf_model* m, const int32_t* d_tokens, int32_t k, fl
  * verify (BVF_E_STATE: commit it first); a refusal changes nothing. */
 bvf_status bvf_prefill(bvf_model* m, const int32_t* d_tokens, int32_t n, float* d_last_logits);
 
-/* Graph replay of bvf_verify_batch (1) or direct launches (0, the default). With 1 the pass is
- * captured once into a HIP graph (on a private stream) and replayed on the model's stream; the
- * replayed pass reads the positions held from device memory (set by a one-thread kernel launched
- * before each replay), so the capture serves every position of a 256-position span (P with the same
- * P / 256, below max_ctx - k) while k and the three buffer pointers stay the same; it is taken again
- * when any of them changes. Both modes plan the attention for the span's last position, so their
- * results are identical bit for bit. */
+/* Graph replay (1) or direct launches (0, the default) of bvf_verify_batch on a verify model and of
+ * bvf_draft_block_forward with a block on a draft model. With 1 the pass is captured into a HIP graph
+ * (on a private stream) and replayed on the model's stream; the replayed pass reads the positions
+ * held from device memory (set by a one-thread kernel launched before each replay).
+ * Verify: the capture serves every position of a 256-position span (P with the same P / 256, below
+ * max_ctx - k) while k and the three buffer pointers stay the same; it is taken again when any of
+ * them changes. Both modes plan the attention for the span's last position, so their results are
+ * identical bit for bit.
+ * Draft: one capture per context-row count n_new (0 .. 16), kept while the layers' attention plans
+ * at the current positions (constant once the context window is full), the block size, the
+ * embedding scale, the mask token, the target model and the four buffer pointers stay the same.
+ * A replay runs the launches of the direct path with the same plans, so the results are identical
+ * bit for bit. The append-only call (block 0) always launches directly. */
 bvf_status bvf_set_graph_mode(bvf_model* m, int32_t on);
-/* Number of verify-pass graph captures the model has taken so far (h_out[0]). */
+/* Number of graph captures the model has taken so far (h_out[0]): verify passes on a verify model,
+ * draft blocks on a draft model. */
 bvf_status bvf_graph_captures(const bvf_model* m, int64_t* h_out);
 
 /* Greedy longest-prefix accept ([CARD], "How it is used"; [PR2236], the acceptance tool): y_i is the

@@ -534,6 +534,50 @@ def test_draft_append_only_then_block():
     assert err < logits_bar(err, dm, run_oracle, arrs, "draft append-only then block")
 
 
+def test_draft_graph_replay_matches_direct_launches():
+    """The draft block replayed from graphs (one capture per context-row count, the positions read
+    from device memory) gives bit-identical proposals, logits and appended K/V rows to a twin with
+    direct launches, over rounds of 1..8 new context rows with eager work between the replays."""
+    tm = synth.tiny_model(max_ctx=160)
+    tw = synth.make_weights(tm)
+    dm = synth.tiny_draft_model(max_ctx=160, window=32)
+    dmg = dataclasses.replace(dm, vocab=tm.vocab)
+    dw = synth.make_weights(dm)
+    kvd = synth.make_kv(dm, 24)
+    T = bvf.Model(tm)
+    T.load_weights(tw)
+    Ds = []
+    for graph in (False, True):
+        D = bvf.Model(dmg)
+        D.load_weights(dw)
+        D.set_context(kvd, 24)
+        D.set_graph_mode(graph)
+        Ds.append(D)
+    B = 8
+    taps = dev(synth.bf16_normal(3, "draft.graph.taps", (B, len(dm.tap_layers), dm.hidden)))
+    last = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = [(torch.zeros(B - 1, dtype=torch.int32, device="cuda"), torch.empty((B - 1, tm.vocab), dtype=torch.float32, device="cuda"))
+           for _ in Ds]
+    n_news = [1, 4, 8, 4, 2, 1, 7, 4, 3, 8, 5, 6, 1]
+    x = dev(synth.bf16_normal(0, "draft.graph.x", (8, tm.hidden)))
+    y = torch.empty((8, 256), dtype=torch.float32, device="cuda")
+    for r, n_new in enumerate(n_news):
+        last.fill_(5 + 3 * r)
+        taps.copy_(dev(synth.bf16_normal(10 + r, "draft.graph.taps", (B, len(dm.tap_layers), dm.hidden))))
+        for D, (props, lg) in zip(Ds, out):
+            lg.fill_(float("nan"))
+            D.draft_block_forward(T, taps[:n_new], n_new, last, B, 1.0, tm.vocab - 1, props, lg)
+            T.q4_1_gemm(0, bvf.Q, x, 8, y)      # eager work between replays
+        assert np.array_equal(host(out[0][1]), host(out[1][1])), f"round {r} (n_new {n_new}) logits"
+        assert np.array_equal(host(out[0][0]), host(out[1][0])), f"round {r} proposals"
+    held = Ds[0].positions_held()
+    assert held == Ds[1].positions_held() == 24 + sum(n_news)
+    for l in range(dm.n_layers):
+        assert np.array_equal(Ds[0].get_kv(l, held), Ds[1].get_kv(l, held)), f"layer {l} plane"
+    print(f"[draft graph] {len(n_news)} rounds, captures {Ds[1].graph_captures()}", flush=True)
+    assert Ds[0].graph_captures() == 0 and Ds[1].graph_captures() == len(set(n_news))
+
+
 # ------------------------------------------------------------------------------------------
 # graph replay
 # ------------------------------------------------------------------------------------------

@@ -164,3 +164,31 @@ def test_spec_loop_sampled_matches_oracle():
         assert T.positions_held() == To.held()
         last = emitted[a]
     assert compared_draws >= 40 and compared_a >= 4
+
+
+def test_spec_loop_graphs_equal_direct_launches():
+    """Twelve steered rounds with both models replayed from graphs (the verify pass and the draft
+    block) give the same proposals, accepted lengths and emitted tokens as direct launches, bit for
+    bit, and the draft takes one capture per context-row count it met."""
+    tm, dm, tw, dw, kv, kvd = models()
+    steer = synth.accept_lengths(1, 12, max_a=BLOCK - 1)
+    runs = []
+    for graph in (False, True):
+        T, D = gpu_pair(tm, dm, tw, dw, kv, kvd)
+        T.set_graph_mode(graph)
+        D.set_graph_mode(graph)
+        loop = SpecLoop(T, D, BLOCK, steer_bonus=BONUS)
+        loop.start(17)
+        rounds = []
+        for a_want in steer:
+            a, emitted = loop.round(int(a_want))
+            rounds.append((a, emitted, host(loop.toks).tolist(), host(loop.logits)))
+        runs.append((rounds, D.graph_captures(), T.positions_held(), D.positions_held()))
+    (rd, cd, td, dd), (rg, cg, tg_, dg) = runs
+    for r, (x, y) in enumerate(zip(rd, rg)):
+        assert x[0] == y[0] and x[1] == y[1] and x[2] == y[2], f"round {r}"
+        assert np.array_equal(x[3], y[3]), f"round {r} verify logits"
+    assert (td, dd) == (tg_, dg)
+    n_news = {0} | {int(a) + 1 for a in steer[:-1]}
+    print(f"[loop graphs] draft captures {cg} for context-row counts {sorted(n_news)}", flush=True)
+    assert cd == 0 and cg == len(n_news)
