@@ -516,6 +516,11 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
             }
         }
     }
+    // RESID without a K split: the residual rows of the wave's first item are loaded before the ring,
+    // so the epilogue does not wait for them (they land with the staging loads)
+    floatx4 y_first = {0.f, 0.f, 0.f, 0.f};
+    const bool y_early = EPI == EPI_RESID && MT == 1 && S == 1 && kp == 0 && my_items > 0;
+    if (y_early) y_first = load_resid_rows(a, first + ts, lane, 0);
     // fill the ring: the weight loads overlap the staging of the activation rows. Exactly R slots
     // are filled (slots past the wave's stream repeat its first superblock, an L2 hit, and are never
     // read), so the staging's own waits can count the copies that follow its loads.
@@ -695,7 +700,7 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             if (16 * t >= a.M) break;
-            if (S == 1) epilogue<EPI>(a, acc[t], tile, lane, 16 * t);
+            if (S == 1) epilogue<EPI>(a, acc[t], tile, lane, 16 * t, y_early && it == 0, y_first);
             else if (MT > 1) splitk_store_plain(a, acc[t], tile, split, lane, 16 * t);
             else splitk_store(a, acc[t], tile, split, lane, 16 * t);
         }
