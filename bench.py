@@ -206,12 +206,26 @@ def run_loop(args):
     D.restore(snap_d)
     loop.start(17)
     torch.cuda.synchronize()
+    # events around each draft block (recorded on the stream, no synchronisation): the round's split
+    draft_ev = []
+    draft_call = D.draft_block_forward
+
+    def timed_draft(*a, **kw):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev[0].record()
+        draft_call(*a, **kw)
+        ev[1].record()
+        draft_ev.append(ev)
+
+    D.draft_block_forward = timed_draft
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     toks = loop.run(args.loop, steer)
     e1.record()
     torch.cuda.synchronize()
+    D.draft_block_forward = draft_call
     ms = e0.elapsed_time(e1)
+    draft_ms = float(np.mean([a.elapsed_time(b) for a, b in draft_ev]))
     rounds = len(loop.accepted)
     assert loop.accepted == [int(a) for a in steer[:rounds]], "steered accept lengths not reproduced"
     res = {
@@ -233,6 +247,7 @@ def run_loop(args):
         "tokens_per_target_pass": round(len(toks) / rounds, 3),
         "mean_accepted_drafts": round(float(np.mean(loop.accepted)), 3),
         "ms_per_round": round(ms / rounds, 4),
+        "draft_block_ms": round(draft_ms, 4),
         "verify_graph_captures": T.graph_captures(),
         "draft_graph_captures": D.graph_captures(),
     }
