@@ -254,6 +254,80 @@ def run_loop(args):
     print(json.dumps(res), flush=True)
 
 
+def run_draft(args):
+    """The draft block forward at its real size: 5 layers (hidden 2560, 32 query / 8 KV heads of 128,
+    FFN 5120, window 1024), fc over 5 tapped target rows, a block of 8, args.ctx cached context
+    positions, and the target's tied bf16 head (args.vocab rows) on rows 1..7. Times args.steps blocks
+    with 1 and with 8 new context rows (HIP events; the draft restored from a snapshot before each
+    series) and reports ms per block and the bytes a block streams (the draft's Q4_1 layers, the bf16
+    fc, the head, the visible context K/V) over that time against the 8 TB/s HBM peak."""
+    import dataclasses
+    import torch
+    from block_verify_forward_amd import bvf, synth
+
+    threads = min(16, os.cpu_count() or 8)
+    B = 8
+    max_ctx = args.ctx + 8 * (args.steps + args.warmup) + 64
+    tm = synth.target_model(max_ctx=max_ctx, n_layers=1, vocab=args.vocab)   # the embedding and head only
+    dm = planes(synth.draft_model(max_ctx=max_ctx), args, verify=False)
+    t0 = time.time()
+    tw = synth.make_weights(tm, args.seed, threads=threads)
+    dw = synth.make_weights(dm, args.seed, threads=threads)
+    kvd = synth.make_kv(dm, args.ctx, args.seed, threads=threads)
+    log(f"synthetic draft, head and context drawn in {time.time() - t0:.1f} s")
+    T = bvf.Model(tm)
+    T.load_weights(tw)
+    D = bvf.Model(dataclasses.replace(dm, vocab=tm.vocab))
+    D.load_weights(dw)
+    D.set_context(kvd, args.ctx)
+    if args.graph and not args.no_graph:
+        D.set_graph_mode(True)
+    taps = torch.from_numpy(synth.bf16_normal(args.seed, "bench.draft.taps", (B, len(dm.tap_layers), dm.hidden))).cuda()
+    last = torch.full((1,), 17, dtype=torch.int32, device="cuda")
+    props = torch.zeros(B - 1, dtype=torch.int32, device="cuda")
+    snap = D.snapshot_take()
+    res = {}
+    for n_new in (1, 8):
+        D.restore(snap)
+        for _ in range(args.warmup):
+            D.draft_block_forward(T, taps[:n_new], n_new, last, B, 1.0, tm.vocab - 1, props)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            D.draft_block_forward(T, taps[:n_new], n_new, last, B, 1.0, tm.vocab - 1, props)
+        e1.record()
+        torch.cuda.synchronize()
+        res[n_new] = e0.elapsed_time(e1) / args.steps
+        log(f"draft block, {n_new} new context rows: {res[n_new]:.4f} ms")
+    q4, _ = D.pass_bytes()
+    _, head = T.pass_bytes()
+    fc = len(dm.tap_layers) * dm.hidden * dm.hidden * 2
+    kv_w = sum(2 * L.n_kv_heads * L.head_dim for L in dm.layers)   # K and V floats per position, all layers
+    kv = (min(args.ctx, dm.draft_window) + B) * kv_w * (2 if args.kv_bf16 else 4)
+    total = q4 + fc + head + kv
+    gbs = total / (res[8] * 1e-3) / 1e9
+    out = {
+        "metric": "draft block forward ms (block 8: fc over the new taps, 5 layers, head on rows 1..7, argmax)",
+        "value": round(res[8], 4),
+        "unit": "ms per block",
+        "n_gpus": 1,
+        "higher_is_better": False,
+        "vs_baseline": None,
+        "data": f"synthetic (seeded draws, seed {args.seed})",
+        "config": {"workload": f"draft block forward: 5 layers hidden 2560 Q4_1, fc 12800x2560 bf16, head {tm.vocab}x2560 "
+                               f"bf16, {args.ctx} cached context positions, block 8, 8 new context rows",
+                   "kv_planes": "bf16" if args.kv_bf16 else "fp32",
+                   "launches": "graph replay" if args.graph and not args.no_graph else "direct"},
+        "ms_per_block_1_new_row": round(res[1], 4),
+        "bytes_per_block": {"q4_1": q4, "fc_bf16": fc, "head_bf16": head, "context_kv": kv, "total": total},
+        "gbs": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "ms_at_hbm_peak": round(total / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def run_prefill(args):
     """Chunked prefill: args.prefill prompt tokens on top of args.ctx cached positions, in batched
     passes of up to 64 rows (one pass over the weights per chunk, four 16-row MFMA tiles per weight
@@ -367,6 +441,9 @@ def main():
     ap.add_argument("--loop", type=int, default=0,
                     help="instead of the verify step: the speculative loop (draft block of 8 + batched verify + "
                          "accept + commit) until this many tokens, steered acceptance, full-size draft and target")
+    ap.add_argument("--draft", action="store_true",
+                    help="instead of the verify step: the draft block forward alone at its real size (1 and 8 new "
+                         "context rows), ms per block and bytes over time")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain fp32 copy kernel (neg) of this many MiB three times first: the known-size "
                          "dispatch that scales HBM counters")
@@ -382,6 +459,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     if args.loop > 0:
         return run_loop(args)
+    if args.draft:
+        return run_draft(args)
     if args.prefill > 0:
         return run_prefill(args)
     threads = min(16, os.cpu_count() or 8)
