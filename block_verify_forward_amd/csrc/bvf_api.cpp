@@ -791,22 +791,23 @@ Attn draft_attn(bvf_model* dr, int l, int n_new, int B, const int64_t* dpos) {
 
 // The draft block's launches on stream st: the context rows (fc), the block rows [last token,
 // mask x (B - 1)] through the draft layers, the final norm and the target's head on rows 1..B-1,
-// their argmax. The attention norm runs as its own kernel (the block's q|k|v also takes the
-// context rows, normalised by fc's hidden norm); the MLP norm is folded into the gate|up GEMM's
-// staging and the final norm into the head's, from the per-tile sums of squares that the o and down
-// GEMMs leave in ss_x.
+// their argmax. Every RMSNorm of the block rows is folded into the staging of the GEMM that reads
+// them, from the per-tile sums of squares that the embedding and the o and down GEMMs leave in ss_x:
+// the attention norm into q|k|v (whose rows B.. are the context rows, copied as fc's hidden norm
+// left them), the MLP norm into gate|up, the final norm into the head.
 hipError_t enqueue_draft(bvf_model* dr, const bvf_model* tg, const uint16_t* d_new_taps, int n_new,
                          const int32_t* d_last_token, int B, float embedding_scale, int mask_token, int32_t* d_proposals,
                          float* d_logits, hipStream_t st, const int64_t* dpos) {
     const int H = dr->d.hidden, V = tg->d.vocab;
     hipError_t e = enqueue_draft_fc(dr, d_new_taps, n_new, B, st);
     if (e != hipSuccess) return e;
-    if ((e = launch_embed(d_last_token, mask_token, B, tg->embed, V, H, embedding_scale, dr->x, nullptr, st)) != hipSuccess)
+    if ((e = launch_embed(d_last_token, mask_token, B, tg->embed, V, H, embedding_scale, dr->x, dr->ss_x, st)) != hipSuccess)
         return e;
     for (int l = 0; l < dr->d.n_layers; ++l) {
         Layer& L = dr->L[l];
-        if ((e = launch_rmsnorm(dr->x, H, B, H, L.attn_norm, dr->d.rms_eps, dr->act, H, st)) != hipSuccess) return e;
         GemmLaunch g = gemm_for(dr, L.qkv, EPI_STORE);
+        g.xsrc = dr->x; g.ldx = H; g.ss_in = dr->ss_x; g.n_ss = H / kTile; g.gain = L.attn_norm; g.eps = dr->d.rms_eps;
+        g.n_fold = B;
         g.A = dr->act; g.lda = H; g.M = B + n_new; g.y = dr->qkv; g.ldy = L.qkv.n_out; g.ss_out = dr->ss_qkv;
         if ((e = launch_gemm(g, st)) != hipSuccess) return e;
         if ((e = launch_attention(draft_attn(dr, l, n_new, B, dpos), st)) != hipSuccess) return e;

@@ -58,8 +58,10 @@ struct GemmLaunch {
     int* counters = nullptr;     // split-K arrival counters (zero between launches)
     int n_counters = 0;
     int half = -1;               // STORE on a gate|up image: -1 all columns, 0 gate, 1 up
-    // RMSNorm folded into the A staging: A = bf16(xsrc * rinv * gain), rinv from ss_in [M][n_ss]
+    // RMSNorm folded into the A staging: A = bf16(xsrc * rinv * gain), rinv from ss_in [M][n_ss];
+    // with n_fold in 1 .. M - 1 only rows < n_fold are, and rows n_fold .. M - 1 are copied from A
     const float* xsrc = nullptr;
+    int n_fold = 0;              // 0: every row (when xsrc is set)
     int ldx = 0;
     const float* ss_in = nullptr;
     int n_ss = 0;

@@ -77,8 +77,10 @@ struct KArgs {
     uint64_t mag_stride;
     int half;   // STORE on a gate|up image: -1 all 16 columns, 0 the gate half, 1 the up half
     // RMSNorm folded into the staging of A (xsrc != nullptr): A = bf16(x * rinv * gain) with
-    // rinv = 1 / sqrt(sum(ss_in[m][0 .. n_ss)) / K + eps)
+    // rinv = 1 / sqrt(sum(ss_in[m][0 .. n_ss)) / K + eps), for rows m < NF (NF = M unless a mixed
+    // staging folds only the first rows); rows NF .. M - 1 are copied from A
     const float* xsrc;
+    int NF;
     int ldx;
     const float* ss_in;
     int n_ss;
@@ -473,8 +475,9 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
     // bf16 activation rows: direct global->LDS copies (1 KB = 4 superblocks of one row per
     // instruction), issued before the ring so the wave's first wait covers them
     const int chunks = (nsb + 3) / 4;
-    if (!a.xsrc) {
-        int m = 0, q = wave;   // copy i = m chunks + q, i = wave, wave + nw, ...
+    const int NF = a.xsrc ? a.NF : 0;   // rows [0, NF) normalised from xsrc, [NF, M) copied from A
+    if (NF < a.M) {
+        int m = NF, q = wave;   // copy i = (m - NF) chunks + q, i = wave, wave + nw, ...
         while (q >= chunks) { q -= chunks; ++m; }
         for (; m < a.M; q += nw) {
             while (q >= chunks) { q -= chunks; ++m; }
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
     __shared__ float rinv_s[kMaxGemmRows];
     const int pieces = nsb * (kSuper / 8);
     const int p0 = threadIdx.x;
-    const int rows0 = min(a.M, 8);
+    const int rows0 = min(NF, 8);
     float4 xv[8][2];
     u32x4 gv0 = {0u, 0u, 0u, 0u};
     float sv[4][4];   // sums of squares of rows wave + nw r (r < 4), lanes lane + 64 t (t < 4)
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int i = lane + 64 * t;
-                sv[r][t] = m < a.M && i < a.n_ss ? a.ss_in[(size_t)m * a.n_ss + i] : 0.f;
+                sv[r][t] = m < NF && i < a.n_ss ? a.ss_in[(size_t)m * a.n_ss + i] : 0.f;
             }
         }
         if (p0 < pieces) {
@@ -551,14 +554,14 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = wave + nw * r;
-            if (m >= a.M) break;
+            if (m >= NF) break;
             float q = (sv[r][0] + sv[r][1]) + (sv[r][2] + sv[r][3]);
             for (int i = lane + 256; i < a.n_ss; i += 64) q += a.ss_in[(size_t)m * a.n_ss + i];
             q = wave_sum_dpp(q);
             if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
         }
         // rows past 4 nw (wide chunks): the same sums, loaded now
-        for (int m = wave + 4 * nw; m < a.M; m += nw) {
+        for (int m = wave + 4 * nw; m < NF; m += nw) {
             float t4[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -600,11 +603,11 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
         // p0 of batch 0, loaded above, is converted outside the loop (so the compiler's wait for
         // its loads is not merged with the loop's). The four pieces of a block sit in four
         // consecutive lanes of one iteration (pieces and the thread count are multiples of 4).
-        const int n_items = pieces * ((a.M + 7) >> 3);
+        const int n_items = pieces * ((NF + 7) >> 3);
         if (p0 < pieces) convert(p0, 0, rows0, gv0, xv);
         for (int i = p0 < pieces ? p0 + nthr : p0; i < n_items; i += nthr) {
             const int b = i / pieces, p = i - b * pieces;
-            const int m0 = 8 * b, nrows = min(8, a.M - m0);
+            const int m0 = 8 * b, nrows = min(8, NF - m0);
             const int k0 = g0 * kSuper + p * 8;
             const u32x4 gv = *(const u32x4*)(a.gain + k0);
 #pragma unroll
@@ -620,15 +623,15 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
         wait_vm<LPS * R>();
     }
     lds_barrier();
-    if (FMT == W_Q4_1 && !a.xsrc) {
-        // block sums S[b][m] = sum of the 32 bf16 of block b of row m < M (the copied rows; the
-        // normalised rows got theirs while being converted); the four pieces of a block sit in
+    if (FMT == W_Q4_1 && NF < a.M) {
+        // block sums S[b][m] = sum of the 32 bf16 of block b of row m (the copied rows NF .. M - 1;
+        // the normalised rows got theirs while being converted); the four pieces of a block sit in
         // four consecutive lanes; eight rows' LDS reads are issued together; work items as in the
-        // normalised staging (piece p of 8-row batch b)
-        const int n_items = pieces * ((a.M + 7) >> 3);
+        // normalised staging (piece p of 8-row batch b, from row NF)
+        const int n_items = pieces * ((a.M - NF + 7) >> 3);
         for (int i = threadIdx.x; i < n_items; i += nthr) {
             const int b = i / pieces, p = i - b * pieces;
-            const int m0 = 8 * b;
+            const int m0 = NF + 8 * b;
             u32x4 o[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) o[r] = lds_read16_untracked(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
@@ -968,6 +971,7 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
     k.n_cols = L.n_run_tiles * kTile;
     k.half = L.half;
     k.xsrc = L.xsrc;
+    k.NF = L.xsrc ? (L.n_fold > 0 && L.n_fold < L.M ? L.n_fold : L.M) : 0;
     k.ldx = L.ldx;
     k.ss_in = L.ss_in;
     k.n_ss = L.n_ss;
