@@ -460,7 +460,7 @@ def test_shared_layers_read_owner_planes():
 # DFlash draft block
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("window, n_ctx, n_new, block", [(0, 12, 4, 8), (6, 20, 3, 8), (0, 0, 8, 8), (0, 9, 1, 4),
-                                                     (0, 30, 0, 8)])
+                                                     (0, 30, 0, 8), (0, 10, 4, 12), (0, 10, 0, 16), (5, 14, 7, 9)])
 def test_draft_block_parity(window, n_ctx, n_new, block):
     """Context: n_ctx rows of cached draft K/V (set directly) plus n_new rows appended from taps;
     then the block [17, mask x (block - 1)] and the target head on rows 1.."""
