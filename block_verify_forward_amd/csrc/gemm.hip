@@ -488,32 +488,44 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
                                                  (lds_void*)(As + m * lds_ld + q * 512), 16, 0, 0);
         }
     }
-    // RMSNorm folded in: the loads of the first batch (the sums of squares of the rows, and per
-    // thread piece p = 8 elements of K of up to 8 rows plus the gains) are issued before the ring,
-    // so they are not queued behind the weight stream
+    // RMSNorm folded in. Work items (piece p = 8 elements of the K range, batch b of RG rows), item
+    // i = b pieces + p, thread t takes items t, t + nthr, ...; the loads of the first item (the RG
+    // rows' pieces and the gains) and of the rows' sums of squares go out before the ring, so they are
+    // not queued behind the weight stream. When the items leave waves without a first item, those
+    // waves come first and compute the rows' factors rinv (their few loads go out ahead of the rows'),
+    // and the converting waves pass the barrier that publishes rinv without waiting for their own
+    // loads. Otherwise every wave computes its rows' factors once all its loads are in.
     __shared__ float rinv_s[kMaxGemmRows];
+    constexpr int RG = 4;
     const int pieces = nsb * (kSuper / 8);
-    const int p0 = threadIdx.x;
-    const int rows0 = min(NF, 8);
-    float4 xv[8][2];
+    const int n_items = a.xsrc ? pieces * ((NF + RG - 1) / RG) : 0;
+    const int conv_waves = min(nw, (n_items + 63) >> 6);   // waves that hold a first item
+    const int n_rw = nw - conv_waves;                      // > 0: waves 0 .. n_rw - 1 compute rinv
+    const int p0 = (int)threadIdx.x - 64 * n_rw;            // the thread's first item (< 0: none)
+    const bool has0 = p0 >= 0 && p0 < n_items;
+    const int b0 = has0 ? p0 / pieces : 0, pp0 = has0 ? p0 - b0 * pieces : 0;
+    const int rw_n = n_rw > 0 ? n_rw : nw;
+    const int rw_idx = wave;
+    const bool my_rinv = n_rw == 0 || wave < n_rw;         // uniform in the wave
+    float4 xv[RG][2];
     u32x4 gv0 = {0u, 0u, 0u, 0u};
-    float sv[4][4];   // sums of squares of rows wave + nw r (r < 4), lanes lane + 64 t (t < 4)
+    float sv[4][4];   // sums of squares of rows rw_idx + rw_n r (r < 4), lanes lane + 64 t (t < 4)
     if (a.xsrc) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = wave + nw * r;
+            const int m = rw_idx + rw_n * r;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int i = lane + 64 * t;
-                sv[r][t] = m < NF && i < a.n_ss ? a.ss_in[(size_t)m * a.n_ss + i] : 0.f;
+                sv[r][t] = my_rinv && m < NF && i < a.n_ss ? a.ss_in[(size_t)m * a.n_ss + i] : 0.f;
             }
         }
-        if (p0 < pieces) {
-            const int k0 = g0 * kSuper + p0 * 8;
+        if (has0) {
+            const int k0 = g0 * kSuper + pp0 * 8;
             gv0 = *(const u32x4*)(a.gain + k0);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int m = r < rows0 ? r : rows0 - 1;
+            for (int r = 0; r < RG; ++r) {
+                const int m = min(RG * b0 + r, NF - 1);
                 xv[r][0] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0);
                 xv[r][1] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0 + 4);
             }
@@ -547,39 +559,63 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
     }
     int s_issue = total < R ? total : R;
 
-    if (a.xsrc) {
-        // the staging loads have returned once only the R ring slots are younger
-        wait_vm<LPS * R>();
-        // rinv from the producer's per-tile sums of squares (n_ss > 256 continues in a loop)
+    // block sums S[b][m] = sum of the 32 bf16 of block b of row m for the copied rows NF .. M - 1 (the
+    // normalised rows get theirs while being converted); the four pieces of a block sit in four
+    // consecutive lanes; eight rows' LDS reads are issued together; work items (piece p, 8-row batch b
+    // from row NF). Called on each staging path separately, so that neither path's pending loads
+    // reach the other's code.
+    auto copied_block_sums = [&]() __attribute__((always_inline)) {
+        const int n_cb = pieces * ((a.M - NF + 7) >> 3);
+        for (int i = threadIdx.x; i < n_cb; i += nthr) {
+            const int b = i / pieces, p = i - b * pieces;
+            const int m0 = NF + 8 * b;
+            u32x4 o[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = wave + nw * r;
-            if (m >= NF) break;
-            float q = (sv[r][0] + sv[r][1]) + (sv[r][2] + sv[r][3]);
-            for (int i = lane + 256; i < a.n_ss; i += 64) q += a.ss_in[(size_t)m * a.n_ss + i];
-            q = wave_sum_dpp(q);
-            if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
-        }
-        // rows past 4 nw (wide chunks): the same sums, loaded now
-        for (int m = wave + 4 * nw; m < NF; m += nw) {
-            float t4[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int i = lane + 64 * t;
-                t4[t] = i < a.n_ss ? a.ss_in[(size_t)m * a.n_ss + i] : 0.f;
-            }
-            float q = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-            for (int i = lane + 256; i < a.n_ss; i += 64) q += a.ss_in[(size_t)m * a.n_ss + i];
-            q = wave_sum_dpp(q);
-            if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
-        }
-        lds_barrier();
-        auto convert = [&](int p, int m0, int nrows, const u32x4& gv, const float4 (&xr)[8][2]) {
-            float rvs[8];   // the eight rows' factors in registers before any LDS write of the batch
-#pragma unroll
-            for (int r = 0; r < 8; ++r) rvs[r] = rinv_s[m0 + r];
+            for (int r = 0; r < 8; ++r) o[r] = lds_read16_untracked(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
+            wait_lds();
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
+                const float bs = quad_sum(bf16x8_sum(o[r]));
+                if (m0 + r < a.M && (p & 3) == 0) Ss[(p >> 2) * MP + m0 + r] = bs;
+            }
+        }
+    };
+    if (a.xsrc) {
+        if (my_rinv) {
+            // the sums of squares have returned once only the R ring slots are younger (without
+            // rinv waves, this wave's first item's loads too)
+            wait_vm<LPS * R>();
+            // rinv from the producer's per-tile sums of squares (n_ss > 256 continues in a loop)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = rw_idx + rw_n * r;
+                if (m >= NF) break;
+                float q = (sv[r][0] + sv[r][1]) + (sv[r][2] + sv[r][3]);
+                for (int i = lane + 256; i < a.n_ss; i += 64) q += a.ss_in[(size_t)m * a.n_ss + i];
+                q = wave_sum_dpp(q);
+                if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
+            }
+            // rows past 4 rw_n (wide chunks): the same sums, loaded now
+            for (int m = rw_idx + 4 * rw_n; m < NF; m += rw_n) {
+                float t4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int i = lane + 64 * t;
+                    t4[t] = i < a.n_ss ? a.ss_in[(size_t)m * a.n_ss + i] : 0.f;
+                }
+                float q = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+                for (int i = lane + 256; i < a.n_ss; i += 64) q += a.ss_in[(size_t)m * a.n_ss + i];
+                q = wave_sum_dpp(q);
+                if (lane == 0) rinv_s[m] = 1.0f / sqrtf(q / (float)a.K + a.eps);
+            }
+        }
+        lds_barrier();
+        auto convert = [&](int p, int m0, int nrows, const u32x4& gv, const float4 (&xr)[RG][2]) {
+            float rvs[RG];   // the rows' factors in registers before any LDS write of the batch
+#pragma unroll
+            for (int r = 0; r < RG; ++r) rvs[r] = rinv_s[m0 + r];
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
                 if (r >= nrows) break;
                 const int m = m0 + r;
                 const float rv = rvs[r];
@@ -599,50 +635,41 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
                 }
             }
         };
-        // work items i = b pieces + p: piece p of the 8-row batch b, spread over all threads. Item
-        // p0 of batch 0, loaded above, is converted outside the loop (so the compiler's wait for
-        // its loads is not merged with the loop's). The four pieces of a block sit in four
-        // consecutive lanes of one iteration (pieces and the thread count are multiples of 4).
-        const int n_items = pieces * ((NF + 7) >> 3);
-        if (p0 < pieces) convert(p0, 0, rows0, gv0, xv);
-        for (int i = p0 < pieces ? p0 + nthr : p0; i < n_items; i += nthr) {
+        // the first item, loaded above (its loads are in once only the ring slots are younger); the
+        // four pieces of a block sit in four consecutive lanes (pieces and the thread count are
+        // multiples of 4)
+        if (has0) {
+            wait_vm<LPS * R>();
+            convert(pp0, RG * b0, min(RG, NF - RG * b0), gv0, xv);
+        }
+        for (int i = p0 + nthr; i < n_items; i += nthr) {   // (none when there are rinv waves)
             const int b = i / pieces, p = i - b * pieces;
-            const int m0 = 8 * b, nrows = min(8, NF - m0);
+            const int m0 = RG * b, nrows = min(RG, NF - m0);
             const int k0 = g0 * kSuper + p * 8;
             const u32x4 gv = *(const u32x4*)(a.gain + k0);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
+            for (int r = 0; r < RG; ++r) {
                 const int m = m0 + (r < nrows ? r : nrows - 1);
                 xv[r][0] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0);
                 xv[r][1] = *(const float4*)(a.xsrc + (size_t)m * a.ldx + k0 + 4);
             }
             convert(p, m0, nrows, gv, xv);
         }
+        // every staging load of the wave has returned by now; the wait says so to the compiler
+        wait_vm<LPS * R>();
+        lds_barrier();
+        if (FMT == W_Q4_1 && NF < a.M) {
+            copied_block_sums();
+            lds_barrier();
+        }
     } else {
         // this wave's activation copies have landed (they are older than its R ring slots)
         wait_vm<LPS * R>();
-    }
-    lds_barrier();
-    if (FMT == W_Q4_1 && NF < a.M) {
-        // block sums S[b][m] = sum of the 32 bf16 of block b of row m (the copied rows NF .. M - 1;
-        // the normalised rows got theirs while being converted); the four pieces of a block sit in
-        // four consecutive lanes; eight rows' LDS reads are issued together; work items as in the
-        // normalised staging (piece p of 8-row batch b, from row NF)
-        const int n_items = pieces * ((a.M - NF + 7) >> 3);
-        for (int i = threadIdx.x; i < n_items; i += nthr) {
-            const int b = i / pieces, p = i - b * pieces;
-            const int m0 = NF + 8 * b;
-            u32x4 o[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) o[r] = lds_read16_untracked(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
-            wait_lds();
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float bs = quad_sum(bf16x8_sum(o[r]));
-                if (m0 + r < a.M && (p & 3) == 0) Ss[(p >> 2) * MP + m0 + r] = bs;
-            }
-        }
         lds_barrier();
+        if (FMT == W_Q4_1) {
+            copied_block_sums();
+            lds_barrier();
+        }
     }
     if (items == 0) return;   // uniform in the workgroup
 
