@@ -165,15 +165,23 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// 16-byte LDS read that the compiler's wait-count insertion does not see. A plain LDS read of a
+// Eight 16-byte LDS reads that the compiler's wait-count insertion does not see, issued together and
+// complete when the asm block ends (so no output register is in flight past it; the outputs are
+// early-clobber, since an address is read after earlier reads are issued). A plain LDS read of a
 // region that direct global->LDS copies wrote makes the compiler wait for every outstanding global
-// load, the weight ring's included; the caller orders this read itself (the copies it depends on
-// are complete after its own wait and a barrier) and calls wait_lds() before using the value.
-__device__ __forceinline__ u32x4 lds_read16_untracked(const void* p) {
-    u32x4 v;
-    const uint32_t addr = (uint32_t)(uintptr_t)(lds_void*)p;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-    return v;
+// load first, the weight ring's included; the caller orders these reads itself (the copies they
+// depend on are complete after its own wait and a barrier).
+__device__ __forceinline__ void lds_read16x8_untracked(u32x4 (&o)[8], const void* const (&p)[8]) {
+    uint32_t ad[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) ad[r] = (uint32_t)(uintptr_t)(lds_void*)p[r];
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
 }
 
 // Direct loads of one (tile, superblock) of weights into a ring slot of this wave. The slot's
@@ -570,9 +578,10 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) __attribute__((amdgpu_waves_p
             const int b = i / pieces, p = i - b * pieces;
             const int m0 = NF + 8 * b;
             u32x4 o[8];
+            const void* src[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) o[r] = lds_read16_untracked(As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8);
-            wait_lds();
+            for (int r = 0; r < 8; ++r) src[r] = As + (m0 + r < a.M ? m0 + r : m0) * lds_ld + p * 8;
+            lds_read16x8_untracked(o, src);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const float bs = quad_sum(bf16x8_sum(o[r]));
