@@ -405,37 +405,90 @@ __device__ __forceinline__ void splitk_store_plain(const KArgs& a, const floatx4
     }
 }
 
-// The S partials of the four rows m0 + 4 sub + r of column tile * 16 + c (this lane), summed in split
-// order; the loads of eight splits go out together.
-__device__ __forceinline__ floatx4 splitk_sum_plain(const KArgs& a, int tile, int lane, int m0) {
-    const int c = lane & 15, sub = lane >> 4;
-    const float* base = a.partial + tile * kTile + c;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int sp0 = 0; sp0 < a.S; sp0 += 8) {
-        float v[4][8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = m0 + 4 * sub + r < a.M ? m0 + 4 * sub + r : 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[r][i] = sp0 + i < a.S ? base[((size_t)(sp0 + i) * a.M + m) * a.n_cols] : 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[r] += v[r][i];
-    }
-    return acc;
-}
-
-// Wide chunks, second kernel: one wave per (column tile, row tile of 16), lanes in the MFMA output
-// layout, so the epilogue is the GEMM's own.
+// Wide chunks, second kernel: the S partials of every output summed in split order, then the
+// GEMM's epilogue. One wave per (4 rows, 64 columns): lane l owns column 64 g + l of the 4 rows,
+// so each load of a partial row reads 256 contiguous bytes (the MFMA layout would read 64-byte
+// pieces); the epilogue's 16-column tiles are groups of 16 lanes (n_cols is a multiple of 16), whose
+// gate/up halves and per-tile sums of squares meet by shuffles inside the group.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_splitk_epilogue(KArgs a, int n_rt) {
     const int lane = threadIdx.x & 63;
     const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wv >= a.n_tiles * n_rt) return;   // uniform in the wave
-    const int tile = wv / n_rt, t = wv - tile * n_rt;
-    epilogue<EPI>(a, splitk_sum_plain(a, tile, lane, 16 * t), tile, lane, 16 * t);
+    const int n_cg = (a.n_cols + 63) >> 6;
+    if (wv >= n_cg * n_rt) return;   // uniform in the wave
+    const int cg = wv / n_rt, rt = wv - cg * n_rt;
+    const int n = cg * 64 + lane;
+    const bool live = n < a.n_cols;            // whole 16-lane groups
+    const int c = lane & 15, tile = n >> 4;
+    constexpr int RE = 4;
+    const int m0 = RE * rt, nr = min(RE, a.M - m0);   // rows of this wave (uniform)
+    const float* col = a.partial + (live ? n : 0);
+    float acc[RE];
+#pragma unroll
+    for (int r = 0; r < RE; ++r) acc[r] = 0.f;
+    // the loads of four splits go out together; the sums run in split order
+    for (int sp0 = 0; sp0 < a.S; sp0 += 4) {
+        float v[4][RE];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float* ps = col + (size_t)min(sp0 + i, a.S - 1) * a.M * a.n_cols;
+#pragma unroll
+            for (int r = 0; r < RE; ++r) v[i][r] = ps[(size_t)(m0 + (r < nr ? r : nr - 1)) * a.n_cols];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < RE; ++r) acc[r] += sp0 + i < a.S ? v[i][r] : 0.f;
+    }
+    float yp[RE];   // RESID: the residual rows, loaded together
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+        for (int r = 0; r < RE; ++r) yp[r] = a.y[(size_t)(m0 + (r < nr ? r : nr - 1)) * a.ldy + (live ? n : 0)];
+    }
+    const float rs = EPI == EPI_RESID && a.rscale ? __builtin_bit_cast(float, (uint32_t)a.rscale[0] << 16) : 1.f;
+#pragma unroll
+    for (int r = 0; r < RE; ++r) {
+        if (r >= nr) break;
+        const int m = m0 + r;
+        const float v = acc[r];
+        if constexpr (EPI == EPI_PLE) {
+            if (live) {
+                int t = a.tokens[m];
+                t = t < 0 ? 0 : (t >= a.vocab ? a.vocab - 1 : t);
+                const float p = __builtin_bit_cast(float, (uint32_t)a.ple[(size_t)t * a.ple_ld + n] << 16);
+                a.out[(size_t)m * a.ldo + n] = f32_to_bf16(v / (1.0f + expf(-v)) * p);
+            }
+            continue;
+        }
+        if constexpr (EPI == EPI_SWIGLU) {
+            // gate columns in lanes c < 8 of a tile, the matching up columns in c + 8
+            const float up = __shfl_xor(v, 8);
+            if (live && c < 8) a.out[(size_t)m * a.ldo + tile * 8 + c] = f32_to_bf16(v / (1.0f + expf(-v)) * up);
+            continue;
+        }
+        float vo;
+        if constexpr (EPI == EPI_STORE) {
+            vo = v;
+            if (live) {
+                if (a.half < 0) a.y[(size_t)m * a.ldy + n] = v;
+                else if ((c >> 3) == a.half) a.y[(size_t)m * a.ldy + tile * 8 + (c & 7)] = v;
+            }
+        } else {
+            float w = yp[r] + v;
+            if (a.rscale) w *= rs;
+            vo = w;
+            if (live) {
+                a.y[(size_t)m * a.ldy + n] = w;
+                if (a.taps) a.taps[(size_t)m * a.ldt + n] = f32_to_bf16(w);
+            }
+        }
+        if (a.ss_out) {
+            float q = vo * vo;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) q += __shfl_xor(q, o);
+            if (live && c == 0) a.ss_out[(size_t)m * (a.n_cols / kTile) + tile] = q;
+        }
+    }
 }
 
 // Workgroup (u, split) of the grid U x S and W = blockDim / 64 waves: split = the cross-workgroup
@@ -798,8 +851,8 @@ hipError_t launch_r(const KArgs& k, int grid, int waves, size_t lds, hipStream_t
         if (k.S > 1) {
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            const int n_rt = (k.M + 15) / 16;
-            const int waves_total = k.n_tiles * n_rt;
+            const int n_rt = (k.M + 3) / 4;   // groups of 4 rows (the summing kernel's waves)
+            const int waves_total = (k.n_cols + 63) / 64 * n_rt;
             hipLaunchKernelGGL(k_splitk_epilogue<EPI>, dim3((waves_total + 3) / 4), dim3(256), 0, st, k, n_rt);
         }
     }
