@@ -491,8 +491,16 @@ hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps
     const int H = m->d.hidden;
     hipStream_t st = m->st;
     hipError_t e;
+    // Up to one 16-row tile the RMSNorms fold into the GEMMs' staging of fp32 x. Wider prefill chunks
+    // run each norm once as its own kernel into bf16 rows instead: a 64-row chunk would otherwise have
+    // every workgroup stage 64 fp32 rows (four times the bytes of the bf16 copy).
     GemmLaunch g = gemm_for(m, L.qkv, EPI_STORE);
-    g.xsrc = x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile; g.gain = L.attn_norm; g.eps = m->d.rms_eps;
+    if (k > kMaxRows) {
+        if ((e = launch_rmsnorm(x, H, k, H, L.attn_norm, m->d.rms_eps, m->act, H, st)) != hipSuccess) return e;
+        g.A = m->act; g.lda = H;
+    } else {
+        g.xsrc = x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile; g.gain = L.attn_norm; g.eps = m->d.rms_eps;
+    }
     g.M = k; g.y = m->qkv; g.ldy = L.qkv.n_out; g.ss_out = m->ss_qkv;
     if ((e = launch_gemm(g, st)) != hipSuccess) return e;
     Attn at = attn_for(m, L, k);
@@ -512,7 +520,12 @@ hipError_t run_layer(bvf_model* m, int l, float* x, int k, int P, uint16_t* taps
     g.A = m->obuf; g.lda = L.qd; g.M = k; g.y = x; g.ldy = H; g.ss_out = m->ss_x;
     if ((e = launch_gemm(g, st)) != hipSuccess) return e;
     g = gemm_for(m, L.gu, EPI_SWIGLU);
-    g.xsrc = x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile; g.gain = L.mlp_norm; g.eps = m->d.rms_eps;
+    if (k > kMaxRows) {
+        if ((e = launch_rmsnorm(x, H, k, H, L.mlp_norm, m->d.rms_eps, m->act, H, st)) != hipSuccess) return e;
+        g.A = m->act; g.lda = H;
+    } else {
+        g.xsrc = x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile; g.gain = L.mlp_norm; g.eps = m->d.rms_eps;
+    }
     g.M = k; g.out = m->mbuf; g.ldo = L.d.ffn;
     if ((e = launch_gemm(g, st)) != hipSuccess) return e;
     g = gemm_for(m, L.down, EPI_RESID);
@@ -1286,8 +1299,12 @@ bvf_status bvf_time_gemms(bvf_model* m, int32_t rows, int32_t iters, float* h_ms
                 GemmLaunch g;
                 if (cls == 0 || cls == 2) {
                     g = gemm_for(m, cls == 0 ? L.qkv : L.gu, cls == 0 ? EPI_STORE : EPI_SWIGLU);
-                    g.xsrc = m->x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile;
-                    g.gain = cls == 0 ? L.attn_norm : L.mlp_norm; g.eps = m->d.rms_eps;
+                    if (rows > kMaxRows) {   // wide chunks stage the bf16 rows of the separate norm
+                        g.A = m->act; g.lda = H;
+                    } else {
+                        g.xsrc = m->x; g.ldx = H; g.ss_in = m->ss_x; g.n_ss = H / kTile;
+                        g.gain = cls == 0 ? L.attn_norm : L.mlp_norm; g.eps = m->d.rms_eps;
+                    }
                     if (cls == 0) { g.y = m->qkv; g.ldy = L.qkv.n_out; g.ss_out = m->ss_qkv; }
                     else { g.out = m->mbuf; g.ldo = L.d.ffn; }
                 } else if (cls == 1) {

@@ -300,7 +300,8 @@ bvf_status bvf_layer_forward(bvf_model* m, int32_t layer, float* d_x, int32_t ro
  * events recorded on the model's stream, and synchronises. Class 0 = fused q|k|v, 1 = o (+residual),
  * 2 = gate|up (+SwiGLU), 3 = down (+residual), 4 = the bf16 head. h_ms[5]: average milliseconds per
  * launch; h_bytes[5]: average weight bytes streamed per launch. 1 <= rows <= 64; above 16 rows (the
- * prefill chunk widths) the head is not run and class 4 reports 0. Overwrites the scratch
+ * prefill chunk widths) the head is not run and class 4 reports 0, and classes 0 and 2 stage the bf16
+ * rows that the pass's own RMSNorm kernel writes (that kernel is not timed). Overwrites the scratch
  * activations. */
 bvf_status bvf_time_gemms(bvf_model* m, int32_t rows, int32_t iters, float* h_ms, int64_t* h_bytes);
 /* Q4_1 bytes (packed image: 5 bits per weight) and bf16 head bytes one verify pass streams. */

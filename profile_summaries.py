@@ -154,8 +154,9 @@ def mfma(ARGV):
     # the GEMMs of a layer: q|k|v (store epilogue, followed by attention), o (residual, before
     # gate|up), gate|up (SwiGLU epilogue), down (residual, right after gate|up). Wide launches
     # (prefill chunks) are each followed by their split-sum kernel (k_splitk_epilogue): it is
-    # skipped when looking at neighbours, and its duration is reported beside the GEMM's.
-    seq = [e for e in allseq if "k_splitk_epilogue" not in e["name"]]
+    # skipped when looking at neighbours, and its duration is reported beside the GEMM's. Such chunks
+    # also run their RMSNorms as k_rmsnorm before q|k|v and gate|up: skipped the same way.
+    seq = [e for e in allseq if "k_splitk_epilogue" not in e["name"] and "k_rmsnorm" not in e["name"]]
     follow = {}
     for i, e in enumerate(allseq):
         if "k_gemm" in e["name"] and i + 1 < len(allseq) and "k_splitk_epilogue" in allseq[i + 1]["name"]:
