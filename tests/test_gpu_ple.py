@@ -55,7 +55,8 @@ def test_ple_verify_parity(mk, P, k):
 
 def test_ple_graph_replay_and_prefill():
     """The captured pass of a PLE model replays bit-identically to direct launches; a chunked
-    prefill of 21 tokens (two chunks) leaves the context the oracle leaves."""
+    prefill of 21 tokens (one chunk of two row tiles, its RMSNorms as their own kernel) leaves the
+    context the oracle leaves."""
     m = ple_two_width()
     g, o, w, kv = build_pair(m, 12)
     toks = synth.tokens(0, "ple.graph", 8, m.vocab)

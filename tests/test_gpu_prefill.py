@@ -1,7 +1,9 @@
 """Chunked prefill on the GPU against the oracle, and snapshot/restore as a prefix cache.
 
 The prefill runs the batched body in chunks of up to 64 rows (37: one chunk of three row tiles
-and a ragged fourth; 100 and 150: full 64-row chunks and a ragged tail) and keeps every row; the oracle runs
+and a ragged fourth; 100 and 150: full 64-row chunks and a ragged tail; 72: a 64-row chunk, whose
+RMSNorms run as their own kernel, then an 8-row chunk, whose RMSNorms fold into the GEMMs'
+staging) and keeps every row; the oracle runs
 the same rows as one batched verify plus commit (its batched verify equals sequential steps bit for
 bit). Compared: positions held and plane floats exactly; the last row's logits and the logits of a
 verify that follows, within the stack bar (2e-3, or three times the oracle's own spread under
@@ -35,7 +37,7 @@ def gpu_model(m, w, kv):
     return g
 
 
-@pytest.mark.parametrize("n", [1, 16, 37, 64, 100, 150])
+@pytest.mark.parametrize("n", [1, 16, 37, 64, 72, 100, 150])
 def test_prefill_matches_oracle(setup, n):
     m, w, kv = setup
     g = gpu_model(m, w, kv)
